@@ -1,0 +1,227 @@
+"""CPU oracle for the BF16 -> MXFP4 -> block-scaled FP8 path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+(``block_scaled_precision_bf16tofp4row_amd``) never imports it and shares no
+code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, one element at
+a time).  This module compiles it with gcc, loads it with ctypes and splits big
+matrices into row ranges that run on a thread pool (ctypes releases the GIL, so
+each thread runs the unchanged C code on its own range).
+
+Method: "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs",
+technical summary section 2 "Methodology" (MXFP4 spec, direct FP4->FP8
+conversion with hierarchical scale alignment, row / transposed-column kernels
+over ragged expert segments).  The conventions the page leaves open are stated
+in the header of ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+             "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_quantize_block.argtypes = [P, P, P]
+    lib.oracle_quantize_rows.argtypes = [P, I64, I64, I64, P, P]
+    lib.oracle_fp8_rows.argtypes = [P, P, I64, I64, I64, P, P]
+    lib.oracle_fp8_cols.argtypes = [P, P, P, ctypes.c_int32, I64, I64, I64, P, P]
+    lib.oracle_e2m1_encode.argtypes = [ctypes.c_double]
+    lib.oracle_e2m1_encode.restype = ctypes.c_int
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.oracle_e4m3_encode.restype = ctypes.c_int
+    lib.oracle_e2m1_magnitude.argtypes = [ctypes.c_int]
+    lib.oracle_e2m1_magnitude.restype = ctypes.c_double
+    lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_value.restype = ctypes.c_double
+    lib.oracle_scale_for_amax.argtypes = [ctypes.c_double]
+    lib.oracle_scale_for_amax.restype = ctypes.c_int
+    lib.oracle_fp8_of_code.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.oracle_fp8_of_code.restype = ctypes.c_uint8
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def default_threads() -> int:
+    """Host threads the multi-range drivers use (the process's CPU affinity)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _ranges(n: int, parts: int):
+    parts = max(1, min(parts, n)) if n > 0 else 1
+    step = (n + parts - 1) // parts if n > 0 else 0
+    return [(i, min(n, i + step)) for i in range(0, n, step)] if n > 0 else []
+
+
+# ---- scalar helpers (used by the pins) -------------------------------------
+
+def e2m1_encode(y: float) -> int:
+    return _load().oracle_e2m1_encode(float(y))
+
+
+def e4m3_encode(v: float) -> int:
+    return _load().oracle_e4m3_encode(float(v))
+
+
+def e2m1_magnitude(code: int) -> float:
+    return _load().oracle_e2m1_magnitude(int(code))
+
+
+def bf16_value(bits: int) -> float:
+    return _load().oracle_bf16_value(int(bits))
+
+
+def scale_for_amax(amax: float) -> int:
+    return _load().oracle_scale_for_amax(float(amax))
+
+
+def fp8_of_code(code: int, s: int, S: int) -> int:
+    return _load().oracle_fp8_of_code(int(code), int(s), int(S))
+
+
+# ---- array drivers -----------------------------------------------------------
+
+def quantize_block(x32: np.ndarray):
+    """One 32-element block of BF16 bits -> (16 packed bytes, scale byte)."""
+    lib = _load()
+    x32 = np.ascontiguousarray(x32, dtype=np.uint16)
+    assert x32.size == 32
+    packed = np.zeros(16, np.uint8)
+    sc = np.zeros(1, np.uint8)
+    lib.oracle_quantize_block(_ptr(x32), _ptr(packed), _ptr(sc))
+    return packed, int(sc[0])
+
+
+def quantize_rows(x_bits: np.ndarray, rows: int | None = None, threads: int = 1,
+                  codes: np.ndarray | None = None, scales: np.ndarray | None = None):
+    """BF16 bits [M, K] -> (codes [M, K/2] uint8, scales [M, K/32] uint8).
+
+    Only rows [0, rows) are computed (rows defaults to M); the rest stay zero."""
+    lib = _load()
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    assert K % 32 == 0
+    rows = M if rows is None else rows
+    if codes is None:
+        codes = np.zeros((M, K // 2), np.uint8)
+    if scales is None:
+        scales = np.zeros((M, K // 32), np.uint8)
+
+    def run(r):
+        lib.oracle_quantize_rows(_ptr(x_bits), K, r[0], r[1], _ptr(codes), _ptr(scales))
+
+    _run_ranges(run, _ranges(rows, threads * 4), threads)
+    return codes, scales
+
+
+def fp8_rows(codes: np.ndarray, scales: np.ndarray, rows: int | None = None,
+             threads: int = 1, y: np.ndarray | None = None, y_scales: np.ndarray | None = None):
+    """Row layout: codes [M, K/2], scales [M, K/32] -> (y [M, K], y_scales [M, K/128])."""
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    M = codes.shape[0]
+    K = codes.shape[1] * 2
+    assert K % 128 == 0 and scales.shape == (M, K // 32)
+    rows = M if rows is None else rows
+    if y is None:
+        y = np.zeros((M, K), np.uint8)
+    if y_scales is None:
+        y_scales = np.zeros((M, K // 128), np.uint8)
+
+    def run(r):
+        lib.oracle_fp8_rows(_ptr(codes), _ptr(scales), K, r[0], r[1], _ptr(y), _ptr(y_scales))
+
+    _run_ranges(run, _ranges(rows, threads * 4), threads)
+    return y, y_scales
+
+
+def blocks_per_group(offs: np.ndarray) -> np.ndarray:
+    counts = np.diff(np.asarray(offs, dtype=np.int64))
+    return (counts + 127) // 128
+
+
+def cols_scale_size(offs: np.ndarray, K: int) -> int:
+    return int(blocks_per_group(offs).sum()) * K
+
+
+def fp8_cols(codes: np.ndarray, scales: np.ndarray, offs: np.ndarray, threads: int = 1,
+             yT: np.ndarray | None = None, yT_scales: np.ndarray | None = None,
+             groups=None):
+    """Transposed column layout over ragged expert segments.
+
+    Returns (yT, yT_scales) as flat uint8 arrays: expert g's [K, M_g] transpose
+    at byte K*offs[g], its [nblocks_g, K] scales at byte K*B_g."""
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    M = codes.shape[0]
+    K = codes.shape[1] * 2
+    G = offs.size - 1
+    assert K % 128 == 0
+    if yT is None:
+        yT = np.zeros(M * K, np.uint8)
+    if yT_scales is None:
+        yT_scales = np.zeros(max(1, cols_scale_size(offs, K)), np.uint8)
+    nbg = blocks_per_group(offs)
+    groups = range(G) if groups is None else groups
+    work = []
+    for g in groups:
+        for b0, b1 in _ranges(int(nbg[g]), max(1, threads)):
+            work.append((g, b0, b1))
+
+    def run(w):
+        lib.oracle_fp8_cols(_ptr(codes), _ptr(scales), _ptr(offs), w[0], K, w[1], w[2],
+                            _ptr(yT), _ptr(yT_scales))
+
+    _run_ranges(run, work, threads)
+    return yT, yT_scales
+
+
+def _run_ranges(fn, work, threads):
+    if threads <= 1 or len(work) <= 1:
+        for w in work:
+            fn(w)
+        return
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(fn, work))

@@ -1,0 +1,252 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the BF16 -> MXFP4 -> block-scaled FP8 path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file; only the test suite, the smoke check and the benchmark's CPU-baseline
+ * leg use it.  It shares no code, header, table or constant generator with the HIP
+ * kernels: every value here is computed from the format definitions in double
+ * precision, one element at a time, in the order the method states it.
+ *
+ * Method source: "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs"
+ * (technical summary, section 2 "Methodology"):
+ *   - item 1, MXFP4 spec: 32-element blocks share one power-of-two UE8M0 scale,
+ *     elements are E2M1 (1 sign, 2 exponent, 1 mantissa bit);
+ *   - item 1, FP8 target: E4M3 with 128-element blocks, reached by a direct
+ *     FP4 -> FP8 conversion with no BF16 intermediate;
+ *   - item 1, hierarchical scale alignment: the four 32-element MX scales of a
+ *     128-element FP8 block are aligned to the largest one and each sub-block's
+ *     exponent is shifted by the difference, keeping values numerically equal;
+ *   - item 2, forward pass: codes packed two per uint8 container;
+ *   - item 3, kernels: row layout (FPROP), transposed column layout (Wgrad) with
+ *     transpose fused into the conversion, ragged per-expert token counts with no
+ *     padding.
+ * Readings where the page is silent (rounding, scale rule, nibble order, layouts)
+ * follow the OCP Microscaling (MX) v1.0 conventions and are listed with each
+ * function below:
+ *   - shared exponent = floor(log2(amax)) - emax_elem, emax_elem = 2 for E2M1,
+ *     stored biased by 127 and clamped to [0, 254]; an all-zero block gets 0;
+ *   - E2M1: round to nearest, ties to even code, saturating at +-6;
+ *   - E4M3 (OCP "E4M3FN": bias 7, no infinities): round to nearest, ties to even,
+ *     used when a sub-block shift pushes a value into the subnormal range;
+ *   - the sign of zero is kept (a negative value that rounds to 0 gives -0);
+ *   - element 2i goes in the low nibble of byte i, element 2i+1 in the high nibble.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---- value decoding ---------------------------------------------------- */
+
+/* BF16 bits -> exact double.  BF16 is the top half of an IEEE binary32:
+ * 1 sign bit, 8 exponent bits (bias 127), 7 mantissa bits. */
+static double bf16_value(uint16_t b)
+{
+    int sign = b >> 15;
+    int e = (b >> 7) & 0xFF;
+    int m = b & 0x7F;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)m, -126 - 7);             /* subnormal */
+    else
+        mag = ldexp((double)(128 + m), e - 127 - 7);   /* normal; e == 255 not allowed */
+    return sign ? -mag : mag;
+}
+
+static int bf16_negative(uint16_t b) { return b >> 15; }
+
+/* Magnitude of an E2M1 code (low three bits): 2 exponent bits with bias 1,
+ * 1 mantissa bit; exponent field 0 is subnormal (0 or 0.5). */
+static double e2m1_magnitude(int code)
+{
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    if (e == 0)
+        return ldexp((double)m, -1);
+    return ldexp(1.0 + 0.5 * m, e - 1);
+}
+
+/* ---- generic binary minifloat rounding --------------------------------- */
+
+/* Round the non-negative finite value v to the nearest value of a binary
+ * minifloat with `mbits` mantissa bits and exponent bias `bias` (exponent field
+ * 0 = subnormal, same quantum as the smallest normal binade), ties to the
+ * encoding whose mantissa LSB is 0.  Returns the magnitude code
+ * (exponent_field << mbits | mantissa).  Values above the largest code
+ * `max_code` saturate to it. */
+static int minifloat_round_nearest_even(double v, int mbits, int bias, int max_code)
+{
+    if (v == 0.0)
+        return 0;
+    int e2;
+    frexp(v, &e2);               /* v = f * 2^e2, f in [0.5, 1) */
+    int E = e2 - 1;              /* v in [2^E, 2^(E+1)) */
+    int emin = 1 - bias;         /* exponent of the smallest normal binade */
+    if (E < emin)
+        E = emin;                /* subnormals use the quantum of the first binade */
+    double quantum = ldexp(1.0, E - mbits);
+    double n = v / quantum;      /* exact: division by a power of two */
+    double fl = floor(n);
+    double frac = n - fl;
+    long q = (long)fl;
+    if (frac > 0.5 || (frac == 0.5 && (q & 1)))
+        q += 1;
+    long code;
+    if (E == emin && q < (1L << mbits))
+        code = q;                                            /* subnormal */
+    else
+        code = ((long)(E + bias) << mbits) + (q - (1L << mbits)); /* normal (q may carry) */
+    if (code > max_code)
+        code = max_code;
+    return (int)code;
+}
+
+/* E2M1, saturating: largest magnitude code 7 (= 6.0). */
+static int e2m1_encode(double y) { return minifloat_round_nearest_even(y, 1, 1, 7); }
+
+/* OCP E4M3FN: bias 7, 3 mantissa bits, largest finite code 0x7E (= 448).
+ * On this path magnitudes never exceed 6, so saturation is never reached. */
+static int e4m3_encode(double v) { return minifloat_round_nearest_even(v, 3, 7, 0x7E); }
+
+/* ---- step a1/a2: block amax and shared UE8M0 scale --------------------- */
+
+/* Shared scale byte of a 32-element block whose largest magnitude is `amax`:
+ * floor(log2(amax)) - 2 + 127, clamped to [0, 254]; 0 for an all-zero block. */
+static int ue8m0_scale_for_amax(double amax)
+{
+    if (amax == 0.0)
+        return 0;
+    int e2;
+    frexp(amax, &e2);            /* floor(log2(amax)) = e2 - 1 */
+    int s = (e2 - 1) - 2 + 127;
+    if (s < 0) s = 0;
+    if (s > 254) s = 254;
+    return s;
+}
+
+/* ---- public entry points (C linkage for ctypes) ------------------------ */
+
+/* One 32-element block: x[0..31] BF16 bits -> 16 packed bytes + 1 scale byte. */
+void oracle_quantize_block(const uint16_t *x, uint8_t *packed16, uint8_t *scale)
+{
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) {
+        double a = fabs(bf16_value(x[i]));
+        if (a > amax)
+            amax = a;
+    }
+    int s = ue8m0_scale_for_amax(amax);
+    *scale = (uint8_t)s;
+    uint8_t codes[32];
+    for (int i = 0; i < 32; ++i) {
+        double y = ldexp(fabs(bf16_value(x[i])), 127 - s);   /* |x| / 2^(s-127), exact */
+        int c = e2m1_encode(y);
+        if (bf16_negative(x[i]))
+            c |= 8;
+        codes[i] = (uint8_t)c;
+    }
+    for (int i = 0; i < 16; ++i)
+        packed16[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+}
+
+/* Quantize rows [row_begin, row_end) of a row-major BF16 matrix with K columns
+ * (K a multiple of 32).  codes: [*, K/2] bytes, scales: [*, K/32] bytes. */
+void oracle_quantize_rows(const uint16_t *x, int64_t K, int64_t row_begin, int64_t row_end,
+                          uint8_t *codes, uint8_t *scales)
+{
+    int64_t nb = K / 32;
+    for (int64_t m = row_begin; m < row_end; ++m)
+        for (int64_t j = 0; j < nb; ++j)
+            oracle_quantize_block(x + m * K + 32 * j, codes + m * (K / 2) + 16 * j,
+                                  scales + m * nb + j);
+}
+
+/* Unpack code k of a packed row: even k in the low nibble. */
+static int code_at(const uint8_t *packed_row, int64_t k)
+{
+    uint8_t b = packed_row[k / 2];
+    return (k & 1) ? (b >> 4) : (b & 15);
+}
+
+/* The FP8 byte of one E2M1 code whose MX scale is s and whose FP8 block scale is S
+ * (S >= s): value e2m1(c) * 2^(s - S), rounded to E4M3, sign of the code kept. */
+static uint8_t fp8_of_code(int c, int s, int S)
+{
+    double v = ldexp(e2m1_magnitude(c & 7), s - S);
+    int b = e4m3_encode(v);
+    if (c & 8)
+        b |= 0x80;
+    return (uint8_t)b;
+}
+
+/* Row layout (FPROP), rows [row_begin, row_end): each 128-element block along K
+ * gets the UE8M0 scale S = max of its four MX scales; y: [*, K] E4M3 bytes,
+ * y_scales: [*, K/128] UE8M0 bytes.  K a multiple of 128. */
+void oracle_fp8_rows(const uint8_t *codes, const uint8_t *scales, int64_t K,
+                     int64_t row_begin, int64_t row_end, uint8_t *y, uint8_t *y_scales)
+{
+    int64_t nb32 = K / 32, nb128 = K / 128;
+    for (int64_t m = row_begin; m < row_end; ++m) {
+        const uint8_t *crow = codes + m * (K / 2);
+        const uint8_t *srow = scales + m * nb32;
+        for (int64_t b = 0; b < nb128; ++b) {
+            int S = 0;
+            for (int j = 0; j < 4; ++j)
+                if (srow[4 * b + j] > S)
+                    S = srow[4 * b + j];
+            y_scales[m * nb128 + b] = (uint8_t)S;
+            for (int64_t k = 128 * b; k < 128 * (b + 1); ++k)
+                y[m * K + k] = fp8_of_code(code_at(crow, k), srow[k / 32], S);
+        }
+    }
+}
+
+/* Column layout (Wgrad) for expert g, row blocks [blk_begin, blk_end) of that
+ * expert.  Expert g owns rows [offs[g], offs[g+1]); M_g = offs[g+1] - offs[g];
+ * its rows are cut into ceil(M_g/128) blocks of 128 (the last one partial).
+ * For block b and column k the FP8 scale is the max of the MX scales of group
+ * k/32 over the rows of the block that exist.  Output for expert g is the
+ * transpose [K, M_g] at byte offset K*offs[g]; element (k, m') at k*M_g + m'.
+ * Scales for expert g are [nblocks_g, K] at byte offset K*B_g, where B_g is the
+ * number of row blocks of experts 0..g-1. */
+void oracle_fp8_cols(const uint8_t *codes, const uint8_t *scales, const int32_t *offs,
+                     int32_t g, int64_t K, int64_t blk_begin, int64_t blk_end,
+                     uint8_t *yT, uint8_t *yT_scales)
+{
+    int64_t nb32 = K / 32;
+    int64_t Bg = 0;
+    for (int32_t h = 0; h < g; ++h)
+        Bg += ((int64_t)offs[h + 1] - offs[h] + 127) / 128;
+    int64_t row0 = offs[g];
+    int64_t Mg = (int64_t)offs[g + 1] - offs[g];
+    uint8_t *outT = yT + K * row0;
+    uint8_t *outS = yT_scales + K * Bg;
+    for (int64_t b = blk_begin; b < blk_end; ++b) {
+        int64_t mlo = 128 * b;
+        int64_t mhi = mlo + 128 < Mg ? mlo + 128 : Mg;
+        for (int64_t j = 0; j < nb32; ++j) {
+            int S = 0;
+            for (int64_t m = mlo; m < mhi; ++m) {
+                int s = scales[(row0 + m) * nb32 + j];
+                if (s > S)
+                    S = s;
+            }
+            for (int64_t k = 32 * j; k < 32 * (j + 1); ++k) {
+                outS[b * K + k] = (uint8_t)S;
+                for (int64_t m = mlo; m < mhi; ++m) {
+                    const uint8_t *crow = codes + (row0 + m) * (K / 2);
+                    int s = scales[(row0 + m) * nb32 + j];
+                    outT[k * Mg + m] = fp8_of_code(code_at(crow, k), s, S);
+                }
+            }
+        }
+    }
+}
+
+/* ---- small helpers exported for the pins ------------------------------- */
+
+int oracle_e2m1_encode(double y) { return e2m1_encode(y); }
+int oracle_e4m3_encode(double v) { return e4m3_encode(v); }
+double oracle_e2m1_magnitude(int code) { return e2m1_magnitude(code); }
+double oracle_bf16_value(uint16_t b) { return bf16_value(b); }
+int oracle_scale_for_amax(double amax) { return ue8m0_scale_for_amax(amax); }
+uint8_t oracle_fp8_of_code(int c, int s, int S) { return fp8_of_code(c, s, S); }

@@ -1,0 +1,389 @@
+"""Pins for the CPU oracle, checked against things other than itself: the format
+facts in tests/golden/formats.json, brute-force rational search (exact_ref),
+torch's float8_e4m3fn codec (a library routine), closed forms and invariants.
+
+Method: "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs",
+technical summary section 2 (Methodology), item 1 (MXFP4 spec, direct FP4->FP8
+conversion, hierarchical scale alignment) and item 3 (row / column kernels).
+"""
+import json
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import exact_ref
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "formats.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def bf16_bits_of(v: float) -> int:
+    b = struct.unpack("<I", struct.pack("<f", v))[0]
+    assert b & 0xFFFF == 0, v
+    return b >> 16
+
+
+# ---- format facts ------------------------------------------------------------------
+
+def test_e2m1_values_match_format_facts():
+    g = golden()["e2m1"]
+    vals = exact_ref.e2m1_code_values()
+    assert g["sign_bits"] + g["exponent_bits"] + g["mantissa_bits"] == 4
+    assert len(vals) == 2 ** (g["exponent_bits"] + g["mantissa_bits"])
+    assert vals == sorted(vals) and len(set(vals)) == len(vals)
+    assert vals[-1] == Fraction(g["max_normal"])
+    assert vals[1] == Fraction(g["max_subnormal"]) == Fraction(g["min_subnormal"])
+    assert min(v for v in vals if v >= 1) == Fraction(g["min_normal"])
+    for code in range(16):
+        assert oracle.e2m1_magnitude(code & 7) == float(vals[code & 7])
+
+
+def test_e4m3_values_match_format_facts():
+    g = golden()["fp8_target"]
+    vals = exact_ref.e4m3_code_values()
+    assert vals[-1] == Fraction(g["max_normal"])
+    assert vals[1] == Fraction(g["min_subnormal"])
+    assert vals[8] == Fraction(g["min_normal"])
+
+
+def test_block_sizes_match_page():
+    g = golden()
+    assert g["mx_block"]["elements"] == 32
+    assert g["fp8_target"]["block"] == 128
+    assert g["alignment"]["sub_blocks_per_fp8_block"] * g["mx_block"]["elements"] == g["fp8_target"]["block"]
+    assert g["packing"]["codes_per_byte"] == 2
+
+
+# ---- E2M1 rounding -------------------------------------------------------------------
+
+def _e2m1_probe_values():
+    vals = exact_ref.e2m1_code_values()
+    ys = set()
+    for k in range(0, 900):                      # every multiple of 1/128 in [0, 7.03)
+        ys.add(Fraction(k, 128))
+    for a, b in zip(vals, vals[1:]):             # ties and their neighbours
+        mid = (a + b) / 2
+        for eps in (Fraction(0), Fraction(1, 2 ** 20), -Fraction(1, 2 ** 20)):
+            ys.add(mid + eps)
+    for big in (6, Fraction(13, 2), 7, Fraction(15, 2), 8, 100, 2 ** 30):
+        ys.add(Fraction(big))
+    return sorted(y for y in ys if y >= 0)
+
+
+def test_e2m1_encode_brute_force():
+    for y in _e2m1_probe_values():
+        assert oracle.e2m1_encode(float(y)) == exact_ref.e2m1_encode(y), y
+
+
+def test_e2m1_tie_points_go_to_even_code():
+    expect = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for y, c in expect.items():
+        assert oracle.e2m1_encode(y) == c
+        assert exact_ref.e2m1_encode(Fraction(y)) == c
+    assert oracle.e2m1_encode(7.9) == 7          # saturates to 6.0
+
+
+# ---- E4M3 rounding -------------------------------------------------------------------
+
+def test_e4m3_encode_matches_torch_on_all_shifted_codes():
+    vals = [oracle.e2m1_magnitude(c) for c in range(8)]
+    xs, want = [], []
+    for v in vals:
+        for d in range(0, 150):
+            x = math.ldexp(v, -d)
+            xs.append(x)
+            want.append(oracle.e4m3_encode(x))
+    t = torch.tensor(xs, dtype=torch.float64).to(torch.float32).to(torch.float8_e4m3fn)
+    got = t.view(torch.uint8).tolist()
+    assert got == want
+
+
+def test_e4m3_encode_matches_torch_on_dense_grid():
+    # every multiple of 2^-12 below 8: exercises ties of every subnormal and normal binade
+    xs = np.arange(0, 8 * 4096, dtype=np.float64) / 4096.0
+    want = [oracle.e4m3_encode(float(x)) for x in xs]
+    got = torch.from_numpy(xs).to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).tolist()
+    assert got == want
+
+
+def test_shift_table_brute_force_all_codes_all_gaps():
+    """All 16 codes x every gap d = S - s in [0, 254]: oracle == rational nearest search."""
+    for c in range(16):
+        for d in range(0, 255):
+            S = 254
+            s = S - d
+            v = exact_ref.e2m1_code_values()[c & 7] * Fraction(2) ** (-d)
+            want = exact_ref.e4m3_encode(v) | (0x80 if c & 8 else 0)
+            assert oracle.fp8_of_code(c, s, S) == want, (c, d)
+
+
+def test_shift_table_special_rows():
+    # d = 0 map (page: the max-scale sub-block keeps its values exactly)
+    d0 = [oracle.fp8_of_code(c, 127, 127) for c in range(8)]
+    assert d0 == [0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0x48, 0x4C]
+    # every gap >= 13 underflows to (signed) zero
+    for c in range(16):
+        for d in (13, 20, 254):
+            assert oracle.fp8_of_code(c, 254 - d, 254) == (0x80 if c & 8 else 0)
+    # ties at 2^-9 granularity resolve to even
+    assert oracle.fp8_of_code(1, 127 - 9, 127) == 0x00   # 0.5 unit -> 0
+    assert oracle.fp8_of_code(3, 127 - 9, 127) == 0x02   # 1.5 units -> 2
+    assert oracle.fp8_of_code(7, 127 - 11, 127) == 0x02  # 1.5 units -> 2
+
+
+# ---- scale rule ----------------------------------------------------------------------
+
+def test_scale_rule_closed_form_every_bf16_magnitude():
+    for b in range(0, 0x7F80):          # every finite non-negative BF16
+        a = oracle.bf16_value(b)
+        e_field = b >> 7
+        closed = max(e_field - 2, 0)     # biased exponent field minus emax(E2M1) = 2
+        assert oracle.scale_for_amax(a) == closed, hex(b)
+        if a > 0:
+            m, e = math.frexp(a)
+            assert closed == min(254, max(0, (e - 1) - 2 + 127))
+
+
+def test_bf16_decode_matches_float32_reinterpretation():
+    for b in list(range(0, 0x10000, 37)) + [0x0001, 0x007F, 0x0080, 0x7F7F, 0x8001, 0xFF7F]:
+        if (b & 0x7F80) == 0x7F80:
+            continue
+        want = struct.unpack("<f", struct.pack("<I", b << 16))[0]
+        assert oracle.bf16_value(b) == want
+
+
+# ---- quantize -----------------------------------------------------------------------
+
+def _rand_bits(rng, shape, kind):
+    if kind == "normal":
+        x = rng.standard_normal(shape).astype(np.float32)
+    elif kind == "ties":
+        grid = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 4.0, 0.5, 7.0], np.float32)
+        x = rng.choice(grid, size=shape) * rng.choice([-1.0, 1.0], size=shape).astype(np.float32)
+        x *= np.float32(2.0) ** rng.integers(-3, 4, size=shape[:-1] + (1,)).astype(np.float32)
+    elif kind == "tiny":
+        x = rng.standard_normal(shape).astype(np.float32) * np.float32(2.0 ** -128)
+    elif kind == "raw":
+        bits = rng.integers(0, 0x10000, size=shape, dtype=np.uint32).astype(np.uint16)
+        bits[(bits & 0x7F80) == 0x7F80] &= 0x807F   # drop Inf/NaN patterns
+        return bits
+    else:
+        raise ValueError(kind)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "tiny", "raw"])
+def test_quantize_matches_brute_force(kind):
+    rng = np.random.default_rng(11)
+    x = _rand_bits(rng, (3, 64), kind)
+    x[0, 32:64] = 0                      # an all-zero block
+    x[1, 5] = 0x8000                     # negative zero
+    c_o, s_o = oracle.quantize_rows(x)
+    c_r, s_r = exact_ref.quantize(x)
+    np.testing.assert_array_equal(s_o, s_r)
+    np.testing.assert_array_equal(c_o, c_r)
+
+
+def test_quantize_every_bf16_magnitude_at_several_scales():
+    """Each row is one block: element 0 fixes amax (so the scale), elements 1..31
+    walk through every BF16 magnitude at or below it with alternating signs."""
+    vals = exact_ref.e2m1_code_values()
+    for e_amax in (0, 1, 2, 3, 4, 60, 127, 200, 254):
+        amax_bits = (e_amax << 7) | 0x7F
+        cands = np.arange(0, amax_bits + 1, dtype=np.uint32)
+        cands = cands[(cands & 0x7F80) != 0x7F80]
+        n = (cands.size + 30) // 31
+        pad = np.zeros(n * 31, np.uint32)
+        pad[:cands.size] = cands
+        x = np.zeros((n, 32), np.uint16)
+        x[:, 0] = amax_bits
+        body = pad.reshape(n, 31).astype(np.uint16)
+        body[:, 1::2] |= 0x8000
+        x[:, 1:] = body
+        codes, scales = oracle.quantize_rows(x)
+        s = max(e_amax - 2, 0)
+        assert np.all(scales == s)
+        # per-element check against rational nearest search, on a subsample that
+        # always includes every element near the rounding thresholds
+        unpacked = np.zeros((n, 32), np.uint8)
+        unpacked[:, 0::2] = codes & 15
+        unpacked[:, 1::2] = codes >> 4
+        rng = np.random.default_rng(e_amax)
+        rows = np.unique(np.concatenate([rng.integers(0, n, 64), [0, n - 1]]))
+        for r in rows:
+            for i in range(32):
+                b = int(x[r, i])
+                y = abs(exact_ref.bf16_to_fraction(b)) / Fraction(2) ** (s - 127)
+                want = exact_ref.e2m1_encode(y) | (8 if b & 0x8000 else 0)
+                assert unpacked[r, i] == want, (e_amax, r, i, hex(b))
+        # thresholds: all elements within 1 ulp of every E2M1 tie value are checked
+        for a, bnd in zip(vals, vals[1:]):
+            mid = (a + bnd) / 2 * Fraction(2) ** (s - 127)
+            for r in range(n):
+                for i in range(1, 32):
+                    b = int(x[r, i])
+                    v = abs(exact_ref.bf16_to_fraction(b))
+                    if v != 0 and abs(v - mid) <= mid / 64:
+                        y = v / Fraction(2) ** (s - 127)
+                        want = exact_ref.e2m1_encode(y) | (8 if b & 0x8000 else 0)
+                        assert unpacked[r, i] == want
+
+
+def test_quantize_invariants():
+    rng = np.random.default_rng(5)
+    x = _rand_bits(rng, (64, 256), "normal")
+    x[:, 7] = bf16_bits_of(2.0)         # a power-of-two amax in block 0 of every row
+    codes, scales = oracle.quantize_rows(x)
+    unpacked = np.zeros(x.shape, np.uint8)
+    unpacked[:, 0::2] = codes & 15
+    unpacked[:, 1::2] = codes >> 4
+    vals = np.array([oracle.bf16_value(int(b)) for b in x.reshape(-1)]).reshape(x.shape)
+    for m in range(x.shape[0]):
+        for j in range(x.shape[1] // 32):
+            blk = vals[m, 32 * j:32 * j + 32]
+            amax = np.max(np.abs(blk))
+            s = int(scales[m, j])
+            if amax > 0 and (int(x[m, 32 * j:32 * j + 32].max()) & 0x7F80) >= (2 << 7):
+                assert 4.0 <= amax / 2.0 ** (s - 127) < 8.0
+                assert (unpacked[m, 32 * j:32 * j + 32] & 7).max() in (6, 7)
+    # amax exactly 2^1 -> scale = 1 + 125, and that element becomes code 6 (4.0)
+    assert np.all(scales[:, 0] == 126)
+    assert np.all(unpacked[:, 7] == 6)
+
+
+def test_packing_nibble_order_and_round_trip():
+    # element 0 = +0.5 (code 1), element 1 = -6 (code 15) in a block whose amax is 6
+    x = np.zeros((1, 32), np.uint16)
+    x[0, 0] = bf16_bits_of(0.5)
+    x[0, 1] = bf16_bits_of(-6.0)
+    codes, scales = oracle.quantize_rows(x)
+    assert scales[0, 0] == 127            # floor(log2 6) - 2 + 127
+    assert codes[0, 0] == (1 | (15 << 4))
+    assert codes.shape == (1, 16) and scales.shape == (1, 1)
+    for byte in range(256):
+        lo, hi = byte & 15, byte >> 4
+        assert (lo | (hi << 4)) == byte
+
+
+# ---- rows -----------------------------------------------------------------------------
+
+def _codes_and_gapped_scales(rng, M, K, max_gap):
+    codes = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint16).astype(np.uint8)
+    S = rng.integers(max_gap, 255, size=(M, K // 128))
+    gaps = rng.integers(0, max_gap + 1, size=(M, K // 32))
+    gaps[:, ::4] = 0                      # at least one sub-block sits at the block max
+    perm = rng.permuted(np.arange(4)[None, :].repeat(M * K // 128, 0), axis=1)
+    gaps = np.take_along_axis(gaps.reshape(-1, 4), perm, axis=1).reshape(M, K // 32)
+    scales = (np.repeat(S, 4, axis=1) - gaps).astype(np.uint8)
+    return codes, scales
+
+
+def test_rows_match_brute_force():
+    rng = np.random.default_rng(3)
+    codes, scales = _codes_and_gapped_scales(rng, 3, 256, 16)
+    scales[2, 4:8] = [200, 0, 3, 254 - 200]    # extreme gaps, including > 13
+    y_o, ys_o = oracle.fp8_rows(codes, scales)
+    y_r, ys_r = exact_ref.fp8_rows(codes, scales)
+    np.testing.assert_array_equal(ys_o, ys_r)
+    np.testing.assert_array_equal(y_o, y_r)
+
+
+def test_rows_numerical_equivalence_when_gap_small():
+    """Max-scale alignment keeps values equal: e4m3(out) * 2^(S-127) equals
+    e2m1(code) * 2^(s-127) exactly whenever the gap S - s <= 8."""
+    rng = np.random.default_rng(4)
+    codes, scales = _codes_and_gapped_scales(rng, 16, 512, 8)
+    y, ys = oracle.fp8_rows(codes, scales)
+    e4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    e2 = np.array([exact_ref.e2m1_code_values()[c & 7] * (-1 if c & 8 else 1) for c in range(16)],
+                  dtype=np.float64)
+    un = np.zeros((16, 512), np.uint8)
+    un[:, 0::2] = codes & 15
+    un[:, 1::2] = codes >> 4
+    lhs = e4[y] * np.exp2(np.repeat(ys, 128, axis=1).astype(np.float64) - 127)
+    rhs = e2[un] * np.exp2(np.repeat(scales, 32, axis=1).astype(np.float64) - 127)
+    np.testing.assert_array_equal(lhs, rhs)
+    # the block scale is the max of the four MX scales
+    np.testing.assert_array_equal(ys, scales.reshape(16, -1, 4).max(axis=2))
+
+
+# ---- cols -------------------------------------------------------------------------------
+
+def test_cols_match_brute_force_ragged():
+    rng = np.random.default_rng(6)
+    counts = [0, 3, 130, 1, 0, 129]
+    M = sum(counts)
+    K = 128
+    codes = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint16).astype(np.uint8)
+    scales = rng.integers(100, 125, size=(M, K // 32)).astype(np.uint8)
+    scales[5, 1] = 0
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    yT_o, ys_o = oracle.fp8_cols(codes, scales, offs)
+    yT_r, ys_r = exact_ref.fp8_cols(codes, scales, offs)
+    np.testing.assert_array_equal(ys_o, ys_r)
+    np.testing.assert_array_equal(yT_o, yT_r)
+
+
+def test_cols_equal_transposed_rows_when_scales_are_constant():
+    rng = np.random.default_rng(8)
+    counts = [200, 0, 56, 300]
+    M, K = sum(counts), 256
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    codes = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint16).astype(np.uint8)
+    scales = np.full((M, K // 32), 119, np.uint8)
+    y, _ = oracle.fp8_rows(codes, scales)
+    yT, ysT = oracle.fp8_cols(codes, scales, offs)
+    for g in range(len(counts)):
+        r0, r1 = offs[g], offs[g + 1]
+        seg = yT[K * r0:K * r1].reshape(K, r1 - r0)
+        np.testing.assert_array_equal(seg, y[r0:r1].T)
+    assert np.all(ysT == 119)
+
+
+def test_cols_single_segment_whole_matrix_transpose():
+    rng = np.random.default_rng(9)
+    M, K = 256, 128
+    codes = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint16).astype(np.uint8)
+    scales = np.full((M, K // 32), 127, np.uint8)
+    offs = np.array([0, M], np.int32)
+    y, _ = oracle.fp8_rows(codes, scales)
+    yT, _ = oracle.fp8_cols(codes, scales, offs)
+    np.testing.assert_array_equal(yT.reshape(K, M), y.T)
+
+
+def test_cols_scale_is_max_over_block_rows():
+    rng = np.random.default_rng(10)
+    counts = [300]
+    M, K = 300, 128
+    offs = np.array([0, M], np.int32)
+    codes = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint16).astype(np.uint8)
+    scales = rng.integers(0, 255, size=(M, K // 32)).astype(np.uint8)
+    _, ys = oracle.fp8_cols(codes, scales, offs)
+    ys = ys.reshape(3, K)
+    for b in range(3):
+        blk = scales[128 * b:min(M, 128 * b + 128)]
+        np.testing.assert_array_equal(ys[b], np.repeat(blk.max(axis=0), 32))
+
+
+def test_threaded_drivers_equal_single_thread():
+    rng = np.random.default_rng(12)
+    x = _rand_bits(rng, (300, 256), "normal")
+    c1, s1 = oracle.quantize_rows(x, threads=1)
+    c4, s4 = oracle.quantize_rows(x, threads=4)
+    np.testing.assert_array_equal(c1, c4)
+    np.testing.assert_array_equal(s1, s4)
+    offs = np.array([0, 10, 10, 290, 300], np.int32)
+    a1 = oracle.fp8_cols(c1, s1, offs, threads=1)
+    a4 = oracle.fp8_cols(c1, s1, offs, threads=4)
+    np.testing.assert_array_equal(a1[0], a4[0])
+    np.testing.assert_array_equal(a1[1], a4[1])
