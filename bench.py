@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark: achieved HBM GB/s of the BF16 -> MXFP4 -> block-scaled FP8 path.
+
+A step is one pass of the whole path over one batch of synthetic input, every
+launch on torch's current stream:
+
+  for each segment (hidden 7168, intermediate 2048):
+      mxfp4_quantize_rows -> mxfp4_to_fp8_rows -> mxfp4_to_fp8_cols_ragged
+
+on the forward-chain workload (one GPU's share of a 256-expert MoE: 8 local
+experts, 65536 routed rows, Zipf(1.2) counts with two empty experts).  Inputs
+are resident in HBM before the timed region.  ``value`` is algorithmic bytes per
+step / wall time per step.  ``roofline`` reports the dominant kernel (largest
+time per step): algorithmic bytes per launch / its mean launch time, measured
+with HIP events on the launch stream inside the timed region, against the
+8 TB/s HBM peak.  ``cpu_baseline`` times the CPU oracle on a bounded sample of
+the same workload on this host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload config5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "HBM GB/s & % peak: BF16→MXFP4 quant + MXFP4→FP8 row/col conversion"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor datasheet
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "block_scaled_precision_bf16tofp4row_amd", "csrc")
+KERNEL_SOURCES = {
+    "quantize": ["quantize.hip", "common.h"],
+    "rows": ["rows.hip", "common.h"],
+    "cols": ["cols.hip", "common.h"],
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def alg_bytes(kernel: str, M_tot: int, K: int, col_scale_bytes: int = 0) -> int:
+    """Bytes the method must move (per launch)."""
+    n = M_tot * K
+    if kernel == "quantize":            # 2 B in, 1/2 + 1/32 B out
+        return 2 * n + n // 2 + n // 32
+    if kernel == "rows":                # 1/2 + 1/32 B in, 1 + 1/128 B out
+        return n // 2 + n // 32 + n + n // 128
+    if kernel == "cols":                # 1/2 + 1/32 B in, 1 B out + one scale byte per (block, k)
+        return n // 2 + n // 32 + n + col_scale_bytes
+    raise ValueError(kernel)
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, segment: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None when
+    there is none or the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"<!-- traffic-json (\{.*?\}) -->", text, re.S)
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    ent = data.get(f"{kernel}/{segment}")
+    if not ent or ent.get("source_sha") != source_hash(kernel):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def affinity_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# ---- CPU baseline (oracle, bounded sample) --------------------------------------------
+
+def cpu_baseline(workload, target_s: float = 15.0):
+    import oracle
+    threads = affinity_threads()
+    oracle._load()
+
+    def run(rows_frac_rows):
+        total_bytes = 0
+        t0 = time.perf_counter()
+        for seg in workload.segments:
+            R = min(seg.M_tot, rows_frac_rows)
+            offs = np.minimum(seg.offs, R).astype(np.int32)
+            x = seg.x_bits[:R]
+            c, s = oracle.quantize_rows(x, threads=threads)
+            total_bytes += alg_bytes("quantize", R, seg.K)
+            if "rows" in workload.kernels:
+                oracle.fp8_rows(c, s, threads=threads)
+                total_bytes += alg_bytes("rows", R, seg.K)
+            if "cols" in workload.kernels:
+                oracle.fp8_cols(c, s, offs, threads=threads)
+                total_bytes += alg_bytes("cols", R, seg.K, oracle.cols_scale_size(offs, seg.K))
+        return total_bytes, time.perf_counter() - t0
+
+    probe_rows = 512
+    b, t = run(probe_rows)
+    max_rows = max(seg.M_tot for seg in workload.segments)
+    rows = int(min(max_rows, max(probe_rows, probe_rows * target_s / max(t, 1e-6))))
+    rows = max(128, rows - rows % 128)
+    b, t = run(rows)
+    frac = rows / max_rows
+    return {
+        "value": round(b / t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"first {rows} of {max_rows} routed rows of every segment "
+                   f"({frac:.1%} of a step: the same kernels, offsets clipped to the sample), "
+                   f"{t:.1f} s wall on {threads} threads"),
+    }
+
+
+# ---- GPU run -----------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="config5", choices=["config2", "config3", "config4", "config5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain device copy of known size (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards by rows "
+              f"and experts across GPUs but multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_precision_bf16tofp4row_amd as mx
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mx.load_library()
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+
+    t0 = time.perf_counter()
+    w = workloads.make_config(int(args.workload[-1]), 0)
+    log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s: {w.description}")
+
+    segs = []
+    for seg in w.segments:
+        x = torch.from_numpy(seg.x_bits.view(np.int16)).to(dev)
+        offs = torch.from_numpy(seg.offs).to(dev)
+        codes, scales = mx.alloc_quantize_outputs(seg.M_cap, seg.K, dev)
+        d = {"seg": seg, "x": x, "offs": offs, "codes": codes, "scales": scales}
+        if "rows" in w.kernels:
+            d["y"], d["ys"] = mx.alloc_rows_outputs(seg.M_cap, seg.K, dev)
+        if "cols" in w.kernels:
+            d["yT"], d["ysT"] = mx.alloc_cols_outputs(seg.M_cap, seg.K, seg.G, dev)
+            nb = (np.diff(seg.offs.astype(np.int64)) + 127) // 128
+            d["col_scale_bytes"] = int(nb.sum()) * seg.K
+        segs.append(d)
+    torch.cuda.synchronize()
+
+    launches = []     # (kernel, segment name, fn, alg bytes)
+    for d in segs:
+        seg = d["seg"]
+        launches.append(("quantize", seg.name,
+                         lambda d=d: mx.mxfp4_quantize_rows(d["x"], d["codes"], d["scales"], d["offs"]),
+                         alg_bytes("quantize", seg.M_tot, seg.K)))
+        if "rows" in w.kernels:
+            launches.append(("rows", seg.name,
+                             lambda d=d: mx.mxfp4_to_fp8_rows(d["codes"], d["scales"], d["y"], d["ys"],
+                                                              d["offs"]),
+                             alg_bytes("rows", seg.M_tot, seg.K)))
+        if "cols" in w.kernels:
+            launches.append(("cols", seg.name,
+                             lambda d=d: mx.mxfp4_to_fp8_cols_ragged(d["codes"], d["scales"], d["yT"],
+                                                                     d["ysT"], d["offs"]),
+                             alg_bytes("cols", seg.M_tot, seg.K, d["col_scale_bytes"])))
+    step_bytes = sum(l[3] for l in launches)
+
+    def step(events=None):
+        for i, (_, _, fn, _) in enumerate(launches):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in launches] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1000.0 / args.steps
+
+    per_kernel = []
+    for i, (kern, segname, _, nbytes) in enumerate(launches):
+        ms = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        mean_ms = float(np.mean(ms))
+        per_kernel.append({
+            "kernel": kern, "segment": segname, "alg_bytes": nbytes,
+            "mean_us": round(mean_ms * 1000.0, 2), "median_us": round(float(np.median(ms)) * 1000.0, 2),
+            "GBps": round(nbytes / (mean_ms / 1000.0) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (mean_ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+        })
+    dom = max(per_kernel, key=lambda p: p["mean_us"])
+    achieved = dom["GBps"]
+    traffic = read_traffic(dom["kernel"], w.name, dom["segment"])
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: 3 x {n} bytes read + {n} bytes written")
+        del a, b
+
+    value = step_bytes / (ms_per_step / 1000.0) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name + ": " + w.description,
+            "segments": [{"name": d["seg"].name, "M_cap": d["seg"].M_cap, "M_tot": d["seg"].M_tot,
+                          "K": d["seg"].K, "G": d["seg"].G} for d in segs],
+            "kernels_per_step": [f"{k}/{s}" for k, s, _, _ in launches],
+            "alg_bytes_per_step": step_bytes,
+            "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+            "device": props.name,
+            "cus": props.multi_processor_count,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"{dom['kernel']}/{dom['segment']}",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": dom["alg_bytes"],
+            "mean_launch_us": dom["mean_us"],
+        },
+        "per_kernel": per_kernel,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

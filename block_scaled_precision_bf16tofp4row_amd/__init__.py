@@ -1,0 +1,187 @@
+"""MI355X-native BF16 -> MXFP4 -> block-scaled FP8 conversion path.
+
+Thin ctypes binding over ``libmxfp4cvt.so`` (C ABI in ``include/mxfp4cvt.h``).
+The Python layer only marshals arguments: every step of the path runs in the
+gfx950 HIP kernels of the library.  PyTorch provides device memory and streams.
+
+Method: "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs",
+technical summary section 2 (Methodology), items 1-3.
+
+The binding has the same names as the C ABI:
+
+* ``mxfp4_quantize_rows(x, codes, scales, offs, ...)``
+* ``mxfp4_to_fp8_rows(codes, scales, y, y_scales, offs, ...)``
+* ``mxfp4_to_fp8_cols_ragged(codes, scales, yT, yT_scales, offs, ...)``
+* ``mxfp4_cols_scale_capacity(M_cap, K, G)``, ``mxfp4_validate_offsets(offs, ...)``,
+  ``mxfp4_status_string(status)``
+
+Array arguments are torch tensors on the GPU (BF16 input as ``torch.bfloat16``
+or ``torch.int16``/``torch.uint16`` bits; uint8 outputs; int32 offsets).  The
+stream defaults to torch's current stream.  A non-OK status raises
+``Mxfp4Error``.  If the library is not built the import still works but every
+call raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmxfp4cvt.so")
+
+MXFP4_OK = 0
+MXFP4_ERR_NULL = 1
+MXFP4_ERR_SHAPE = 2
+MXFP4_ERR_ALIGN = 3
+MXFP4_ERR_HIP = 4
+
+EXPORTED = (
+    "mxfp4_quantize_rows",
+    "mxfp4_to_fp8_rows",
+    "mxfp4_to_fp8_cols_ragged",
+    "mxfp4_cols_scale_capacity",
+    "mxfp4_validate_offsets",
+    "mxfp4_status_string",
+)
+
+
+class Mxfp4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {mxfp4_status_string(status)}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmxfp4cvt.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m block_scaled_precision_bf16tofp4row_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    st = ctypes.c_int
+    lib.mxfp4_quantize_rows.argtypes = [P, P, P, P, I32, I64, I64, P]
+    lib.mxfp4_quantize_rows.restype = st
+    lib.mxfp4_to_fp8_rows.argtypes = [P, P, P, P, P, I32, I64, I64, P]
+    lib.mxfp4_to_fp8_rows.restype = st
+    lib.mxfp4_to_fp8_cols_ragged.argtypes = [P, P, P, P, P, I32, I64, I64, P]
+    lib.mxfp4_to_fp8_cols_ragged.restype = st
+    lib.mxfp4_cols_scale_capacity.argtypes = [I64, I64, I32]
+    lib.mxfp4_cols_scale_capacity.restype = I64
+    lib.mxfp4_validate_offsets.argtypes = [P, I32, I64, P]
+    lib.mxfp4_validate_offsets.restype = st
+    lib.mxfp4_status_string.argtypes = [st]
+    lib.mxfp4_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def mxfp4_status_string(status: int) -> str:
+    return load_library().mxfp4_status_string(int(status)).decode()
+
+
+def mxfp4_cols_scale_capacity(M_cap: int, K: int, G: int) -> int:
+    return int(load_library().mxfp4_cols_scale_capacity(int(M_cap), int(K), int(G)))
+
+
+# ---- marshalling -------------------------------------------------------------------
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != MXFP4_OK:
+        raise Mxfp4Error(status, what)
+
+
+def _dims(x, offs, G, M_cap, K):
+    if G is None:
+        G = offs.numel() - 1
+    if M_cap is None:
+        M_cap = x.shape[0]
+    if K is None:
+        K = x.shape[1]
+    return int(G), int(M_cap), int(K)
+
+
+def mxfp4_quantize_rows(x, codes, scales, offs, G=None, M_cap=None, K=None, stream=None):
+    """BF16 [M_cap, K] -> codes [M_cap, K/2] uint8 + scales [M_cap, K/32] uint8."""
+    G, M_cap, K = _dims(x, offs, G, M_cap, K)
+    lib = load_library()
+    _check(lib.mxfp4_quantize_rows(_ptr(x), _ptr(codes), _ptr(scales), _ptr(offs), G, M_cap, K,
+                                   _stream(stream)), "mxfp4_quantize_rows")
+
+
+def mxfp4_to_fp8_rows(codes, scales, y, y_scales, offs, G=None, M_cap=None, K=None, stream=None):
+    """codes/scales -> E4M3 y [M_cap, K] + UE8M0 y_scales [M_cap, K/128]."""
+    if K is None:
+        K = codes.shape[1] * 2
+    G, M_cap, K = _dims(codes, offs, G, M_cap, K)
+    lib = load_library()
+    _check(lib.mxfp4_to_fp8_rows(_ptr(codes), _ptr(scales), _ptr(y), _ptr(y_scales), _ptr(offs),
+                                 G, M_cap, K, _stream(stream)), "mxfp4_to_fp8_rows")
+
+
+def mxfp4_to_fp8_cols_ragged(codes, scales, yT, yT_scales, offs, G=None, M_cap=None, K=None,
+                             stream=None):
+    """codes/scales -> per-expert transposed E4M3 yT + UE8M0 yT_scales (see the header)."""
+    if K is None:
+        K = codes.shape[1] * 2
+    G, M_cap, K = _dims(codes, offs, G, M_cap, K)
+    lib = load_library()
+    _check(lib.mxfp4_to_fp8_cols_ragged(_ptr(codes), _ptr(scales), _ptr(yT), _ptr(yT_scales),
+                                        _ptr(offs), G, M_cap, K, _stream(stream)),
+           "mxfp4_to_fp8_cols_ragged")
+
+
+def mxfp4_validate_offsets(offs, G=None, M_cap=None, stream=None) -> bool:
+    """True if the device offsets satisfy the preconditions (synchronizes the stream)."""
+    if G is None:
+        G = offs.numel() - 1
+    if M_cap is None:
+        raise ValueError("M_cap is required")
+    st = load_library().mxfp4_validate_offsets(_ptr(offs), int(G), int(M_cap), _stream(stream))
+    if st == MXFP4_ERR_SHAPE:
+        return False
+    _check(st, "mxfp4_validate_offsets")
+    return True
+
+
+# ---- output allocation (plumbing: torch device memory) ----------------------------
+
+def alloc_quantize_outputs(M_cap: int, K: int, device="cuda"):
+    import torch
+    return (torch.empty((M_cap, K // 2), dtype=torch.uint8, device=device),
+            torch.empty((M_cap, K // 32), dtype=torch.uint8, device=device))
+
+
+def alloc_rows_outputs(M_cap: int, K: int, device="cuda"):
+    import torch
+    return (torch.empty((M_cap, K), dtype=torch.uint8, device=device),
+            torch.empty((M_cap, K // 128), dtype=torch.uint8, device=device))
+
+
+def alloc_cols_outputs(M_cap: int, K: int, G: int, device="cuda"):
+    import torch
+    cap = mxfp4_cols_scale_capacity(M_cap, K, G)
+    return (torch.empty(max(1, M_cap * K), dtype=torch.uint8, device=device),
+            torch.empty(max(1, cap), dtype=torch.uint8, device=device))

@@ -1,0 +1,145 @@
+// abi.hip -- the C ABI of libmxfp4cvt (declared in include/mxfp4cvt.h): synchronous
+// argument validation, then one kernel launch on the caller's stream.
+#include <stdlib.h>
+#include <string.h>
+
+#include "mxfp4cvt.h"
+#include "common.h"
+
+namespace mxfp4 {
+hipError_t launch_quantize_rows(const uint16_t*, uint8_t*, uint8_t*, const int32_t*, int32_t,
+                                int64_t, int64_t, hipStream_t);
+hipError_t launch_fp8_rows(const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, const int32_t*,
+                           int32_t, int64_t, int64_t, hipStream_t);
+hipError_t launch_fp8_cols(const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, const int32_t*,
+                           int32_t, int64_t, int64_t, hipStream_t);
+int64_t cols_block_capacity(int64_t M_cap, int32_t G);
+}  // namespace mxfp4
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Largest M_cap * K the kernels index: every byte count stays far inside int64.
+constexpr int64_t kMaxElems = (int64_t)1 << 50;
+
+mxfp4_status check_shape(int32_t G, int64_t M_cap, int64_t K, int64_t k_multiple)
+{
+    if (G < 1 || M_cap < 0 || K <= 0 || K % k_multiple != 0)
+        return MXFP4_ERR_SHAPE;
+    if (M_cap > 0 && K > kMaxElems / M_cap)
+        return MXFP4_ERR_SHAPE;
+    if (M_cap > INT32_MAX)                   // offsets are int32
+        return MXFP4_ERR_SHAPE;
+    return MXFP4_OK;
+}
+
+mxfp4_status from_hip(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+mxfp4_status mxfp4_quantize_rows(const uint16_t* x_bf16, uint8_t* codes, uint8_t* scales,
+                                 const int32_t* group_offsets, int32_t G, int64_t M_cap,
+                                 int64_t K, hipStream_t stream)
+{
+    if (!x_bf16 || !codes || !scales || !group_offsets)
+        return MXFP4_ERR_NULL;
+    mxfp4_status st = check_shape(G, M_cap, K, 32);
+    if (st != MXFP4_OK)
+        return st;
+    if (!aligned(x_bf16, 16) || !aligned(codes, 16) || !aligned(scales, 16) ||
+        !aligned(group_offsets, 4))
+        return MXFP4_ERR_ALIGN;
+    if (M_cap == 0)
+        return MXFP4_OK;
+    return from_hip(mxfp4::launch_quantize_rows(x_bf16, codes, scales, group_offsets, G, M_cap,
+                                                K, stream));
+}
+
+mxfp4_status mxfp4_to_fp8_rows(const uint8_t* codes, const uint8_t* scales, uint8_t* y_e4m3,
+                               uint8_t* y_scales, const int32_t* group_offsets, int32_t G,
+                               int64_t M_cap, int64_t K, hipStream_t stream)
+{
+    if (!codes || !scales || !y_e4m3 || !y_scales || !group_offsets)
+        return MXFP4_ERR_NULL;
+    mxfp4_status st = check_shape(G, M_cap, K, 128);
+    if (st != MXFP4_OK)
+        return st;
+    if (!aligned(codes, 16) || !aligned(scales, 16) || !aligned(y_e4m3, 16) ||
+        !aligned(y_scales, 16) || !aligned(group_offsets, 4))
+        return MXFP4_ERR_ALIGN;
+    if (M_cap == 0)
+        return MXFP4_OK;
+    return from_hip(mxfp4::launch_fp8_rows(codes, scales, y_e4m3, y_scales, group_offsets, G,
+                                           M_cap, K, stream));
+}
+
+mxfp4_status mxfp4_to_fp8_cols_ragged(const uint8_t* codes, const uint8_t* scales,
+                                      uint8_t* yT_e4m3, uint8_t* yT_scales,
+                                      const int32_t* group_offsets, int32_t G, int64_t M_cap,
+                                      int64_t K, hipStream_t stream)
+{
+    if (!codes || !scales || !yT_e4m3 || !yT_scales || !group_offsets)
+        return MXFP4_ERR_NULL;
+    mxfp4_status st = check_shape(G, M_cap, K, 128);
+    if (st != MXFP4_OK)
+        return st;
+    if (!aligned(codes, 16) || !aligned(scales, 16) || !aligned(yT_e4m3, 16) ||
+        !aligned(yT_scales, 16) || !aligned(group_offsets, 4))
+        return MXFP4_ERR_ALIGN;
+    if (M_cap == 0)
+        return MXFP4_OK;
+    return from_hip(mxfp4::launch_fp8_cols(codes, scales, yT_e4m3, yT_scales, group_offsets, G,
+                                           M_cap, K, stream));
+}
+
+int64_t mxfp4_cols_scale_capacity(int64_t M_cap, int64_t K, int32_t G)
+{
+    if (check_shape(G, M_cap, K, 128) != MXFP4_OK)
+        return -1;
+    return K * mxfp4::cols_block_capacity(M_cap, G);
+}
+
+mxfp4_status mxfp4_validate_offsets(const int32_t* group_offsets, int32_t G, int64_t M_cap,
+                                    hipStream_t stream)
+{
+    if (!group_offsets)
+        return MXFP4_ERR_NULL;
+    if (G < 1 || M_cap < 0 || M_cap > INT32_MAX)
+        return MXFP4_ERR_SHAPE;
+    int32_t* h = (int32_t*)malloc(sizeof(int32_t) * ((size_t)G + 1));
+    if (!h)
+        return MXFP4_ERR_HIP;
+    hipError_t e = hipMemcpyAsync(h, group_offsets, sizeof(int32_t) * ((size_t)G + 1),
+                                  hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    mxfp4_status st = from_hip(e);
+    if (st == MXFP4_OK) {
+        if (h[0] != 0)
+            st = MXFP4_ERR_SHAPE;
+        for (int32_t g = 0; g < G && st == MXFP4_OK; ++g)
+            if (h[g + 1] < h[g])
+                st = MXFP4_ERR_SHAPE;
+        if (st == MXFP4_OK && (int64_t)h[G] > M_cap)
+            st = MXFP4_ERR_SHAPE;
+    }
+    free(h);
+    return st;
+}
+
+const char* mxfp4_status_string(mxfp4_status status)
+{
+    switch (status) {
+    case MXFP4_OK: return "MXFP4_OK";
+    case MXFP4_ERR_NULL: return "MXFP4_ERR_NULL: a required pointer is NULL";
+    case MXFP4_ERR_SHAPE: return "MXFP4_ERR_SHAPE: invalid G, M_cap or K";
+    case MXFP4_ERR_ALIGN: return "MXFP4_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case MXFP4_ERR_HIP: return "MXFP4_ERR_HIP: HIP runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// common.h -- device helpers shared by the three gfx950 kernels of libmxfp4cvt.
+//
+// Formats (from "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs",
+// technical summary section 2, item 1): MXFP4 = 32 E2M1 codes (1 sign, 2 exponent,
+// 1 mantissa bit) sharing one UE8M0 power-of-two scale; codes are stored two per byte
+// (item 2), element 2i in the low nibble.  FP8 target = OCP E4M3FN with one UE8M0
+// scale per 128 elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfp4 {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// A 16-byte vector with byte alignment: gfx950 global stores accept any byte address.
+typedef u32x4 u32x4_unaligned __attribute__((aligned(1)));
+
+constexpr int kThreads = 256;   // 4 wave64 per workgroup
+
+// ---- memory ---------------------------------------------------------------------
+
+// Every byte of this path is touched exactly once: stream it past the caches.
+__device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x2 load_stream(const u32x2* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+
+// ---- cross-lane -----------------------------------------------------------------
+
+// DPP quad permutations (lanes 4q..4q+3 exchange inside their quad).
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadSwap1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadSwap2, 0xF, 0xF, false));
+    return v;
+}
+
+// Byte permute: result byte i = byte sel[i] of the 8-byte value {hi:lo}.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// ---- E2M1 code -> E4M3FN byte after a scale shift ---------------------------------
+
+// E4M3FN byte of the E2M1 magnitude code c (0..7) multiplied by 2^-d, round to
+// nearest even.  Twice the E2M1 magnitude is the integer k below; the value in
+// units of 2^-9 (the smallest E4M3 subnormal) is k * 2^(8-d).  Below 16 units the
+// E4M3 byte equals the unit count (subnormals and the first normal binade are
+// linear in the byte); above, the value is normalised to 8..15 units times 2^(E-1)
+// with E the exponent field.  For d > 8 the unit count is k / 2^(d-8), rounded.
+constexpr uint8_t e4m3_of_e2m1_shifted(int c, int d)
+{
+    constexpr int twice[8] = {0, 1, 2, 3, 4, 6, 8, 12};
+    int k = twice[c];
+    if (k == 0)
+        return 0;
+    if (d <= 8) {
+        int v = k << (8 - d);        // exact: k has at most two significant bits
+        int E = 1;
+        while (v >= 16) {
+            v >>= 1;
+            ++E;
+        }
+        return (uint8_t)(v < 8 ? v : ((E << 3) | (v - 8)));
+    }
+    int sh = d - 8;
+    if (sh >= 8)
+        return 0;
+    int q = k >> sh;
+    int rem = k & ((1 << sh) - 1);
+    int half = 1 << (sh - 1);
+    if (rem > half || (rem == half && (q & 1)))
+        ++q;
+    return (uint8_t)q;
+}
+
+// Gaps at or above this value flush every code to (signed) zero.
+constexpr int kMaxGap = 13;
+
+// The 8-entry byte table for gap d, as two dwords (codes 0..3, codes 4..7).
+constexpr uint32_t lut_word(int d, int half)
+{
+    uint32_t w = 0;
+    for (int i = 0; i < 4; ++i)
+        w |= (uint32_t)e4m3_of_e2m1_shifted(4 * half + i, d) << (8 * i);
+    return w;
+}
+
+struct GapLut {
+    uint32_t w[kMaxGap + 1][2];
+};
+
+constexpr GapLut make_gap_lut()
+{
+    GapLut t{};
+    for (int d = 0; d <= kMaxGap; ++d) {
+        t.w[d][0] = lut_word(d, 0);
+        t.w[d][1] = lut_word(d, 1);
+    }
+    return t;
+}
+
+// Spread 4 packed codes (16 bits of `w` starting at byte `b`: nibbles n0..n3) into
+// one byte each: result byte i = n_i (sign bit kept in bit 3).
+__device__ __forceinline__ uint32_t spread_nibbles(uint32_t w, uint32_t sel_bytes)
+{
+    uint32_t t = perm(w, w, sel_bytes);                 // [b, b, b+1, b+1]
+    return (t & 0x000F000Fu) | ((t >> 4) & 0x0F000F00u);
+}
+
+// Four E4M3 bytes for four spread codes, with the gap table (lo, hi) of this sub-block.
+__device__ __forceinline__ uint32_t convert4(uint32_t nib4, uint32_t lut_lo, uint32_t lut_hi)
+{
+    uint32_t mag = perm(lut_hi, lut_lo, nib4 & 0x07070707u);
+    return mag | ((nib4 << 4) & 0x80808080u);
+}
+
+// Eight codes (one dword of packed nibbles) -> eight E4M3 bytes (two dwords).
+__device__ __forceinline__ u32x2 convert8(uint32_t w, uint32_t lut_lo, uint32_t lut_hi)
+{
+    return u32x2{convert4(spread_nibbles(w, 0x01010000u), lut_lo, lut_hi),
+                 convert4(spread_nibbles(w, 0x03030202u), lut_lo, lut_hi)};
+}
+
+// ---- workgroup -> XCD-aware tile order ---------------------------------------------
+
+// Workgroups are dispatched round-robin over the 8 XCDs.  Remap so that each XCD
+// receives a contiguous range of logical tiles (neighbouring tiles then share an L2).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks)
+{
+    constexpr uint32_t kXcd = 8;
+    uint32_t per = nblocks / kXcd;
+    uint32_t full = per * kXcd;
+    if (bid >= full)
+        return bid;                       // the ragged remainder keeps its order
+    return (bid % kXcd) * per + bid / kXcd;
+}
+
+}  // namespace mxfp4

@@ -1,0 +1,115 @@
+/*
+ * mxfp4cvt.h -- C ABI of libmxfp4cvt: BF16 -> MXFP4 quantization and direct MXFP4 ->
+ * block-scaled FP8 (E4M3) conversion, row and transposed-column layouts, over ragged
+ * per-expert token segments, on AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs"
+ * (technical summary, section 2 "Methodology"):
+ *   item 1  MXFP4 = E2M1 elements (1 sign, 2 exponent, 1 mantissa bit) sharing one
+ *           UE8M0 power-of-two scale per 32 elements; the FP8 target is E4M3 with
+ *           128-element blocks, reached by a direct bitwise FP4 -> FP8 conversion
+ *           (no BF16 intermediate) with hierarchical scale alignment to the
+ *           largest of the four MX scales of a 128-block;
+ *   item 2  activations are quantized right before the expert all-to-all and packed
+ *           two codes per uint8;
+ *   item 3  layout-aware kernels: row quantizer, row conversion (FPROP), column
+ *           conversion with the transpose fused (Wgrad), ragged tensors without
+ *           padding.
+ * Conventions the page leaves open follow OCP MX v1.0: shared exponent
+ * floor(log2 amax) - 2 (clamped to the UE8M0 range, 0 for an all-zero block), E2M1
+ * round-to-nearest-even saturating at 6, E4M3FN (OCP, bias 7, no Inf) round-to-
+ * nearest-even where a shift underflows, sign of zero kept, element 2i in the low
+ * nibble of byte i.
+ *
+ * Common conventions of every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates and frees nothing and keeps no state; calls are thread-safe.
+ *   - Work is enqueued on `stream` and the call returns at once (no host sync, the
+ *     offsets are never read on the host).
+ *   - group_offsets: int32 [G+1] on the device, offs[0] = 0, non-decreasing,
+ *     offs[G] = M_tot <= M_cap.  Expert g owns rows [offs[g], offs[g+1]).  These
+ *     are preconditions (not checked; mxfp4_validate_offsets checks them with a
+ *     host sync).  Rows [M_tot, M_cap) of every output are left untouched, so a
+ *     capacity-sized launch needs no host knowledge of M_tot.
+ *   - Arguments are validated before anything is enqueued; on any error nothing is
+ *     enqueued:  NULL array pointer -> MXFP4_ERR_NULL;  G < 1, M_cap < 0, K <= 0,
+ *     K not a multiple of 32 (quantize) or 128 (conversions), or sizes whose byte
+ *     counts overflow int64 -> MXFP4_ERR_SHAPE;  an array pointer not 16-byte aligned
+ *     (group_offsets: 4-byte) -> MXFP4_ERR_ALIGN.  A failed kernel launch ->
+ *     MXFP4_ERR_HIP.
+ *   - Outputs must not alias inputs.
+ *   - UE8M0 scale bytes decode as 2^(b - 127); b = 0 is 2^-127 (an fp32 subnormal).
+ */
+#ifndef MXFP4CVT_H
+#define MXFP4CVT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MXFP4_OK = 0,
+    MXFP4_ERR_NULL = 1,
+    MXFP4_ERR_SHAPE = 2,
+    MXFP4_ERR_ALIGN = 3,
+    MXFP4_ERR_HIP = 4
+} mxfp4_status;
+
+/* BF16 -> MXFP4 (the page's BF16ToFP4Row; technical summary section 2, items 1-2).
+ *   x_bf16  [M_cap, K] row-major BF16 bits (finite values).
+ *   codes   [M_cap, K/2]  E2M1 codes, element 2i in the low nibble of byte i.
+ *   scales  [M_cap, K/32] UE8M0 bytes: floor(log2 amax) - 2 + 127 clamped to [0, 254].
+ *   Rows [0, offs[G]) are written.  K must be a multiple of 32. */
+mxfp4_status mxfp4_quantize_rows(const uint16_t* x_bf16, uint8_t* codes, uint8_t* scales,
+                                 const int32_t* group_offsets, int32_t G, int64_t M_cap,
+                                 int64_t K, hipStream_t stream);
+
+/* MXFP4 -> FP8 E4M3FN, row layout for FPROP (the page's FP4RowToFP8Row; technical
+ * summary section 2, item 1, hierarchical scale alignment).
+ *   codes, scales  as produced by mxfp4_quantize_rows.
+ *   y_e4m3    [M_cap, K]     E4M3FN bytes: e2m1(c) * 2^(s - S) rounded to nearest even.
+ *   y_scales  [M_cap, K/128] UE8M0 bytes S = max of the four MX scales of the block.
+ *   Rows [0, offs[G]) are written.  K must be a multiple of 128. */
+mxfp4_status mxfp4_to_fp8_rows(const uint8_t* codes, const uint8_t* scales, uint8_t* y_e4m3,
+                               uint8_t* y_scales, const int32_t* group_offsets, int32_t G,
+                               int64_t M_cap, int64_t K, hipStream_t stream);
+
+/* MXFP4 -> FP8 E4M3FN, transposed column layout per expert for Wgrad (the page's
+ * FP4RowToFP8Col; technical summary section 2, item 3: transpose fused, ragged, no
+ * padding).  With M_g = offs[g+1] - offs[g], nb_g = ceil(M_g / 128) and
+ * B_g = nb_0 + ... + nb_{g-1}:
+ *   yT_e4m3    expert g: [K, M_g] at byte K*offs[g], element (k, m') at k*M_g + m'
+ *              (m' = row - offs[g]); capacity K*M_cap bytes.
+ *   yT_scales  expert g: [nb_g, K] at byte K*B_g; entry (b, k) = max of the MX
+ *              scales of group k/32 over the rows of block b that exist (a partial
+ *              last block uses only its rows); capacity
+ *              mxfp4_cols_scale_capacity(M_cap, K, G) bytes.
+ *   Element (k, m') = e2m1(c) * 2^(s - S) rounded to nearest even, s the row's own
+ *   MX scale.  Bytes past each expert's M_g (and past offs[G]) are not written.
+ *   K must be a multiple of 128. */
+mxfp4_status mxfp4_to_fp8_cols_ragged(const uint8_t* codes, const uint8_t* scales,
+                                      uint8_t* yT_e4m3, uint8_t* yT_scales,
+                                      const int32_t* group_offsets, int32_t G, int64_t M_cap,
+                                      int64_t K, hipStream_t stream);
+
+/* Bytes the column-layout scale buffer needs for any offsets with offs[G] <= M_cap:
+ * K * (ceil(M_cap / 128) + G).  Returns -1 for invalid sizes. */
+int64_t mxfp4_cols_scale_capacity(int64_t M_cap, int64_t K, int32_t G);
+
+/* Debug helper: copies the G+1 offsets to the host (synchronizing `stream`) and
+ * checks offs[0] == 0, non-decreasing, offs[G] <= M_cap.  MXFP4_OK if they hold,
+ * MXFP4_ERR_SHAPE if not, MXFP4_ERR_NULL / MXFP4_ERR_HIP as usual. */
+mxfp4_status mxfp4_validate_offsets(const int32_t* group_offsets, int32_t G, int64_t M_cap,
+                                    hipStream_t stream);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* mxfp4_status_string(mxfp4_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4CVT_H */

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments synchronously (before any HIP call)
+with the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_bf16tofp4row_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4cvt.h")
+
+# fake, never-dereferenced device addresses (validation fails before any launch)
+A = 0x7F0000000000
+A2 = A + 0x100000
+A3 = A + 0x200000
+A4 = A + 0x300000
+OFFS = A + 0x400000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mx.load_library()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(mx.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = ctypes.CDLL(mx.LIB_PATH)
+    for name in declared_functions():
+        getattr(nm, name)
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = mx.mxfp4_status_string(code)
+        assert s.startswith("MXFP4_")
+    assert mx.mxfp4_status_string(99) == "unknown status"
+
+
+def test_cols_scale_capacity():
+    assert mx.mxfp4_cols_scale_capacity(32768, 2048, 32) == 2048 * (256 + 32)
+    assert mx.mxfp4_cols_scale_capacity(1, 128, 1) == 128 * 2
+    assert mx.mxfp4_cols_scale_capacity(0, 128, 3) == 128 * 3
+    assert mx.mxfp4_cols_scale_capacity(10, 100, 1) == -1
+    assert mx.mxfp4_cols_scale_capacity(10, 128, 0) == -1
+
+
+def _q(lib, x=A, c=A2, s=A3, o=OFFS, G=1, M=4, K=64):
+    return lib.mxfp4_quantize_rows(x, c, s, o, G, M, K, None)
+
+
+def _r(lib, fn, c=A, s=A2, y=A3, ys=A4, o=OFFS, G=1, M=4, K=128):
+    return getattr(lib, fn)(c, s, y, ys, o, G, M, K, None)
+
+
+def test_quantize_argument_errors(lib):
+    assert _q(lib, x=None) == mx.MXFP4_ERR_NULL
+    assert _q(lib, c=None) == mx.MXFP4_ERR_NULL
+    assert _q(lib, s=None) == mx.MXFP4_ERR_NULL
+    assert _q(lib, o=None) == mx.MXFP4_ERR_NULL
+    assert _q(lib, K=48) == mx.MXFP4_ERR_SHAPE
+    assert _q(lib, K=0) == mx.MXFP4_ERR_SHAPE
+    assert _q(lib, K=-32) == mx.MXFP4_ERR_SHAPE
+    assert _q(lib, M=-1) == mx.MXFP4_ERR_SHAPE
+    assert _q(lib, G=0) == mx.MXFP4_ERR_SHAPE
+    assert _q(lib, M=1 << 40, K=1 << 20) == mx.MXFP4_ERR_SHAPE
+    assert _q(lib, x=A + 2) == mx.MXFP4_ERR_ALIGN
+    assert _q(lib, c=A2 + 8) == mx.MXFP4_ERR_ALIGN
+    assert _q(lib, s=A3 + 1) == mx.MXFP4_ERR_ALIGN
+    assert _q(lib, o=OFFS + 2) == mx.MXFP4_ERR_ALIGN
+    # K = 32 is legal for the quantizer; M_cap = 0 enqueues nothing and succeeds
+    assert _q(lib, M=0, K=32) == mx.MXFP4_OK
+
+
+@pytest.mark.parametrize("fn", ["mxfp4_to_fp8_rows", "mxfp4_to_fp8_cols_ragged"])
+def test_conversion_argument_errors(lib, fn):
+    for kw in ("c", "s", "y", "ys", "o"):
+        assert _r(lib, fn, **{kw: None}) == mx.MXFP4_ERR_NULL
+    assert _r(lib, fn, K=64) == mx.MXFP4_ERR_SHAPE      # conversions need K % 128 == 0
+    assert _r(lib, fn, K=0) == mx.MXFP4_ERR_SHAPE
+    assert _r(lib, fn, M=-5) == mx.MXFP4_ERR_SHAPE
+    assert _r(lib, fn, G=-1) == mx.MXFP4_ERR_SHAPE
+    assert _r(lib, fn, M=(1 << 31), K=128) == mx.MXFP4_ERR_SHAPE
+    assert _r(lib, fn, c=A + 4) == mx.MXFP4_ERR_ALIGN
+    assert _r(lib, fn, y=A3 + 1) == mx.MXFP4_ERR_ALIGN
+    assert _r(lib, fn, ys=A4 + 3) == mx.MXFP4_ERR_ALIGN
+    assert _r(lib, fn, o=OFFS + 1) == mx.MXFP4_ERR_ALIGN
+    assert _r(lib, fn, M=0) == mx.MXFP4_OK
+
+
+def test_validate_offsets_argument_errors(lib):
+    assert lib.mxfp4_validate_offsets(None, 1, 4, None) == mx.MXFP4_ERR_NULL
+    assert lib.mxfp4_validate_offsets(OFFS, 0, 4, None) == mx.MXFP4_ERR_SHAPE
+    assert lib.mxfp4_validate_offsets(OFFS, 1, -1, None) == mx.MXFP4_ERR_SHAPE
+
+
+def test_python_binding_raises_on_error_status():
+    class Fake:
+        def __init__(self, ptr, shape):
+            self._p, self.shape = ptr, shape
+
+        def data_ptr(self):
+            return self._p
+
+        def numel(self):
+            return self.shape[0]
+
+    x = Fake(A + 2, (4, 64))
+    with pytest.raises(mx.Mxfp4Error) as ei:
+        mx.mxfp4_quantize_rows(x, Fake(A2, (4, 32)), Fake(A3, (4, 2)), Fake(OFFS, (2,)), stream=0)
+    assert ei.value.status == mx.MXFP4_ERR_ALIGN
+
+
+def test_product_package_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "block_scaled_precision_bf16tofp4row_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "oracle.c" not in text, f
