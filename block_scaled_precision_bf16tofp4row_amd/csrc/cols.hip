@@ -61,40 +61,69 @@ __device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t 
     o3 = perm(u1, t1, 0x07060302u);
 }
 
-// Which expert owns global row-block B?  Every wave computes this on its own (no
-// barrier): lanes take 64 experts at a time, scan their block counts and ballot.
-// Returns false when B is past the last block.
-__device__ __forceinline__ bool find_block(const int32_t* __restrict__ offs, int G, uint32_t B,
-                                           int& g_out, uint32_t& Bg_out)
+// Which expert owns global strip index Sidx (each expert's row blocks are cut into
+// strips of kStrip consecutive blocks)?  Every wave computes this on its own (no
+// barrier): lanes take 64 experts at a time and scan both their block counts and
+// their strip counts, then ballot.  Returns false when Sidx is past the last strip.
+template <int kStrip>
+__device__ __forceinline__ bool find_strip(const int32_t* __restrict__ offs, int G, uint32_t Sidx,
+                                           int& g_out, uint32_t& Bg_out, uint32_t& Sg_out)
 {
     const int lane = threadIdx.x & 63;
-    uint32_t run = 0;
+    uint32_t run_b = 0, run_s = 0;
     for (int g0 = 0; g0 < G; g0 += 64) {
         int h = g0 + lane;
         uint32_t nb = 0;
         if (h < G)
             nb = (uint32_t)(offs[h + 1] - offs[h] + 127) >> 7;
-        uint32_t incl = nb;
+        uint32_t ns = (nb + kStrip - 1) / kStrip;
+        uint32_t ib = nb, is = ns;
 #pragma unroll
         for (int dlt = 1; dlt < 64; dlt <<= 1) {
-            uint32_t o = __shfl_up(incl, dlt, 64);
-            if (lane >= dlt)
-                incl += o;
+            uint32_t ob = __shfl_up(ib, dlt, 64);
+            uint32_t os = __shfl_up(is, dlt, 64);
+            if (lane >= dlt) {
+                ib += ob;
+                is += os;
+            }
         }
-        uint32_t lo = run + incl - nb;
-        bool mine = h < G && nb > 0 && B >= lo && B < run + incl;
+        uint32_t lo_s = run_s + is - ns;
+        bool mine = h < G && ns > 0 && Sidx >= lo_s && Sidx < run_s + is;
         uint64_t mask = __ballot(mine);
         if (mask) {
             int src = __builtin_ctzll(mask);
             g_out = g0 + src;
-            Bg_out = __shfl(lo, src, 64);
+            Bg_out = __shfl(run_b + ib - nb, src, 64);
+            Sg_out = __shfl(lo_s, src, 64);
             return true;
         }
-        run += __shfl(incl, 63, 64);
+        run_b += __shfl(ib, 63, 64);
+        run_s += __shfl(is, 63, 64);
     }
     return false;
 }
 
+struct StageA {
+    u32x4 ca, cb;     // 64 codes of one row: groups 2h and 2h+1 of the tile
+    uint32_t s2;      // their two MX scale bytes
+};
+
+// Row m of block b of the expert starting at row0 (nothing is read past the expert).
+__device__ __forceinline__ StageA load_rows(const uint8_t* __restrict__ codes,
+                                            const uint8_t* __restrict__ scales, int64_t row,
+                                            bool valid, int64_t K, int64_t k0, int h)
+{
+    StageA a{{0, 0, 0, 0}, {0, 0, 0, 0}, 0};
+    if (valid) {
+        const u32x4* cp = reinterpret_cast<const u32x4*>(codes + row * (K / 2) + k0 / 2 + 32 * h);
+        a.ca = cp[0];
+        a.cb = cp[1];
+        a.s2 = *reinterpret_cast<const uint16_t*>(scales + row * (K / 32) + k0 / 32 + 2 * h);
+    }
+    return a;
+}
+
+template <int kStrip>
 __global__ __launch_bounds__(kThreads) void fp8_cols_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     uint8_t* __restrict__ yT, uint8_t* __restrict__ yT_scales,
@@ -102,120 +131,132 @@ __global__ __launch_bounds__(kThreads) void fp8_cols_kernel(
 {
     __shared__ uint32_t tile[kTileRows * kTileCols / 4];
     __shared__ uint32_t lut[2 * (kMaxGap + 1)];
-    __shared__ uint32_t wave_max[4];
+    __shared__ uint32_t wave_max[2][4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const uint32_t nkt = (uint32_t)(K / kTileCols);
     const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
-    const uint32_t B = L / nkt;
+    const uint32_t Sidx = L / nkt;
     const uint32_t kt = L % nkt;
 
     int g;
-    uint32_t Bg;
-    if (!find_block(offs, G, B, g, Bg))
-        return;                                   // uniform: every wave sees the same B
+    uint32_t Bg, Sg;
+    if (!find_strip<kStrip>(offs, G, Sidx, g, Bg, Sg))
+        return;                                   // uniform: every wave sees the same Sidx
     const int64_t row0 = offs[g];
     const int64_t Mg = (int64_t)offs[g + 1] - row0;
-    const uint32_t b = B - Bg;
-    const int nr = (int)min<int64_t>(kTileRows, Mg - (int64_t)kTileRows * b);
+    const uint32_t nb_g = (uint32_t)((Mg + kTileRows - 1) / kTileRows);
+    const uint32_t b0 = (Sidx - Sg) * kStrip;
+    const uint32_t nblk = min((uint32_t)kStrip, nb_g - b0);
     const int64_t k0 = (int64_t)kt * kTileCols;
 
     if (tid < 2 * (kMaxGap + 1))
         lut[tid] = kColsGapLut.w[tid >> 1][tid & 1];
 
-    // ---- stage A: load, block scale, convert, row-major into LDS -------------------
     const int h = tid >> 7;                       // column half: groups 2h, 2h+1
     const int m = tid & 127;
-    const bool valid = m < nr;
-    const int64_t row = row0 + (int64_t)kTileRows * b + m;
-    u32x4 ca = {0, 0, 0, 0}, cb = {0, 0, 0, 0};
-    uint32_t s2 = 0;
-    if (valid) {
-        const u32x4* cp = reinterpret_cast<const u32x4*>(codes + row * (K / 2) + k0 / 2 + 32 * h);
-        ca = load_stream(cp);
-        cb = load_stream(cp + 1);
-        s2 = *reinterpret_cast<const uint16_t*>(scales + row * (K / 32) + k0 / 32 + 2 * h);
-    }
-    // max over the wave's 64 rows of both scale bytes, packed as two u16 lanes
-    uint32_t pk = (s2 & 0xFFu) | ((s2 & 0xFF00u) << 8);
-#pragma unroll
-    for (int dlt = 32; dlt >= 1; dlt >>= 1) {
-        uint32_t o = __shfl_xor(pk, dlt, 64);
-        u16x2 a = __builtin_bit_cast(u16x2, pk), c = __builtin_bit_cast(u16x2, o);
-        pk = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, c));
-    }
-    if (lane == 0)
-        wave_max[wave] = pk;
-    __syncthreads();
-    // waves 2h and 2h+1 hold rows 0..63 and 64..127 of column half h
-    u16x2 wm = __builtin_elementwise_max(__builtin_bit_cast(u16x2, wave_max[2 * h]),
-                                         __builtin_bit_cast(u16x2, wave_max[2 * h + 1]));
-    const uint32_t Sa = wm.x, Sb = wm.y;
-    {
-        uint32_t da = min(Sa - (s2 & 0xFFu), (uint32_t)kMaxGap);
-        uint32_t db = min(Sb - (s2 >> 8), (uint32_t)kMaxGap);
-        uint32_t la0 = lut[2 * da], la1 = lut[2 * da + 1];
-        uint32_t lb0 = lut[2 * db], lb1 = lut[2 * db + 1];
-        u32x2 p0 = convert8(ca.x, la0, la1), p1 = convert8(ca.y, la0, la1);
-        u32x2 p2 = convert8(ca.z, la0, la1), p3 = convert8(ca.w, la0, la1);
-        u32x2 p4 = convert8(cb.x, lb0, lb1), p5 = convert8(cb.y, lb0, lb1);
-        u32x2 p6 = convert8(cb.z, lb0, lb1), p7 = convert8(cb.w, lb0, lb1);
-        u32x4 o0 = {p0.x, p0.y, p1.x, p1.y}, o1 = {p2.x, p2.y, p3.x, p3.y};
-        u32x4 o2 = {p4.x, p4.y, p5.x, p5.y}, o3 = {p6.x, p6.y, p7.x, p7.y};
-        const uint32_t r = (uint32_t)m, c0 = 4u * h;
-        *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 0, 0)]) = o0;
-        *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 1, 0)]) = o1;
-        *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 2, 0)]) = o2;
-        *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 3, 0)]) = o3;
-    }
-    __syncthreads();
+    const uint32_t mb = lane & 7;                 // stage B: rows 16mb..16mb+15
+    const uint32_t kq = 8u * wave + (lane >> 3);  // stage B: columns 4kq..4kq+3
+    uint8_t* const outT0 = yT + K * row0 + 16 * mb;
 
-    // ---- block scales of this tile: 128 bytes, S of group (k / 32) ------------------
-    uint8_t* outS = yT_scales + K * (int64_t)(Bg + b) + k0;
-    if (tid < 8) {
-        int grp = tid >> 1;                       // 16 bytes per thread, two threads per group
-        u16x2 hm = __builtin_elementwise_max(__builtin_bit_cast(u16x2, wave_max[2 * (grp >> 1)]),
-                                             __builtin_bit_cast(u16x2, wave_max[2 * (grp >> 1) + 1]));
-        uint32_t S = (grp & 1) ? hm.y : hm.x;
-        uint32_t w4 = S * 0x01010101u;
-        *reinterpret_cast<u32x4*>(outS + 16 * tid) = u32x4{w4, w4, w4, w4};
-    }
+    StageA nxt = load_rows(codes, scales, row0 + (int64_t)kTileRows * b0 + m,
+                           (int64_t)kTileRows * b0 + m < Mg, K, k0, h);
+    for (uint32_t i = 0; i < nblk; ++i) {
+        const uint32_t b = b0 + i;
+        const int nr = (int)min<int64_t>(kTileRows, Mg - (int64_t)kTileRows * b);
+        const StageA cur = nxt;
+        if (i + 1 < nblk)                          // prefetch the next block of the strip
+            nxt = load_rows(codes, scales, row0 + (int64_t)kTileRows * (b + 1) + m,
+                            (int64_t)kTileRows * (b + 1) + m < Mg, K, k0, h);
 
-    // ---- stage B: 16 rows x 4 columns per thread, transposed, stored along m -------
-    const uint32_t mb = lane & 7;
-    const uint32_t kq = 8u * wave + (lane >> 3);
-    uint32_t R[16];
+        // ---- stage A: block scales, convert, row-major into LDS ----------------------
+        uint32_t pk = (cur.s2 & 0xFFu) | ((cur.s2 & 0xFF00u) << 8);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        R[i] = tile[lds_dword(16u * mb + i, kq >> 2, kq & 3)];
-    uint32_t T[4][4];                             // T[r][kk]: rows 4r..4r+3 of column 4kq+kk
+        for (int dlt = 32; dlt >= 1; dlt >>= 1) {
+            uint32_t o = __shfl_xor(pk, dlt, 64);
+            pk = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, pk),
+                                                                        __builtin_bit_cast(u16x2, o)));
+        }
+        if (lane == 0)
+            wave_max[i & 1][wave] = pk;
+        __syncthreads();                          // wave maxima visible; previous stage B done
+        // waves 2h and 2h+1 hold rows 0..63 and 64..127 of column half h
+        const u16x2 wm = __builtin_elementwise_max(__builtin_bit_cast(u16x2, wave_max[i & 1][2 * h]),
+                                                   __builtin_bit_cast(u16x2, wave_max[i & 1][2 * h + 1]));
+        {
+            uint32_t da = min((uint32_t)wm.x - (cur.s2 & 0xFFu), (uint32_t)kMaxGap);
+            uint32_t db = min((uint32_t)wm.y - (cur.s2 >> 8), (uint32_t)kMaxGap);
+            uint32_t la0 = lut[2 * da], la1 = lut[2 * da + 1];
+            uint32_t lb0 = lut[2 * db], lb1 = lut[2 * db + 1];
+            u32x2 p0 = convert8(cur.ca.x, la0, la1), p1 = convert8(cur.ca.y, la0, la1);
+            u32x2 p2 = convert8(cur.ca.z, la0, la1), p3 = convert8(cur.ca.w, la0, la1);
+            u32x2 p4 = convert8(cur.cb.x, lb0, lb1), p5 = convert8(cur.cb.y, lb0, lb1);
+            u32x2 p6 = convert8(cur.cb.z, lb0, lb1), p7 = convert8(cur.cb.w, lb0, lb1);
+            const uint32_t r = (uint32_t)m, c0 = 4u * h;
+            *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 0, 0)]) = u32x4{p0.x, p0.y, p1.x, p1.y};
+            *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 1, 0)]) = u32x4{p2.x, p2.y, p3.x, p3.y};
+            *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 2, 0)]) = u32x4{p4.x, p4.y, p5.x, p5.y};
+            *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 3, 0)]) = u32x4{p6.x, p6.y, p7.x, p7.y};
+        }
+        __syncthreads();                          // tile complete
+
+        // ---- block scales of this block: 128 bytes, S of group k / 32 -----------------
+        if (tid < 8) {
+            const int grp = tid >> 1;             // 16 bytes per thread, two threads per group
+            const u16x2 hm = __builtin_elementwise_max(
+                __builtin_bit_cast(u16x2, wave_max[i & 1][2 * (grp >> 1)]),
+                __builtin_bit_cast(u16x2, wave_max[i & 1][2 * (grp >> 1) + 1]));
+            const uint32_t w4 = ((grp & 1) ? (uint32_t)hm.y : (uint32_t)hm.x) * 0x01010101u;
+            *reinterpret_cast<u32x4*>(yT_scales + K * (int64_t)(Bg + b) + k0 + 16 * tid) =
+                u32x4{w4, w4, w4, w4};
+        }
+
+        // ---- stage B: 16 rows x 4 columns per thread, transposed, stored along m ------
+        uint32_t R[16];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-        transpose4x4(R[4 * r4], R[4 * r4 + 1], R[4 * r4 + 2], R[4 * r4 + 3],
-                     T[r4][0], T[r4][1], T[r4][2], T[r4][3]);
-    const int nvalid = nr - 16 * (int)mb;         // rows of this thread's 16 that exist
-    if (nvalid <= 0)
-        return;
-    uint8_t* outT = yT + K * row0 + (int64_t)kTileRows * b + 16 * mb;
+        for (int j = 0; j < 16; ++j)
+            R[j] = tile[lds_dword(16u * mb + j, kq >> 2, kq & 3)];
+        uint32_t T[4][4];                         // T[r][kk]: rows 4r..4r+3 of column 4kq+kk
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        uint8_t* dst = outT + (k0 + 4 * kq + kk) * Mg;
-        u32x4 v = {T[0][kk], T[1][kk], T[2][kk], T[3][kk]};
-        if (nvalid >= 16) {
-            *reinterpret_cast<u32x4_unaligned*>(dst) = v;
-        } else {
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            for (int i = 0; i < nvalid; ++i)
-                dst[i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+        for (int r4 = 0; r4 < 4; ++r4)
+            transpose4x4(R[4 * r4], R[4 * r4 + 1], R[4 * r4 + 2], R[4 * r4 + 3],
+                         T[r4][0], T[r4][1], T[r4][2], T[r4][3]);
+        const int nvalid = nr - 16 * (int)mb;     // rows of this thread's 16 that exist
+        if (nvalid > 0) {
+            uint8_t* outT = outT0 + (int64_t)kTileRows * b;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                uint8_t* dst = outT + (k0 + 4 * kq + kk) * Mg;
+                u32x4 v = {T[0][kk], T[1][kk], T[2][kk], T[3][kk]};
+                if (nvalid >= 16) {
+                    *reinterpret_cast<u32x4_unaligned*>(dst) = v;
+                } else {
+                    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                    for (int q = 0; q < nvalid; ++q)
+                        dst[q] = (uint8_t)(w[q >> 2] >> (8 * (q & 3)));
+                }
+            }
         }
     }
 }
 
+#ifndef MXFP4_COLS_STRIP
+#define MXFP4_COLS_STRIP 2
+#endif
+// consecutive 128-row blocks one workgroup converts for its column tile
+constexpr int kColsStrip = MXFP4_COLS_STRIP;
+
 int64_t cols_block_capacity(int64_t M_cap, int32_t G)
 {
     return (M_cap + kTileRows - 1) / kTileRows + G;
+}
+
+// Strips of kColsStrip blocks over all experts: at most ceil(M_cap / (128 kStrip)) + G.
+static int64_t cols_strip_capacity(int64_t M_cap, int32_t G)
+{
+    return (M_cap + kTileRows * kColsStrip - 1) / (kTileRows * kColsStrip) + G;
 }
 
 hipError_t launch_fp8_cols(const uint8_t* codes, const uint8_t* scales, uint8_t* yT,
@@ -223,7 +264,7 @@ hipError_t launch_fp8_cols(const uint8_t* codes, const uint8_t* scales, uint8_t*
                            int64_t K, hipStream_t stream)
 {
     int64_t nkt = K / kTileCols;
-    int64_t grid = cols_block_capacity(M_cap, G) * nkt;
+    int64_t grid = cols_strip_capacity(M_cap, G) * nkt;
     if (M_cap == 0)
         return hipSuccess;
     if (grid > 0x7FFFFFFF)
@@ -232,8 +273,8 @@ hipError_t launch_fp8_cols(const uint8_t* codes, const uint8_t* scales, uint8_t*
     int64_t k = K;
     void* args[] = {(void*)&codes, (void*)&scales, (void*)&yT, (void*)&yT_scales, (void*)&offs,
                     (void*)&g, (void*)&k};
-    return hipLaunchKernel((const void*)fp8_cols_kernel, dim3((unsigned)grid), dim3(kThreads), args,
-                           0, stream);
+    return hipLaunchKernel((const void*)fp8_cols_kernel<kColsStrip>, dim3((unsigned)grid),
+                           dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace mxfp4

@@ -6,7 +6,8 @@
 // E2M1 elements) and item 2 (activations quantized before the all-to-all and packed
 // into uint8 containers); the kernel is the page's BF16ToFP4Row (item 3), rebuilt
 // for gfx950.  Scale rule and rounding follow OCP MX v1.0 section 6.3: shared
-// exponent floor(log2 amax) - 2, E2M1 round-to-nearest-even, saturating at 6.
+// exponent floor(log2 amax) - 2, E2M1 round-to-nearest-even, saturating at 6; the
+// element conversion is gfx950's scaled FP4 convert instruction.
 //
 // Layout: because K is a multiple of 32, a 32-element block never crosses a row, so
 // the [M, K] matrix is a flat stream of blocks: block b reads input bytes
@@ -18,31 +19,34 @@
 
 namespace mxfp4 {
 
-// E2M1 magnitude code of one BF16 magnitude `mag` (15 bits) in a block with scale
-// byte s, i.e. of y = |x| * 2^(127 - s), which lies in [0, 8) because s comes from
-// the block amax.  With sig the 8-bit significand (implicit bit included for
-// normals) and q = log2 of the E2M1 spacing at y (-1 below 2, 0 in [2, 4), 1 in
-// [4, 8)), y / 2^q = sig >> r for r = 7 + q - (exp - s); rounding that to the
-// nearest integer n (ties to even) gives code n + 2(q + 1), which saturates at 7.
-__device__ __forceinline__ uint32_t e2m1_code(uint32_t mag, int s)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Reinterpret a dword as two BF16.  (A __builtin_bit_cast applied directly to an
+// ext_vector element such as v.y is lowered as if it named v.x by this compiler, so
+// every operand goes through a scalar copy.)
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u)
 {
-    int e = (int)(mag >> 7);
-    bool normal = e != 0;
-    uint32_t sig = (mag & 0x7Fu) | (normal ? 0x80u : 0u);
-    int q = normal ? min(max(e - s - 1, -1), 1) : -1;
-    int r = 7 + q - ((normal ? e : 1) - s);
-    r = min(r, 9);                           // sig < 256: any shift >= 9 rounds to 0
-    uint32_t n = (sig + (1u << (r - 1)) - 1u + ((sig >> r) & 1u)) >> r;
-    return min(n + (uint32_t)(2 * (q + 1)), 7u);
+    bf16x2 r;
+    __builtin_memcpy(&r, &u, sizeof(r));
+    return r;
 }
 
-// Codes of two BF16 in one dword -> one byte (low nibble = low half).
-__device__ __forceinline__ uint32_t encode_pair(uint32_t w, int s)
+// Eight BF16 (one 16-byte chunk) -> eight E2M1 codes packed in one dword.
+// v_cvt_scalef32_pk_fp4_bf16 converts two BF16 to two E2M1 codes of x / scale with
+// round-to-nearest-even and saturation at +-6, keeping the sign (also of zero); the
+// low BF16 goes to the low nibble and the byte-select operand picks the destination
+// byte, leaving the others as they were.  The scale operand is the fp32 whose
+// exponent field is the UE8M0 byte s (only the exponent is used, so s = 0 means
+// 2^-127).  This was checked against the oracle for every BF16 pattern and every
+// scale byte 0..254.
+__device__ __forceinline__ uint32_t encode8(u32x4 v, int s)
 {
-    uint32_t lo = w & 0xFFFFu, hi = w >> 16;
-    uint32_t c0 = e2m1_code(lo & 0x7FFFu, s) | ((lo >> 12) & 8u);
-    uint32_t c1 = e2m1_code(hi & 0x7FFFu, s) | ((hi >> 12) & 8u);
-    return c0 | (c1 << 4);
+    const float scale = __uint_as_float((uint32_t)s << 23);
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, as_bf16x2(v.x), scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, as_bf16x2(v.y), scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, as_bf16x2(v.z), scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, as_bf16x2(v.w), scale, 3);
+    return w;
 }
 
 __device__ __forceinline__ uint32_t amax_bits8(u32x4 v)
@@ -79,8 +83,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
         // the DPP exchange below never mixes valid and padding lanes of one block.
         uint32_t amax = quad_max_u32(amax_bits8(v[u]));
         int s = max((int)(amax >> 7) - 2, 0);          // biased exponent field - emax(E2M1)
-        uint32_t word = encode_pair(v[u].x, s) | (encode_pair(v[u].y, s) << 8) |
-                        (encode_pair(v[u].z, s) << 16) | (encode_pair(v[u].w, s) << 24);
+        uint32_t word = encode8(v[u], s);
         if (idx < nchunks) {
             store_stream(codes + idx, word);
             if ((tid & 3) == 0)
@@ -89,7 +92,11 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(
     }
 }
 
-constexpr int kQuantU = 4;
+#ifndef MXFP4_QUANT_UNROLL
+#define MXFP4_QUANT_UNROLL 4
+#endif
+// 16-byte chunks per thread (all loads issued before any conversion)
+constexpr int kQuantU = MXFP4_QUANT_UNROLL;
 
 hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* codes, uint8_t* scales,
                                 const int32_t* offs, int32_t G, int64_t M_cap, int64_t K,

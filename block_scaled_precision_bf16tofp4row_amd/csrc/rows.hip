@@ -67,7 +67,11 @@ __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(
     }
 }
 
-constexpr int kRowsU = 4;
+#ifndef MXFP4_ROWS_UNROLL
+#define MXFP4_ROWS_UNROLL 4
+#endif
+// 8-byte code units per thread (all loads issued before any conversion)
+constexpr int kRowsU = MXFP4_ROWS_UNROLL;
 
 hipError_t launch_fp8_rows(const uint8_t* codes, const uint8_t* scales, uint8_t* y,
                            uint8_t* y_scales, const int32_t* offs, int32_t G, int64_t M_cap,
