@@ -16,20 +16,27 @@
 // (k, m') at k*M_g + m'.  Its block scales [nb_g, K] start at byte K*B_g, B_g the
 // number of 128-row blocks of experts 0..g-1 (nb_h = ceil(M_h / 128)).
 //
-// Tile = one 128-row block of one expert x 128 columns, 256 threads:
-//   stage A  thread (h = t>>7, m = t&127) loads 32 code bytes of row m (columns
-//            64h..64h+63) and its two MX scales; a wave max + LDS gives the four
-//            per-group block scales; the 64 codes are converted with the gap table
-//            and written row-major (128 B per row) into a 16 KiB LDS tile;
-//   stage B  thread (mb = l&7, kq = 8w + l>>3) reads a 16-row x 4-column patch as
-//            16 dwords, transposes it in registers with v_perm_b32 (4x4 byte
-//            transposes) and stores four 16-byte runs along m; lanes 8i..8i+7 cover
-//            one contiguous 128-byte output row segment.
-// LDS skew: 16-byte chunk c of logical row r lives at physical row P(r), chunk
-// c ^ f(r), with f(r) = (r ^ (r>>4)) & 7 and P(r) = r ^ (((r>>3) ^ (r>>4)) & 1).
-// Stage A's 16-byte writes (16 consecutive rows, one chunk) and stage B's dword
-// reads (8 row groups x 8 columns) then hit distinct banks for both a 32-bank and a
-// 64-bank LDS.
+// Tile = 128 columns (four MX groups) x a strip of up to 256 rows (two FP8 blocks) of
+// one expert, 256 threads:
+//   stage A  thread (kc = lane & 3, rq) loads the 16 code bytes of group kc for rows
+//            4rq..4rq+3 and their MX scale bytes; four consecutive lanes cover one row's
+//            64 contiguous code bytes and 4 contiguous scale bytes.  The FP8 scale of
+//            each (128-row block, group) is a DPP / cross-lane max inside the wave and
+//            an LDS exchange between the block's two waves.  Each row is converted with
+//            the gap table of its own scale, then 4x4 byte transposes (v_perm_b32) turn
+//            4 rows x 32 columns into 32 dwords (4 rows of one column each), written
+//            into an LDS tile that is k-major: one LDS row per output column k, holding
+//            that column's 256 strip bytes in output order;
+//   stage B  16 lanes per output row: lane c stores the 16-byte aligned chunk c of the
+//            strip's output range [A, A + nrows).  The range's misalignment delta =
+//            A & 15 becomes an unaligned 16-byte LDS read (gfx950 reads LDS at any
+//            byte address), so every global store is an aligned 16-byte store and 16
+//            lanes cover one contiguous 256-byte run.  Only the first and last chunk
+//            of a strip can be partial; they are written one byte per lane.
+// LDS skew: the tile row of column k starts at byte 288k + 64 (k >> 5); 32 rows of 288
+// bytes span a whole number of bank cycles, so the 64-byte shift per MX group puts the
+// stage-A dword writes of the four groups (16 rows each per wave) in 64 distinct
+// banks.  This plays the role of the page's padded, skewed shared-memory layout.
 #include "common.h"
 
 namespace mxfp4 {
@@ -37,16 +44,6 @@ namespace mxfp4 {
 __constant__ GapLut kColsGapLut = make_gap_lut();
 
 constexpr int kTileRows = 128;
-constexpr int kTileCols = 128;
-
-__device__ __forceinline__ uint32_t skew_f(uint32_t r) { return (r ^ (r >> 4)) & 7u; }
-__device__ __forceinline__ uint32_t skew_p(uint32_t r) { return r ^ (((r >> 3) ^ (r >> 4)) & 1u); }
-// dword index of (logical row r, 16-byte chunk c, dword w in the chunk)
-__device__ __forceinline__ uint32_t lds_dword(uint32_t r, uint32_t c, uint32_t w)
-{
-    return skew_p(r) * 32u + ((c ^ skew_f(r)) << 2) + w;
-}
-
 // 4x4 byte transpose: a[i] holds bytes (row i, col 0..3); o[j] gets bytes (row 0..3, col j).
 __device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
                                              uint32_t& o0, uint32_t& o1, uint32_t& o2, uint32_t& o3)
@@ -103,39 +100,34 @@ __device__ __forceinline__ bool find_strip(const int32_t* __restrict__ offs, int
     return false;
 }
 
-struct StageA {
-    u32x4 ca, cb;     // 64 codes of one row: groups 2h and 2h+1 of the tile
-    uint32_t s2;      // their two MX scale bytes
-};
+// ---- tile geometry -------------------------------------------------------------------
+constexpr int kTileCols = 128;                        // four MX groups
+constexpr int kStripRows = 256;                       // two FP8 row blocks
+constexpr int kStripBlocks = kStripRows / kTileRows;
+constexpr int kLdsRowBytes = 16 + kStripRows + 16;    // front pad, data, back pad
+constexpr int kLdsBytes = kTileCols * kLdsRowBytes + 64 * 3;
+static_assert(kStripRows == 4 * 64, "stage A maps 64 quads of rows over the 4 waves");
+static_assert((32 * (kLdsRowBytes / 4)) % 64 == 0, "32 tile rows must span a multiple of 64 banks");
 
-// Row m of block b of the expert starting at row0 (nothing is read past the expert).
-__device__ __forceinline__ StageA load_rows(const uint8_t* __restrict__ codes,
-                                            const uint8_t* __restrict__ scales, int64_t row,
-                                            bool valid, int64_t K, int64_t k0, int h)
+__device__ __forceinline__ uint32_t lds_row(uint32_t k) { return kLdsRowBytes * k + 64 * (k >> 5); }
+
+__device__ __forceinline__ uint32_t u16max2(uint32_t a, uint32_t b)
 {
-    StageA a{{0, 0, 0, 0}, {0, 0, 0, 0}, 0};
-    if (valid) {
-        const u32x4* cp = reinterpret_cast<const u32x4*>(codes + row * (K / 2) + k0 / 2 + 32 * h);
-        a.ca = cp[0];
-        a.cb = cp[1];
-        a.s2 = *reinterpret_cast<const uint16_t*>(scales + row * (K / 32) + k0 / 32 + 2 * h);
-    }
-    return a;
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
 }
 
-template <int kStrip>
 __global__ __launch_bounds__(kThreads) void fp8_cols_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     uint8_t* __restrict__ yT, uint8_t* __restrict__ yT_scales,
     const int32_t* __restrict__ offs, int G, int64_t K)
 {
-    __shared__ uint32_t tile[kTileRows * kTileCols / 4];
-    __shared__ uint32_t lut[2 * (kMaxGap + 1)];
-    __shared__ uint32_t wave_max[2][4];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kLdsBytes];
+    __shared__ uint32_t wave_max[4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const uint32_t nkt = (uint32_t)(K / kTileCols);
     const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
     const uint32_t Sidx = L / nkt;
@@ -143,128 +135,122 @@ __global__ __launch_bounds__(kThreads) void fp8_cols_kernel(
 
     int g;
     uint32_t Bg, Sg;
-    if (!find_strip<kStrip>(offs, G, Sidx, g, Bg, Sg))
-        return;                                   // uniform: every wave sees the same Sidx
+    if (!find_strip<kStripBlocks>(offs, G, Sidx, g, Bg, Sg))
+        return;                                      // uniform: every wave sees the same Sidx
     const int64_t row0 = offs[g];
     const int64_t Mg = (int64_t)offs[g + 1] - row0;
-    const uint32_t nb_g = (uint32_t)((Mg + kTileRows - 1) / kTileRows);
-    const uint32_t b0 = (Sidx - Sg) * kStrip;
-    const uint32_t nblk = min((uint32_t)kStrip, nb_g - b0);
-    const int64_t k0 = (int64_t)kt * kTileCols;
+    const int64_t r_lo = (int64_t)(Sidx - Sg) * kStripRows;   // strip start, relative to row0
+    const int nrows = (int)min<int64_t>(kStripRows, Mg - r_lo);
 
-    if (tid < 2 * (kMaxGap + 1))
-        lut[tid] = kColsGapLut.w[tid >> 1][tid & 1];
-
-    const int h = tid >> 7;                       // column half: groups 2h, 2h+1
-    const int m = tid & 127;
-    const uint32_t mb = lane & 7;                 // stage B: rows 16mb..16mb+15
-    const uint32_t kq = 8u * wave + (lane >> 3);  // stage B: columns 4kq..4kq+3
-    uint8_t* const outT0 = yT + K * row0 + 16 * mb;
-
-    StageA nxt = load_rows(codes, scales, row0 + (int64_t)kTileRows * b0 + m,
-                           (int64_t)kTileRows * b0 + m < Mg, K, k0, h);
-    for (uint32_t i = 0; i < nblk; ++i) {
-        const uint32_t b = b0 + i;
-        const int nr = (int)min<int64_t>(kTileRows, Mg - (int64_t)kTileRows * b);
-        const StageA cur = nxt;
-        if (i + 1 < nblk)                          // prefetch the next block of the strip
-            nxt = load_rows(codes, scales, row0 + (int64_t)kTileRows * (b + 1) + m,
-                            (int64_t)kTileRows * (b + 1) + m < Mg, K, k0, h);
-
-        // ---- stage A: block scales, convert, row-major into LDS ----------------------
-        uint32_t pk = (cur.s2 & 0xFFu) | ((cur.s2 & 0xFF00u) << 8);
+    // ---- stage A -----------------------------------------------------------------------
+    const int kc = lane & 3;                         // MX group inside the tile
+    const int rq = (lane >> 2) + 16 * wave;          // rows 4rq..4rq+3 of the strip
+    const int64_t rbase = row0 + r_lo + 4 * rq;
+    u32x4 c4[4];
+    uint32_t s[4];
 #pragma unroll
-        for (int dlt = 32; dlt >= 1; dlt >>= 1) {
-            uint32_t o = __shfl_xor(pk, dlt, 64);
-            pk = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, pk),
-                                                                        __builtin_bit_cast(u16x2, o)));
-        }
-        if (lane == 0)
-            wave_max[i & 1][wave] = pk;
-        __syncthreads();                          // wave maxima visible; previous stage B done
-        // waves 2h and 2h+1 hold rows 0..63 and 64..127 of column half h
-        const u16x2 wm = __builtin_elementwise_max(__builtin_bit_cast(u16x2, wave_max[i & 1][2 * h]),
-                                                   __builtin_bit_cast(u16x2, wave_max[i & 1][2 * h + 1]));
-        {
-            uint32_t da = min((uint32_t)wm.x - (cur.s2 & 0xFFu), (uint32_t)kMaxGap);
-            uint32_t db = min((uint32_t)wm.y - (cur.s2 >> 8), (uint32_t)kMaxGap);
-            uint32_t la0 = lut[2 * da], la1 = lut[2 * da + 1];
-            uint32_t lb0 = lut[2 * db], lb1 = lut[2 * db + 1];
-            u32x2 p0 = convert8(cur.ca.x, la0, la1), p1 = convert8(cur.ca.y, la0, la1);
-            u32x2 p2 = convert8(cur.ca.z, la0, la1), p3 = convert8(cur.ca.w, la0, la1);
-            u32x2 p4 = convert8(cur.cb.x, lb0, lb1), p5 = convert8(cur.cb.y, lb0, lb1);
-            u32x2 p6 = convert8(cur.cb.z, lb0, lb1), p7 = convert8(cur.cb.w, lb0, lb1);
-            const uint32_t r = (uint32_t)m, c0 = 4u * h;
-            *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 0, 0)]) = u32x4{p0.x, p0.y, p1.x, p1.y};
-            *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 1, 0)]) = u32x4{p2.x, p2.y, p3.x, p3.y};
-            *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 2, 0)]) = u32x4{p4.x, p4.y, p5.x, p5.y};
-            *reinterpret_cast<u32x4*>(&tile[lds_dword(r, c0 + 3, 0)]) = u32x4{p6.x, p6.y, p7.x, p7.y};
-        }
-        __syncthreads();                          // tile complete
-
-        // ---- block scales of this block: 128 bytes, S of group k / 32 -----------------
-        if (tid < 8) {
-            const int grp = tid >> 1;             // 16 bytes per thread, two threads per group
-            const u16x2 hm = __builtin_elementwise_max(
-                __builtin_bit_cast(u16x2, wave_max[i & 1][2 * (grp >> 1)]),
-                __builtin_bit_cast(u16x2, wave_max[i & 1][2 * (grp >> 1) + 1]));
-            const uint32_t w4 = ((grp & 1) ? (uint32_t)hm.y : (uint32_t)hm.x) * 0x01010101u;
-            *reinterpret_cast<u32x4*>(yT_scales + K * (int64_t)(Bg + b) + k0 + 16 * tid) =
-                u32x4{w4, w4, w4, w4};
-        }
-
-        // ---- stage B: 16 rows x 4 columns per thread, transposed, stored along m ------
-        uint32_t R[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-            R[j] = tile[lds_dword(16u * mb + j, kq >> 2, kq & 3)];
-        uint32_t T[4][4];                         // T[r][kk]: rows 4r..4r+3 of column 4kq+kk
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-            transpose4x4(R[4 * r4], R[4 * r4 + 1], R[4 * r4 + 2], R[4 * r4 + 3],
-                         T[r4][0], T[r4][1], T[r4][2], T[r4][3]);
-        const int nvalid = nr - 16 * (int)mb;     // rows of this thread's 16 that exist
-        if (nvalid > 0) {
-            uint8_t* outT = outT0 + (int64_t)kTileRows * b;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                uint8_t* dst = outT + (k0 + 4 * kq + kk) * Mg;
-                u32x4 v = {T[0][kk], T[1][kk], T[2][kk], T[3][kk]};
-                if (nvalid >= 16) {
-                    *reinterpret_cast<u32x4_unaligned*>(dst) = v;
-                } else {
-                    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                    for (int q = 0; q < nvalid; ++q)
-                        dst[q] = (uint8_t)(w[q >> 2] >> (8 * (q & 3)));
-                }
-            }
+    for (int i = 0; i < 4; ++i) {
+        const bool ok = 4 * rq + i < nrows;
+        const int64_t row = rbase + i;
+        c4[i] = ok ? *reinterpret_cast<const u32x4*>(codes + row * (K / 2) + 64 * (int64_t)kt + 16 * kc)
+                   : u32x4{0, 0, 0, 0};
+        s[i] = ok ? (uint32_t)scales[row * (K / 32) + 4 * (int64_t)kt + kc] : 0u;
+    }
+    // max over the wave's 64 rows for each group: lanes kc, kc+4, ... (16 of them)
+    uint32_t m = max(max(s[0], s[1]), max(s[2], s[3]));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x124, 0xF, 0xF, false));  // row_ror:4
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x128, 0xF, 0xF, false));  // row_ror:8
+    m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+    // lanes 0..3 now hold groups 0..3; pack them as four bytes for the partner wave
+    const uint32_t packed = __builtin_amdgcn_readlane(m, 0) | (__builtin_amdgcn_readlane(m, 1) << 8) |
+                            (__builtin_amdgcn_readlane(m, 2) << 16) | (__builtin_amdgcn_readlane(m, 3) << 24);
+    if (lane == 0)
+        wave_max[wave] = packed;
+    __syncthreads();
+    // block 0 = waves 0, 1; block 1 = waves 2, 3
+    const uint32_t bmax = __builtin_amdgcn_readfirstlane(
+        __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+            __builtin_bit_cast(u8x4, wave_max[wave & 2]), __builtin_bit_cast(u8x4, wave_max[(wave & 2) + 1]))));
+    const uint32_t S = (bmax >> (8 * kc)) & 0xFF;
+    if (tid < 16) {                                  // block scales: 2 blocks x 128 columns
+        const int blk = tid >> 3, piece = tid & 7;
+        if (kTileRows * blk < nrows) {
+            const uint32_t both = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+                __builtin_bit_cast(u8x4, wave_max[2 * blk]), __builtin_bit_cast(u8x4, wave_max[2 * blk + 1])));
+            const uint32_t w4 = ((both >> (8 * (piece >> 1))) & 0xFF) * 0x01010101u;
+            *reinterpret_cast<u32x4*>(yT_scales + K * (int64_t)(Bg + r_lo / kTileRows + blk) +
+                                      kTileCols * (int64_t)kt + 16 * piece) = u32x4{w4, w4, w4, w4};
         }
     }
-}
+    uint32_t F[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t d = min(S - s[i], (uint32_t)kMaxGap);
+        const uint32_t lo = kColsGapLut.w[d][0], hi = kColsGapLut.w[d][1];
+        u32x2 p0 = convert8(c4[i].x, lo, hi), p1 = convert8(c4[i].y, lo, hi);
+        u32x2 p2 = convert8(c4[i].z, lo, hi), p3 = convert8(c4[i].w, lo, hi);
+        F[i][0] = p0.x; F[i][1] = p0.y; F[i][2] = p1.x; F[i][3] = p1.y;
+        F[i][4] = p2.x; F[i][5] = p2.y; F[i][6] = p3.x; F[i][7] = p3.y;
+    }
+    // column 32kc + 4q + kk: dword of rows 4rq..4rq+3 at strip byte 4rq of its LDS row
+    const uint32_t wbase = lds_row(32 * kc) + 16 + 4 * rq;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        uint32_t o[4];
+        transpose4x4(F[0][q], F[1][q], F[2][q], F[3][q], o[0], o[1], o[2], o[3]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            *reinterpret_cast<uint32_t*>(tile + wbase + kLdsRowBytes * (4 * q + kk)) = o[kk];
+    }
+    __syncthreads();
 
-#ifndef MXFP4_COLS_STRIP
-#define MXFP4_COLS_STRIP 2
-#endif
-// consecutive 128-row blocks one workgroup converts for its column tile
-constexpr int kColsStrip = MXFP4_COLS_STRIP;
+    // ---- stage B: 16 lanes per output row, 4 rows per step, 32 rows per wave ---------
+    // Output row k of expert g starts at byte K*offs[g] + k*M_g; the strip's bytes are
+    // [A, A + nrows) with A = that + r_lo.  Chunk c is memory [A - delta + 16c, +16)
+    // with delta = A & 15, i.e. strip bytes [16c - delta, 16c - delta + 16).
+    const int c = lane & 15;
+#pragma unroll 2
+    for (int it = 0; it < 8; ++it) {
+        const uint32_t kl = 32 * wave + 4 * it + (lane >> 4);
+        const int64_t A = K * row0 + (kTileCols * (int64_t)kt + kl) * Mg + r_lo;
+        const int delta = (int)(A & 15);
+        uint8_t* const C0 = yT + (A - delta);
+        const int c_first = delta > 0 ? 1 : 0;         // first full chunk
+        const int c_end = (delta + nrows) >> 4;         // one past the last full chunk
+        const uint8_t* rowp = tile + lds_row(kl) + 16 - delta;   // rowp[16c + p] = chunk byte p
+        if (c >= c_first && c < c_end)
+            *reinterpret_cast<u32x4*>(C0 + 16 * (int64_t)c) =
+                *reinterpret_cast<const u32x4_unaligned*>(rowp + 16 * c);
+        // partial chunks (head: chunk 0 when delta > 0; tail: chunk c_end when the range
+        // does not end on a chunk boundary; one chunk when the range is that short):
+        // lane c writes byte c of each, if it belongs to the strip
+        const bool head = delta > 0;
+        const bool tail = ((delta + nrows) & 15) != 0 && !(head && c_end == 0);
+        if (head && c >= delta && c - delta < nrows)
+            C0[c] = rowp[c];
+        const int ti = 16 * c_end + c;                 // byte of the tail chunk
+        if (tail && ti >= delta && ti - delta < nrows)
+            C0[ti] = rowp[ti];
+    }
+}
 
 int64_t cols_block_capacity(int64_t M_cap, int32_t G)
 {
     return (M_cap + kTileRows - 1) / kTileRows + G;
 }
 
-// Strips of kColsStrip blocks over all experts: at most ceil(M_cap / (128 kStrip)) + G.
+// Strips of kStripRows rows over all experts: at most ceil(M_cap / kStripRows) + G.
 static int64_t cols_strip_capacity(int64_t M_cap, int32_t G)
 {
-    return (M_cap + kTileRows * kColsStrip - 1) / (kTileRows * kColsStrip) + G;
+    return (M_cap + kStripRows - 1) / kStripRows + G;
 }
 
 hipError_t launch_fp8_cols(const uint8_t* codes, const uint8_t* scales, uint8_t* yT,
                            uint8_t* yT_scales, const int32_t* offs, int32_t G, int64_t M_cap,
                            int64_t K, hipStream_t stream)
 {
-    int64_t nkt = K / kTileCols;
-    int64_t grid = cols_strip_capacity(M_cap, G) * nkt;
+    int64_t grid = cols_strip_capacity(M_cap, G) * (K / kTileCols);
     if (M_cap == 0)
         return hipSuccess;
     if (grid > 0x7FFFFFFF)
@@ -273,8 +259,8 @@ hipError_t launch_fp8_cols(const uint8_t* codes, const uint8_t* scales, uint8_t*
     int64_t k = K;
     void* args[] = {(void*)&codes, (void*)&scales, (void*)&yT, (void*)&yT_scales, (void*)&offs,
                     (void*)&g, (void*)&k};
-    return hipLaunchKernel((const void*)fp8_cols_kernel<kColsStrip>, dim3((unsigned)grid),
-                           dim3(kThreads), args, 0, stream);
+    return hipLaunchKernel((const void*)fp8_cols_kernel, dim3((unsigned)grid), dim3(kThreads), args,
+                           0, stream);
 }
 
 }  // namespace mxfp4

@@ -15,6 +15,7 @@ namespace mxfp4 {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned char u8x4 __attribute__((ext_vector_type(4)));
 // A 16-byte vector with byte alignment: gfx950 global stores accept any byte address.
 typedef u32x4 u32x4_unaligned __attribute__((aligned(1)));
 
