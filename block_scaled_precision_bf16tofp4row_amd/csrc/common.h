@@ -108,26 +108,24 @@ constexpr GapLut make_gap_lut()
     return t;
 }
 
-// Spread 4 packed codes (16 bits of `w` starting at byte `b`: nibbles n0..n3) into
-// one byte each: result byte i = n_i (sign bit kept in bit 3).
-__device__ __forceinline__ uint32_t spread_nibbles(uint32_t w, uint32_t sel_bytes)
+// Eight codes (one dword of packed nibbles: byte b holds code 2b in its low nibble and
+// code 2b+1 in its high nibble) -> E4M3 bytes, as two dwords: even = codes 0, 2, 4, 6
+// and odd = codes 1, 3, 5, 7.  One v_perm_b32 looks up four magnitudes in the 8-byte
+// gap table (lut_lo = codes 0..3, lut_hi = codes 4..7); the sign bit of each code
+// (bit 3 of its nibble) becomes bit 7 of its byte.
+__device__ __forceinline__ void convert8_split(uint32_t w, uint32_t lut_lo, uint32_t lut_hi,
+                                               uint32_t& even, uint32_t& odd)
 {
-    uint32_t t = perm(w, w, sel_bytes);                 // [b, b, b+1, b+1]
-    return (t & 0x000F000Fu) | ((t >> 4) & 0x0F000F00u);
+    even = perm(lut_hi, lut_lo, w & 0x07070707u) | ((w << 4) & 0x80808080u);
+    odd = perm(lut_hi, lut_lo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
 }
 
-// Four E4M3 bytes for four spread codes, with the gap table (lo, hi) of this sub-block.
-__device__ __forceinline__ uint32_t convert4(uint32_t nib4, uint32_t lut_lo, uint32_t lut_hi)
-{
-    uint32_t mag = perm(lut_hi, lut_lo, nib4 & 0x07070707u);
-    return mag | ((nib4 << 4) & 0x80808080u);
-}
-
-// Eight codes (one dword of packed nibbles) -> eight E4M3 bytes (two dwords).
+// Eight codes -> eight E4M3 bytes in element order (two dwords: codes 0..3, 4..7).
 __device__ __forceinline__ u32x2 convert8(uint32_t w, uint32_t lut_lo, uint32_t lut_hi)
 {
-    return u32x2{convert4(spread_nibbles(w, 0x01010000u), lut_lo, lut_hi),
-                 convert4(spread_nibbles(w, 0x03030202u), lut_lo, lut_hi)};
+    uint32_t e, o;
+    convert8_split(w, lut_lo, lut_hi, e, o);
+    return u32x2{perm(o, e, 0x05010400u), perm(o, e, 0x07030602u)};
 }
 
 // ---- workgroup -> XCD-aware tile order ---------------------------------------------

@@ -66,6 +66,18 @@ def test_many_experts_scan_chunks():
     check_chain(seg.x_bits, seg.offs)
 
 
+def test_cols_carry_across_strips():
+    """Wide K (56 column tiles) and enough rows that each workgroup of the column
+    kernel converts several consecutive 256-row strips of one expert, so the chunk
+    straddling two strips is carried; expert sizes 256n + r with small r put short
+    last strips (r rows) behind a carried chunk."""
+    counts = [257, 771, 514, 1025, 263, 2051, 258, 1031, 5, 270, 2307, 769, 1283, 259, 517,
+              1797, 3, 261, 1539, 130]
+    say(f"carry counts={counts} K=7168")
+    seg = workloads.ragged_case(counts, 7168, seed=21, values="t3", M_cap=sum(counts) + 11)
+    check_chain(seg.x_bits, seg.offs, kernels=("quantize", "cols"))
+
+
 def test_config1_full_chain():
     w = workloads.config1(0)
     seg = w.segments[0]
