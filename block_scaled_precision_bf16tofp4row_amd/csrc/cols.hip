@@ -34,11 +34,12 @@
 //            strip's output range.  The range's misalignment delta (the same for every
 //            strip of an expert) becomes an unaligned 16-byte LDS read, so every global
 //            store is an aligned 16-byte store and 16 lanes cover a contiguous 256-byte
-//            run.  The chunk that straddles two strips of the same expert is written
-//            once, whole: the last 16 bytes of each LDS row are kept in front of the
-//            row for the next strip.  Only at the ends of a workgroup's run inside an
-//            expert are partial chunks written, one byte per lane.
-// LDS skew: the tile row of column k starts at byte 288k + 64 (k >> 5); 32 rows of 288
+//            run.  A row's stores advance on 128-byte line boundaries: the bytes past
+//            a strip's last line boundary are carried in LDS and written with the next
+//            strip, so in the steady state every store belongs to a whole 128-byte line
+//            (partial lines cost the memory system a read-modify-write).  Only at the
+//            ends of a workgroup's run inside an expert are partial lines written.
+// LDS skew: the tile row of column k starts at byte 400k + 64 (k >> 5); 32 rows of 400
 // bytes span a whole number of bank cycles, so the 64-byte shift per MX group puts the
 // stage-A dword writes of the four groups (16 rows each per wave) in 64 distinct banks.
 // This plays the role of the page's padded, skewed shared-memory layout.
@@ -51,9 +52,13 @@ __constant__ GapLut kColsGapLut = make_gap_lut();
 constexpr int kTileRows = 128;                        // FP8 block along the tokens
 constexpr int kTileCols = 128;                        // four MX groups
 constexpr int kStripRows = 256;                       // two FP8 blocks
-constexpr int kLdsRowBytes = 16 + kStripRows + 16;    // carry / front pad, data, back pad
+// LDS row of one output column: 16 bytes of slack, a 128-byte carry area holding the
+// previous strip's bytes past the last 128-byte line boundary, then the strip's bytes.
+constexpr int kCarryBytes = 128;
+constexpr int kData = 16 + kCarryBytes;               // strip byte 0 of an LDS row
+constexpr int kLdsRowBytes = kData + kStripRows;
 constexpr int kLdsBytes = kTileCols * kLdsRowBytes + 64 * 3;
-constexpr int kWgPerCu = 4;                           // LDS-limited residency
+constexpr int kWgPerCu = 3;                           // LDS-limited residency
 static_assert(kStripRows == 4 * 64, "stage A maps 64 quads of rows over the 4 waves");
 static_assert((32 * (kLdsRowBytes / 4)) % 64 == 0, "32 tile rows must span a multiple of 64 banks");
 
@@ -204,8 +209,8 @@ __global__ __launch_bounds__(kThreads) void fp8_cols_kernel(
     const int kc = lane & 3;                      // MX group inside the tile
     const int rq = (lane >> 2) + 16 * wave;       // rows 4rq..4rq+3 of the strip
     const int c = lane & 15;                      // stage B chunk
-    const uint32_t wbase = lds_row(32 * kc) + 16 + 4 * rq;                 // stage A writes
-    const uint32_t rbase = lds_row(32 * wave + (lane >> 4)) + 16;          // stage B rows
+    const uint32_t wbase = lds_row(32 * kc) + kData + 4 * rq;              // stage A writes
+    const uint32_t rbase = lds_row(32 * wave + (lane >> 4)) + kData;       // stage B rows
 
     StripInfo cur = locate(offs, G, t0, s0);
     int64_t r_lo = (int64_t)(s0 - cur.sb) * kStripRows;
@@ -282,39 +287,43 @@ __global__ __launch_bounds__(kThreads) void fp8_cols_kernel(
 
         // ---- stage B: 16 lanes per output row, 4 rows per step, 32 rows per wave ---------
         // Output row k of expert g starts at byte K*offs[g] + k*M_g; this strip's bytes
-        // are [A, A + nrows) with A = that + r_lo.  Chunk c' is memory
-        // [A - delta + 16c', +16) with delta = A & 15: strip bytes [16c' - delta, +16).
+        // are [A, A + nrows) with A = that + r_lo.  A row's stores advance a frontier on
+        // 128-byte line boundaries: with the previous strip's tail carried in, this strip
+        // writes [align128(A), ...), and when the next strip continues the row it stops
+        // at the last line boundary, leaving the rest in the carry area.  So in the steady
+        // state every store is part of a whole 128-byte line (16 lanes x 16 bytes = two
+        // lines per row).  Bytes of the written range map to LDS row byte kData + (b - A).
         int64_t A = K * cur.row0 + (kTileCols * (int64_t)kt + 32 * wave + (lane >> 4)) * cur.mg + r_lo;
         const int64_t dA = 4 * cur.mg;
-        const bool head_done = carry_in;                 // chunk 0 completes the previous strip's tail
+        const bool edges = !(carry_in && carry_out);       // some range ends are not line-aligned
 #pragma unroll 2
         for (int it = 0; it < 8; ++it, A += dA) {
-            const int delta = (int)(A & 15);
-            uint8_t* const C0 = yT + (A - delta);
-            const uint8_t* rowp = tile + rbase + kLdsRowBytes * 4 * it - delta;   // rowp[16c'+p]
-            const int c_first = (delta > 0 && !head_done) ? 1 : 0;
-            const int c_end = (delta + nrows) >> 4;      // one past the last full chunk
-            if (c >= c_first && c < c_end)
-                *reinterpret_cast<u32x4*>(C0 + 16 * (int64_t)c) =
-                    *reinterpret_cast<const u32x4_unaligned*>(rowp + 16 * c);
-            if (c_first > 0 || (((delta + nrows) & 15) != 0 && !carry_out)) {
-                // partial head (chunk 0 without carried bytes) and tail (chunk c_end): one
-                // byte per lane.  Chunk byte p is strip byte 16c' + p - delta; bytes before
-                // the strip exist only as carried bytes (head_done), in chunk 0.
-                const bool head = c_first > 0;
-                const bool tail = ((delta + nrows) & 15) != 0 && !carry_out && !(head && c_end == 0);
-                if (head && c >= delta && c - delta < nrows)
-                    C0[c] = rowp[c];
-                const int ti = 16 * c_end + c;
-                if (tail && (ti >= delta || head_done) && ti - delta < nrows)
-                    C0[ti] = rowp[ti];
+            const int64_t E = A + nrows;
+            const int64_t W_lo = carry_in ? (A & ~(int64_t)127) : A;
+            const int64_t W_hi = carry_out ? (E & ~(int64_t)127) : E;
+            const uint8_t* rowp = tile + rbase + kLdsRowBytes * 4 * it;   // LDS byte of strip byte 0
+            const int64_t j0 = W_lo >> 4;                     // first 16-byte chunk touched
+            const int nch = W_hi > W_lo ? (int)(((W_hi + 15) >> 4) - j0) : 0;
+            for (int jj = c; jj < nch; jj += 16) {
+                const int64_t b0 = (j0 + jj) << 4;            // chunk start byte
+                if (!edges || (b0 >= W_lo && b0 + 16 <= W_hi)) {
+                    *reinterpret_cast<u32x4*>(yT + b0) =
+                        *reinterpret_cast<const u32x4_unaligned*>(rowp + (b0 - A));
+                } else {
+                    const int64_t lo = max(b0, W_lo), hi = min(b0 + 16, W_hi);
+                    for (int64_t q = lo; q < hi; ++q)
+                        yT[q] = rowp[q - A];
+                }
             }
         }
-        // keep the last 16 strip bytes of each of this wave's rows in front of the row: the
-        // next strip's chunk 0 needs them (only this wave reads these rows in stage B)
-        if (carry_out && lane < 32) {
-            uint8_t* row = tile + lds_row(32 * wave + lane);
-            *reinterpret_cast<u32x4*>(row) = *reinterpret_cast<const u32x4*>(row + 16 + kStripRows - 16);
+        // the next strip continues these rows: move the last 128 strip bytes of each of
+        // this wave's 32 rows into the carry area (only this wave reads these rows)
+        if (carry_out) {
+            uint8_t* row = tile + lds_row(32 * wave + (lane >> 1)) + 64 * (lane & 1);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<u32x4*>(row + 16 + 16 * q) =
+                    *reinterpret_cast<const u32x4*>(row + kData + kStripRows - kCarryBytes + 16 * q);
         }
 
         carry_in = carry_out;
