@@ -21,7 +21,7 @@
 // The grid is persistent: each workgroup owns one 128-column tile (four MX groups)
 // and a contiguous range of strips, which it converts in order.
 //   stage A  thread (kc = lane & 3, rq) holds the 16 code bytes of group kc for rows
-//            4rq..4rq+3 of the strip and their MX scale bytes (loaded one strip
+//            4rq..4rq+3 of the strip and their MX scale bytes (loaded two strips
 //            ahead); four consecutive lanes cover one row's 64 contiguous code bytes
 //            and 4 contiguous scale bytes.  The FP8 scale of each (block, group) is a
 //            DPP / cross-lane max inside the wave plus an LDS exchange between the
@@ -31,9 +31,11 @@
 //            each), written into a k-major LDS tile: one LDS row per output column k
 //            holding that column's strip bytes in output order;
 //   stage B  16 lanes per output row: lane c stores the 16-byte aligned chunk c of the
-//            strip's output range.  The range's misalignment delta (the same for every
-//            strip of an expert) becomes an unaligned 16-byte LDS read, so every global
-//            store is an aligned 16-byte store and 16 lanes cover a contiguous 256-byte
+//            strip's output range.  The four rows of one step are 16 columns apart, so
+//            their misalignment delta (mod 16) is the same and the realignment is two
+//            aligned 16-byte LDS reads plus v_alignbyte_b32 under a wave-uniform
+//            branch; every global store is an aligned 16-byte store and 16 lanes cover a
+//            contiguous 256-byte
 //            run.  A row's stores advance on 128-byte line boundaries: the bytes past
 //            a strip's last line boundary are carried in LDS and written with the next
 //            strip, so in the steady state every store belongs to a whole 128-byte line
@@ -57,7 +59,7 @@ constexpr int kStripRows = 256;                       // two FP8 blocks
 constexpr int kCarryBytes = 128;
 constexpr int kData = 16 + kCarryBytes;               // strip byte 0 of an LDS row
 constexpr int kLdsRowBytes = kData + kStripRows;
-constexpr int kLdsBytes = kTileCols * kLdsRowBytes + 64 * 3;
+constexpr int kLdsBytes = kTileCols * kLdsRowBytes + 64 * 3 + 16;   // + slack for the last row's window
 constexpr int kWgPerCu = 3;                           // LDS-limited residency
 static_assert(kStripRows == 4 * 64, "stage A maps 64 quads of rows over the 4 waves");
 static_assert((32 * (kLdsRowBytes / 4)) % 64 == 0, "32 tile rows must span a multiple of 64 banks");
@@ -76,6 +78,24 @@ __device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t 
     o1 = perm(u0, t0, 0x07060302u);
     o2 = perm(u1, t1, 0x05040100u);
     o3 = perm(u1, t1, 0x07060302u);
+}
+
+// 16 bytes starting `o` bytes into the 32 bytes (lo, hi); o is wave-uniform, so the
+// switch is a scalar branch and each output dword is one v_alignbyte_b32.
+__device__ __forceinline__ u32x4 window16(const u32x4& lo, const u32x4& hi, uint32_t o)
+{
+    const uint32_t D[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const uint32_t v = o & 3;
+#define MXFP4_WINDOW(U) \
+    u32x4{__builtin_amdgcn_alignbyte(D[U + 1], D[U], v), __builtin_amdgcn_alignbyte(D[U + 2], D[U + 1], v), \
+          __builtin_amdgcn_alignbyte(D[U + 3], D[U + 2], v), __builtin_amdgcn_alignbyte(D[U + 4], D[U + 3], v)}
+    switch (o >> 2) {
+    case 0: return MXFP4_WINDOW(0);
+    case 1: return MXFP4_WINDOW(1);
+    case 2: return MXFP4_WINDOW(2);
+    default: return MXFP4_WINDOW(3);
+    }
+#undef MXFP4_WINDOW
 }
 
 // ---- strips of experts ----------------------------------------------------------------
@@ -117,6 +137,8 @@ __device__ __forceinline__ ExpertTable expert_chunk(const int32_t* __restrict__ 
 struct StripInfo {
     int64_t row0, mg;          // expert's first row and row count
     uint32_t sb, bb;           // expert's first strip and first 128-row block
+    int64_t r_lo;              // the strip's first row, relative to row0
+    int nrows;                 // rows in the strip
 };
 
 // Expert of global strip s (s < total strips).  `cached` is the table of experts
@@ -138,11 +160,27 @@ __device__ __forceinline__ StripInfo locate(const int32_t* __restrict__ offs, in
             r.mg = __builtin_amdgcn_readlane(t.mg, src);
             r.sb = __builtin_amdgcn_readlane(t.sb, src);
             r.bb = __builtin_amdgcn_readlane(t.bb, src);
+            r.r_lo = (int64_t)(s - r.sb) * kStripRows;
+            r.nrows = (int)min<int64_t>(kStripRows, r.mg - r.r_lo);
             return r;
         }
         run_s += t.total_s;
         run_b += t.total_b;
     }
+}
+
+// Info of strip s, reusing `prev` (an earlier strip) when s is in the same expert.
+__device__ __forceinline__ StripInfo strip_after(const int32_t* __restrict__ offs, int G,
+                                                 const ExpertTable& cached, const StripInfo& prev,
+                                                 uint32_t s)
+{
+    if (s < prev.sb + (uint32_t)((prev.mg + kStripRows - 1) / kStripRows)) {
+        StripInfo r = prev;
+        r.r_lo = (int64_t)(s - r.sb) * kStripRows;
+        r.nrows = (int)min<int64_t>(kStripRows, r.mg - r.r_lo);
+        return r;
+    }
+    return locate(offs, G, cached, s);
 }
 
 // ---- the kernel ---------------------------------------------------------------------------
@@ -152,6 +190,9 @@ struct RowsIn {
     uint32_t s[4];             // their MX scale bytes (0 for rows past the strip)
 };
 
+// Loads are unconditional (rows past the strip are clamped to its last row and zeroed
+// after the load), so every strip issues the same straight-line sequence of loads and the
+// compiler can wait for exactly the loads it needs.
 __device__ __forceinline__ RowsIn load_rows(const uint8_t* __restrict__ codes,
                                             const uint8_t* __restrict__ scales, int64_t K,
                                             int64_t row_first, int nrows, int rq, int kc,
@@ -160,13 +201,22 @@ __device__ __forceinline__ RowsIn load_rows(const uint8_t* __restrict__ codes,
     RowsIn in;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const bool ok = 4 * rq + i < nrows;
-        const int64_t row = row_first + 4 * rq + i;
-        in.c[i] = ok ? *reinterpret_cast<const u32x4*>(codes + row * (K / 2) + 64 * (int64_t)kt + 16 * kc)
-                     : u32x4{0, 0, 0, 0};
-        in.s[i] = ok ? (uint32_t)scales[row * (K / 32) + 4 * (int64_t)kt + kc] : 0u;
+        const int r = min(4 * rq + i, nrows - 1);
+        const int64_t row = row_first + r;
+        in.c[i] = *reinterpret_cast<const u32x4*>(codes + row * (K / 2) + 64 * (int64_t)kt + 16 * kc);
+        in.s[i] = scales[row * (K / 32) + 4 * (int64_t)kt + kc];
     }
     return in;
+}
+
+__device__ __forceinline__ void mask_rows(RowsIn& in, int nrows, int rq)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool ok = 4 * rq + i < nrows;
+        in.c[i] = ok ? in.c[i] : u32x4{0, 0, 0, 0};
+        in.s[i] = ok ? in.s[i] : 0u;
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void fp8_cols_kernel(
@@ -210,28 +260,18 @@ __global__ __launch_bounds__(kThreads) void fp8_cols_kernel(
     const int rq = (lane >> 2) + 16 * wave;       // rows 4rq..4rq+3 of the strip
     const int c = lane & 15;                      // stage B chunk
     const uint32_t wbase = lds_row(32 * kc) + kData + 4 * rq;              // stage A writes
-    const uint32_t rbase = lds_row(32 * wave + (lane >> 4)) + kData;       // stage B rows
+    // stage B: wave (half hb, parity pb) converts output rows 64hb + 8pb + it + 16q
+    // (it = 0..7 steps, q = lane >> 4): rows 16 apart share their misalignment mod 16
+    const int hb = wave >> 1, pb = wave & 1;
+    const uint32_t kb0 = 64 * hb + 8 * pb + 16 * (lane >> 4);              // row at it = 0
 
-    StripInfo cur = locate(offs, G, t0, s0);
-    int64_t r_lo = (int64_t)(s0 - cur.sb) * kStripRows;
-    int nrows = (int)min<int64_t>(kStripRows, cur.mg - r_lo);
-    RowsIn in = load_rows(codes, scales, K, cur.row0 + r_lo, nrows, rq, kc, kt);
-    bool carry_in = false;                        // LDS row fronts hold the previous strip's tail
 
-    for (uint32_t s = s0; s < s1; ++s) {
-        // ---- next strip: where, and prefetch its rows --------------------------------------
-        const bool has_next = s + 1 < s1;
-        StripInfo nxt = cur;
-        int64_t r_lo_n = r_lo + kStripRows;
-        if (has_next && s + 1 >= cur.sb + (uint32_t)((cur.mg + kStripRows - 1) / kStripRows)) {
-            nxt = locate(offs, G, t0, s + 1);
-            r_lo_n = (int64_t)(s + 1 - nxt.sb) * kStripRows;
-        }
-        const int nrows_n = has_next ? (int)min<int64_t>(kStripRows, nxt.mg - r_lo_n) : 0;
-        const bool carry_out = has_next && nxt.sb == cur.sb;    // next strip continues this expert
-        RowsIn nin;
-        if (has_next)
-            nin = load_rows(codes, scales, K, nxt.row0 + r_lo_n, nrows_n, rq, kc, kt);
+    // one strip is converted while the next one is loaded; the loop is unrolled by two
+    // so the two register sets alternate roles without copies
+    auto convert_strip = [&](const StripInfo& cur, RowsIn in, bool carry_in, bool carry_out) {
+        const int64_t r_lo = cur.r_lo;
+        const int nrows = cur.nrows;
+        mask_rows(in, nrows, rq);
 
         // ---- stage A: block scales ---------------------------------------------------------
         uint32_t m = max(max(in.s[0], in.s[1]), max(in.s[2], in.s[3]));
@@ -289,48 +329,88 @@ __global__ __launch_bounds__(kThreads) void fp8_cols_kernel(
         // Output row k of expert g starts at byte K*offs[g] + k*M_g; this strip's bytes
         // are [A, A + nrows) with A = that + r_lo.  A row's stores advance a frontier on
         // 128-byte line boundaries: with the previous strip's tail carried in, this strip
-        // writes [align128(A), ...), and when the next strip continues the row it stops
-        // at the last line boundary, leaving the rest in the carry area.  So in the steady
-        // state every store is part of a whole 128-byte line (16 lanes x 16 bytes = two
-        // lines per row).  Bytes of the written range map to LDS row byte kData + (b - A).
-        int64_t A = K * cur.row0 + (kTileCols * (int64_t)kt + 32 * wave + (lane >> 4)) * cur.mg + r_lo;
-        const int64_t dA = 4 * cur.mg;
-        const bool edges = !(carry_in && carry_out);       // some range ends are not line-aligned
+        // writes from align128(A), and when the next strip continues the row it stops at
+        // the last line boundary, leaving the rest in the carry area.  So in the steady
+        // state every store belongs to a whole 128-byte line (16 lanes x 16 bytes = two
+        // lines per row).  Memory byte b of the row maps to LDS row byte kData + (b - A);
+        // since b is 16-aligned, the offset inside the aligned LDS chunk is
+        // o = (16 - (A & 15)) & 15 for every chunk of the four rows of a step.
+        int64_t A = K * cur.row0 + (kTileCols * (int64_t)kt + kb0) * cur.mg + r_lo;
+        const bool steady = carry_in && carry_out;
 #pragma unroll 2
-        for (int it = 0; it < 8; ++it, A += dA) {
-            const int64_t E = A + nrows;
-            const int64_t W_lo = carry_in ? (A & ~(int64_t)127) : A;
-            const int64_t W_hi = carry_out ? (E & ~(int64_t)127) : E;
-            const uint8_t* rowp = tile + rbase + kLdsRowBytes * 4 * it;   // LDS byte of strip byte 0
-            const int64_t j0 = W_lo >> 4;                     // first 16-byte chunk touched
-            const int nch = W_hi > W_lo ? (int)(((W_hi + 15) >> 4) - j0) : 0;
-            for (int jj = c; jj < nch; jj += 16) {
-                const int64_t b0 = (j0 + jj) << 4;            // chunk start byte
-                if (!edges || (b0 >= W_lo && b0 + 16 <= W_hi)) {
-                    *reinterpret_cast<u32x4*>(yT + b0) =
-                        *reinterpret_cast<const u32x4_unaligned*>(rowp + (b0 - A));
-                } else {
-                    const int64_t lo = max(b0, W_lo), hi = min(b0 + 16, W_hi);
-                    for (int64_t q = lo; q < hi; ++q)
-                        yT[q] = rowp[q - A];
+        for (int it = 0; it < 8; ++it, A += cur.mg) {
+            const uint32_t kl = kb0 + it;
+            const uint8_t* rowp = tile + lds_row(kl) + kData;          // LDS byte of strip byte 0
+            const uint32_t o = __builtin_amdgcn_readfirstlane((uint32_t)(16 - (A & 15)) & 15);
+            if (steady) {
+                const int64_t b0 = (A & ~(int64_t)127) + 16 * c;       // two whole lines
+                const uint8_t* src = rowp + (b0 - A) - o;              // 16-byte aligned
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
+                u32x4 v = lo;
+                if (o != 0)
+                    v = window16(lo, *reinterpret_cast<const u32x4*>(src + 16), o);
+                *reinterpret_cast<u32x4*>(yT + b0) = v;
+            } else {
+                const int64_t E = A + nrows;
+                const int64_t W_lo = carry_in ? (A & ~(int64_t)127) : A;
+                const int64_t W_hi = carry_out ? (E & ~(int64_t)127) : E;
+                const int64_t j0 = W_lo >> 4;                          // first 16-byte chunk
+                const int nch = W_hi > W_lo ? (int)(((W_hi + 15) >> 4) - j0) : 0;
+                for (int pass = 0; pass < 2; ++pass) {
+                    const int jj = c + 16 * pass;
+                    if (jj >= nch)
+                        continue;
+                    const int64_t b0 = (j0 + jj) << 4;
+                    const uint8_t* src = rowp + (b0 - A) - o;
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
+                    u32x4 v = lo;
+                    if (o != 0)
+                        v = window16(lo, *reinterpret_cast<const u32x4*>(src + 16), o);
+                    if (b0 >= W_lo && b0 + 16 <= W_hi) {
+                        *reinterpret_cast<u32x4*>(yT + b0) = v;
+                    } else {
+                        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                        for (int q = 0; q < 16; ++q)
+                            if (b0 + q >= W_lo && b0 + q < W_hi)
+                                yT[b0 + q] = (uint8_t)(w4[q >> 2] >> (8 * (q & 3)));
+                    }
                 }
             }
         }
         // the next strip continues these rows: move the last 128 strip bytes of each of
         // this wave's 32 rows into the carry area (only this wave reads these rows)
         if (carry_out) {
-            uint8_t* row = tile + lds_row(32 * wave + (lane >> 1)) + 64 * (lane & 1);
+            const int r = lane >> 1;                                   // 0..31
+            uint8_t* row = tile + lds_row(64 * hb + 8 * pb + (r & 7) + 16 * (r >> 3)) + 64 * (lane & 1);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 *reinterpret_cast<u32x4*>(row + 16 + 16 * q) =
                     *reinterpret_cast<const u32x4*>(row + kData + kStripRows - kCarryBytes + 16 * q);
         }
 
-        carry_in = carry_out;
-        cur = nxt;
-        r_lo = r_lo_n;
-        nrows = nrows_n;
-        in = nin;
+    };
+
+    StripInfo info = locate(offs, G, t0, s0);
+    RowsIn inA = load_rows(codes, scales, K, info.row0 + info.r_lo, info.nrows, rq, kc, kt);
+    RowsIn inB;
+    bool carry = false;                           // LDS carry areas hold the previous strip's tail
+    for (uint32_t s = s0; s < s1; s += 2) {
+        // strip s (registers A); load strip s + 1 (registers B) meanwhile
+        const bool has1 = s + 1 < s1;
+        const StripInfo info1 = has1 ? strip_after(offs, G, t0, info, s + 1) : info;
+        inB = load_rows(codes, scales, K, info1.row0 + info1.r_lo, info1.nrows, rq, kc, kt);
+        const bool c1 = has1 && info1.sb == info.sb;
+        convert_strip(info, inA, carry, c1);
+        if (!has1)
+            break;
+        // strip s + 1 (registers B); load strip s + 2 (registers A) meanwhile
+        const bool has2 = s + 2 < s1;
+        const StripInfo info2 = has2 ? strip_after(offs, G, t0, info1, s + 2) : info1;
+        inA = load_rows(codes, scales, K, info2.row0 + info2.r_lo, info2.nrows, rq, kc, kt);
+        const bool c2 = has2 && info2.sb == info1.sb;
+        convert_strip(info1, inB, c1, c2);
+        info = info2;
+        carry = c2;
     }
 }
 
