@@ -76,7 +76,7 @@ def read_traffic(kernel: str, workload: str, segment: str):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"<!-- traffic-json (\{.*?\}) -->", text, re.S)
+    m = re.search(r"<!-- traffic-json (\{.*\}) -->", text)
     if not m:
         return None
     data = json.loads(m.group(1))
