@@ -22,6 +22,8 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 // Largest M_cap * K the kernels index: every byte count stays far inside int64.
 constexpr int64_t kMaxElems = (int64_t)1 << 50;
+// Largest K of the column conversion.
+constexpr int64_t kMaxColsK = (int64_t)1 << 24;
 
 mxfp4_status check_shape(int32_t G, int64_t M_cap, int64_t K, int64_t k_multiple)
 {
@@ -86,6 +88,8 @@ mxfp4_status mxfp4_to_fp8_cols_ragged(const uint8_t* codes, const uint8_t* scale
     mxfp4_status st = check_shape(G, M_cap, K, 128);
     if (st != MXFP4_OK)
         return st;
+    if (K > kMaxColsK)                       // the kernel's per-strip row offsets are 32-bit
+        return MXFP4_ERR_SHAPE;
     if (!aligned(codes, 16) || !aligned(scales, 16) || !aligned(yT_e4m3, 16) ||
         !aligned(yT_scales, 16) || !aligned(group_offsets, 4))
         return MXFP4_ERR_ALIGN;

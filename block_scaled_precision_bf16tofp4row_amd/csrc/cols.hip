@@ -16,55 +16,78 @@
 // (k, m') at k*M_g + m'.  Its block scales [nb_g, K] start at byte K*B_g, B_g the
 // number of 128-row blocks of experts 0..g-1 (nb_h = ceil(M_h / 128)).
 //
-// Work: a strip is up to 256 consecutive rows (two FP8 blocks) of one expert; each
-// expert's rows are cut into strips and all strips are numbered in expert order.
-// The grid is persistent: each workgroup owns one 128-column tile (four MX groups)
-// and a contiguous range of strips, which it converts in order.
-//   stage A  thread (kc = lane & 3, rq) holds the 16 code bytes of group kc for rows
-//            4rq..4rq+3 of the strip and their MX scale bytes (loaded two strips
-//            ahead); four consecutive lanes cover one row's 64 contiguous code bytes
-//            and 4 contiguous scale bytes.  The FP8 scale of each (block, group) is a
-//            DPP / cross-lane max inside the wave plus an LDS exchange between the
-//            block's two waves.  Each row is converted with the gap table of its own
-//            scale (even and odd codes separately, one v_perm_b32 each), and 4x4 byte
-//            transposes turn 4 rows x 32 columns into 32 dwords (4 rows of one column
-//            each), written into a k-major LDS tile: one LDS row per output column k
-//            holding that column's strip bytes in output order;
-//   stage B  16 lanes per output row: lane c stores the 16-byte aligned chunk c of the
-//            strip's output range.  The four rows of one step are 16 columns apart, so
-//            their misalignment delta (mod 16) is the same and the realignment is two
-//            aligned 16-byte LDS reads plus v_alignbyte_b32 under a wave-uniform
-//            branch; every global store is an aligned 16-byte store and 16 lanes cover a
-//            contiguous 256-byte
-//            run.  A row's stores advance on 128-byte line boundaries: the bytes past
-//            a strip's last line boundary are carried in LDS and written with the next
-//            strip, so in the steady state every store belongs to a whole 128-byte line
-//            (partial lines cost the memory system a read-modify-write).  Only at the
-//            ends of a workgroup's run inside an expert are partial lines written.
-// LDS skew: the tile row of column k starts at byte 400k + 64 (k >> 5); 32 rows of 400
-// bytes span a whole number of bank cycles, so the 64-byte shift per MX group puts the
-// stage-A dword writes of the four groups (16 rows each per wave) in 64 distinct banks.
-// This plays the role of the page's padded, skewed shared-memory layout.
+// Work: a strip is one 128-row block of one expert; the strips of all experts are
+// numbered in expert order (strip s is row s of the block-scale output).  The grid
+// is persistent, one workgroup per compute unit: each owns a 256-column tile (eight
+// MX groups, so every row it reads is one whole 128-byte line of codes) and a
+// contiguous range of strips.  Its eight waves have two roles, so that no wave
+// both loads and stores (a wave's loads and stores share one in-order completion
+// counter, and waiting for a load must not wait for older stores):
+//   producers (waves 0-3)  wave w converts MX groups 2w, 2w+1 of a strip: lane
+//            (half = lane >> 5, rq = lane & 31) holds the 16 code bytes of rows
+//            4rq..4rq+3 of group 2w + half and their scale bytes, loaded two strips
+//            ahead.  The block scale of a group is a max over the 32 lanes of that
+//            half (DPP inside the wave).  Each row is converted with the gap table
+//            of its own scale, 4x4 byte transposes turn 4 rows x 32 columns into 32
+//            dwords (4 rows of one column each), written into a k-major LDS ring:
+//            one LDS row per output column k holding the last three strips' bytes
+//            of that column in order;
+//   consumers (waves 4-7)  write the previous strip: 8 lanes per output column, lane
+//            c stores the 16-byte aligned chunk c of the column's output range, 8
+//            columns per instruction.  Those 8 columns are 16 apart, so their
+//            misalignment (mod 16) is the same and the realignment is two aligned
+//            16-byte LDS reads plus v_alignbyte_b32 under a wave-uniform branch.  A
+//            column's stores advance on 128-byte line boundaries: the bytes past a
+//            strip's last line boundary stay in the ring and are written with the
+//            next strip, so in the steady state every store belongs to a whole
+//            128-byte line (partial lines cost the memory system a read-modify-
+//            write).  Only at the ends of a workgroup's run inside an expert are
+//            partial lines written.
+// One barrier per step: producers fill ring slot j % 3 with strip j while consumers
+// write strip j - 1 (whose carried-in bytes sit in slot (j - 2) % 3).
+// LDS skew: column k's ring starts at byte 384k + 128 ((k >> 4) + (k >> 5)).  The
+// producers' dword writes cover columns k and k + 32 (32 rows each, k < 32 mod 64)
+// and the consumers' 16-byte reads columns k and k + 16 (128 bytes each, k < 16 mod
+// 32); each pair is an odd multiple of 128 bytes apart, so it falls in disjoint
+// halves of the banks.  This plays the role of the page's padded, skewed
+// shared-memory layout.
 #include "common.h"
 
 namespace mxfp4 {
 
 __constant__ GapLut kColsGapLut = make_gap_lut();
 
-constexpr int kTileRows = 128;                        // FP8 block along the tokens
-constexpr int kTileCols = 128;                        // four MX groups
-constexpr int kStripRows = 256;                       // two FP8 blocks
-// LDS row of one output column: 16 bytes of slack, a 128-byte carry area holding the
-// previous strip's bytes past the last 128-byte line boundary, then the strip's bytes.
-constexpr int kCarryBytes = 128;
-constexpr int kData = 16 + kCarryBytes;               // strip byte 0 of an LDS row
-constexpr int kLdsRowBytes = kData + kStripRows;
-constexpr int kLdsBytes = kTileCols * kLdsRowBytes + 64 * 3 + 16;   // + slack for the last row's window
-constexpr int kWgPerCu = 3;                           // LDS-limited residency
-static_assert(kStripRows == 4 * 64, "stage A maps 64 quads of rows over the 4 waves");
-static_assert((32 * (kLdsRowBytes / 4)) % 64 == 0, "32 tile rows must span a multiple of 64 banks");
+constexpr int kStripRows = 128;                      // one FP8 block along the tokens
+constexpr int kTileCols = 256;                       // eight MX groups
+constexpr int kSlots = 4;                            // ring slots (strips) per column
+constexpr int kRing = kSlots * kStripRows;           // 512
+constexpr int kMirror = 32;                          // ring bytes 0..31 repeated after the ring
+constexpr int kColBytes = kRing + kMirror;           // 544
+// column k's ring starts at byte 544k + 32 (k >> 5): non-decreasing, so the rings
+// never overlap
+constexpr int kTileBytes = kTileCols * kColBytes + 32 * ((kTileCols - 1) / 32);
+constexpr int kProducerWaves = 4;
+constexpr int kConsumerWaves = 8;
+constexpr int kColsThreads = 64 * (kProducerWaves + kConsumerWaves);
+static_assert(kStripRows == 32 * kProducerWaves, "a producer wave converts 32 rows");
+static_assert(kTileCols == 32 * 8, "a producer lane converts one MX group of 8");
+static_assert((kRing & (kRing - 1)) == 0, "the ring position wraps with a mask");
 
-__device__ __forceinline__ uint32_t lds_row(uint32_t k) { return kLdsRowBytes * k + 64 * (k >> 5); }
+// Values the compiler cannot prove wave-uniform (they come through cross-lane ops or
+// LDS) are moved to scalar registers, so branches on them are scalar branches.
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t lds_col(uint32_t kk)
+{
+    return kColBytes * kk + 32 * (kk >> 5);
+}
 
 // 4x4 byte transpose: a[i] holds bytes (row i, col 0..3); o[j] gets bytes (row 0..3, col j).
 __device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
@@ -100,16 +123,16 @@ __device__ __forceinline__ u32x4 window16(const u32x4& lo, const u32x4& hi, uint
 
 // ---- strips of experts ----------------------------------------------------------------
 
-// Per-lane expert table for experts 64*chunk + lane: first strip, first 128-row block,
-// first row and row count.  Every wave builds it on its own (no barrier).
+// Per-lane expert table for experts g0 + lane: first strip, strip count, first row and
+// row count.  Every wave builds it on its own (no barrier).
 struct ExpertTable {
-    uint32_t sb, bb, ns;       // first strip, first block, strip count (lane's expert)
+    uint32_t sb, ns;           // first strip, strip count (lane's expert)
     int32_t row0, mg;          // first row, rows
-    uint32_t total_s, total_b; // strips / blocks of the whole chunk
+    uint32_t total;            // strips of the whole chunk
 };
 
 __device__ __forceinline__ ExpertTable expert_chunk(const int32_t* __restrict__ offs, int G, int g0,
-                                                    uint32_t run_s, uint32_t run_b)
+                                                    uint32_t run)
 {
     const int lane = threadIdx.x & 63;
     const int h = g0 + lane;
@@ -117,306 +140,446 @@ __device__ __forceinline__ ExpertTable expert_chunk(const int32_t* __restrict__ 
     t.row0 = h < G ? offs[h] : 0;
     t.mg = h < G ? offs[h + 1] - t.row0 : 0;
     t.ns = (uint32_t)(t.mg + kStripRows - 1) / kStripRows;
-    const uint32_t nb = (uint32_t)(t.mg + kTileRows - 1) / kTileRows;
-    uint32_t is = t.ns, ib = nb;
+    uint32_t incl = t.ns;
 #pragma unroll
     for (int dlt = 1; dlt < 64; dlt <<= 1) {
-        uint32_t os = __shfl_up(is, dlt, 64), ob = __shfl_up(ib, dlt, 64);
-        if (lane >= dlt) {
-            is += os;
-            ib += ob;
-        }
+        uint32_t other = __shfl_up(incl, dlt, 64);
+        if (lane >= dlt)
+            incl += other;
     }
-    t.sb = run_s + is - t.ns;
-    t.bb = run_b + ib - nb;
-    t.total_s = __shfl(is, 63, 64);
-    t.total_b = __shfl(ib, 63, 64);
+    t.sb = run + incl - t.ns;
+    t.total = uniform((uint32_t)__shfl(incl, 63, 64));
     return t;
 }
 
 struct StripInfo {
     int64_t row0, mg;          // expert's first row and row count
-    uint32_t sb, bb;           // expert's first strip and first 128-row block
+    uint32_t g;                // expert
+    uint32_t sb, ns;           // expert's first strip and strip count
+    uint32_t s;                // this strip (= its row in the block-scale output)
     int64_t r_lo;              // the strip's first row, relative to row0
     int nrows;                 // rows in the strip
 };
 
-// Expert of global strip s (s < total strips).  `cached` is the table of experts
-// 0..63, used directly when G <= 64; larger G rescans 64 experts at a time.
+__device__ __forceinline__ void set_rows(StripInfo& r)
+{
+    r.r_lo = (int64_t)(r.s - r.sb) * kStripRows;
+    r.nrows = (int)min<int64_t>(kStripRows, r.mg - r.r_lo);
+}
+
+// Expert of global strip s (s < total strips), searched 64 experts at a time with
+// one lane per expert.  `cached` is the table of experts 0..63.  Used once per
+// workgroup, before the strip loop.
 __device__ __forceinline__ StripInfo locate(const int32_t* __restrict__ offs, int G,
                                             const ExpertTable& cached, uint32_t s)
 {
     ExpertTable t = cached;
-    uint32_t run_s = 0, run_b = 0;
+    uint32_t run = 0;
     for (int g0 = 0;; g0 += 64) {
         if (g0 > 0)
-            t = expert_chunk(offs, G, g0, run_s, run_b);
+            t = expert_chunk(offs, G, g0, run);
         const bool mine = t.ns > 0 && s >= t.sb && s < t.sb + t.ns;
         const uint64_t mask = __ballot(mine);
         if (mask || g0 + 64 >= G) {
             const int src = mask ? __builtin_ctzll(mask) : 0;
             StripInfo r;
-            r.row0 = __builtin_amdgcn_readlane(t.row0, src);
-            r.mg = __builtin_amdgcn_readlane(t.mg, src);
-            r.sb = __builtin_amdgcn_readlane(t.sb, src);
-            r.bb = __builtin_amdgcn_readlane(t.bb, src);
-            r.r_lo = (int64_t)(s - r.sb) * kStripRows;
-            r.nrows = (int)min<int64_t>(kStripRows, r.mg - r.r_lo);
+            r.row0 = uniform((int32_t)__builtin_amdgcn_readlane(t.row0, src));
+            r.mg = uniform((int32_t)__builtin_amdgcn_readlane(t.mg, src));
+            r.sb = uniform((uint32_t)__builtin_amdgcn_readlane(t.sb, src));
+            r.ns = uniform((uint32_t)__builtin_amdgcn_readlane(t.ns, src));
+            r.g = (uint32_t)(g0 + src);
+            r.s = s;
+            set_rows(r);
             return r;
         }
-        run_s += t.total_s;
-        run_b += t.total_b;
+        run += t.total;
     }
 }
 
-// Info of strip s, reusing `prev` (an earlier strip) when s is in the same expert.
-__device__ __forceinline__ StripInfo strip_after(const int32_t* __restrict__ offs, int G,
-                                                 const ExpertTable& cached, const StripInfo& prev,
-                                                 uint32_t s)
+// Strip p.s + 1 (which exists).  Inside the strip loop the experts are walked one
+// by one with scalar loads of the offsets (counted apart from the vector loads, so
+// the prefetched rows are never waited for early).
+__device__ __forceinline__ StripInfo next_strip(const int32_t* __restrict__ offs, int G,
+                                                const StripInfo& p)
 {
-    if (s < prev.sb + (uint32_t)((prev.mg + kStripRows - 1) / kStripRows)) {
-        StripInfo r = prev;
-        r.r_lo = (int64_t)(s - r.sb) * kStripRows;
-        r.nrows = (int)min<int64_t>(kStripRows, r.mg - r.r_lo);
-        return r;
+    StripInfo r = p;
+    r.s = p.s + 1;
+    if (r.s >= r.sb + r.ns) {
+        r.sb += r.ns;
+        int64_t end = r.row0 + r.mg;
+        uint32_t g = r.g;
+        do {                                   // skip empty experts
+            ++g;
+            r.row0 = end;
+            end = offs[g + 1];
+        } while (end == r.row0 && (int)g + 1 < G);
+        r.g = g;
+        r.mg = end - r.row0;
+        r.ns = (uint32_t)((r.mg + kStripRows - 1) / kStripRows);
     }
-    return locate(offs, G, cached, s);
+    set_rows(r);
+    return r;
 }
 
-// ---- the kernel ---------------------------------------------------------------------------
+// What the producers hand to the consumers for one ring slot.
+struct SlotInfo {
+    int64_t A0;                // output byte of (tile column 0, strip row 0)
+    int32_t mg;                // rows of the expert (= output row length)
+    int32_t nrows;             // rows in the strip
+    uint32_t blk;              // row of the block-scale output
+    uint32_t flags;            // bit 0: the previous strip continues the same rows;
+                               // bit 1: the next strip does
+    uint32_t S[2];             // block scale byte of MX groups 0..7 of the tile
+};
+
+// ---- producers ---------------------------------------------------------------------------
 
 struct RowsIn {
-    u32x4 c[4];                // codes of group kc, rows 4rq..4rq+3
-    uint32_t s[4];             // their MX scale bytes (0 for rows past the strip)
+    u32x4 c[4];                // 32 codes of the lane's group, rows 4rq..4rq+3 of its 32
+    uint32_t s[4];             // the aligned dword holding each row's MX scale byte
+};
+
+// Byte offsets of the lane's four rows inside a strip: its 16 code bytes and the dword
+// holding the scale byte of its group, relative to the strip's first row of the tile
+// (fit in 32 bits: 128 rows x K/2 bytes with K <= 2^24).  Eight consecutive lanes read
+// one row's whole 128-byte line of codes, so a load instruction touches 8 lines.
+// Scales are loaded as whole dwords (a byte load would be zero-extended where the loop
+// carries it, which makes the compiler wait for the prefetched loads early); the byte
+// is extracted at use.
+struct LaneRows {
+    uint32_t c[4], s[4];
 };
 
 // Loads are unconditional (rows past the strip are clamped to its last row and zeroed
-// after the load), so every strip issues the same straight-line sequence of loads and the
-// compiler can wait for exactly the loads it needs.
+// after the load), so every strip issues the same straight-line sequence of loads and
+// the compiler can wait for exactly the loads it needs.
 __device__ __forceinline__ RowsIn load_rows(const uint8_t* __restrict__ codes,
                                             const uint8_t* __restrict__ scales, int64_t K,
-                                            int64_t row_first, int nrows, int rq, int kc,
-                                            uint32_t kt)
+                                            const StripInfo& st, const LaneRows& lr, int row_q,
+                                            uint32_t cbyte, uint32_t sbyte, uint32_t kt)
 {
     RowsIn in;
+    const int64_t row_first = st.row0 + st.r_lo;                      // uniform
+    const uint8_t* const cb = codes + row_first * (K / 2) + 128 * (int64_t)kt;
+    const uint8_t* const sb = scales + row_first * (K / 32) + 8 * (int64_t)kt;
+    if (st.nrows == kStripRows) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = min(4 * rq + i, nrows - 1);
-        const int64_t row = row_first + r;
-        in.c[i] = *reinterpret_cast<const u32x4*>(codes + row * (K / 2) + 64 * (int64_t)kt + 16 * kc);
-        in.s[i] = scales[row * (K / 32) + 4 * (int64_t)kt + kc];
+        for (int i = 0; i < 4; ++i) {
+            in.c[i] = *reinterpret_cast<const u32x4*>(cb + lr.c[i]);
+            in.s[i] = *reinterpret_cast<const uint32_t*>(sb + lr.s[i]);
+        }
+    } else {
+        const uint32_t kc = (uint32_t)(K / 2), ks = (uint32_t)(K / 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t r = (uint32_t)min(row_q + i, st.nrows - 1);
+            in.c[i] = *reinterpret_cast<const u32x4*>(cb + (r * kc + cbyte));
+            in.s[i] = *reinterpret_cast<const uint32_t*>(sb + (r * ks + sbyte));
+        }
     }
     return in;
 }
 
-__device__ __forceinline__ void mask_rows(RowsIn& in, int nrows, int rq)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const bool ok = 4 * rq + i < nrows;
-        in.c[i] = ok ? in.c[i] : u32x4{0, 0, 0, 0};
-        in.s[i] = ok ? in.s[i] : 0u;
-    }
-}
+// ---- consumers ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kThreads) void fp8_cols_kernel(
+// A consumer lane writes one aligned 16-byte chunk of one column per strip: lane
+// (mc = lane >> 3, c = lane & 7) of instruction `it` of consumer wave v owns tile column
+// kk = 2v + (it >> 1) + 16 mc + 128 (it & 1) and bytes [16c, 16c + 16) of the column's
+// 128-byte output line of the strip, so the 8 lanes of a column store one whole line.
+// Within a run of strips of one expert the column's line phase is fixed, so this
+// state is set at the first strip and advanced by 128 bytes per strip.
+struct ColState {
+    uint32_t q[4];             // ring offset of the lane's chunk, minus the strip's slot base
+    uint8_t* p[4];             // output address of the lane's chunk
+    uint32_t o[4];             // misalignment (wave-uniform): (-A) & 15
+};
+
+// ---- the kernel ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     uint8_t* __restrict__ yT, uint8_t* __restrict__ yT_scales,
     const int32_t* __restrict__ offs, int G, int64_t K, int parts)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kLdsBytes];
-    __shared__ uint32_t wave_max[4];
-    __shared__ uint32_t lut[2 * (kMaxGap + 1)];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
+    __shared__ __attribute__((aligned(16))) SlotInfo info[kSlots];
+    __shared__ __attribute__((aligned(16))) uint32_t lut[2 * (kMaxGap + 1)];
+    // per ring slot, per MX group: the max MX scale byte over each producer wave's 32 rows
+    __shared__ __attribute__((aligned(16))) uint32_t pmax[kSlots][8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-    const uint32_t nkt = (uint32_t)(K / kTileCols);
+    const uint32_t nkt = (uint32_t)((K + kTileCols - 1) / kTileCols);
     const uint32_t lambda = xcd_remap(blockIdx.x, gridDim.x);
     const uint32_t kt = lambda % nkt;
     const uint32_t part = lambda / nkt;
-
-    if (tid < 2 * (kMaxGap + 1))
-        lut[tid] = kColsGapLut.w[tid >> 1][tid & 1];
+    // the last tile is 128 columns wide when K is an odd multiple of 128
+    const int ncols = (int)min<int64_t>(kTileCols, K - (int64_t)kTileCols * kt);
 
     // strips of all experts; this workgroup takes strips [s0, s1) of column tile kt
-    const ExpertTable t0 = expert_chunk(offs, G, 0, 0, 0);
-    uint32_t n_strips = t0.total_s;
-    {
-        uint32_t run_s = t0.total_s, run_b = t0.total_b;
-        for (int g0 = 64; g0 < G; g0 += 64) {
-            const ExpertTable t = expert_chunk(offs, G, g0, run_s, run_b);
-            run_s += t.total_s;
-            run_b += t.total_b;
-        }
-        n_strips = run_s;
-    }
+    const ExpertTable t0 = expert_chunk(offs, G, 0, 0);
+    uint32_t n_strips = t0.total;
+    for (int g0 = 64; g0 < G; g0 += 64)
+        n_strips = uniform(n_strips + expert_chunk(offs, G, g0, n_strips).total);
     const uint32_t s0 = (uint32_t)(((uint64_t)n_strips * part) / (uint32_t)parts);
     const uint32_t s1 = (uint32_t)(((uint64_t)n_strips * (part + 1)) / (uint32_t)parts);
     if (s0 >= s1)
         return;                                   // uniform over the workgroup
+    const uint32_t n = s1 - s0;                   // steps 0..n-1 produce, 1..n consume
 
-    const int kc = lane & 3;                      // MX group inside the tile
-    const int rq = (lane >> 2) + 16 * wave;       // rows 4rq..4rq+3 of the strip
-    const int c = lane & 15;                      // stage B chunk
-    const uint32_t wbase = lds_row(32 * kc) + kData + 4 * rq;              // stage A writes
-    // stage B: wave (half hb, parity pb) converts output rows 64hb + 8pb + it + 16q
-    // (it = 0..7 steps, q = lane >> 4): rows 16 apart share their misalignment mod 16
-    const int hb = wave >> 1, pb = wave & 1;
-    const uint32_t kb0 = 64 * hb + 8 * pb + 16 * (lane >> 4);              // row at it = 0
-
-
-    // one strip is converted while the next one is loaded; the loop is unrolled by two
-    // so the two register sets alternate roles without copies
-    auto convert_strip = [&](const StripInfo& cur, RowsIn in, bool carry_in, bool carry_out) {
-        const int64_t r_lo = cur.r_lo;
-        const int nrows = cur.nrows;
-        mask_rows(in, nrows, rq);
-
-        // ---- stage A: block scales ---------------------------------------------------------
-        uint32_t m = max(max(in.s[0], in.s[1]), max(in.s[2], in.s[3]));
-        m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x124, 0xF, 0xF, false)); // row_ror:4
-        m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x128, 0xF, 0xF, false)); // row_ror:8
-        m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
-        const uint32_t packed = __builtin_amdgcn_readlane(m, 0) | (__builtin_amdgcn_readlane(m, 1) << 8) |
-                                (__builtin_amdgcn_readlane(m, 2) << 16) | (__builtin_amdgcn_readlane(m, 3) << 24);
-        if (lane == 0)
-            wave_max[wave] = packed;
-        __syncthreads();              // (1) wave maxima visible; every wave is past stage B
-        const uint32_t bmax = __builtin_amdgcn_readfirstlane(
-            __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
-                __builtin_bit_cast(u8x4, wave_max[wave & 2]), __builtin_bit_cast(u8x4, wave_max[(wave & 2) + 1]))));
-        const uint32_t S = (bmax >> (8 * kc)) & 0xFF;
-        if (tid < 16) {               // block scales: 2 blocks x 128 columns
-            const int blk = tid >> 3, piece = tid & 7;
-            if (kTileRows * blk < nrows) {
-                const uint32_t both = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
-                    __builtin_bit_cast(u8x4, wave_max[2 * blk]), __builtin_bit_cast(u8x4, wave_max[2 * blk + 1])));
-                const uint32_t w4 = ((both >> (8 * (piece >> 1))) & 0xFF) * 0x01010101u;
-                *reinterpret_cast<u32x4*>(yT_scales + K * (int64_t)(cur.bb + r_lo / kTileRows + blk) +
-                                          kTileCols * (int64_t)kt + 16 * piece) = u32x4{w4, w4, w4, w4};
-            }
-        }
-
-        // ---- stage A: convert, transpose, k-major into LDS ------------------------------
-        uint32_t E[4][4], O[4][4];    // [row][code dword]: even / odd codes of 8 columns
+    if (wave < kProducerWaves) {
+        // ================= producers =================
+        // wave w converts rows 32w..32w+31 of each strip; lane (rq, c) holds group c
+        // (tile columns 32c..32c+31) of rows 32w + 4rq .. + 3
+        const int c = lane & 7;
+        const int rq = lane >> 3;
+        const int row_q = 32 * wave + 4 * rq;     // first of the lane's four rows
+        // the narrow last tile has groups 0..3: lanes of groups 4..7 repeat group c - 4
+        // (their columns are never written out)
+        const uint32_t cl = 32 * c < ncols ? (uint32_t)c : (uint32_t)(c & 3);
+        const uint32_t cbyte = 16 * cl;
+        const uint32_t sbyte = 4 * (cl >> 2);
+        const uint32_t sshift = 8 * (cl & 3);
+        if (tid < 2 * (kMaxGap + 1))
+            lut[tid] = kColsGapLut.w[tid >> 1][tid & 1];
+        LaneRows lr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t d = min(S - in.s[i], (uint32_t)kMaxGap);
-            const uint32_t lo = lut[2 * d], hi = lut[2 * d + 1];
-            convert8_split(in.c[i].x, lo, hi, E[i][0], O[i][0]);
-            convert8_split(in.c[i].y, lo, hi, E[i][1], O[i][1]);
-            convert8_split(in.c[i].z, lo, hi, E[i][2], O[i][2]);
-            convert8_split(in.c[i].w, lo, hi, E[i][3], O[i][3]);
+            lr.c[i] = (uint32_t)(row_q + i) * (uint32_t)(K / 2) + cbyte;
+            lr.s[i] = (uint32_t)(row_q + i) * (uint32_t)(K / 32) + sbyte;
         }
-        // code dword q covers columns 8q..8q+7 of the group: even codes -> columns 8q+2m,
-        // odd codes -> 8q+2m+1; each transposed dword holds rows 4rq..4rq+3 of a column
+        // column 32c + j of the tile sits at LDS byte lds_col(32c) + 544 j
+        const uint32_t wbase = lds_col(32 * c) + row_q;
+
+        // the lane's four MX scale bytes (zero for rows past the strip)
+        auto row_scales = [&](const StripInfo& st, const RowsIn& in, uint32_t (&sc)[4]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint32_t e[4], o[4];
-            transpose4x4(E[0][q], E[1][q], E[2][q], E[3][q], e[0], e[1], e[2], e[3]);
-            transpose4x4(O[0][q], O[1][q], O[2][q], O[3][q], o[0], o[1], o[2], o[3]);
+            for (int i = 0; i < 4; ++i) {
+                sc[i] = __builtin_amdgcn_ubfe(in.s[i], sshift, 8);
+                if (st.nrows < kStripRows)
+                    sc[i] = row_q + i < st.nrows ? sc[i] : 0u;
+            }
+        };
+        // this wave's max scale of each group over its 32 rows, for the block scale of
+        // the strip (combined over the four producer waves after the next barrier)
+        auto publish_max = [&](const StripInfo& st, const RowsIn& in, uint32_t slot) {
+            uint32_t sc[4];
+            row_scales(st, in, sc);
+            uint32_t m = max(max(sc[0], sc[1]), max(sc[2], sc[3]));
+            m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x128, 0xF, 0xF, false)); // row_ror:8
+            m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+            if (rq == 0)
+                reinterpret_cast<uint8_t*>(pmax[slot])[4 * c + wave] = (uint8_t)m;
+        };
+
+        auto produce = [&](const StripInfo& st, const RowsIn& in, const uint32_t slot, const uint32_t flags) {
+            uint32_t sc[4];
+            row_scales(st, in, sc);
+            const u8x4 pm = __builtin_bit_cast(u8x4, pmax[slot][c]);
+            const uint32_t S = max(max((uint32_t)pm.x, (uint32_t)pm.y), max((uint32_t)pm.z, (uint32_t)pm.w));
+            if (wave == 0) {
+                if (rq == 0)
+                    reinterpret_cast<uint8_t*>(info[slot].S)[c] = (uint8_t)S;
+                if (lane == 0) {
+                    info[slot].A0 = K * st.row0 + st.r_lo + (int64_t)kTileCols * kt * st.mg;
+                    info[slot].mg = (int32_t)st.mg;
+                    info[slot].nrows = st.nrows;
+                    info[slot].blk = st.s;
+                    info[slot].flags = flags;
+                }
+            }
+            // convert each row with its own gap table (even / odd codes apart); rows past
+            // the strip have scale 0 and are converted from whatever was loaded: their
+            // bytes are never written out
+            uint32_t E[4][4], O[4][4];    // [row][code dword]
 #pragma unroll
-            for (int mm = 0; mm < 4; ++mm) {
-                *reinterpret_cast<uint32_t*>(tile + wbase + kLdsRowBytes * (8 * q + 2 * mm)) = e[mm];
-                *reinterpret_cast<uint32_t*>(tile + wbase + kLdsRowBytes * (8 * q + 2 * mm + 1)) = o[mm];
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t d = min(S - sc[i], (uint32_t)kMaxGap);
+                const u32x2 t = *reinterpret_cast<const u32x2*>(lut + 2 * d);
+                convert8_split(in.c[i].x, t.x, t.y, E[i][0], O[i][0]);
+                convert8_split(in.c[i].y, t.x, t.y, E[i][1], O[i][1]);
+                convert8_split(in.c[i].z, t.x, t.y, E[i][2], O[i][2]);
+                convert8_split(in.c[i].w, t.x, t.y, E[i][3], O[i][3]);
+            }
+            // code dword q covers columns 8q..8q+7 of the group: even codes -> columns
+            // 8q+2mm, odd codes -> 8q+2mm+1; each transposed dword holds the lane's four
+            // rows of one column
+            uint32_t T[32];               // T[j]: the four rows of column 32c + j
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                transpose4x4(E[0][q], E[1][q], E[2][q], E[3][q], T[8 * q + 0], T[8 * q + 2], T[8 * q + 4], T[8 * q + 6]);
+                transpose4x4(O[0][q], O[1][q], O[2][q], O[3][q], T[8 * q + 1], T[8 * q + 3], T[8 * q + 5], T[8 * q + 7]);
+            }
+            uint8_t* const w = tile + wbase + kStripRows * slot;
+#pragma unroll
+            for (int j = 0; j < 32; ++j)
+                *reinterpret_cast<uint32_t*>(w + kColBytes * j) = T[j];
+            // ring bytes 0..31 (rows 0..31 of slot 0) are repeated after the ring, so a
+            // 32-byte read window never wraps
+            if (slot == 0 && wave == 0) {
+#pragma unroll
+                for (int j = 0; j < 32; ++j)
+                    *reinterpret_cast<uint32_t*>(w + kRing + kColBytes * j) = T[j];
+            }
+        };
+        auto flags_of = [](uint32_t prev_sb, const StripInfo& cur, bool has_next, const StripInfo& next) {
+            return (prev_sb == cur.sb ? 1u : 0u) | (has_next && next.sb == cur.sb ? 2u : 0u);
+        };
+
+        // Step j converts strip j (register set j % 3) into ring slot j % 4; it first
+        // refills the set freed by step j - 1 with strip j + 2 (a repeat of the last
+        // strip past the range, so the load sequence never varies) and last publishes
+        // the per-wave scale maxima of strip j + 1.  Unrolled by three so the register
+        // sets keep fixed registers.
+        StripInfo I0 = locate(offs, G, t0, s0);
+        StripInfo I1 = 1 < n ? next_strip(offs, G, I0) : I0;
+        StripInfo I2;
+        RowsIn R0 = load_rows(codes, scales, K, I0, lr, row_q, cbyte, sbyte, kt);
+        RowsIn R1 = load_rows(codes, scales, K, I1, lr, row_q, cbyte, sbyte, kt);
+        RowsIn R2;
+        publish_max(I0, R0, 0);
+        uint32_t prev_sb = 0xFFFFFFFFu;
+        __syncthreads();                           // LUT and the maxima of strip 0
+        for (uint32_t j = 0;; j += 3) {
+            I2 = j + 2 < n ? next_strip(offs, G, I1) : I1;
+            R2 = load_rows(codes, scales, K, I2, lr, row_q, cbyte, sbyte, kt);
+            produce(I0, R0, j % kSlots, flags_of(prev_sb, I0, j + 1 < n, I1));
+            prev_sb = I0.sb;
+            if (j + 1 < n)
+                publish_max(I1, R1, (j + 1) % kSlots);
+            __syncthreads();
+            if (j + 1 >= n)
+                break;
+
+            I0 = j + 3 < n ? next_strip(offs, G, I2) : I2;
+            R0 = load_rows(codes, scales, K, I0, lr, row_q, cbyte, sbyte, kt);
+            produce(I1, R1, (j + 1) % kSlots, flags_of(prev_sb, I1, j + 2 < n, I2));
+            prev_sb = I1.sb;
+            if (j + 2 < n)
+                publish_max(I2, R2, (j + 2) % kSlots);
+            __syncthreads();
+            if (j + 2 >= n)
+                break;
+
+            I1 = j + 4 < n ? next_strip(offs, G, I0) : I0;
+            R1 = load_rows(codes, scales, K, I1, lr, row_q, cbyte, sbyte, kt);
+            produce(I2, R2, (j + 2) % kSlots, flags_of(prev_sb, I2, j + 3 < n, I0));
+            prev_sb = I2.sb;
+            if (j + 3 < n)
+                publish_max(I0, R0, (j + 3) % kSlots);
+            __syncthreads();
+            if (j + 3 >= n)
+                break;
+        }
+        __syncthreads();                           // the consumers' last step
+        return;
+    }
+
+    // ================= consumers =================
+    const int v = wave - kProducerWaves;          // 0..7
+    const int mc = lane >> 3;                     // column 2v + (it >> 1) + 16 mc + 128 (it & 1)
+    const int c = lane & 7;                       // bytes [16c, 16c + 16) of the line
+    // LDS ring of tile column u + 16 mc + 128 h (u < 16): lane part + 544 u
+    const uint32_t lb0 = lds_col(16 * mc);
+    const uint32_t lb1 = lds_col(16 * mc + 128);
+    ColState cs;
+    __syncthreads();                              // LUT written (setup)
+    __syncthreads();                              // step 0: strip 0 produced
+    for (uint32_t j = 1; j <= n; ++j) {
+        const uint32_t slot = (j - 1) % kSlots;
+        const int64_t A0 = uniform(info[slot].A0);
+        const int64_t mg = uniform(info[slot].mg);
+        const int64_t nrows = uniform(info[slot].nrows);
+        const uint32_t flags = uniform(info[slot].flags);
+        const bool cin = flags & 1u, cout = flags & 2u;
+        const uint32_t slot_base = kStripRows * slot;
+
+        // block scales of this strip: one byte per column, 16 lanes x 16 bytes
+        if (v == 0 && lane < 16 && 16 * lane < ncols) {
+            const uint32_t word = info[slot].S[lane >> 3];
+            const uint32_t w4 = ((word >> (8 * ((lane >> 1) & 3))) & 0xFFu) * 0x01010101u;
+            *reinterpret_cast<u32x4*>(yT_scales + K * (int64_t)uniform(info[slot].blk) + kTileCols * (int64_t)kt +
+                                      16 * lane) = u32x4{w4, w4, w4, w4};
+        }
+
+        // Output row k of expert g starts at byte K*offs[g] + k*M_g; this strip's bytes
+        // of tile column kk are [A, A + nrows) with A = A0 + kk*M_g.  Memory byte b of
+        // the column maps to ring byte slot_base + (b - A) (mod 512); since b is
+        // 16-aligned, the offset inside the aligned ring chunk is o = (-A) & 15 for every
+        // chunk of the 8 columns of an instruction (they are 16 apart).
+        if (!cin) {                               // a new run of strips of one expert
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const uint32_t kk = 2 * v + (it >> 1) + 16 * mc + 128 * (it & 1);
+                const int64_t A = A0 + (int64_t)kk * mg;
+                const uint32_t a = (uint32_t)A & 127;
+                cs.o[it] = uniform((uint32_t)(16 - (A & 15)) & 15);
+                cs.q[it] = 16 * c - a - cs.o[it];
+                cs.p[it] = yT + (A - a) + 16 * c;
             }
         }
-        __syncthreads();              // (2) tile complete
-
-        // ---- stage B: 16 lanes per output row, 4 rows per step, 32 rows per wave ---------
-        // Output row k of expert g starts at byte K*offs[g] + k*M_g; this strip's bytes
-        // are [A, A + nrows) with A = that + r_lo.  A row's stores advance a frontier on
-        // 128-byte line boundaries: with the previous strip's tail carried in, this strip
-        // writes from align128(A), and when the next strip continues the row it stops at
-        // the last line boundary, leaving the rest in the carry area.  So in the steady
-        // state every store belongs to a whole 128-byte line (16 lanes x 16 bytes = two
-        // lines per row).  Memory byte b of the row maps to LDS row byte kData + (b - A);
-        // since b is 16-aligned, the offset inside the aligned LDS chunk is
-        // o = (16 - (A & 15)) & 15 for every chunk of the four rows of a step.
-        int64_t A = K * cur.row0 + (kTileCols * (int64_t)kt + kb0) * cur.mg + r_lo;
-        const bool steady = carry_in && carry_out;
-#pragma unroll 2
-        for (int it = 0; it < 8; ++it, A += cur.mg) {
-            const uint32_t kl = kb0 + it;
-            const uint8_t* rowp = tile + lds_row(kl) + kData;          // LDS byte of strip byte 0
-            const uint32_t o = __builtin_amdgcn_readfirstlane((uint32_t)(16 - (A & 15)) & 15);
-            if (steady) {
-                const int64_t b0 = (A & ~(int64_t)127) + 16 * c;       // two whole lines
-                const uint8_t* src = rowp + (b0 - A) - o;              // 16-byte aligned
+        if (cin && cout) {
+            // steady state: the 8 lanes of a column write its whole line
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                if ((it & 1) && ncols <= 128)
+                    continue;                     // uniform: the narrow last tile
+                const uint32_t lb = (it & 1) ? lb1 : lb0;
+                const uint8_t* const src = tile + lb + kColBytes * (2 * v + (it >> 1)) +
+                                           ((cs.q[it] + slot_base) & (kRing - 1));
                 const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
-                u32x4 v = lo;
-                if (o != 0)
-                    v = window16(lo, *reinterpret_cast<const u32x4*>(src + 16), o);
-                *reinterpret_cast<u32x4*>(yT + b0) = v;
-            } else {
+                u32x4 val = lo;
+                if (cs.o[it] != 0)
+                    val = window16(lo, *reinterpret_cast<const u32x4*>(src + 16), cs.o[it]);
+                *reinterpret_cast<u32x4*>(cs.p[it]) = val;
+                cs.p[it] += kStripRows;
+            }
+        } else {
+            // the ends of a run: a column's bytes [W_lo, W_hi), partial lines byte-wise
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                if ((it & 1) && ncols <= 128)
+                    continue;
+                const uint32_t kk = 2 * v + (it >> 1) + 16 * mc + 128 * (it & 1);
+                const int64_t A = A0 + (int64_t)kk * mg;
+                const uint32_t o = cs.o[it];
                 const int64_t E = A + nrows;
-                const int64_t W_lo = carry_in ? (A & ~(int64_t)127) : A;
-                const int64_t W_hi = carry_out ? (E & ~(int64_t)127) : E;
+                const int64_t W_lo = cin ? (A & ~(int64_t)127) : A;
+                const int64_t W_hi = cout ? (E & ~(int64_t)127) : E;
                 const int64_t j0 = W_lo >> 4;                          // first 16-byte chunk
                 const int nch = W_hi > W_lo ? (int)(((W_hi + 15) >> 4) - j0) : 0;
+                const uint8_t* const colp = tile + ((it & 1) ? lb1 : lb0) + kColBytes * (2 * v + (it >> 1));
                 for (int pass = 0; pass < 2; ++pass) {
-                    const int jj = c + 16 * pass;
+                    const int jj = c + 8 * pass;
                     if (jj >= nch)
                         continue;
                     const int64_t b0 = (j0 + jj) << 4;
-                    const uint8_t* src = rowp + (b0 - A) - o;
-                    const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
-                    u32x4 v = lo;
+                    const uint32_t pos = (slot_base + (uint32_t)(b0 - A) - o) & (kRing - 1);
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(colp + pos);
+                    u32x4 val = lo;
                     if (o != 0)
-                        v = window16(lo, *reinterpret_cast<const u32x4*>(src + 16), o);
+                        val = window16(lo, *reinterpret_cast<const u32x4*>(colp + pos + 16), o);
                     if (b0 >= W_lo && b0 + 16 <= W_hi) {
-                        *reinterpret_cast<u32x4*>(yT + b0) = v;
+                        *reinterpret_cast<u32x4*>(yT + b0) = val;
                     } else {
-                        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                        const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
                         for (int q = 0; q < 16; ++q)
                             if (b0 + q >= W_lo && b0 + q < W_hi)
                                 yT[b0 + q] = (uint8_t)(w4[q >> 2] >> (8 * (q & 3)));
                     }
                 }
+                cs.p[it] += kStripRows;           // the next strip continues the run
             }
         }
-        // the next strip continues these rows: move the last 128 strip bytes of each of
-        // this wave's 32 rows into the carry area (only this wave reads these rows)
-        if (carry_out) {
-            const int r = lane >> 1;                                   // 0..31
-            uint8_t* row = tile + lds_row(64 * hb + 8 * pb + (r & 7) + 16 * (r >> 3)) + 64 * (lane & 1);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<u32x4*>(row + 16 + 16 * q) =
-                    *reinterpret_cast<const u32x4*>(row + kData + kStripRows - kCarryBytes + 16 * q);
-        }
-
-    };
-
-    StripInfo info = locate(offs, G, t0, s0);
-    RowsIn inA = load_rows(codes, scales, K, info.row0 + info.r_lo, info.nrows, rq, kc, kt);
-    RowsIn inB;
-    bool carry = false;                           // LDS carry areas hold the previous strip's tail
-    for (uint32_t s = s0; s < s1; s += 2) {
-        // strip s (registers A); load strip s + 1 (registers B) meanwhile
-        const bool has1 = s + 1 < s1;
-        const StripInfo info1 = has1 ? strip_after(offs, G, t0, info, s + 1) : info;
-        inB = load_rows(codes, scales, K, info1.row0 + info1.r_lo, info1.nrows, rq, kc, kt);
-        const bool c1 = has1 && info1.sb == info.sb;
-        convert_strip(info, inA, carry, c1);
-        if (!has1)
-            break;
-        // strip s + 1 (registers B); load strip s + 2 (registers A) meanwhile
-        const bool has2 = s + 2 < s1;
-        const StripInfo info2 = has2 ? strip_after(offs, G, t0, info1, s + 2) : info1;
-        inA = load_rows(codes, scales, K, info2.row0 + info2.r_lo, info2.nrows, rq, kc, kt);
-        const bool c2 = has2 && info2.sb == info1.sb;
-        convert_strip(info1, inB, c1, c2);
-        info = info2;
-        carry = c2;
+        __syncthreads();                          // step j: strip j produced, slot free
     }
 }
 
 int64_t cols_block_capacity(int64_t M_cap, int32_t G)
 {
-    return (M_cap + kTileRows - 1) / kTileRows + G;
+    return (M_cap + kStripRows - 1) / kStripRows + G;
 }
 
 static int device_cus()
@@ -440,11 +603,11 @@ hipError_t launch_fp8_cols(const uint8_t* codes, const uint8_t* scales, uint8_t*
 {
     if (M_cap == 0)
         return hipSuccess;
-    const int64_t nkt = K / kTileCols;
-    // one resident wave of workgroups: parts per column tile so that nkt * parts fills the
-    // GPU, but never more parts than the capacity in strips
-    const int64_t cap_strips = (M_cap + kStripRows - 1) / kStripRows + G;
-    int64_t parts = (int64_t)device_cus() * kWgPerCu / nkt;
+    const int64_t nkt = (K + kTileCols - 1) / kTileCols;
+    // one workgroup per compute unit (the LDS ring takes most of a CU's LDS): parts per
+    // column tile so that nkt * parts fills the GPU, never more parts than strips
+    const int64_t cap_strips = cols_block_capacity(M_cap, G);
+    int64_t parts = (int64_t)device_cus() / nkt;
     parts = parts < 1 ? 1 : parts;
     parts = parts > cap_strips ? cap_strips : parts;
     const int64_t grid = nkt * parts;
@@ -455,7 +618,7 @@ hipError_t launch_fp8_cols(const uint8_t* codes, const uint8_t* scales, uint8_t*
     int p = (int)parts;
     void* args[] = {(void*)&codes, (void*)&scales, (void*)&yT, (void*)&yT_scales, (void*)&offs,
                     (void*)&g, (void*)&k, (void*)&p};
-    return hipLaunchKernel((const void*)fp8_cols_kernel, dim3((unsigned)grid), dim3(kThreads), args,
+    return hipLaunchKernel((const void*)fp8_cols_kernel, dim3((unsigned)grid), dim3(kColsThreads), args,
                            0, stream);
 }
 

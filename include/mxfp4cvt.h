@@ -89,7 +89,7 @@ mxfp4_status mxfp4_to_fp8_rows(const uint8_t* codes, const uint8_t* scales, uint
  *              mxfp4_cols_scale_capacity(M_cap, K, G) bytes.
  *   Element (k, m') = e2m1(c) * 2^(s - S) rounded to nearest even, s the row's own
  *   MX scale.  Bytes past each expert's M_g (and past offs[G]) are not written.
- *   K must be a multiple of 128. */
+ *   K must be a multiple of 128 and at most 2^24 (larger K -> MXFP4_ERR_SHAPE). */
 mxfp4_status mxfp4_to_fp8_cols_ragged(const uint8_t* codes, const uint8_t* scales,
                                       uint8_t* yT_e4m3, uint8_t* yT_scales,
                                       const int32_t* group_offsets, int32_t G, int64_t M_cap,

@@ -99,6 +99,9 @@ def test_conversion_argument_errors(lib, fn):
     assert _r(lib, fn, ys=A4 + 3) == mx.MXFP4_ERR_ALIGN
     assert _r(lib, fn, o=OFFS + 1) == mx.MXFP4_ERR_ALIGN
     assert _r(lib, fn, M=0) == mx.MXFP4_OK
+    if fn == "mxfp4_to_fp8_cols_ragged":      # documented K limit of the column call
+        assert _r(lib, fn, M=1, K=(1 << 24) + 128) == mx.MXFP4_ERR_SHAPE
+        assert _r(lib, fn, M=0, K=1 << 24) == mx.MXFP4_OK
 
 
 def test_validate_offsets_argument_errors(lib):

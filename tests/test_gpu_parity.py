@@ -44,6 +44,8 @@ RAGGED = [
     ([1], 128, "normal", 0),
     ([0, 0, 0], 256, "normal", 64),                 # no rows at all, capacity left over
     ([200, 77, 513], 7168, "t3", 5),
+    ([129, 0, 300, 256], 640, "normal", 3),        # last 256-column tile is 128 wide
+    ([1, 383, 128], 384, "t3", 0),
 ]
 
 
