@@ -68,6 +68,10 @@ constexpr int kColBytes = kRing + kMirror;           // 544
 constexpr int kTileBytes = kTileCols * kColBytes + 32 * ((kTileCols - 1) / 32);
 constexpr int kProducerWaves = 4;
 constexpr int kConsumerWaves = 8;
+#ifndef MXFP4_COLS_PREFETCH
+#define MXFP4_COLS_PREFETCH 3
+#endif
+constexpr int kPrefetch = MXFP4_COLS_PREFETCH;    // strips of loads in flight per producer wave
 constexpr int kColsThreads = 64 * (kProducerWaves + kConsumerWaves);
 static_assert(kStripRows == 32 * kProducerWaves, "a producer wave converts 32 rows");
 static_assert(kTileCols == 32 * 8, "a producer lane converts one MX group of 8");
@@ -87,6 +91,32 @@ __device__ __forceinline__ int64_t uniform(int64_t x)
 __device__ __forceinline__ uint32_t lds_col(uint32_t kk)
 {
     return kColBytes * kk + 32 * (kk >> 5);
+}
+
+// ---- progress counters in LDS --------------------------------------------------------
+
+// Polls of a counter before a wave gives up (about a second): only a broken protocol
+// could wait that long, and the wave then leaves the kernel instead of hanging.
+constexpr uint32_t kSpinLimit = 1u << 24;
+
+// Wait (wave-uniformly) until *ctr >= target.  The acquire orders this wave's later
+// LDS reads after the writes that the counter's release published.
+__device__ __forceinline__ bool wait_at_least(uint32_t* ctr, uint32_t target)
+{
+    for (uint32_t i = 0; i < kSpinLimit; ++i) {
+        if (uniform(__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) >= target)
+            return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
+// Count this wave's step as done: the release waits for the wave's own LDS accesses
+// (writes it publishes, reads of a slot it frees) before the increment.
+__device__ __forceinline__ void signal(uint32_t* ctr)
+{
+    if ((threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // 4x4 byte transpose: a[i] holds bytes (row i, col 0..3); o[j] gets bytes (row 0..3, col j).
@@ -234,49 +264,48 @@ struct SlotInfo {
 
 // ---- producers ---------------------------------------------------------------------------
 
-struct RowsIn {
-    u32x4 c[4];                // 32 codes of the lane's group, rows 4rq..4rq+3 of its 32
-    uint32_t s[4];             // the aligned dword holding each row's MX scale byte
+// A lane's four rows of a strip: eight consecutive lanes read one row's whole 128-byte
+// line of codes, so a load instruction touches 8 lines.  Scales are loaded as whole
+// dwords (a byte load would be zero-extended where the loop carries it, which makes the
+// compiler wait for the prefetched loads early); the byte is extracted at use.  Row
+// offsets within a strip fit in 32 bits (128 rows x K/2 bytes with K <= 2^24).
+struct Codes {
+    u32x4 c[4];                // 32 codes of the lane's group for each of its four rows
+};
+struct Scales {
+    uint32_t s;                // lane L: dword L & 1 of the 8 scale bytes of wave row L >> 1
 };
 
-// Byte offsets of the lane's four rows inside a strip: its 16 code bytes and the dword
-// holding the scale byte of its group, relative to the strip's first row of the tile
-// (fit in 32 bits: 128 rows x K/2 bytes with K <= 2^24).  Eight consecutive lanes read
-// one row's whole 128-byte line of codes, so a load instruction touches 8 lines.
-// Scales are loaded as whole dwords (a byte load would be zero-extended where the loop
-// carries it, which makes the compiler wait for the prefetched loads early); the byte
-// is extracted at use.
-struct LaneRows {
-    uint32_t c[4], s[4];
-};
-
-// Loads are unconditional (rows past the strip are clamped to its last row and zeroed
-// after the load), so every strip issues the same straight-line sequence of loads and
-// the compiler can wait for exactly the loads it needs.
-__device__ __forceinline__ RowsIn load_rows(const uint8_t* __restrict__ codes,
-                                            const uint8_t* __restrict__ scales, int64_t K,
-                                            const StripInfo& st, const LaneRows& lr, int row_q,
-                                            uint32_t cbyte, uint32_t sbyte, uint32_t kt)
+// Loads are unconditional (rows past the strip are clamped to its last row and masked
+// at use), so every strip issues the same straight-line sequence of loads and the
+// compiler can wait for exactly the loads it needs.
+__device__ __forceinline__ Codes load_codes(const uint8_t* __restrict__ codes, int64_t K,
+                                            const StripInfo& st, int row_q, uint32_t cbyte, uint32_t kt)
 {
-    RowsIn in;
-    const int64_t row_first = st.row0 + st.r_lo;                      // uniform
-    const uint8_t* const cb = codes + row_first * (K / 2) + 128 * (int64_t)kt;
-    const uint8_t* const sb = scales + row_first * (K / 32) + 8 * (int64_t)kt;
-    if (st.nrows == kStripRows) {
+    Codes in;
+    const uint8_t* const cb = codes + (st.row0 + st.r_lo) * (K / 2) + 128 * (int64_t)kt;
+    const uint32_t kc = (uint32_t)(K / 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            in.c[i] = *reinterpret_cast<const u32x4*>(cb + lr.c[i]);
-            in.s[i] = *reinterpret_cast<const uint32_t*>(sb + lr.s[i]);
-        }
-    } else {
-        const uint32_t kc = (uint32_t)(K / 2), ks = (uint32_t)(K / 32);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t r = (uint32_t)min(row_q + i, st.nrows - 1);
-            in.c[i] = *reinterpret_cast<const u32x4*>(cb + (r * kc + cbyte));
-            in.s[i] = *reinterpret_cast<const uint32_t*>(sb + (r * ks + sbyte));
-        }
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t r = (uint32_t)min(row_q + i, st.nrows - 1);
+        in.c[i] = *reinterpret_cast<const u32x4*>(cb + (r * kc + cbyte));
     }
+    return in;
+}
+
+// The 8 scale bytes (groups 0..7 of the tile) of the wave's 32 rows: one dword per lane,
+// a single load instruction per strip; lanes fetch their own rows' bytes with
+// ds_bpermute at use.  The narrow last tile has groups 0..3 only (one dword per row).
+__device__ __forceinline__ Scales load_scales(const uint8_t* __restrict__ scales, int64_t K,
+                                              const StripInfo& st, int wave_row0, bool narrow,
+                                              uint32_t kt)
+{
+    Scales in;
+    const uint8_t* const sb = scales + (st.row0 + st.r_lo) * (K / 32) + 8 * (int64_t)kt;
+    const int lane = threadIdx.x & 63;
+    const uint32_t r = (uint32_t)min(wave_row0 + (lane >> 1), st.nrows - 1);
+    const uint32_t dw = narrow ? 0u : (uint32_t)(lane & 1);
+    in.s = *reinterpret_cast<const uint32_t*>(sb + (r * (uint32_t)(K / 32) + 4 * dw));
     return in;
 }
 
@@ -306,6 +335,9 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     __shared__ __attribute__((aligned(16))) uint32_t lut[2 * (kMaxGap + 1)];
     // per ring slot, per MX group: the max MX scale byte over each producer wave's 32 rows
     __shared__ __attribute__((aligned(16))) uint32_t pmax[kSlots][8];
+    // progress: strips written by producer waves, partial maxima published by producer
+    // waves, and per ring slot the strips drained by consumer waves (all monotonic)
+    __shared__ uint32_t produced, published, drained[kSlots];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -326,7 +358,17 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     const uint32_t s1 = (uint32_t)(((uint64_t)n_strips * (part + 1)) / (uint32_t)parts);
     if (s0 >= s1)
         return;                                   // uniform over the workgroup
-    const uint32_t n = s1 - s0;                   // steps 0..n-1 produce, 1..n consume
+    const uint32_t n = s1 - s0;                   // strips of this workgroup
+
+    if (tid < 2 * (kMaxGap + 1))
+        lut[tid] = kColsGapLut.w[tid >> 1][tid & 1];
+    if (tid == 0) {
+        produced = 0;
+        published = 0;
+        for (int k = 0; k < kSlots; ++k)
+            drained[k] = 0;
+    }
+    __syncthreads();                              // the only barrier: LUT and counters set
 
     if (wave < kProducerWaves) {
         // ================= producers =================
@@ -339,34 +381,31 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
         // (their columns are never written out)
         const uint32_t cl = 32 * c < ncols ? (uint32_t)c : (uint32_t)(c & 3);
         const uint32_t cbyte = 16 * cl;
-        const uint32_t sbyte = 4 * (cl >> 2);
         const uint32_t sshift = 8 * (cl & 3);
-        if (tid < 2 * (kMaxGap + 1))
-            lut[tid] = kColsGapLut.w[tid >> 1][tid & 1];
-        LaneRows lr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            lr.c[i] = (uint32_t)(row_q + i) * (uint32_t)(K / 2) + cbyte;
-            lr.s[i] = (uint32_t)(row_q + i) * (uint32_t)(K / 32) + sbyte;
-        }
         // column 32c + j of the tile sits at LDS byte lds_col(32c) + 544 j
         const uint32_t wbase = lds_col(32 * c) + row_q;
 
         // the lane's four MX scale bytes (zero for rows past the strip)
-        auto row_scales = [&](const StripInfo& st, const RowsIn& in, uint32_t (&sc)[4]) {
+        struct RowScales {
+            uint32_t b[4];
+        };
+        auto row_scales = [&](const StripInfo& st, const Scales& in) {
+            RowScales sc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                sc[i] = __builtin_amdgcn_ubfe(in.s[i], sshift, 8);
+                // wave row 4rq + i sits in lanes 2 (4rq + i) and 2 (4rq + i) + 1
+                const int src = 2 * (4 * rq + i) + (int)(cl >> 2);
+                const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src, (int)in.s);
+                sc.b[i] = __builtin_amdgcn_ubfe(w, sshift, 8);
                 if (st.nrows < kStripRows)
-                    sc[i] = row_q + i < st.nrows ? sc[i] : 0u;
+                    sc.b[i] = row_q + i < st.nrows ? sc.b[i] : 0u;
             }
+            return sc;
         };
         // this wave's max scale of each group over its 32 rows, for the block scale of
-        // the strip (combined over the four producer waves after the next barrier)
-        auto publish_max = [&](const StripInfo& st, const RowsIn& in, uint32_t slot) {
-            uint32_t sc[4];
-            row_scales(st, in, sc);
-            uint32_t m = max(max(sc[0], sc[1]), max(sc[2], sc[3]));
+        // the strip (combined over the four producer waves once all have published)
+        auto publish_max = [&](const RowScales& sc, uint32_t slot) {
+            uint32_t m = max(max(sc.b[0], sc.b[1]), max(sc.b[2], sc.b[3]));
             m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x128, 0xF, 0xF, false)); // row_ror:8
             m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
             m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
@@ -374,9 +413,8 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                 reinterpret_cast<uint8_t*>(pmax[slot])[4 * c + wave] = (uint8_t)m;
         };
 
-        auto produce = [&](const StripInfo& st, const RowsIn& in, const uint32_t slot, const uint32_t flags) {
-            uint32_t sc[4];
-            row_scales(st, in, sc);
+        auto produce = [&](const StripInfo& st, const Codes& in, const RowScales& sc, const uint32_t slot,
+                           const uint32_t flags) {
             const u8x4 pm = __builtin_bit_cast(u8x4, pmax[slot][c]);
             const uint32_t S = max(max((uint32_t)pm.x, (uint32_t)pm.y), max((uint32_t)pm.z, (uint32_t)pm.w));
             if (wave == 0) {
@@ -396,7 +434,7 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
             uint32_t E[4][4], O[4][4];    // [row][code dword]
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t d = min(S - sc[i], (uint32_t)kMaxGap);
+                const uint32_t d = min(S - sc.b[i], (uint32_t)kMaxGap);
                 const u32x2 t = *reinterpret_cast<const u32x2*>(lut + 2 * d);
                 convert8_split(in.c[i].x, t.x, t.y, E[i][0], O[i][0]);
                 convert8_split(in.c[i].y, t.x, t.y, E[i][1], O[i][1]);
@@ -428,53 +466,55 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
             return (prev_sb == cur.sb ? 1u : 0u) | (has_next && next.sb == cur.sb ? 2u : 0u);
         };
 
-        // Step j converts strip j (register set j % 3) into ring slot j % 4; it first
-        // refills the set freed by step j - 1 with strip j + 2 (a repeat of the last
-        // strip past the range, so the load sequence never varies) and last publishes
-        // the per-wave scale maxima of strip j + 1.  Unrolled by three so the register
-        // sets keep fixed registers.
-        StripInfo I0 = locate(offs, G, t0, s0);
-        StripInfo I1 = 1 < n ? next_strip(offs, G, I0) : I0;
-        StripInfo I2;
-        RowsIn R0 = load_rows(codes, scales, K, I0, lr, row_q, cbyte, sbyte, kt);
-        RowsIn R1 = load_rows(codes, scales, K, I1, lr, row_q, cbyte, sbyte, kt);
-        RowsIn R2;
-        publish_max(I0, R0, 0);
+        // Loads run kPrefetch strips ahead of the conversion (repeats of the last strip
+        // past the range, so the load sequence never varies): under a full store
+        // stream a load takes several strip-times to land.  Step t waits until the
+        // consumers have drained strip t - 3 (whose slot carries into strip t - 2, the
+        // last reader of slot t % 4) and until all producer waves have published their
+        // partial maxima of strip t, converts strip t, signals it, and publishes its own
+        // partial maxima of strip t + 1.  Register sets rotate over kPrefetch + 1 strips;
+        // the loop is unrolled by that much so each set keeps fixed registers.
+        constexpr int kSets = kPrefetch + 1;
         uint32_t prev_sb = 0xFFFFFFFFu;
-        __syncthreads();                           // LUT and the maxima of strip 0
-        for (uint32_t j = 0;; j += 3) {
-            I2 = j + 2 < n ? next_strip(offs, G, I1) : I1;
-            R2 = load_rows(codes, scales, K, I2, lr, row_q, cbyte, sbyte, kt);
-            produce(I0, R0, j % kSlots, flags_of(prev_sb, I0, j + 1 < n, I1));
-            prev_sb = I0.sb;
-            if (j + 1 < n)
-                publish_max(I1, R1, (j + 1) % kSlots);
-            __syncthreads();
-            if (j + 1 >= n)
-                break;
-
-            I0 = j + 3 < n ? next_strip(offs, G, I2) : I2;
-            R0 = load_rows(codes, scales, K, I0, lr, row_q, cbyte, sbyte, kt);
-            produce(I1, R1, (j + 1) % kSlots, flags_of(prev_sb, I1, j + 2 < n, I2));
-            prev_sb = I1.sb;
-            if (j + 2 < n)
-                publish_max(I2, R2, (j + 2) % kSlots);
-            __syncthreads();
-            if (j + 2 >= n)
-                break;
-
-            I1 = j + 4 < n ? next_strip(offs, G, I0) : I0;
-            R1 = load_rows(codes, scales, K, I1, lr, row_q, cbyte, sbyte, kt);
-            produce(I2, R2, (j + 2) % kSlots, flags_of(prev_sb, I2, j + 3 < n, I0));
-            prev_sb = I2.sb;
-            if (j + 3 < n)
-                publish_max(I0, R0, (j + 3) % kSlots);
-            __syncthreads();
-            if (j + 3 >= n)
-                break;
+        StripInfo I[kSets];
+        Codes C[kSets];
+        Scales Sc[kSets];
+        I[0] = locate(offs, G, t0, s0);
+#pragma unroll
+        for (int u = 1; u < kPrefetch; ++u)
+            I[u] = (uint32_t)u < n ? next_strip(offs, G, I[u - 1]) : I[u - 1];
+#pragma unroll
+        for (int u = 0; u < kPrefetch; ++u) {
+            Sc[u] = load_scales(scales, K, I[u], 32 * wave, ncols <= 128, kt);
+            C[u] = load_codes(codes, K, I[u], row_q, cbyte, kt);
         }
-        __syncthreads();                           // the consumers' last step
-        return;
+        RowScales sc = row_scales(I[0], Sc[0]);   // strip t
+        publish_max(sc, 0);
+        signal(&published);
+        for (uint32_t t = 0;; t += kSets) {
+#pragma unroll
+            for (int u = 0; u < kSets; ++u) {
+                const uint32_t tt = t + u;
+                const int ld = (u + kPrefetch) % kSets;          // set receiving strip tt + kPrefetch
+                const int pv = (u + kPrefetch - 1) % kSets;      // set of strip tt + kPrefetch - 1
+                I[ld] = tt + kPrefetch < n ? next_strip(offs, G, I[pv]) : I[pv];
+                Sc[ld] = load_scales(scales, K, I[ld], 32 * wave, ncols <= 128, kt);
+                C[ld] = load_codes(codes, K, I[ld], row_q, cbyte, kt);
+                const int nx = (u + 1) % kSets;                  // set of strip tt + 1
+                if (tt >= 3 && !wait_at_least(&drained[(tt - 3) % kSlots], kConsumerWaves * ((tt - 3) / kSlots + 1)))
+                    return;
+                if (!wait_at_least(&published, kProducerWaves * (tt + 1)))
+                    return;
+                produce(I[u], C[u], sc, tt % kSlots, flags_of(prev_sb, I[u], tt + 1 < n, I[nx]));
+                prev_sb = I[u].sb;
+                signal(&produced);
+                if (tt + 1 >= n)
+                    return;
+                sc = row_scales(I[nx], Sc[nx]);
+                publish_max(sc, (tt + 1) % kSlots);
+                signal(&published);
+            }
+        }
     }
 
     // ================= consumers =================
@@ -485,10 +525,10 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     const uint32_t lb0 = lds_col(16 * mc);
     const uint32_t lb1 = lds_col(16 * mc + 128);
     ColState cs;
-    __syncthreads();                              // LUT written (setup)
-    __syncthreads();                              // step 0: strip 0 produced
-    for (uint32_t j = 1; j <= n; ++j) {
-        const uint32_t slot = (j - 1) % kSlots;
+    for (uint32_t t = 0; t < n; ++t) {
+        if (!wait_at_least(&produced, kProducerWaves * (t + 1)))
+            return;
+        const uint32_t slot = t % kSlots;
         const int64_t A0 = uniform(info[slot].A0);
         const int64_t mg = uniform(info[slot].mg);
         const int64_t nrows = uniform(info[slot].nrows);
@@ -573,7 +613,7 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                 cs.p[it] += kStripRows;           // the next strip continues the run
             }
         }
-        __syncthreads();                          // step j: strip j produced, slot free
+        signal(&drained[slot]);                   // this wave is done with the slot
     }
 }
 
