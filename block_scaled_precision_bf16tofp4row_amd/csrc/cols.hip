@@ -20,37 +20,38 @@
 // numbered in expert order (strip s is row s of the block-scale output).  The grid
 // is persistent, one workgroup per compute unit: each owns a 256-column tile (eight
 // MX groups, so every row it reads is one whole 128-byte line of codes) and a
-// contiguous range of strips.  Its eight waves have two roles, so that no wave
-// both loads and stores (a wave's loads and stores share one in-order completion
-// counter, and waiting for a load must not wait for older stores):
-//   producers (waves 0-3)  wave w converts MX groups 2w, 2w+1 of a strip: lane
-//            (half = lane >> 5, rq = lane & 31) holds the 16 code bytes of rows
-//            4rq..4rq+3 of group 2w + half and their scale bytes, loaded two strips
-//            ahead.  The block scale of a group is a max over the 32 lanes of that
-//            half (DPP inside the wave).  Each row is converted with the gap table
-//            of its own scale, 4x4 byte transposes turn 4 rows x 32 columns into 32
-//            dwords (4 rows of one column each), written into a k-major LDS ring:
-//            one LDS row per output column k holding the last three strips' bytes
-//            of that column in order;
-//   consumers (waves 4-7)  write the previous strip: 8 lanes per output column, lane
-//            c stores the 16-byte aligned chunk c of the column's output range, 8
-//            columns per instruction.  Those 8 columns are 16 apart, so their
-//            misalignment (mod 16) is the same and the realignment is two aligned
-//            16-byte LDS reads plus v_alignbyte_b32 under a wave-uniform branch.  A
-//            column's stores advance on 128-byte line boundaries: the bytes past a
-//            strip's last line boundary stay in the ring and are written with the
-//            next strip, so in the steady state every store belongs to a whole
-//            128-byte line (partial lines cost the memory system a read-modify-
+// contiguous range of strips.  Its twelve waves have two roles, so that no wave both
+// loads and stores (a wave's loads and stores share one in-order completion counter,
+// and waiting for a load must not wait for older stores):
+//   producers (waves 0-3)   wave w converts rows 32w..32w+31 of every strip: lane
+//            (rq = lane >> 3, c = lane & 7) holds the 16 code bytes of group c for
+//            rows 32w + 4rq .. + 3, loaded three strips ahead.  The block scale of a
+//            group is the max over the strip's 128 rows: each wave reduces its 32
+//            rows (DPP and lane shuffles) and publishes the partial max in LDS, and
+//            every wave takes the max of the four.  Each row is converted with the
+//            gap table of its own scale; 4x4 byte transposes turn 4 rows x 32 columns
+//            into 32 dwords (4 rows of one column each), written into a k-major LDS
+//            ring: one ring per output column k holding the column's bytes of the
+//            last four strips in order;
+//   consumers (waves 4-11)  write the output lines of the strip before: 8 lanes per
+//            output column, lane c stores bytes [16c, 16c + 16) of the column's
+//            128-byte line, 8 columns per instruction.  Those 8 columns are 16 apart,
+//            so their misalignment (mod 16) is the same and the realignment is two
+//            aligned 16-byte LDS reads plus v_alignbyte_b32 under a wave-uniform
+//            branch.  A column's stores advance on 128-byte line boundaries: the
+//            bytes past a strip's last line boundary stay in the ring and go out with
+//            the next strip, so in the steady state every store covers whole
+//            128-byte lines (a partial line costs the memory system a read-modify-
 //            write).  Only at the ends of a workgroup's run inside an expert are
-//            partial lines written.
-// One barrier per step: producers fill ring slot j % 3 with strip j while consumers
-// write strip j - 1 (whose carried-in bytes sit in slot (j - 2) % 3).
-// LDS skew: column k's ring starts at byte 384k + 128 ((k >> 4) + (k >> 5)).  The
-// producers' dword writes cover columns k and k + 32 (32 rows each, k < 32 mod 64)
-// and the consumers' 16-byte reads columns k and k + 16 (128 bytes each, k < 16 mod
-// 32); each pair is an odd multiple of 128 bytes apart, so it falls in disjoint
-// halves of the banks.  This plays the role of the page's padded, skewed
-// shared-memory layout.
+//            partial lines written.  The output is written once and never re-read
+//            here, so the stores are streaming (non-temporal).
+// Synchronisation is by monotonic counters in LDS (no barrier inside the strip loop):
+// the producers count strips converted and partial maxima published, the consumers
+// count per ring slot the strips drained; every wait is bounded (a wave that waits
+// about a second gives up and leaves the kernel instead of hanging).
+// LDS layout: column k's ring (512 bytes, with its first 32 bytes repeated after it so
+// a 32-byte read window never wraps) starts at byte 544k + 32 (k >> 5).  This plays the
+// role of the page's padded, skewed shared-memory layout against bank conflicts.
 #include "common.h"
 
 namespace mxfp4 {
@@ -573,7 +574,7 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                 u32x4 val = lo;
                 if (cs.o[it] != 0)
                     val = window16(lo, *reinterpret_cast<const u32x4*>(src + 16), cs.o[it]);
-                *reinterpret_cast<u32x4*>(cs.p[it]) = val;
+                store_stream(reinterpret_cast<u32x4*>(cs.p[it]), val);
                 cs.p[it] += kStripRows;
             }
         } else {
@@ -602,7 +603,7 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                     if (o != 0)
                         val = window16(lo, *reinterpret_cast<const u32x4*>(colp + pos + 16), o);
                     if (b0 >= W_lo && b0 + 16 <= W_hi) {
-                        *reinterpret_cast<u32x4*>(yT + b0) = val;
+                        store_stream(reinterpret_cast<u32x4*>(yT + b0), val);
                     } else {
                         const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
                         for (int q = 0; q < 16; ++q)
