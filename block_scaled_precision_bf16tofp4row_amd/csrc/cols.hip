@@ -258,8 +258,9 @@ struct SlotInfo {
     int32_t mg;                // rows of the expert (= output row length)
     int32_t nrows;             // rows in the strip
     uint32_t blk;              // row of the block-scale output
-    uint32_t flags;            // bit 0: the previous strip continues the same rows;
-                               // bit 1: the next strip does
+    uint32_t flags;            // bit 0: the ring holds the previous strip of the same expert;
+                               // bit 1: the next strip (of the whole numbering) is of the
+                               // same expert; bit 2: lead-in strip (write nothing)
     uint32_t S[2];             // block scale byte of MX groups 0..7 of the tile
 };
 
@@ -359,7 +360,14 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     const uint32_t s1 = (uint32_t)(((uint64_t)n_strips * (part + 1)) / (uint32_t)parts);
     if (s0 >= s1)
         return;                                   // uniform over the workgroup
-    const uint32_t n = s1 - s0;                   // strips of this workgroup
+    // A range that starts inside an expert also converts the strip before it (a lead-in
+    // strip that writes nothing): its bytes past its last line boundary complete the
+    // first output line of the range, so the workgroup writes that line whole and the
+    // workgroup before it stops at its last line boundary.  Lines split between two
+    // workgroups would otherwise be written partially twice.
+    const StripInfo first = locate(offs, G, t0, s0);
+    const uint32_t lead = first.s > first.sb ? 1u : 0u;
+    const uint32_t n = s1 - s0 + lead;            // strips this workgroup converts
 
     if (tid < 2 * (kMaxGap + 1))
         lut[tid] = kColsGapLut.w[tid >> 1][tid & 1];
@@ -463,8 +471,8 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                     *reinterpret_cast<uint32_t*>(w + kRing + kColBytes * j) = T[j];
             }
         };
-        auto flags_of = [](uint32_t prev_sb, const StripInfo& cur, bool has_next, const StripInfo& next) {
-            return (prev_sb == cur.sb ? 1u : 0u) | (has_next && next.sb == cur.sb ? 2u : 0u);
+        auto flags_of = [](uint32_t prev_sb, const StripInfo& cur, bool lead_in) {
+            return (prev_sb == cur.sb ? 1u : 0u) | (cur.s + 1 < cur.sb + cur.ns ? 2u : 0u) | (lead_in ? 4u : 0u);
         };
 
         // Loads run kPrefetch strips ahead of the conversion (repeats of the last strip
@@ -480,7 +488,9 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
         StripInfo I[kSets];
         Codes C[kSets];
         Scales Sc[kSets];
-        I[0] = locate(offs, G, t0, s0);
+        I[0] = first;
+        I[0].s -= lead;
+        set_rows(I[0]);
 #pragma unroll
         for (int u = 1; u < kPrefetch; ++u)
             I[u] = (uint32_t)u < n ? next_strip(offs, G, I[u - 1]) : I[u - 1];
@@ -506,7 +516,7 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                     return;
                 if (!wait_at_least(&published, kProducerWaves * (tt + 1)))
                     return;
-                produce(I[u], C[u], sc, tt % kSlots, flags_of(prev_sb, I[u], tt + 1 < n, I[nx]));
+                produce(I[u], C[u], sc, tt % kSlots, flags_of(prev_sb, I[u], tt == 0 && lead != 0));
                 prev_sb = I[u].sb;
                 signal(&produced);
                 if (tt + 1 >= n)
@@ -534,11 +544,11 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
         const int64_t mg = uniform(info[slot].mg);
         const int64_t nrows = uniform(info[slot].nrows);
         const uint32_t flags = uniform(info[slot].flags);
-        const bool cin = flags & 1u, cout = flags & 2u;
+        const bool cin = flags & 1u, cout = flags & 2u, skip = flags & 4u;
         const uint32_t slot_base = kStripRows * slot;
 
         // block scales of this strip: one byte per column, 16 lanes x 16 bytes
-        if (v == 0 && lane < 16 && 16 * lane < ncols) {
+        if (!skip && v == 0 && lane < 16 && 16 * lane < ncols) {
             const uint32_t word = info[slot].S[lane >> 3];
             const uint32_t w4 = ((word >> (8 * ((lane >> 1) & 3))) & 0xFFu) * 0x01010101u;
             *reinterpret_cast<u32x4*>(yT_scales + K * (int64_t)uniform(info[slot].blk) + kTileCols * (int64_t)kt +
@@ -561,7 +571,13 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                 cs.p[it] = yT + (A - a) + 16 * c;
             }
         }
-        if (cin && cout) {
+        if (skip) {
+            // lead-in strip: its lines up to its last line boundary belong to the
+            // workgroup before; the rest stays in the ring for the next strip
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                cs.p[it] += kStripRows;
+        } else if (cin && cout) {
             // steady state: the 8 lanes of a column write its whole line
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
