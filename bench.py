@@ -13,10 +13,14 @@ are resident in HBM before the timed region.  ``value`` is algorithmic bytes per
 step / wall time per step.  ``roofline`` reports the dominant kernel (largest
 time per step): algorithmic bytes per launch / its mean launch time, measured
 with HIP events on the launch stream inside the timed region, against the
-8 TB/s HBM peak.  ``cpu_baseline`` times the CPU oracle on a bounded sample of
-the same workload on this host.
+8 TB/s HBM peak.  ``per_config_scrubbed`` adds, for the dispatch workload
+(32768 x 7168 over 32 experts), the dense workload (65536 x 7168) and the
+forward chain, every launch's median over 20 launches each preceded by a 512 MB
+scrub read (so inputs come from HBM, not the caches), next to a device copy
+moving the same bytes.  ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same workload on this host (all allowed threads, and one thread).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload config5]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload config5] [--no-scrubbed]
 """
 from __future__ import annotations
 
@@ -125,6 +129,14 @@ def cpu_baseline(workload, target_s: float = 15.0):
     rows = max(128, rows - rows % 128)
     b, t = run(rows)
     frac = rows / max_rows
+    # the plain single-threaded oracle on a smaller sample (about a third of the time)
+    threads_all = threads
+    threads = 1
+    b1, t1 = run(probe_rows)
+    rows1 = max(128, int(probe_rows * (target_s / 3) / max(t1, 1e-6)) // 128 * 128)
+    rows1 = min(rows1, max_rows - max_rows % 128 or 128)
+    b1, t1 = run(rows1)
+    threads = threads_all
     return {
         "value": round(b / t / 1e9, 4),
         "unit": "GB/s",
@@ -133,7 +145,101 @@ def cpu_baseline(workload, target_s: float = 15.0):
         "sample": (f"first {rows} of {max_rows} routed rows of every segment "
                    f"({frac:.1%} of a step: the same kernels, offsets clipped to the sample), "
                    f"{t:.1f} s wall on {threads} threads"),
+        "single_thread": {"value": round(b1 / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                          "sample": f"first {rows1} routed rows of every segment, {t1:.1f} s wall"},
     }
+
+
+# ---- per-kernel timing with the caches scrubbed -----------------------------------------
+
+def build_launches(mx, workload, dev, torch):
+    """Buffers and the ordered launches (kernel, segment, fn, algorithmic bytes) of one
+    step of a workload: quantize -> rows -> cols per segment, as the workload lists."""
+    segs = []
+    for seg in workload.segments:
+        x = torch.from_numpy(seg.x_bits.view(np.int16)).to(dev)
+        offs = torch.from_numpy(seg.offs).to(dev)
+        codes, scales = mx.alloc_quantize_outputs(seg.M_cap, seg.K, dev)
+        d = {"seg": seg, "x": x, "offs": offs, "codes": codes, "scales": scales}
+        if "rows" in workload.kernels:
+            d["y"], d["ys"] = mx.alloc_rows_outputs(seg.M_cap, seg.K, dev)
+        if "cols" in workload.kernels:
+            d["yT"], d["ysT"] = mx.alloc_cols_outputs(seg.M_cap, seg.K, seg.G, dev)
+            nb = (np.diff(seg.offs.astype(np.int64)) + 127) // 128
+            d["col_scale_bytes"] = int(nb.sum()) * seg.K
+        segs.append(d)
+    launches = []
+    for d in segs:
+        seg = d["seg"]
+        launches.append(("quantize", seg.name,
+                         lambda d=d: mx.mxfp4_quantize_rows(d["x"], d["codes"], d["scales"], d["offs"]),
+                         alg_bytes("quantize", seg.M_tot, seg.K)))
+        if "rows" in workload.kernels:
+            launches.append(("rows", seg.name,
+                             lambda d=d: mx.mxfp4_to_fp8_rows(d["codes"], d["scales"], d["y"], d["ys"],
+                                                              d["offs"]),
+                             alg_bytes("rows", seg.M_tot, seg.K)))
+        if "cols" in workload.kernels:
+            launches.append(("cols", seg.name,
+                             lambda d=d: mx.mxfp4_to_fp8_cols_ragged(d["codes"], d["scales"], d["yT"],
+                                                                     d["ysT"], d["offs"]),
+                             alg_bytes("cols", seg.M_tot, seg.K, d["col_scale_bytes"])))
+    return segs, launches
+
+
+def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=512 << 20):
+    """Per launch of each workload: median over `reps` launches, each preceded by a
+    scrub that reads `scrub_bytes` (evicting the L2s and the memory-side cache, whose
+    dirty lines from the previous launch are written back before the timed region,
+    while the scrub's own lines are clean), timed with HIP events on the launch
+    stream; next to it a device copy (torch copy_) moving the same number of bytes
+    (half read, half written), timed the same way."""
+    import workloads
+    stream = torch.cuda.current_stream()
+    scrub = torch.ones(scrub_bytes // 4, dtype=torch.int32, device=dev)
+
+    def median_us(fn):
+        for i in range(warmup):
+            torch.amax(scrub)
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            torch.amax(scrub)
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1000.0
+
+    out = {}
+    for cid in config_ids:
+        w = workloads.make_config(cid, 0)
+        segs, launches = build_launches(mx, w, dev, torch)
+        for _, _, fn, _ in launches:      # valid codes for the conversions
+            fn()
+        torch.cuda.synchronize()
+        rows = []
+        for kern, segname, fn, nbytes in launches:
+            us = median_us(fn)
+            half = (nbytes // 2 + 15) // 16 * 16
+            src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
+            dst = torch.empty(half, dtype=torch.uint8, device=dev)
+            cus = median_us(lambda: dst.copy_(src))
+            del src, dst
+            gbs = nbytes / (us * 1e-6) / 1e9
+            copy_gbs = 2 * half / (cus * 1e-6) / 1e9
+            rows.append({"kernel": kern, "segment": segname, "alg_bytes": nbytes,
+                         "median_us": round(us, 2), "GBps": round(gbs, 1),
+                         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                         "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4)})
+            log(f"[bench] scrubbed {w.name} {kern}/{segname}: {us:.1f} us, {gbs:.0f} GB/s "
+                f"({gbs / HBM_PEAK_GBS:.1%} of peak, {gbs / copy_gbs:.1%} of a same-size copy)")
+        out[w.name] = rows
+        del segs, launches
+        torch.cuda.empty_cache()
+    del scrub
+    torch.cuda.empty_cache()
+    return out
 
 
 # ---- GPU run -----------------------------------------------------------------------
@@ -147,6 +253,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
+    ap.add_argument("--no-scrubbed", action="store_true",
+                    help="skip the per-kernel scrubbed medians of configs 2, 4 and 5")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -168,37 +276,8 @@ def main():
     w = workloads.make_config(int(args.workload[-1]), 0)
     log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s: {w.description}")
 
-    segs = []
-    for seg in w.segments:
-        x = torch.from_numpy(seg.x_bits.view(np.int16)).to(dev)
-        offs = torch.from_numpy(seg.offs).to(dev)
-        codes, scales = mx.alloc_quantize_outputs(seg.M_cap, seg.K, dev)
-        d = {"seg": seg, "x": x, "offs": offs, "codes": codes, "scales": scales}
-        if "rows" in w.kernels:
-            d["y"], d["ys"] = mx.alloc_rows_outputs(seg.M_cap, seg.K, dev)
-        if "cols" in w.kernels:
-            d["yT"], d["ysT"] = mx.alloc_cols_outputs(seg.M_cap, seg.K, seg.G, dev)
-            nb = (np.diff(seg.offs.astype(np.int64)) + 127) // 128
-            d["col_scale_bytes"] = int(nb.sum()) * seg.K
-        segs.append(d)
+    segs, launches = build_launches(mx, w, dev, torch)   # (kernel, segment, fn, alg bytes)
     torch.cuda.synchronize()
-
-    launches = []     # (kernel, segment name, fn, alg bytes)
-    for d in segs:
-        seg = d["seg"]
-        launches.append(("quantize", seg.name,
-                         lambda d=d: mx.mxfp4_quantize_rows(d["x"], d["codes"], d["scales"], d["offs"]),
-                         alg_bytes("quantize", seg.M_tot, seg.K)))
-        if "rows" in w.kernels:
-            launches.append(("rows", seg.name,
-                             lambda d=d: mx.mxfp4_to_fp8_rows(d["codes"], d["scales"], d["y"], d["ys"],
-                                                              d["offs"]),
-                             alg_bytes("rows", seg.M_tot, seg.K)))
-        if "cols" in w.kernels:
-            launches.append(("cols", seg.name,
-                             lambda d=d: mx.mxfp4_to_fp8_cols_ragged(d["codes"], d["scales"], d["yT"],
-                                                                     d["ysT"], d["offs"]),
-                             alg_bytes("cols", seg.M_tot, seg.K, d["col_scale_bytes"])))
     step_bytes = sum(l[3] for l in launches)
 
     def step(events=None):
@@ -284,8 +363,14 @@ def main():
             "mean_launch_us": dom["mean_us"],
         },
         "per_kernel": per_kernel,
+        "per_config_scrubbed": None,
         "cpu_baseline": None,
     }
+    if not args.no_scrubbed:
+        del segs, launches, ev
+        torch.cuda.empty_cache()
+        log("[bench] per-kernel medians with the caches scrubbed (configs 2, 4, 5)")
+        result["per_config_scrubbed"] = scrubbed_medians(mx, torch, dev, (2, 4, 5))
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w)
