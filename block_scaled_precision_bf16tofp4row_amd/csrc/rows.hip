@@ -68,9 +68,10 @@ __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(
 }
 
 #ifndef MXFP4_ROWS_UNROLL
-#define MXFP4_ROWS_UNROLL 4
+#define MXFP4_ROWS_UNROLL 2
 #endif
-// 8-byte code units per thread (all loads issued before any conversion)
+// 8-byte code units per thread (all loads issued before any conversion); two measured
+// slightly faster than one, four or eight on MI355X
 constexpr int kRowsU = MXFP4_ROWS_UNROLL;
 
 hipError_t launch_fp8_rows(const uint8_t* codes, const uint8_t* scales, uint8_t* y,
