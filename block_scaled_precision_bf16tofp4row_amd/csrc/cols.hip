@@ -36,8 +36,8 @@
 //   consumers (waves 4-11)  write the output lines of the strip before: 8 lanes per
 //            output column, lane c stores bytes [16c, 16c + 16) of the column's
 //            128-byte line, 8 columns per instruction.  Those 8 columns are 16 apart,
-//            so their misalignment (mod 16) is the same and the realignment is two
-//            aligned 16-byte LDS reads plus v_alignbyte_b32 under a wave-uniform
+//            so their misalignment (mod 16) is the same (wave-uniform) and the
+//            realignment is five dword LDS reads plus four v_alignbyte_b32, with no
 //            branch.  A column's stores advance on 128-byte line boundaries: the
 //            bytes past a strip's last line boundary stay in the ring and go out with
 //            the next strip, so in the steady state every store covers whole
@@ -134,22 +134,18 @@ __device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t 
     o3 = perm(u1, t1, 0x07060302u);
 }
 
-// 16 bytes starting `o` bytes into the 32 bytes (lo, hi); o is wave-uniform, so the
-// switch is a scalar branch and each output dword is one v_alignbyte_b32.
-__device__ __forceinline__ u32x4 window16(const u32x4& lo, const u32x4& hi, uint32_t o)
+// The 16 LDS bytes starting `o` (< 16) bytes past the 16-byte aligned address src: five
+// dwords read from the dword-aligned start, each output dword one v_alignbyte_b32 by o & 3
+// (a shift of zero returns the low dword).  No branch on o; the bytes read lie in
+// [src, src + 32).  (An unaligned ds_read_b128 gives the same bytes but measured about
+// twelve times slower on MI355X.)
+__device__ __forceinline__ u32x4 read_window16(const uint8_t* src, uint32_t o)
 {
-    const uint32_t D[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    const uint32_t v = o & 3;
-#define MXFP4_WINDOW(U) \
-    u32x4{__builtin_amdgcn_alignbyte(D[U + 1], D[U], v), __builtin_amdgcn_alignbyte(D[U + 2], D[U + 1], v), \
-          __builtin_amdgcn_alignbyte(D[U + 3], D[U + 2], v), __builtin_amdgcn_alignbyte(D[U + 4], D[U + 3], v)}
-    switch (o >> 2) {
-    case 0: return MXFP4_WINDOW(0);
-    case 1: return MXFP4_WINDOW(1);
-    case 2: return MXFP4_WINDOW(2);
-    default: return MXFP4_WINDOW(3);
-    }
-#undef MXFP4_WINDOW
+    const uint32_t* const w = reinterpret_cast<const uint32_t*>(src + (o & ~3u));
+    const uint32_t d0 = w[0], d1 = w[1], d2 = w[2], d3 = w[3], d4 = w[4];
+    const uint32_t b = o & 3u;
+    return u32x4{__builtin_amdgcn_alignbyte(d1, d0, b), __builtin_amdgcn_alignbyte(d2, d1, b),
+                 __builtin_amdgcn_alignbyte(d3, d2, b), __builtin_amdgcn_alignbyte(d4, d3, b)};
 }
 
 // ---- strips of experts ----------------------------------------------------------------
@@ -586,11 +582,7 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                 const uint32_t lb = (it & 1) ? lb1 : lb0;
                 const uint8_t* const src = tile + lb + kColBytes * (2 * v + (it >> 1)) +
                                            ((cs.q[it] + slot_base) & (kRing - 1));
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(src);
-                u32x4 val = lo;
-                if (cs.o[it] != 0)
-                    val = window16(lo, *reinterpret_cast<const u32x4*>(src + 16), cs.o[it]);
-                store_stream(reinterpret_cast<u32x4*>(cs.p[it]), val);
+                store_stream(reinterpret_cast<u32x4*>(cs.p[it]), read_window16(src, cs.o[it]));
                 cs.p[it] += kStripRows;
             }
         } else {
@@ -614,10 +606,7 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                         continue;
                     const int64_t b0 = (j0 + jj) << 4;
                     const uint32_t pos = (slot_base + (uint32_t)(b0 - A) - o) & (kRing - 1);
-                    const u32x4 lo = *reinterpret_cast<const u32x4*>(colp + pos);
-                    u32x4 val = lo;
-                    if (o != 0)
-                        val = window16(lo, *reinterpret_cast<const u32x4*>(colp + pos + 16), o);
+                    const u32x4 val = read_window16(colp + pos, o);
                     if (b0 >= W_lo && b0 + 16 <= W_hi) {
                         store_stream(reinterpret_cast<u32x4*>(yT + b0), val);
                     } else {
