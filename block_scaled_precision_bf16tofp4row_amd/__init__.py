@@ -16,10 +16,12 @@ The binding has the same names as the C ABI:
   ``mxfp4_status_string(status)``
 
 Array arguments are torch tensors on the GPU (BF16 input as ``torch.bfloat16``
-or ``torch.int16``/``torch.uint16`` bits; uint8 outputs; int32 offsets).  The
-stream defaults to torch's current stream.  A non-OK status raises
-``Mxfp4Error``.  If the library is not built the import still works but every
-call raises; there is no fallback path.
+or ``torch.int16``/``torch.uint16`` bits; uint8 outputs; int32 offsets), or raw
+device addresses as ints (passed through unchecked).  Tensor arguments are
+checked before the call (size for the launch, dtype, contiguity, device) and a
+violation raises ``ValueError``.  The stream defaults to torch's current stream.
+A non-OK status raises ``Mxfp4Error``.  If the library is not built the import
+still works but every call raises; there is no fallback path.
 """
 from __future__ import annotations
 
@@ -113,6 +115,29 @@ def _check(status: int, what: str):
         raise Mxfp4Error(status, what)
 
 
+def _need(what: str, args):
+    """Check the tensor arguments before any pointer reaches the library: each large
+    enough for the launch, of an accepted dtype and contiguous, then all on the GPU.
+    `args` holds (tensor, bytes needed, name, accepted dtypes); raw int device
+    addresses and None are passed through unchecked."""
+    tensors = [a for a in args if a[0] is not None and not isinstance(a[0], int)]
+    for t, nbytes, name, dtypes in tensors:
+        have = t.numel() * t.element_size()
+        if have < nbytes:
+            raise ValueError(f"{what}: {name} holds {have} bytes, the launch needs {nbytes}")
+        if str(t.dtype).replace("torch.", "") not in dtypes:
+            raise ValueError(f"{what}: {name} has dtype {t.dtype}, expected one of {', '.join(dtypes)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}: {name} must be contiguous")
+    for t, _, name, _ in tensors:
+        if not t.is_cuda:
+            raise ValueError(f"{what}: {name} must be a GPU tensor")
+
+
+_U8 = ("uint8",)
+_FP8 = ("uint8", "float8_e4m3fn")
+
+
 def _dims(x, offs, G, M_cap, K):
     if G is None:
         G = offs.numel() - 1
@@ -126,6 +151,10 @@ def _dims(x, offs, G, M_cap, K):
 def mxfp4_quantize_rows(x, codes, scales, offs, G=None, M_cap=None, K=None, stream=None):
     """BF16 [M_cap, K] -> codes [M_cap, K/2] uint8 + scales [M_cap, K/32] uint8."""
     G, M_cap, K = _dims(x, offs, G, M_cap, K)
+    n = max(M_cap, 0) * max(K, 0)
+    _need("mxfp4_quantize_rows", [(x, 2 * n, "x", ("bfloat16", "int16", "uint16")),
+                                  (codes, n // 2, "codes", _U8), (scales, n // 32, "scales", _U8),
+                                  (offs, 4 * (G + 1), "group_offsets", ("int32",))])
     lib = load_library()
     _check(lib.mxfp4_quantize_rows(_ptr(x), _ptr(codes), _ptr(scales), _ptr(offs), G, M_cap, K,
                                    _stream(stream)), "mxfp4_quantize_rows")
@@ -136,6 +165,10 @@ def mxfp4_to_fp8_rows(codes, scales, y, y_scales, offs, G=None, M_cap=None, K=No
     if K is None:
         K = codes.shape[1] * 2
     G, M_cap, K = _dims(codes, offs, G, M_cap, K)
+    n = max(M_cap, 0) * max(K, 0)
+    _need("mxfp4_to_fp8_rows", [(codes, n // 2, "codes", _U8), (scales, n // 32, "scales", _U8),
+                                (y, n, "y", _FP8), (y_scales, n // 128, "y_scales", _U8),
+                                (offs, 4 * (G + 1), "group_offsets", ("int32",))])
     lib = load_library()
     _check(lib.mxfp4_to_fp8_rows(_ptr(codes), _ptr(scales), _ptr(y), _ptr(y_scales), _ptr(offs),
                                  G, M_cap, K, _stream(stream)), "mxfp4_to_fp8_rows")
@@ -147,6 +180,11 @@ def mxfp4_to_fp8_cols_ragged(codes, scales, yT, yT_scales, offs, G=None, M_cap=N
     if K is None:
         K = codes.shape[1] * 2
     G, M_cap, K = _dims(codes, offs, G, M_cap, K)
+    n = max(M_cap, 0) * max(K, 0)
+    cap = mxfp4_cols_scale_capacity(M_cap, K, G) if n > 0 and G >= 1 else 0
+    _need("mxfp4_to_fp8_cols_ragged", [(codes, n // 2, "codes", _U8), (scales, n // 32, "scales", _U8),
+                                       (yT, n, "yT", _FP8), (yT_scales, max(cap, 0), "yT_scales", _U8),
+                                       (offs, 4 * (G + 1), "group_offsets", ("int32",))])
     lib = load_library()
     _check(lib.mxfp4_to_fp8_cols_ragged(_ptr(codes), _ptr(scales), _ptr(yT), _ptr(yT_scales),
                                         _ptr(offs), G, M_cap, K, _stream(stream)),
@@ -159,6 +197,7 @@ def mxfp4_validate_offsets(offs, G=None, M_cap=None, stream=None) -> bool:
         G = offs.numel() - 1
     if M_cap is None:
         raise ValueError("M_cap is required")
+    _need("mxfp4_validate_offsets", [(offs, 4 * (int(G) + 1), "group_offsets", ("int32",))])
     st = load_library().mxfp4_validate_offsets(_ptr(offs), int(G), int(M_cap), _stream(stream))
     if st == MXFP4_ERR_SHAPE:
         return False

@@ -111,20 +111,52 @@ def test_validate_offsets_argument_errors(lib):
 
 
 def test_python_binding_raises_on_error_status():
-    class Fake:
-        def __init__(self, ptr, shape):
-            self._p, self.shape = ptr, shape
-
-        def data_ptr(self):
-            return self._p
-
-        def numel(self):
-            return self.shape[0]
-
-    x = Fake(A + 2, (4, 64))
+    # raw device addresses pass through the binding unchecked and reach the library's
+    # own validation (a misaligned BF16 pointer)
     with pytest.raises(mx.Mxfp4Error) as ei:
-        mx.mxfp4_quantize_rows(x, Fake(A2, (4, 32)), Fake(A3, (4, 2)), Fake(OFFS, (2,)), stream=0)
+        mx.mxfp4_quantize_rows(A + 2, A2, A3, OFFS, G=1, M_cap=4, K=64, stream=0)
     assert ei.value.status == mx.MXFP4_ERR_ALIGN
+
+
+def test_python_binding_checks_tensor_arguments():
+    """Tensor arguments are checked before any pointer reaches the library: size for
+    the launch, dtype, contiguity, device (CPU tensors here, so no launch happens)."""
+    import torch
+    M, K = 4, 256
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    codes = torch.zeros((M, K // 2), dtype=torch.uint8)
+    scales = torch.zeros((M, K // 32), dtype=torch.uint8)
+    offs = torch.tensor([0, M], dtype=torch.int32)
+    y = torch.zeros((M, K), dtype=torch.uint8)
+    ys = torch.zeros((M, K // 128), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="codes holds 448 bytes, the launch needs 512"):
+        mx.mxfp4_quantize_rows(x, codes[:, :112], scales, offs, stream=0)
+    with pytest.raises(ValueError, match="y_scales holds"):
+        mx.mxfp4_to_fp8_rows(codes, scales, y, ys[:3], offs, stream=0)
+    with pytest.raises(ValueError, match="dtype"):
+        mx.mxfp4_quantize_rows(x.float(), codes, scales, offs, stream=0)
+    with pytest.raises(ValueError, match="group_offsets has dtype"):
+        mx.mxfp4_to_fp8_rows(codes, scales, y, ys, offs.long(), stream=0)
+    with pytest.raises(ValueError, match="contiguous"):
+        mx.mxfp4_to_fp8_rows(codes, scales, torch.zeros((K, M), dtype=torch.uint8).t(), ys, offs, M_cap=M,
+                             K=K, stream=0)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        mx.mxfp4_quantize_rows(x, codes, scales, offs, stream=0)
+
+
+def test_python_binding_checks_cols_scale_capacity(lib):
+    import torch
+    M, K, G = 300, 256, 3
+    codes = torch.zeros((M, K // 2), dtype=torch.uint8)
+    scales = torch.zeros((M, K // 32), dtype=torch.uint8)
+    offs = torch.tensor([0, 100, 200, 300], dtype=torch.int32)
+    yT = torch.zeros(M * K, dtype=torch.uint8)
+    cap = mx.mxfp4_cols_scale_capacity(M, K, G)
+    assert cap == K * ((M + 127) // 128 + G)
+    with pytest.raises(ValueError, match="yT_scales holds"):
+        mx.mxfp4_to_fp8_cols_ragged(codes, scales, yT, torch.zeros(cap - 1, dtype=torch.uint8), offs, stream=0)
+    with pytest.raises(ValueError, match="yT holds"):
+        mx.mxfp4_to_fp8_cols_ragged(codes, scales, yT[:-1], torch.zeros(cap, dtype=torch.uint8), offs, stream=0)
 
 
 def test_product_package_does_not_import_oracle():
