@@ -20,12 +20,12 @@
 // numbered in expert order (strip s is row s of the block-scale output).  The grid
 // is persistent, one workgroup per compute unit: each owns a 256-column tile (eight
 // MX groups, so every row it reads is one whole 128-byte line of codes) and a
-// contiguous range of strips.  Its twelve waves have two roles, so that no wave both
+// contiguous range of strips.  Its sixteen waves have two roles, so that no wave both
 // loads and stores (a wave's loads and stores share one in-order completion counter,
 // and waiting for a load must not wait for older stores):
 //   producers (waves 0-3)   wave w converts rows 32w..32w+31 of every strip: lane
 //            (rq = lane >> 3, c = lane & 7) holds the 16 code bytes of group c for
-//            rows 32w + 4rq .. + 3, loaded three strips ahead.  The block scale of a
+//            rows 32w + 4rq .. + 3, loaded two strips ahead.  The block scale of a
 //            group is the max over the strip's 128 rows: each wave reduces its 32
 //            rows (DPP and lane shuffles) and publishes the partial max in LDS, and
 //            every wave takes the max of the four.  Each row is converted with the
@@ -33,12 +33,14 @@
 //            into 32 dwords (4 rows of one column each), written into a k-major LDS
 //            ring: one ring per output column k holding the column's bytes of the
 //            last four strips in order;
-//   consumers (waves 4-11)  write the output lines of the strip before: 8 lanes per
+//   consumers (waves 4-15)  write the output lines of the strip before: 8 lanes per
 //            output column, lane c stores bytes [16c, 16c + 16) of the column's
-//            128-byte line, 8 columns per instruction.  Those 8 columns are 16 apart,
-//            so their misalignment (mod 16) is the same (wave-uniform) and the
-//            realignment is five dword LDS reads plus four v_alignbyte_b32, with no
-//            branch.  A column's stores advance on 128-byte line boundaries: the
+//            128-byte line, 8 columns per instruction, 32 instructions per strip
+//            spread over the twelve waves (more storing waves keep more stores in
+//            flight; twelve fit beside the producers in 128 VGPRs per lane).  The
+//            8 columns of an instruction are 16 apart, so their misalignment (mod 16)
+//            is the same (wave-uniform) and the realignment is five dword LDS reads
+//            plus four v_alignbyte_b32, with no branch.  A column's stores advance on 128-byte line boundaries: the
 //            bytes past a strip's last line boundary stay in the ring and go out with
 //            the next strip, so in the steady state every store covers whole
 //            128-byte lines (a partial line costs the memory system a read-modify-
@@ -68,9 +70,12 @@ constexpr int kColBytes = kRing + kMirror;           // 544
 // never overlap
 constexpr int kTileBytes = kTileCols * kColBytes + 32 * ((kTileCols - 1) / 32);
 constexpr int kProducerWaves = 4;
-constexpr int kConsumerWaves = 8;
+constexpr int kConsumerWaves = 12;
+// a strip is 32 store instructions (256 columns x 128 bytes); consumer wave v issues
+// instructions v, v + 12, v + 24 (< 32)
+constexpr int kMaxIts = (32 + kConsumerWaves - 1) / kConsumerWaves;
 #ifndef MXFP4_COLS_PREFETCH
-#define MXFP4_COLS_PREFETCH 3
+#define MXFP4_COLS_PREFETCH 2
 #endif
 constexpr int kPrefetch = MXFP4_COLS_PREFETCH;    // strips of loads in flight per producer wave
 constexpr int kColsThreads = 64 * (kProducerWaves + kConsumerWaves);
@@ -310,15 +315,15 @@ __device__ __forceinline__ Scales load_scales(const uint8_t* __restrict__ scales
 // ---- consumers ---------------------------------------------------------------------------
 
 // A consumer lane writes one aligned 16-byte chunk of one column per strip: lane
-// (mc = lane >> 3, c = lane & 7) of instruction `it` of consumer wave v owns tile column
-// kk = 2v + (it >> 1) + 16 mc + 128 (it & 1) and bytes [16c, 16c + 16) of the column's
-// 128-byte output line of the strip, so the 8 lanes of a column store one whole line.
+// (mc = lane >> 3, c = lane & 7) of store instruction g (0..31) of the strip owns tile
+// column kk = 2 (g >> 2) + ((g & 3) >> 1) + 16 mc + 128 (g & 1) and bytes [16c, 16c + 16)
+// of the column's 128-byte output line, so the 8 lanes of a column store one whole line.
 // Within a run of strips of one expert the column's line phase is fixed, so this
 // state is set at the first strip and advanced by 128 bytes per strip.
 struct ColState {
-    uint32_t q[4];             // ring offset of the lane's chunk, minus the strip's slot base
-    uint8_t* p[4];             // output address of the lane's chunk
-    uint32_t o[4];             // misalignment (wave-uniform): (-A) & 15
+    uint32_t q[kMaxIts];       // ring offset of the lane's chunk, minus the strip's slot base
+    uint8_t* p[kMaxIts];       // output address of the lane's chunk
+    uint32_t o[kMaxIts];       // misalignment (wave-uniform): (-A) & 15
 };
 
 // ---- the kernel ---------------------------------------------------------------------------
@@ -525,12 +530,12 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     }
 
     // ================= consumers =================
-    const int v = wave - kProducerWaves;          // 0..7
-    const int mc = lane >> 3;                     // column 2v + (it >> 1) + 16 mc + 128 (it & 1)
+    const int v = wave - kProducerWaves;          // 0 .. kConsumerWaves - 1
+    const int mc = lane >> 3;
     const int c = lane & 7;                       // bytes [16c, 16c + 16) of the line
-    // LDS ring of tile column u + 16 mc + 128 h (u < 16): lane part + 544 u
-    const uint32_t lb0 = lds_col(16 * mc);
-    const uint32_t lb1 = lds_col(16 * mc + 128);
+    // store instruction k of this wave is instruction g = v + kConsumerWaves k (< 32) of the
+    // strip: tile columns 2 (g >> 2) + ((g & 3) >> 1) + 16 mc + 128 (g & 1)
+    auto col_of = [&](int g) { return (uint32_t)(2 * (g >> 2) + ((g & 3) >> 1) + 16 * mc + 128 * (g & 1)); };
     ColState cs;
     for (uint32_t t = 0; t < n; ++t) {
         if (!wait_at_least(&produced, kProducerWaves * (t + 1)))
@@ -543,63 +548,55 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
         const bool cin = flags & 1u, cout = flags & 2u, skip = flags & 4u;
         const uint32_t slot_base = kStripRows * slot;
 
-        // block scales of this strip: one byte per column, 16 lanes x 16 bytes
         if (!skip && v == 0 && lane < 16 && 16 * lane < ncols) {
             const uint32_t word = info[slot].S[lane >> 3];
             const uint32_t w4 = ((word >> (8 * ((lane >> 1) & 3))) & 0xFFu) * 0x01010101u;
             *reinterpret_cast<u32x4*>(yT_scales + K * (int64_t)uniform(info[slot].blk) + kTileCols * (int64_t)kt +
                                       16 * lane) = u32x4{w4, w4, w4, w4};
         }
-
-        // Output row k of expert g starts at byte K*offs[g] + k*M_g; this strip's bytes
-        // of tile column kk are [A, A + nrows) with A = A0 + kk*M_g.  Memory byte b of
-        // the column maps to ring byte slot_base + (b - A) (mod 512); since b is
-        // 16-aligned, the offset inside the aligned ring chunk is o = (-A) & 15 for every
-        // chunk of the 8 columns of an instruction (they are 16 apart).
-        if (!cin) {                               // a new run of strips of one expert
+        if (!cin) {
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const uint32_t kk = 2 * v + (it >> 1) + 16 * mc + 128 * (it & 1);
+            for (int k = 0; k < kMaxIts; ++k) {
+                const int g = v + kConsumerWaves * k;
+                if (g >= 32)
+                    continue;
+                const uint32_t kk = col_of(g);
                 const int64_t A = A0 + (int64_t)kk * mg;
                 const uint32_t a = (uint32_t)A & 127;
-                cs.o[it] = uniform((uint32_t)(16 - (A & 15)) & 15);
-                cs.q[it] = 16 * c - a - cs.o[it];
-                cs.p[it] = yT + (A - a) + 16 * c;
+                cs.o[k] = uniform((uint32_t)(16 - (A & 15)) & 15);
+                cs.q[k] = 16 * c - a - cs.o[k];
+                cs.p[k] = yT + (A - a) + 16 * c;
             }
         }
         if (skip) {
-            // lead-in strip: its lines up to its last line boundary belong to the
-            // workgroup before; the rest stays in the ring for the next strip
 #pragma unroll
-            for (int it = 0; it < 4; ++it)
-                cs.p[it] += kStripRows;
+            for (int k = 0; k < kMaxIts; ++k)
+                cs.p[k] += kStripRows;
         } else if (cin && cout) {
-            // steady state: the 8 lanes of a column write its whole line
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                if ((it & 1) && ncols <= 128)
-                    continue;                     // uniform: the narrow last tile
-                const uint32_t lb = (it & 1) ? lb1 : lb0;
-                const uint8_t* const src = tile + lb + kColBytes * (2 * v + (it >> 1)) +
-                                           ((cs.q[it] + slot_base) & (kRing - 1));
-                store_stream(reinterpret_cast<u32x4*>(cs.p[it]), read_window16(src, cs.o[it]));
-                cs.p[it] += kStripRows;
+            for (int k = 0; k < kMaxIts; ++k) {
+                const int g = v + kConsumerWaves * k;
+                if (g >= 32 || ((g & 1) && ncols <= 128))
+                    continue;
+                const uint8_t* const src = tile + lds_col(col_of(g)) + ((cs.q[k] + slot_base) & (kRing - 1));
+                store_stream(reinterpret_cast<u32x4*>(cs.p[k]), read_window16(src, cs.o[k]));
+                cs.p[k] += kStripRows;
             }
         } else {
-            // the ends of a run: a column's bytes [W_lo, W_hi), partial lines byte-wise
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                if ((it & 1) && ncols <= 128)
+            for (int k = 0; k < kMaxIts; ++k) {
+                const int g = v + kConsumerWaves * k;
+                if (g >= 32 || ((g & 1) && ncols <= 128))
                     continue;
-                const uint32_t kk = 2 * v + (it >> 1) + 16 * mc + 128 * (it & 1);
+                const uint32_t kk = col_of(g);
                 const int64_t A = A0 + (int64_t)kk * mg;
-                const uint32_t o = cs.o[it];
+                const uint32_t o = cs.o[k];
                 const int64_t E = A + nrows;
                 const int64_t W_lo = cin ? (A & ~(int64_t)127) : A;
                 const int64_t W_hi = cout ? (E & ~(int64_t)127) : E;
-                const int64_t j0 = W_lo >> 4;                          // first 16-byte chunk
+                const int64_t j0 = W_lo >> 4;
                 const int nch = W_hi > W_lo ? (int)(((W_hi + 15) >> 4) - j0) : 0;
-                const uint8_t* const colp = tile + ((it & 1) ? lb1 : lb0) + kColBytes * (2 * v + (it >> 1));
+                const uint8_t* const colp = tile + lds_col(kk);
                 for (int pass = 0; pass < 2; ++pass) {
                     const int jj = c + 8 * pass;
                     if (jj >= nch)
@@ -616,10 +613,10 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                                 yT[b0 + q] = (uint8_t)(w4[q >> 2] >> (8 * (q & 3)));
                     }
                 }
-                cs.p[it] += kStripRows;           // the next strip continues the run
+                cs.p[k] += kStripRows;
             }
         }
-        signal(&drained[slot]);                   // this wave is done with the slot
+        signal(&drained[slot]);
     }
 }
 
