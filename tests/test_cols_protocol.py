@@ -1,6 +1,6 @@
 """CPU model of the column kernel's LDS progress-counter protocol.
 
-The column kernel (csrc/cols.hip) splits each workgroup into 4 producer waves and 8
+The column kernel (csrc/cols.hip) splits each workgroup into 4 producer waves and 12
 consumer waves that share a four-slot LDS ring and synchronise only through monotonic
 counters: `published` (partial block-scale maxima), `produced` (strips converted) and
 `drained[slot]` (strips written out).  This model replays the kernel's waits, with the
@@ -22,7 +22,7 @@ import random
 
 import pytest
 
-SLOTS, PW, CW = 4, 4, 8
+SLOTS, PW, CW = 4, 4, 12
 
 
 class Violation(AssertionError):
