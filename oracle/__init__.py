@@ -67,6 +67,10 @@ def _load():
     lib.oracle_scale_for_amax.argtypes = [ctypes.c_double]
     lib.oracle_scale_for_amax.restype = ctypes.c_int
     lib.oracle_fp8_of_code.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.oracle_fp8q_block.argtypes = [P, P, P]
+    lib.oracle_fp8q_rows.argtypes = [P, I64, I64, I64, P, P]
+    lib.oracle_scale_for_amax_e4m3.argtypes = [ctypes.c_double]
+    lib.oracle_scale_for_amax_e4m3.restype = ctypes.c_int
     lib.oracle_fp8_of_code.restype = ctypes.c_uint8
     _lib = lib
     return lib
@@ -170,6 +174,42 @@ def fp8_rows(codes: np.ndarray, scales: np.ndarray, rows: int | None = None,
 
     def run(r):
         lib.oracle_fp8_rows(_ptr(codes), _ptr(scales), K, r[0], r[1], _ptr(y), _ptr(y_scales))
+
+    _run_ranges(run, _ranges(rows, threads * 4), threads)
+    return y, y_scales
+
+
+def scale_for_amax_e4m3(amax: float) -> int:
+    return _load().oracle_scale_for_amax_e4m3(float(amax))
+
+
+def fp8q_block(x128: np.ndarray):
+    """One 128-element block of BF16 bits -> (128 E4M3 bytes, UE8M0 scale byte)."""
+    lib = _load()
+    x128 = np.ascontiguousarray(x128, dtype=np.uint16)
+    assert x128.size == 128
+    y = np.zeros(128, np.uint8)
+    sc = np.zeros(1, np.uint8)
+    lib.oracle_fp8q_block(_ptr(x128), _ptr(y), _ptr(sc))
+    return y, int(sc[0])
+
+
+def fp8q_rows(x_bits: np.ndarray, rows: int | None = None, threads: int = 1,
+              y: np.ndarray | None = None, y_scales: np.ndarray | None = None):
+    """Backward FP8 quantizer, row layout: BF16 bits [M, K] -> (y [M, K] E4M3 bytes,
+    y_scales [M, K/128] UE8M0 bytes).  Only rows [0, rows) are computed."""
+    lib = _load()
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    assert K % 128 == 0
+    rows = M if rows is None else rows
+    if y is None:
+        y = np.zeros((M, K), np.uint8)
+    if y_scales is None:
+        y_scales = np.zeros((M, K // 128), np.uint8)
+
+    def run(r):
+        lib.oracle_fp8q_rows(_ptr(x_bits), K, r[0], r[1], _ptr(y), _ptr(y_scales))
 
     _run_ranges(run, _ranges(rows, threads * 4), threads)
     return y, y_scales

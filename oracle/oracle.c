@@ -104,7 +104,8 @@ static int minifloat_round_nearest_even(double v, int mbits, int bias, int max_c
 static int e2m1_encode(double y) { return minifloat_round_nearest_even(y, 1, 1, 7); }
 
 /* OCP E4M3FN: bias 7, 3 mantissa bits, largest finite code 0x7E (= 448).
- * On this path magnitudes never exceed 6, so saturation is never reached. */
+ * The FP4 -> FP8 conversions never exceed 6; the backward FP8 quantizer does
+ * reach the saturation (see below). */
 static int e4m3_encode(double v) { return minifloat_round_nearest_even(v, 3, 7, 0x7E); }
 
 /* ---- step a1/a2: block amax and shared UE8M0 scale --------------------- */
@@ -242,6 +243,60 @@ void oracle_fp8_cols(const uint8_t *codes, const uint8_t *scales, const int32_t 
     }
 }
 
+/* ---- backward FP8 quantizer: BF16 -> E4M3 with 1x128 blocks ------------ */
+/* Technical summary, section 2 (Methodology): the backward pass of the asymmetric
+ * flow (item 2) stays on the standard FP8 path for gradients, in the E4M3 format with
+ * 128-element blocks (item 1).  The page does not fix
+ * the block scale; the reading here follows the rest of this path and OCP MX: one
+ * UE8M0 byte per 128 elements along the row, shared exponent
+ * floor(log2(amax)) - emax_elem with emax_elem = 8 for E4M3 (its largest normal is
+ * 448 = 1.75 * 2^8), biased by 127 and clamped to [0, 254], 0 for an all-zero
+ * block.  Elements are |x| / 2^(S-127) rounded to E4M3FN, ties to even, into the
+ * subnormals, saturating at 448 (the block maximum lands in [256, 512), so values
+ * above 448 occur and clamp); the sign is kept, -0 included. */
+static int ue8m0_scale_for_amax_e4m3(double amax)
+{
+    if (amax == 0.0)
+        return 0;
+    int e2;
+    frexp(amax, &e2);            /* floor(log2(amax)) = e2 - 1 */
+    int s = (e2 - 1) - 8 + 127;
+    if (s < 0) s = 0;
+    if (s > 254) s = 254;
+    return s;
+}
+
+/* One 128-element block: x[0..127] BF16 bits -> 128 E4M3 bytes + 1 scale byte. */
+void oracle_fp8q_block(const uint16_t *x, uint8_t *y128, uint8_t *scale)
+{
+    double amax = 0.0;
+    for (int i = 0; i < 128; ++i) {
+        double a = fabs(bf16_value(x[i]));
+        if (a > amax)
+            amax = a;
+    }
+    int s = ue8m0_scale_for_amax_e4m3(amax);
+    *scale = (uint8_t)s;
+    for (int i = 0; i < 128; ++i) {
+        double v = ldexp(fabs(bf16_value(x[i])), 127 - s);    /* |x| / 2^(s-127), exact */
+        int b = e4m3_encode(v);
+        if (bf16_negative(x[i]))
+            b |= 0x80;
+        y128[i] = (uint8_t)b;
+    }
+}
+
+/* Row layout, rows [row_begin, row_end) of a row-major BF16 matrix with K columns
+ * (K a multiple of 128): y [*, K] E4M3 bytes, y_scales [*, K/128] UE8M0 bytes. */
+void oracle_fp8q_rows(const uint16_t *x, int64_t K, int64_t row_begin, int64_t row_end,
+                      uint8_t *y, uint8_t *y_scales)
+{
+    int64_t nb = K / 128;
+    for (int64_t m = row_begin; m < row_end; ++m)
+        for (int64_t b = 0; b < nb; ++b)
+            oracle_fp8q_block(x + m * K + 128 * b, y + m * K + 128 * b, y_scales + m * nb + b);
+}
+
 /* ---- small helpers exported for the pins ------------------------------- */
 
 int oracle_e2m1_encode(double y) { return e2m1_encode(y); }
@@ -250,3 +305,4 @@ double oracle_e2m1_magnitude(int code) { return e2m1_magnitude(code); }
 double oracle_bf16_value(uint16_t b) { return bf16_value(b); }
 int oracle_scale_for_amax(double amax) { return ue8m0_scale_for_amax(amax); }
 uint8_t oracle_fp8_of_code(int c, int s, int S) { return fp8_of_code(c, s, S); }
+int oracle_scale_for_amax_e4m3(double amax) { return ue8m0_scale_for_amax_e4m3(amax); }

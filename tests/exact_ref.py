@@ -167,3 +167,40 @@ def fp8_cols(codes: np.ndarray, scales: np.ndarray, offs: np.ndarray):
                     yT[K * r0 + k * Mg + (m - r0)] = _fp8(_code(codes, m, k), int(scales[m, j]), S)
         B += nb[g]
     return yT, ys
+
+
+# ---- backward FP8 quantizer: BF16 -> E4M3 with 1x128 blocks along the row -----------
+# Scale: the OCP MX rule with E4M3's largest exponent, floor(log2 amax) - 8 + 127,
+# clamped to [0, 254], 0 for an all-zero block.  Elements: nearest E4M3FN value of
+# |x| / 2^(S-127), ties to the even code, values above the largest finite value (448)
+# clamped to it (the OCP MX conversion rule for FP8 targets), sign kept.
+
+def e4m3_encode_saturating(v: Fraction) -> int:
+    vals = _e4m3()
+    if v > vals[-1]:
+        return len(vals) - 1
+    return nearest_even(v, vals)
+
+
+def scale_of_block_e4m3(xs: list[Fraction]) -> int:
+    amax = max(abs(v) for v in xs)
+    if amax == 0:
+        return 0
+    return min(254, max(0, floor_log2(amax) - 8 + 127))
+
+
+def fp8q_rows(x_bits: np.ndarray):
+    """[M, K] BF16 bits -> (y [M, K] E4M3 bytes, y_scales [M, K/128])."""
+    M, K = x_bits.shape
+    y = np.zeros((M, K), np.uint8)
+    ys = np.zeros((M, K // 128), np.uint8)
+    for m in range(M):
+        for b in range(K // 128):
+            bits = [int(v) for v in x_bits[m, 128 * b:128 * b + 128]]
+            xs = [bf16_to_fraction(v) for v in bits]
+            S = scale_of_block_e4m3(xs)
+            ys[m, b] = S
+            for i in range(128):
+                v = abs(xs[i]) / Fraction(2) ** (S - 127)
+                y[m, 128 * b + i] = e4m3_encode_saturating(v) | (0x80 if bits[i] & 0x8000 else 0)
+    return y, ys

@@ -387,3 +387,93 @@ def test_threaded_drivers_equal_single_thread():
     a4 = oracle.fp8_cols(c1, s1, offs, threads=4)
     np.testing.assert_array_equal(a1[0], a4[0])
     np.testing.assert_array_equal(a1[1], a4[1])
+
+
+# ---- backward FP8 quantizer (BF16 -> E4M3, 1x128 blocks along the row) -------------
+
+def _fp8q_bits(rng, shape, kind):
+    if kind == "saturate":
+        # every block's maximum has a mantissa in the band that rounds above 448
+        x = rng.standard_normal(shape).astype(np.float32)
+        mant = rng.choice([1.8125, 1.84375, 1.875, 1.90625, 1.9375, 1.96875, 1.75, 1.8125], size=shape[:-1] + (shape[-1] // 128,))
+        e = rng.integers(-20, 20, size=mant.shape)
+        for idx in np.ndindex(mant.shape):
+            blk = x[idx[:-1] + (slice(128 * idx[-1], 128 * idx[-1] + 128),)]
+            blk /= np.abs(blk).max()
+            blk *= np.float32(mant[idx] * 2.0 ** e[idx])
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    if kind == "e4m3ties":
+        # values on E4M3 tie points relative to a block maximum of 256 * 2^e
+        grid = np.array([1, 1.0625, 1.1875, 1.5625, 1.9375, 0.015625 * 1.5, 2.0 ** -9, 3 * 2.0 ** -10,
+                         1.8125, 1.75], np.float32)
+        x = rng.choice(grid, size=shape).astype(np.float32) * rng.choice([-1.0, 1.0], size=shape).astype(np.float32)
+        x[..., ::128] = 1.0
+        x *= np.float32(2.0) ** rng.integers(-10, 10, size=shape[:-1] + (1,)).astype(np.float32)
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    return _rand_bits(rng, shape, kind)
+
+
+@pytest.mark.parametrize("kind", ["normal", "tiny", "raw", "saturate", "e4m3ties"])
+def test_fp8q_matches_brute_force(kind):
+    rng = np.random.default_rng(29)
+    x = _fp8q_bits(rng, (2, 256), kind)
+    x[1, 128:256] = 0                    # an all-zero block
+    x[0, 7] = 0x8000                     # negative zero
+    y_o, s_o = oracle.fp8q_rows(x)
+    y_r, s_r = exact_ref.fp8q_rows(x)
+    np.testing.assert_array_equal(s_o, s_r)
+    np.testing.assert_array_equal(y_o, y_r)
+
+
+def test_fp8q_scale_rule_closed_form_every_bf16_magnitude():
+    """floor(log2 amax) - 8 + 127 clamped to [0, 254], for every finite positive BF16."""
+    for b in range(1, 0x7F80):
+        a = struct.unpack("<f", struct.pack("<I", b << 16))[0]
+        want = min(254, max(0, math.frexp(a)[1] - 1 - 8 + 127))
+        assert oracle.scale_for_amax_e4m3(a) == want, hex(b)
+
+
+def test_fp8q_matches_torch_cast_in_range():
+    """Below the saturation point the element rule is a plain RNE cast of
+    x / 2^(S-127) to E4M3FN, which torch implements independently."""
+    rng = np.random.default_rng(5)
+    x = _fp8q_bits(rng, (64, 512), "normal")
+    y, ys = oracle.fp8q_rows(x, threads=4)
+    xf = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float()
+    scale = torch.from_numpy(ys.astype(np.float32) - 127).repeat_interleave(128, dim=1)
+    v = xf * torch.pow(2.0, -scale)
+    in_range = v.abs() <= 448
+    want = v.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = y
+    m = in_range.numpy()
+    assert m.mean() > 0.5
+    np.testing.assert_array_equal(got[m], want[m])
+    # the rest saturate to +-448
+    assert np.all((got[~m] & 0x7F) == 0x7E)
+
+
+def test_fp8q_invariants_and_special_values():
+    blk = np.zeros(128, np.float32)
+    blk[0] = 2.0 ** 5
+    blk[1] = 2.0 ** 5 * 1.8125               # 464 after scaling -> the tie -> 448
+    blk[2] = -2.0 ** 5 * 1.84375             # 472 -> rounds past 448 -> saturates
+    blk[3] = 2.0 ** 5 * 1.6875               # 432 -> tie between 416 and 448 -> 448
+    blk[4] = 2.0 ** 5 * 2.0 ** -17           # 2^-9 after scaling: smallest subnormal
+    blk[5] = 2.0 ** 5 * 2.0 ** -18           # 2^-10: tie between 0 and 2^-9 -> 0
+    blk[6] = -0.0
+    bits = torch.from_numpy(blk).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    y, s = oracle.fp8q_block(bits)
+    assert s == 5 - 8 + 127                  # floor(log2 amax) = 5 for amax = 2^5 * 1.84375
+    assert y[0] == 0x78                      # 2^5 / 2^-3 = 256 = 2^8 -> biased exponent 15, mantissa 0
+    assert y[1] == 0x7E and y[2] == 0xFE and y[3] == 0x7E
+    assert y[4] == 0x01 and y[5] == 0x00 and y[6] == 0x80
+    # every block: codes never exceed 448, the maximum lands in [256, 448]
+    rng = np.random.default_rng(8)
+    x = _fp8q_bits(rng, (16, 1024), "normal")
+    y, ys = oracle.fp8q_rows(x)
+    assert np.all((y & 0x7F) <= 0x7E)
+    mags = (y & 0x7F).reshape(16, 8, 128).max(axis=2)
+    assert np.all((mags >= 0x78) & (mags <= 0x7E))
+    zero = np.zeros((1, 128), np.uint16)
+    yz, sz = oracle.fp8q_rows(zero)
+    assert sz[0, 0] == 0 and np.all(yz == 0)
