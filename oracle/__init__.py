@@ -69,6 +69,7 @@ def _load():
     lib.oracle_fp8_of_code.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.oracle_fp8q_block.argtypes = [P, P, P]
     lib.oracle_fp8q_rows.argtypes = [P, I64, I64, I64, P, P]
+    lib.oracle_fp8q_cols.argtypes = [P, P, ctypes.c_int32, I64, I64, I64, P, P]
     lib.oracle_scale_for_amax_e4m3.argtypes = [ctypes.c_double]
     lib.oracle_scale_for_amax_e4m3.restype = ctypes.c_int
     lib.oracle_fp8_of_code.restype = ctypes.c_uint8
@@ -265,3 +266,32 @@ def _run_ranges(fn, work, threads):
         return
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(fn, work))
+
+
+def fp8q_cols(x_bits: np.ndarray, offs: np.ndarray, threads: int = 1,
+              yT: np.ndarray | None = None, yT_scales: np.ndarray | None = None, groups=None):
+    """Backward FP8 quantizer, transposed column layout over ragged expert segments:
+    BF16 bits [M, K] -> flat (yT, yT_scales), expert g's [K, M_g] transpose at byte
+    K*offs[g] and its [nblocks_g, K] scales at byte K*B_g (the layout of fp8_cols)."""
+    lib = _load()
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    M, K = x_bits.shape
+    G = offs.size - 1
+    assert K % 128 == 0
+    if yT is None:
+        yT = np.zeros(M * K, np.uint8)
+    if yT_scales is None:
+        yT_scales = np.zeros(max(1, cols_scale_size(offs, K)), np.uint8)
+    nbg = blocks_per_group(offs)
+    groups = range(G) if groups is None else groups
+    work = []
+    for g in groups:
+        for b0, b1 in _ranges(int(nbg[g]), max(1, threads)):
+            work.append((g, b0, b1))
+
+    def run(w):
+        lib.oracle_fp8q_cols(_ptr(x_bits), _ptr(offs), w[0], K, w[1], w[2], _ptr(yT), _ptr(yT_scales))
+
+    _run_ranges(run, work, threads)
+    return yT, yT_scales

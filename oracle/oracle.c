@@ -297,6 +297,47 @@ void oracle_fp8q_rows(const uint16_t *x, int64_t K, int64_t row_begin, int64_t r
             oracle_fp8q_block(x + m * K + 128 * b, y + m * K + 128 * b, y_scales + m * nb + b);
 }
 
+/* Column layout for the Wgrad gradient of expert g, row blocks [blk_begin, blk_end)
+ * of that expert: the transposed counterpart of oracle_fp8q_rows over the same
+ * ragged segments and the same output layout as oracle_fp8_cols.  For block b and
+ * column k the 1x128 block runs along the token dimension: rows
+ * [128b, min(128b+128, M_g)) of the expert (a partial last block uses only its
+ * rows).  Its UE8M0 scale comes from the amax over those rows (rule above) and is
+ * stored at yT_scales[K*B_g + b*K + k]; element (k, m') goes to
+ * yT[K*offs[g] + k*M_g + m']. */
+void oracle_fp8q_cols(const uint16_t *x, const int32_t *offs, int32_t g, int64_t K,
+                      int64_t blk_begin, int64_t blk_end, uint8_t *yT, uint8_t *yT_scales)
+{
+    int64_t Bg = 0;
+    for (int32_t h = 0; h < g; ++h)
+        Bg += ((int64_t)offs[h + 1] - offs[h] + 127) / 128;
+    int64_t row0 = offs[g];
+    int64_t Mg = (int64_t)offs[g + 1] - offs[g];
+    uint8_t *outT = yT + K * row0;
+    uint8_t *outS = yT_scales + K * Bg;
+    for (int64_t b = blk_begin; b < blk_end; ++b) {
+        int64_t mlo = 128 * b;
+        int64_t mhi = mlo + 128 < Mg ? mlo + 128 : Mg;
+        for (int64_t k = 0; k < K; ++k) {
+            double amax = 0.0;
+            for (int64_t m = mlo; m < mhi; ++m) {
+                double a = fabs(bf16_value(x[(row0 + m) * K + k]));
+                if (a > amax)
+                    amax = a;
+            }
+            int s = ue8m0_scale_for_amax_e4m3(amax);
+            outS[b * K + k] = (uint8_t)s;
+            for (int64_t m = mlo; m < mhi; ++m) {
+                uint16_t xb = x[(row0 + m) * K + k];
+                int e = e4m3_encode(ldexp(fabs(bf16_value(xb)), 127 - s));
+                if (bf16_negative(xb))
+                    e |= 0x80;
+                outT[k * Mg + m] = (uint8_t)e;
+            }
+        }
+    }
+}
+
 /* ---- small helpers exported for the pins ------------------------------- */
 
 int oracle_e2m1_encode(double y) { return e2m1_encode(y); }

@@ -204,3 +204,28 @@ def fp8q_rows(x_bits: np.ndarray):
                 v = abs(xs[i]) / Fraction(2) ** (S - 127)
                 y[m, 128 * b + i] = e4m3_encode_saturating(v) | (0x80 if bits[i] & 0x8000 else 0)
     return y, ys
+
+
+def fp8q_cols(x_bits: np.ndarray, offs: np.ndarray):
+    """Per expert g: E4M3 transpose [K, M_g] at K*offs[g]; scales [nb_g, K] at K*B_g;
+    the 1x128 blocks run along the token dimension of each expert."""
+    M, K = x_bits.shape
+    G = len(offs) - 1
+    nb = [(int(offs[g + 1]) - int(offs[g]) + 127) // 128 for g in range(G)]
+    yT = np.zeros(M * K, np.uint8)
+    ys = np.zeros(max(1, sum(nb) * K), np.uint8)
+    B = 0
+    for g in range(G):
+        r0 = int(offs[g])
+        Mg = int(offs[g + 1]) - r0
+        for b in range(nb[g]):
+            rows = range(r0 + 128 * b, r0 + min(Mg, 128 * b + 128))
+            for k in range(K):
+                xs = [bf16_to_fraction(int(x_bits[m, k])) for m in rows]
+                S = scale_of_block_e4m3(xs)
+                ys[K * (B + b) + k] = S
+                for m, v in zip(rows, xs):
+                    code = e4m3_encode_saturating(abs(v) / Fraction(2) ** (S - 127))
+                    yT[K * r0 + k * Mg + (m - r0)] = code | (0x80 if int(x_bits[m, k]) & 0x8000 else 0)
+        B += nb[g]
+    return yT, ys

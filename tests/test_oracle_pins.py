@@ -477,3 +477,79 @@ def test_fp8q_invariants_and_special_values():
     zero = np.zeros((1, 128), np.uint16)
     yz, sz = oracle.fp8q_rows(zero)
     assert sz[0, 0] == 0 and np.all(yz == 0)
+
+
+# ---- backward FP8 quantizer, transposed column layout over ragged segments ----------
+
+def _colsat_bits(rng, M, K, offs):
+    """Values whose per-(block, column) maximum sits in E4M3's saturation band: the
+    block maximum has mantissa 1.8125 (the 464 tie), 1.84375 or 1.96875 times 2^e_k,
+    every other value is below 2^e_k in magnitude."""
+    e = rng.integers(-30, 30, size=K).astype(np.float32)
+    x = rng.uniform(-1, 1, size=(M, K)).astype(np.float32) * np.float32(2.0) ** e
+    for g in range(len(offs) - 1):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        for b0 in range(r0, r1, 128):
+            b1 = min(r1, b0 + 128)
+            pick = rng.integers(b0, b1, size=K)
+            mant = rng.choice([1.8125, 1.84375, 1.96875, 1.75], size=K).astype(np.float32)
+            sign = rng.choice([-1.0, 1.0], size=K).astype(np.float32)
+            x[pick, np.arange(K)] = sign * mant * np.float32(2.0) ** e
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+@pytest.mark.parametrize("kind", ["normal", "tiny", "raw", "colsat"])
+def test_fp8q_cols_match_brute_force_ragged(kind):
+    rng = np.random.default_rng(31)
+    counts = [3, 130, 0, 1]              # partial block, 128 + 2, empty expert, one row
+    M, K = sum(counts), 128
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = _colsat_bits(rng, M, K, offs) if kind == "colsat" else _rand_bits(rng, (M, K), kind)
+    x[133, :] = 0                        # the one-row expert's block becomes all zero
+    x[10, 5] = 0x8000
+    yT_o, ys_o = oracle.fp8q_cols(x, offs)
+    yT_r, ys_r = exact_ref.fp8q_cols(x, offs)
+    np.testing.assert_array_equal(ys_o, ys_r)
+    np.testing.assert_array_equal(yT_o, yT_r)
+    if kind == "colsat":
+        assert np.any((yT_o & 0x7F) == 0x7E)
+
+
+@pytest.mark.parametrize("kind", ["normal", "saturate", "raw"])
+def test_fp8q_cols_equal_row_quantizer_of_the_transpose(kind):
+    """With every segment a multiple of 128 rows, expert g's column output is the
+    row quantizer applied to its transposed [K, M_g] slice."""
+    rng = np.random.default_rng(32)
+    counts = [256, 0, 128, 384]
+    M, K = sum(counts), 256
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    xT = _fp8q_bits(rng, (K, M), kind)      # blocks of 128 along M, as the cols path needs
+    x = np.ascontiguousarray(xT.T)
+    yT, ysT = oracle.fp8q_cols(x, offs, threads=3)
+    B = 0
+    for g in range(len(counts)):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        if r1 == r0:
+            continue
+        y, ys = oracle.fp8q_rows(np.ascontiguousarray(x[r0:r1].T))
+        np.testing.assert_array_equal(yT[K * r0:K * r1].reshape(K, r1 - r0), y)
+        nb = (r1 - r0) // 128
+        np.testing.assert_array_equal(ysT[K * B:K * (B + nb)].reshape(nb, K), ys.T)
+        B += nb
+
+
+def test_fp8q_cols_threaded_and_grouped_drivers_agree():
+    rng = np.random.default_rng(33)
+    counts = [300, 7, 0, 129]
+    M, K = sum(counts), 256
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = _rand_bits(rng, (M, K), "normal")
+    a = oracle.fp8q_cols(x, offs)
+    b = oracle.fp8q_cols(x, offs, threads=4)
+    yT = np.zeros(M * K, np.uint8)
+    ys = np.zeros(oracle.cols_scale_size(offs, K), np.uint8)
+    for g in (3, 0, 1, 2):
+        oracle.fp8q_cols(x, offs, yT=yT, yT_scales=ys, groups=[g])
+    for got in (b, (yT, ys)):
+        np.testing.assert_array_equal(a[0], got[0])
+        np.testing.assert_array_equal(a[1], got[1])
