@@ -12,6 +12,7 @@ The binding has the same names as the C ABI:
 * ``mxfp4_quantize_rows(x, codes, scales, offs, ...)``
 * ``mxfp4_to_fp8_rows(codes, scales, y, y_scales, offs, ...)``
 * ``mxfp4_to_fp8_cols_ragged(codes, scales, yT, yT_scales, offs, ...)``
+* ``mxfp4_bf16_to_fp8_rows(x, y, y_scales, offs, ...)`` (backward FP8 quantizer)
 * ``mxfp4_cols_scale_capacity(M_cap, K, G)``, ``mxfp4_validate_offsets(offs, ...)``,
   ``mxfp4_status_string(status)``
 
@@ -41,6 +42,7 @@ EXPORTED = (
     "mxfp4_quantize_rows",
     "mxfp4_to_fp8_rows",
     "mxfp4_to_fp8_cols_ragged",
+    "mxfp4_bf16_to_fp8_rows",
     "mxfp4_cols_scale_capacity",
     "mxfp4_validate_offsets",
     "mxfp4_status_string",
@@ -73,6 +75,8 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_to_fp8_rows.restype = st
     lib.mxfp4_to_fp8_cols_ragged.argtypes = [P, P, P, P, P, I32, I64, I64, P]
     lib.mxfp4_to_fp8_cols_ragged.restype = st
+    lib.mxfp4_bf16_to_fp8_rows.argtypes = [P, P, P, P, I32, I64, I64, P]
+    lib.mxfp4_bf16_to_fp8_rows.restype = st
     lib.mxfp4_cols_scale_capacity.argtypes = [I64, I64, I32]
     lib.mxfp4_cols_scale_capacity.restype = I64
     lib.mxfp4_validate_offsets.argtypes = [P, I32, I64, P]
@@ -191,6 +195,18 @@ def mxfp4_to_fp8_cols_ragged(codes, scales, yT, yT_scales, offs, G=None, M_cap=N
            "mxfp4_to_fp8_cols_ragged")
 
 
+def mxfp4_bf16_to_fp8_rows(x, y, y_scales, offs, G=None, M_cap=None, K=None, stream=None):
+    """BF16 [M_cap, K] -> E4M3 y [M_cap, K] + UE8M0 y_scales [M_cap, K/128] (1x128 blocks)."""
+    G, M_cap, K = _dims(x, offs, G, M_cap, K)
+    n = max(M_cap, 0) * max(K, 0)
+    _need("mxfp4_bf16_to_fp8_rows", [(x, 2 * n, "x", ("bfloat16", "int16", "uint16")),
+                                     (y, n, "y", _FP8), (y_scales, n // 128, "y_scales", _U8),
+                                     (offs, 4 * (G + 1), "group_offsets", ("int32",))])
+    lib = load_library()
+    _check(lib.mxfp4_bf16_to_fp8_rows(_ptr(x), _ptr(y), _ptr(y_scales), _ptr(offs), G, M_cap, K,
+                                      _stream(stream)), "mxfp4_bf16_to_fp8_rows")
+
+
 def mxfp4_validate_offsets(offs, G=None, M_cap=None, stream=None) -> bool:
     """True if the device offsets satisfy the preconditions (synchronizes the stream)."""
     if G is None:
@@ -217,6 +233,10 @@ def alloc_rows_outputs(M_cap: int, K: int, device="cuda"):
     import torch
     return (torch.empty((M_cap, K), dtype=torch.uint8, device=device),
             torch.empty((M_cap, K // 128), dtype=torch.uint8, device=device))
+
+
+def alloc_fp8q_rows_outputs(M_cap: int, K: int, device="cuda"):
+    return alloc_rows_outputs(M_cap, K, device)
 
 
 def alloc_cols_outputs(M_cap: int, K: int, G: int, device="cuda"):

@@ -28,6 +28,7 @@ __device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_
 __device__ __forceinline__ u32x2 load_stream(const u32x2* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_stream(u32x2* p, u32x2 v) { __builtin_nontemporal_store(v, p); }
 
 // ---- cross-lane -----------------------------------------------------------------
 

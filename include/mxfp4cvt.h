@@ -95,6 +95,20 @@ mxfp4_status mxfp4_to_fp8_cols_ragged(const uint8_t* codes, const uint8_t* scale
                                       const int32_t* group_offsets, int32_t G, int64_t M_cap,
                                       int64_t K, hipStream_t stream);
 
+/* BF16 -> FP8 E4M3FN with one UE8M0 scale per 1x128 block along the row: the
+ * backward quantizer for gradients (DGRAD operand; technical summary section 2,
+ * item 2: the backward pass stays on the standard FP8 path, E4M3 with 128-element
+ * blocks as in item 1).
+ *   x_bf16    [M_cap, K] row-major BF16 bits (finite values).
+ *   y_e4m3    [M_cap, K]     E4M3FN bytes: x / 2^(S-127) rounded to nearest even,
+ *             subnormals included, magnitudes above 448 saturated to 448, sign kept.
+ *   y_scales  [M_cap, K/128] UE8M0 bytes S = floor(log2 amax) - 8 + 127 clamped to
+ *             [0, 254] (8 = E4M3's largest exponent), 0 for an all-zero block.
+ *   Rows [0, offs[G]) are written.  K must be a multiple of 128. */
+mxfp4_status mxfp4_bf16_to_fp8_rows(const uint16_t* x_bf16, uint8_t* y_e4m3, uint8_t* y_scales,
+                                    const int32_t* group_offsets, int32_t G, int64_t M_cap,
+                                    int64_t K, hipStream_t stream);
+
 /* Bytes the column-layout scale buffer needs for any offsets with offs[G] <= M_cap:
  * K * (ceil(M_cap / 128) + G).  Returns -1 for invalid sizes. */
 int64_t mxfp4_cols_scale_capacity(int64_t M_cap, int64_t K, int32_t G);

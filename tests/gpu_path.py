@@ -52,6 +52,28 @@ def gpu_cols(codes_d, scales_d, offs_d, M_cap, K, G):
     return yT, ys
 
 
+def gpu_fp8q_rows(x_d, offs_d, M_cap, K):
+    y = canary((M_cap, K))
+    ys = canary((M_cap, K // 128))
+    mx.mxfp4_bf16_to_fp8_rows(x_d, y, ys, offs_d, M_cap=M_cap, K=K)
+    return y, ys
+
+
+def check_fp8q_rows(x_bits: np.ndarray, offs: np.ndarray, threads: int | None = None):
+    """Backward FP8 quantizer, row layout: GPU vs oracle on rows [0, offs[G]), canary
+    beyond."""
+    threads = oracle.default_threads() if threads is None else threads
+    M_cap, K = x_bits.shape
+    M_tot = int(offs[-1])
+    y_d, ys_d = gpu_fp8q_rows(dev(x_bits), dev(offs), M_cap, K)
+    y_o, ys_o = oracle.fp8q_rows(x_bits, rows=M_tot, threads=threads)
+    y_g, ys_g = host(y_d), host(ys_d)
+    assert_bytes_equal(ys_g[:M_tot], ys_o[:M_tot], "fp8q row scales", row_len=K // 128)
+    assert_bytes_equal(y_g[:M_tot], y_o[:M_tot], "fp8q rows", row_len=K)
+    assert_untouched(y_g[M_tot:], "fp8q rows past offs[G]")
+    assert_untouched(ys_g[M_tot:], "fp8q row scales past offs[G]")
+
+
 def assert_bytes_equal(got: np.ndarray, want: np.ndarray, what: str, row_len: int | None = None):
     got = np.asarray(got)
     want = np.asarray(want)

@@ -104,6 +104,25 @@ def test_conversion_argument_errors(lib, fn):
         assert _r(lib, fn, M=0, K=1 << 24) == mx.MXFP4_OK
 
 
+def _f(lib, x=A, y=A2, ys=A3, o=OFFS, G=1, M=4, K=128):
+    return lib.mxfp4_bf16_to_fp8_rows(x, y, ys, o, G, M, K, None)
+
+
+def test_fp8_quantizer_argument_errors(lib):
+    for kw in ("x", "y", "ys", "o"):
+        assert _f(lib, **{kw: None}) == mx.MXFP4_ERR_NULL
+    assert _f(lib, K=64) == mx.MXFP4_ERR_SHAPE           # 1x128 blocks need K % 128 == 0
+    assert _f(lib, K=0) == mx.MXFP4_ERR_SHAPE
+    assert _f(lib, M=-1) == mx.MXFP4_ERR_SHAPE
+    assert _f(lib, G=0) == mx.MXFP4_ERR_SHAPE
+    assert _f(lib, M=1 << 40, K=1 << 20) == mx.MXFP4_ERR_SHAPE
+    assert _f(lib, x=A + 2) == mx.MXFP4_ERR_ALIGN
+    assert _f(lib, y=A2 + 8) == mx.MXFP4_ERR_ALIGN
+    assert _f(lib, ys=A3 + 1) == mx.MXFP4_ERR_ALIGN
+    assert _f(lib, o=OFFS + 2) == mx.MXFP4_ERR_ALIGN
+    assert _f(lib, M=0) == mx.MXFP4_OK
+
+
 def test_validate_offsets_argument_errors(lib):
     assert lib.mxfp4_validate_offsets(None, 1, 4, None) == mx.MXFP4_ERR_NULL
     assert lib.mxfp4_validate_offsets(OFFS, 0, 4, None) == mx.MXFP4_ERR_SHAPE
