@@ -17,7 +17,9 @@ with HIP events on the launch stream inside the timed region, against the
 (32768 x 7168 over 32 experts), the dense workload (65536 x 7168) and the
 forward chain, every launch's median over 20 launches each preceded by a 512 MB
 scrub read (so inputs come from HBM, not the caches), next to a device copy
-moving the same bytes.  ``cpu_baseline`` times the CPU oracle on a bounded
+moving the same bytes.  ``backward`` times the FP8 gradient quantizer
+(mxfp4_bf16_to_fp8_rows) on the same segments, outside ``value``; the scrubbed
+medians include it.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same workload on this host (all allowed threads, and one thread).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload config5] [--no-scrubbed]
@@ -46,6 +48,7 @@ KERNEL_SOURCES = {
     "quantize": ["quantize.hip", "common.h"],
     "rows": ["rows.hip", "common.h"],
     "cols": ["cols.hip", "common.h"],
+    "fp8q_rows": ["fp8q.hip", "common.h"],
 }
 
 
@@ -62,6 +65,8 @@ def alg_bytes(kernel: str, M_tot: int, K: int, col_scale_bytes: int = 0) -> int:
         return n // 2 + n // 32 + n + n // 128
     if kernel == "cols":                # 1/2 + 1/32 B in, 1 B out + one scale byte per (block, k)
         return n // 2 + n // 32 + n + col_scale_bytes
+    if kernel == "fp8q_rows":           # 2 B in, 1 + 1/128 B out
+        return 2 * n + n + n // 128
     raise ValueError(kernel)
 
 
@@ -152,10 +157,24 @@ def cpu_baseline(workload, target_s: float = 15.0):
 
 # ---- per-kernel timing with the caches scrubbed -----------------------------------------
 
-def build_launches(mx, workload, dev, torch):
+def build_launches(mx, workload, dev, torch, backward: bool = False):
     """Buffers and the ordered launches (kernel, segment, fn, algorithmic bytes) of one
-    step of a workload: quantize -> rows -> cols per segment, as the workload lists."""
+    step of a workload: quantize -> rows -> cols per segment, as the workload lists,
+    or with `backward` the FP8 gradient quantizer per segment (the segment's BF16
+    tensor standing in for a gradient of the same shape)."""
     segs = []
+    if backward:
+        launches = []
+        for seg in workload.segments:
+            x = torch.from_numpy(seg.x_bits.view(np.int16)).to(dev)
+            offs = torch.from_numpy(seg.offs).to(dev)
+            y, ys = mx.alloc_fp8q_rows_outputs(seg.M_cap, seg.K, dev)
+            d = {"seg": seg, "x": x, "offs": offs, "y": y, "ys": ys}
+            segs.append(d)
+            launches.append(("fp8q_rows", seg.name,
+                             lambda d=d: mx.mxfp4_bf16_to_fp8_rows(d["x"], d["y"], d["ys"], d["offs"]),
+                             alg_bytes("fp8q_rows", seg.M_tot, seg.K)))
+        return segs, launches
     for seg in workload.segments:
         x = torch.from_numpy(seg.x_bits.view(np.int16)).to(dev)
         offs = torch.from_numpy(seg.offs).to(dev)
@@ -215,6 +234,8 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
     for cid in config_ids:
         w = workloads.make_config(cid, 0)
         segs, launches = build_launches(mx, w, dev, torch)
+        bsegs, blaunches = build_launches(mx, w, dev, torch, backward=True)
+        launches = launches + blaunches
         for _, _, fn, _ in launches:      # valid codes for the conversions
             fn()
         torch.cuda.synchronize()
@@ -235,7 +256,7 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
             log(f"[bench] scrubbed {w.name} {kern}/{segname}: {us:.1f} us, {gbs:.0f} GB/s "
                 f"({gbs / HBM_PEAK_GBS:.1%} of peak, {gbs / copy_gbs:.1%} of a same-size copy)")
         out[w.name] = rows
-        del segs, launches
+        del segs, launches, bsegs, blaunches
         torch.cuda.empty_cache()
     del scrub
     torch.cuda.empty_cache()
@@ -316,6 +337,42 @@ def main():
     achieved = dom["GBps"]
     traffic = read_traffic(dom["kernel"], w.name, dom["segment"])
 
+    # the backward FP8 quantizer on the same segments, timed the same way (not in `value`)
+    bsegs, blaunches = build_launches(mx, w, dev, torch, backward=True)
+    for _ in range(args.warmup):
+        for _, _, fn, _ in blaunches:
+            fn()
+    bev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in blaunches] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    tb0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, (_, _, fn, _) in enumerate(blaunches):
+            bev[s][i][0].record()
+            fn()
+            bev[s][i][1].record()
+    torch.cuda.synchronize()
+    b_ms_per_step = (time.perf_counter() - tb0) * 1000.0 / args.steps
+    b_per_kernel = []
+    for i, (kern, segname, _, nbytes) in enumerate(blaunches):
+        ms = [bev[s][i][0].elapsed_time(bev[s][i][1]) for s in range(args.steps)]
+        mean_ms = float(np.mean(ms))
+        b_per_kernel.append({
+            "kernel": kern, "segment": segname, "alg_bytes": nbytes,
+            "mean_us": round(mean_ms * 1000.0, 2), "median_us": round(float(np.median(ms)) * 1000.0, 2),
+            "GBps": round(nbytes / (mean_ms / 1000.0) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (mean_ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+        })
+    b_step_bytes = sum(l[3] for l in blaunches)
+    backward = {
+        "what": "backward FP8 gradient quantizer (BF16 -> E4M3, 1x128 blocks) per segment",
+        "alg_bytes_per_step": b_step_bytes,
+        "ms_per_step": round(b_ms_per_step, 4),
+        "GBps": round(b_step_bytes / (b_ms_per_step / 1000.0) / 1e9, 1),
+        "per_kernel": b_per_kernel,
+    }
+    del bsegs, blaunches, bev
+
     if args.calibrate_copy:
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -363,6 +420,7 @@ def main():
             "mean_launch_us": dom["mean_us"],
         },
         "per_kernel": per_kernel,
+        "backward": backward,
         "per_config_scrubbed": None,
         "cpu_baseline": None,
     }
