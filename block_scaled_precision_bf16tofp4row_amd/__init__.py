@@ -12,7 +12,8 @@ The binding has the same names as the C ABI:
 * ``mxfp4_quantize_rows(x, codes, scales, offs, ...)``
 * ``mxfp4_to_fp8_rows(codes, scales, y, y_scales, offs, ...)``
 * ``mxfp4_to_fp8_cols_ragged(codes, scales, yT, yT_scales, offs, ...)``
-* ``mxfp4_bf16_to_fp8_rows(x, y, y_scales, offs, ...)`` (backward FP8 quantizer)
+* ``mxfp4_bf16_to_fp8_rows(x, y, y_scales, offs, ...)`` and
+  ``mxfp4_bf16_to_fp8_cols_ragged(x, yT, yT_scales, offs, ...)`` (backward FP8 quantizer)
 * ``mxfp4_cols_scale_capacity(M_cap, K, G)``, ``mxfp4_validate_offsets(offs, ...)``,
   ``mxfp4_status_string(status)``
 
@@ -43,6 +44,7 @@ EXPORTED = (
     "mxfp4_to_fp8_rows",
     "mxfp4_to_fp8_cols_ragged",
     "mxfp4_bf16_to_fp8_rows",
+    "mxfp4_bf16_to_fp8_cols_ragged",
     "mxfp4_cols_scale_capacity",
     "mxfp4_validate_offsets",
     "mxfp4_status_string",
@@ -77,6 +79,8 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_to_fp8_cols_ragged.restype = st
     lib.mxfp4_bf16_to_fp8_rows.argtypes = [P, P, P, P, I32, I64, I64, P]
     lib.mxfp4_bf16_to_fp8_rows.restype = st
+    lib.mxfp4_bf16_to_fp8_cols_ragged.argtypes = [P, P, P, P, I32, I64, I64, P]
+    lib.mxfp4_bf16_to_fp8_cols_ragged.restype = st
     lib.mxfp4_cols_scale_capacity.argtypes = [I64, I64, I32]
     lib.mxfp4_cols_scale_capacity.restype = I64
     lib.mxfp4_validate_offsets.argtypes = [P, I32, I64, P]
@@ -205,6 +209,20 @@ def mxfp4_bf16_to_fp8_rows(x, y, y_scales, offs, G=None, M_cap=None, K=None, str
     lib = load_library()
     _check(lib.mxfp4_bf16_to_fp8_rows(_ptr(x), _ptr(y), _ptr(y_scales), _ptr(offs), G, M_cap, K,
                                       _stream(stream)), "mxfp4_bf16_to_fp8_rows")
+
+
+def mxfp4_bf16_to_fp8_cols_ragged(x, yT, yT_scales, offs, G=None, M_cap=None, K=None, stream=None):
+    """BF16 [M_cap, K] -> per-expert transposed E4M3 yT + UE8M0 yT_scales (1x128 blocks
+    along the tokens; layout as mxfp4_to_fp8_cols_ragged, see the header)."""
+    G, M_cap, K = _dims(x, offs, G, M_cap, K)
+    n = max(M_cap, 0) * max(K, 0)
+    cap = mxfp4_cols_scale_capacity(M_cap, K, G) if n > 0 and G >= 1 else 0
+    _need("mxfp4_bf16_to_fp8_cols_ragged", [(x, 2 * n, "x", ("bfloat16", "int16", "uint16")),
+                                            (yT, n, "yT", _FP8), (yT_scales, max(cap, 0), "yT_scales", _U8),
+                                            (offs, 4 * (G + 1), "group_offsets", ("int32",))])
+    lib = load_library()
+    _check(lib.mxfp4_bf16_to_fp8_cols_ragged(_ptr(x), _ptr(yT), _ptr(yT_scales), _ptr(offs), G, M_cap, K,
+                                             _stream(stream)), "mxfp4_bf16_to_fp8_cols_ragged")
 
 
 def mxfp4_validate_offsets(offs, G=None, M_cap=None, stream=None) -> bool:

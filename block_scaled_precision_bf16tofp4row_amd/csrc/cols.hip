@@ -54,26 +54,16 @@
 // LDS layout: column k's ring (512 bytes, with its first 32 bytes repeated after it so
 // a 32-byte read window never wraps) starts at byte 544k + 32 (k >> 5).  This plays the
 // role of the page's padded, skewed shared-memory layout against bank conflicts.
-#include "common.h"
+#include "strips.h"
 
 namespace mxfp4 {
 
 __constant__ GapLut kColsGapLut = make_gap_lut();
 
-constexpr int kStripRows = 128;                      // one FP8 block along the tokens
-constexpr int kTileCols = 256;                       // eight MX groups
-constexpr int kSlots = 4;                            // ring slots (strips) per column
-constexpr int kRing = kSlots * kStripRows;           // 512
-constexpr int kMirror = 32;                          // ring bytes 0..31 repeated after the ring
-constexpr int kColBytes = kRing + kMirror;           // 544
-// column k's ring starts at byte 544k + 32 (k >> 5): non-decreasing, so the rings
-// never overlap
-constexpr int kTileBytes = kTileCols * kColBytes + 32 * ((kTileCols - 1) / 32);
 constexpr int kProducerWaves = 4;
 constexpr int kConsumerWaves = 12;
 // a strip is 32 store instructions (256 columns x 128 bytes); consumer wave v issues
 // instructions v, v + 12, v + 24 (< 32)
-constexpr int kMaxIts = (32 + kConsumerWaves - 1) / kConsumerWaves;
 #ifndef MXFP4_COLS_PREFETCH
 #define MXFP4_COLS_PREFETCH 2
 #endif
@@ -82,48 +72,6 @@ constexpr int kColsThreads = 64 * (kProducerWaves + kConsumerWaves);
 static_assert(kStripRows == 32 * kProducerWaves, "a producer wave converts 32 rows");
 static_assert(kTileCols == 32 * 8, "a producer lane converts one MX group of 8");
 static_assert((kRing & (kRing - 1)) == 0, "the ring position wraps with a mask");
-
-// Values the compiler cannot prove wave-uniform (they come through cross-lane ops or
-// LDS) are moved to scalar registers, so branches on them are scalar branches.
-__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int64_t uniform(int64_t x)
-{
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ uint32_t lds_col(uint32_t kk)
-{
-    return kColBytes * kk + 32 * (kk >> 5);
-}
-
-// ---- progress counters in LDS --------------------------------------------------------
-
-// Polls of a counter before a wave gives up (about a second): only a broken protocol
-// could wait that long, and the wave then leaves the kernel instead of hanging.
-constexpr uint32_t kSpinLimit = 1u << 24;
-
-// Wait (wave-uniformly) until *ctr >= target.  The acquire orders this wave's later
-// LDS reads after the writes that the counter's release published.
-__device__ __forceinline__ bool wait_at_least(uint32_t* ctr, uint32_t target)
-{
-    for (uint32_t i = 0; i < kSpinLimit; ++i) {
-        if (uniform(__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) >= target)
-            return true;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    return false;
-}
-
-// Count this wave's step as done: the release waits for the wave's own LDS accesses
-// (writes it publishes, reads of a slot it frees) before the increment.
-__device__ __forceinline__ void signal(uint32_t* ctr)
-{
-    if ((threadIdx.x & 63) == 0)
-        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
 
 // 4x4 byte transpose: a[i] holds bytes (row i, col 0..3); o[j] gets bytes (row 0..3, col j).
 __device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
@@ -138,132 +86,6 @@ __device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t 
     o2 = perm(u1, t1, 0x05040100u);
     o3 = perm(u1, t1, 0x07060302u);
 }
-
-// The 16 LDS bytes starting `o` (< 16) bytes past the 16-byte aligned address src: five
-// dwords read from the dword-aligned start, each output dword one v_alignbyte_b32 by o & 3
-// (a shift of zero returns the low dword).  No branch on o; the bytes read lie in
-// [src, src + 32).  (An unaligned ds_read_b128 gives the same bytes but measured about
-// twelve times slower on MI355X.)
-__device__ __forceinline__ u32x4 read_window16(const uint8_t* src, uint32_t o)
-{
-    const uint32_t* const w = reinterpret_cast<const uint32_t*>(src + (o & ~3u));
-    const uint32_t d0 = w[0], d1 = w[1], d2 = w[2], d3 = w[3], d4 = w[4];
-    const uint32_t b = o & 3u;
-    return u32x4{__builtin_amdgcn_alignbyte(d1, d0, b), __builtin_amdgcn_alignbyte(d2, d1, b),
-                 __builtin_amdgcn_alignbyte(d3, d2, b), __builtin_amdgcn_alignbyte(d4, d3, b)};
-}
-
-// ---- strips of experts ----------------------------------------------------------------
-
-// Per-lane expert table for experts g0 + lane: first strip, strip count, first row and
-// row count.  Every wave builds it on its own (no barrier).
-struct ExpertTable {
-    uint32_t sb, ns;           // first strip, strip count (lane's expert)
-    int32_t row0, mg;          // first row, rows
-    uint32_t total;            // strips of the whole chunk
-};
-
-__device__ __forceinline__ ExpertTable expert_chunk(const int32_t* __restrict__ offs, int G, int g0,
-                                                    uint32_t run)
-{
-    const int lane = threadIdx.x & 63;
-    const int h = g0 + lane;
-    ExpertTable t;
-    t.row0 = h < G ? offs[h] : 0;
-    t.mg = h < G ? offs[h + 1] - t.row0 : 0;
-    t.ns = (uint32_t)(t.mg + kStripRows - 1) / kStripRows;
-    uint32_t incl = t.ns;
-#pragma unroll
-    for (int dlt = 1; dlt < 64; dlt <<= 1) {
-        uint32_t other = __shfl_up(incl, dlt, 64);
-        if (lane >= dlt)
-            incl += other;
-    }
-    t.sb = run + incl - t.ns;
-    t.total = uniform((uint32_t)__shfl(incl, 63, 64));
-    return t;
-}
-
-struct StripInfo {
-    int64_t row0, mg;          // expert's first row and row count
-    uint32_t g;                // expert
-    uint32_t sb, ns;           // expert's first strip and strip count
-    uint32_t s;                // this strip (= its row in the block-scale output)
-    int64_t r_lo;              // the strip's first row, relative to row0
-    int nrows;                 // rows in the strip
-};
-
-__device__ __forceinline__ void set_rows(StripInfo& r)
-{
-    r.r_lo = (int64_t)(r.s - r.sb) * kStripRows;
-    r.nrows = (int)min<int64_t>(kStripRows, r.mg - r.r_lo);
-}
-
-// Expert of global strip s (s < total strips), searched 64 experts at a time with
-// one lane per expert.  `cached` is the table of experts 0..63.  Used once per
-// workgroup, before the strip loop.
-__device__ __forceinline__ StripInfo locate(const int32_t* __restrict__ offs, int G,
-                                            const ExpertTable& cached, uint32_t s)
-{
-    ExpertTable t = cached;
-    uint32_t run = 0;
-    for (int g0 = 0;; g0 += 64) {
-        if (g0 > 0)
-            t = expert_chunk(offs, G, g0, run);
-        const bool mine = t.ns > 0 && s >= t.sb && s < t.sb + t.ns;
-        const uint64_t mask = __ballot(mine);
-        if (mask || g0 + 64 >= G) {
-            const int src = mask ? __builtin_ctzll(mask) : 0;
-            StripInfo r;
-            r.row0 = uniform((int32_t)__builtin_amdgcn_readlane(t.row0, src));
-            r.mg = uniform((int32_t)__builtin_amdgcn_readlane(t.mg, src));
-            r.sb = uniform((uint32_t)__builtin_amdgcn_readlane(t.sb, src));
-            r.ns = uniform((uint32_t)__builtin_amdgcn_readlane(t.ns, src));
-            r.g = (uint32_t)(g0 + src);
-            r.s = s;
-            set_rows(r);
-            return r;
-        }
-        run += t.total;
-    }
-}
-
-// Strip p.s + 1 (which exists).  Inside the strip loop the experts are walked one
-// by one with scalar loads of the offsets (counted apart from the vector loads, so
-// the prefetched rows are never waited for early).
-__device__ __forceinline__ StripInfo next_strip(const int32_t* __restrict__ offs, int G,
-                                                const StripInfo& p)
-{
-    StripInfo r = p;
-    r.s = p.s + 1;
-    if (r.s >= r.sb + r.ns) {
-        r.sb += r.ns;
-        int64_t end = r.row0 + r.mg;
-        uint32_t g = r.g;
-        do {                                   // skip empty experts
-            ++g;
-            r.row0 = end;
-            end = offs[g + 1];
-        } while (end == r.row0 && (int)g + 1 < G);
-        r.g = g;
-        r.mg = end - r.row0;
-        r.ns = (uint32_t)((r.mg + kStripRows - 1) / kStripRows);
-    }
-    set_rows(r);
-    return r;
-}
-
-// What the producers hand to the consumers for one ring slot.
-struct SlotInfo {
-    int64_t A0;                // output byte of (tile column 0, strip row 0)
-    int32_t mg;                // rows of the expert (= output row length)
-    int32_t nrows;             // rows in the strip
-    uint32_t blk;              // row of the block-scale output
-    uint32_t flags;            // bit 0: the ring holds the previous strip of the same expert;
-                               // bit 1: the next strip (of the whole numbering) is of the
-                               // same expert; bit 2: lead-in strip (write nothing)
-    uint32_t S[2];             // block scale byte of MX groups 0..7 of the tile
-};
 
 // ---- producers ---------------------------------------------------------------------------
 
@@ -311,20 +133,6 @@ __device__ __forceinline__ Scales load_scales(const uint8_t* __restrict__ scales
     in.s = *reinterpret_cast<const uint32_t*>(sb + (r * (uint32_t)(K / 32) + 4 * dw));
     return in;
 }
-
-// ---- consumers ---------------------------------------------------------------------------
-
-// A consumer lane writes one aligned 16-byte chunk of one column per strip: lane
-// (mc = lane >> 3, c = lane & 7) of store instruction g (0..31) of the strip owns tile
-// column kk = 2 (g >> 2) + ((g & 3) >> 1) + 16 mc + 128 (g & 1) and bytes [16c, 16c + 16)
-// of the column's 128-byte output line, so the 8 lanes of a column store one whole line.
-// Within a run of strips of one expert the column's line phase is fixed, so this
-// state is set at the first strip and advanced by 128 bytes per strip.
-struct ColState {
-    uint32_t q[kMaxIts];       // ring offset of the lane's chunk, minus the strip's slot base
-    uint8_t* p[kMaxIts];       // output address of the lane's chunk
-    uint32_t o[kMaxIts];       // misalignment (wave-uniform): (-A) & 15
-};
 
 // ---- the kernel ---------------------------------------------------------------------------
 
@@ -530,114 +338,20 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     }
 
     // ================= consumers =================
-    const int v = wave - kProducerWaves;          // 0 .. kConsumerWaves - 1
-    const int mc = lane >> 3;
-    const int c = lane & 7;                       // bytes [16c, 16c + 16) of the line
-    // store instruction k of this wave is instruction g = v + kConsumerWaves k (< 32) of the
-    // strip: tile columns 2 (g >> 2) + ((g & 3) >> 1) + 16 mc + 128 (g & 1)
-    auto col_of = [&](int g) { return (uint32_t)(2 * (g >> 2) + ((g & 3) >> 1) + 16 * mc + 128 * (g & 1)); };
-    ColState cs;
-    for (uint32_t t = 0; t < n; ++t) {
-        if (!wait_at_least(&produced, kProducerWaves * (t + 1)))
-            return;
-        const uint32_t slot = t % kSlots;
-        const int64_t A0 = uniform(info[slot].A0);
-        const int64_t mg = uniform(info[slot].mg);
-        const int64_t nrows = uniform(info[slot].nrows);
-        const uint32_t flags = uniform(info[slot].flags);
-        const bool cin = flags & 1u, cout = flags & 2u, skip = flags & 4u;
-        const uint32_t slot_base = kStripRows * slot;
-
-        if (!skip && v == 0 && lane < 16 && 16 * lane < ncols) {
-            const uint32_t word = info[slot].S[lane >> 3];
-            const uint32_t w4 = ((word >> (8 * ((lane >> 1) & 3))) & 0xFFu) * 0x01010101u;
-            *reinterpret_cast<u32x4*>(yT_scales + K * (int64_t)uniform(info[slot].blk) + kTileCols * (int64_t)kt +
-                                      16 * lane) = u32x4{w4, w4, w4, w4};
-        }
-        if (!cin) {
-#pragma unroll
-            for (int k = 0; k < kMaxIts; ++k) {
-                const int g = v + kConsumerWaves * k;
-                if (g >= 32)
-                    continue;
-                const uint32_t kk = col_of(g);
-                const int64_t A = A0 + (int64_t)kk * mg;
-                const uint32_t a = (uint32_t)A & 127;
-                cs.o[k] = uniform((uint32_t)(16 - (A & 15)) & 15);
-                cs.q[k] = 16 * c - a - cs.o[k];
-                cs.p[k] = yT + (A - a) + 16 * c;
+    consume_strips<kProducerWaves, kConsumerWaves>(
+        tile, info, &produced, drained, yT, ncols, n, wave - kProducerWaves, [&](uint32_t slot) {
+            if (lane < 16 && 16 * lane < ncols) {
+                const uint32_t word = info[slot].S[lane >> 3];
+                const uint32_t w4 = ((word >> (8 * ((lane >> 1) & 3))) & 0xFFu) * 0x01010101u;
+                *reinterpret_cast<u32x4*>(yT_scales + K * (int64_t)uniform(info[slot].blk) +
+                                          kTileCols * (int64_t)kt + 16 * lane) = u32x4{w4, w4, w4, w4};
             }
-        }
-        if (skip) {
-#pragma unroll
-            for (int k = 0; k < kMaxIts; ++k)
-                cs.p[k] += kStripRows;
-        } else if (cin && cout) {
-#pragma unroll
-            for (int k = 0; k < kMaxIts; ++k) {
-                const int g = v + kConsumerWaves * k;
-                if (g >= 32 || ((g & 1) && ncols <= 128))
-                    continue;
-                const uint8_t* const src = tile + lds_col(col_of(g)) + ((cs.q[k] + slot_base) & (kRing - 1));
-                store_stream(reinterpret_cast<u32x4*>(cs.p[k]), read_window16(src, cs.o[k]));
-                cs.p[k] += kStripRows;
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < kMaxIts; ++k) {
-                const int g = v + kConsumerWaves * k;
-                if (g >= 32 || ((g & 1) && ncols <= 128))
-                    continue;
-                const uint32_t kk = col_of(g);
-                const int64_t A = A0 + (int64_t)kk * mg;
-                const uint32_t o = cs.o[k];
-                const int64_t E = A + nrows;
-                const int64_t W_lo = cin ? (A & ~(int64_t)127) : A;
-                const int64_t W_hi = cout ? (E & ~(int64_t)127) : E;
-                const int64_t j0 = W_lo >> 4;
-                const int nch = W_hi > W_lo ? (int)(((W_hi + 15) >> 4) - j0) : 0;
-                const uint8_t* const colp = tile + lds_col(kk);
-                for (int pass = 0; pass < 2; ++pass) {
-                    const int jj = c + 8 * pass;
-                    if (jj >= nch)
-                        continue;
-                    const int64_t b0 = (j0 + jj) << 4;
-                    const uint32_t pos = (slot_base + (uint32_t)(b0 - A) - o) & (kRing - 1);
-                    const u32x4 val = read_window16(colp + pos, o);
-                    if (b0 >= W_lo && b0 + 16 <= W_hi) {
-                        store_stream(reinterpret_cast<u32x4*>(yT + b0), val);
-                    } else {
-                        const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
-                        for (int q = 0; q < 16; ++q)
-                            if (b0 + q >= W_lo && b0 + q < W_hi)
-                                yT[b0 + q] = (uint8_t)(w4[q >> 2] >> (8 * (q & 3)));
-                    }
-                }
-                cs.p[k] += kStripRows;
-            }
-        }
-        signal(&drained[slot]);
-    }
+        });
 }
 
 int64_t cols_block_capacity(int64_t M_cap, int32_t G)
 {
     return (M_cap + kStripRows - 1) / kStripRows + G;
-}
-
-static int device_cus()
-{
-    static int cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
 }
 
 hipError_t launch_fp8_cols(const uint8_t* codes, const uint8_t* scales, uint8_t* yT,

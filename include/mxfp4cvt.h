@@ -109,6 +109,27 @@ mxfp4_status mxfp4_bf16_to_fp8_rows(const uint16_t* x_bf16, uint8_t* y_e4m3, uin
                                     const int32_t* group_offsets, int32_t G, int64_t M_cap,
                                     int64_t K, hipStream_t stream);
 
+/* BF16 -> FP8 E4M3FN in the transposed column layout per expert, one UE8M0 scale per
+ * 1x128 block along the tokens: the backward quantizer for the Wgrad gradient operand
+ * (technical summary section 2, item 2: backward pass on the FP8 path, E4M3 with
+ * 128-element blocks as in item 1; item 3: per-expert transpose over ragged segments
+ * without padding).  With M_g = offs[g+1] - offs[g], nb_g = ceil(M_g / 128) and
+ * B_g = nb_0 + ... + nb_{g-1}:
+ *   x_bf16     [M_cap, K] row-major BF16 bits (finite values).
+ *   yT_e4m3    expert g: [K, M_g] at byte K*offs[g], element (k, m') at k*M_g + m';
+ *              capacity K*M_cap bytes.  Element = x / 2^(S-127) rounded to nearest
+ *              even (subnormals included), magnitudes above 448 saturated, sign kept.
+ *   yT_scales  expert g: [nb_g, K] at byte K*B_g; entry (b, k) = S = floor(log2 amax)
+ *              - 8 + 127 clamped to [0, 254] (0 for an all-zero block), amax over the
+ *              rows of block b that exist (a partial last block uses only its rows);
+ *              capacity mxfp4_cols_scale_capacity(M_cap, K, G) bytes.
+ *   Bytes past each expert's M_g (and past offs[G]) are not written.
+ *   K must be a multiple of 128 and at most 2^24 (larger K -> MXFP4_ERR_SHAPE). */
+mxfp4_status mxfp4_bf16_to_fp8_cols_ragged(const uint16_t* x_bf16, uint8_t* yT_e4m3,
+                                           uint8_t* yT_scales, const int32_t* group_offsets,
+                                           int32_t G, int64_t M_cap, int64_t K,
+                                           hipStream_t stream);
+
 /* Bytes the column-layout scale buffer needs for any offsets with offs[G] <= M_cap:
  * K * (ceil(M_cap / 128) + G).  Returns -1 for invalid sizes. */
 int64_t mxfp4_cols_scale_capacity(int64_t M_cap, int64_t K, int32_t G);

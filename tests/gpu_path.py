@@ -74,6 +74,33 @@ def check_fp8q_rows(x_bits: np.ndarray, offs: np.ndarray, threads: int | None = 
     assert_untouched(ys_g[M_tot:], "fp8q row scales past offs[G]")
 
 
+def gpu_fp8q_cols(x_d, offs_d, M_cap, K, G):
+    yT = canary((max(1, M_cap * K),))
+    cap = mx.mxfp4_cols_scale_capacity(M_cap, K, G)
+    ys = canary((max(1, cap),))
+    mx.mxfp4_bf16_to_fp8_cols_ragged(x_d, yT, ys, offs_d, G=G, M_cap=M_cap, K=K)
+    return yT, ys
+
+
+def check_fp8q_cols(x_bits: np.ndarray, offs: np.ndarray, threads: int | None = None):
+    """Backward FP8 quantizer, transposed column layout: GPU vs oracle on every expert's
+    transpose and scales, canary beyond."""
+    threads = oracle.default_threads() if threads is None else threads
+    M_cap, K = x_bits.shape
+    G = offs.size - 1
+    M_tot = int(offs[-1])
+    yT_d, ys_d = gpu_fp8q_cols(dev(x_bits), dev(offs), M_cap, K, G)
+    used_s = oracle.cols_scale_size(offs, K)
+    yT_o = np.full(max(1, M_cap * K), CANARY, np.uint8)
+    ys_o = np.full(max(1, used_s), CANARY, np.uint8)
+    oracle.fp8q_cols(x_bits, offs, threads=threads, yT=yT_o, yT_scales=ys_o)
+    yT_g, ys_g = host(yT_d), host(ys_d)
+    assert_bytes_equal(ys_g[:used_s], ys_o[:used_s], "fp8q col scales")
+    assert_bytes_equal(yT_g[:M_tot * K], yT_o[:M_tot * K], "fp8q cols")
+    assert_untouched(yT_g[M_tot * K:], "fp8q cols past K*offs[G]")
+    assert_untouched(ys_g[used_s:], "fp8q col scales past the used blocks")
+
+
 def assert_bytes_equal(got: np.ndarray, want: np.ndarray, what: str, row_len: int | None = None):
     got = np.asarray(got)
     want = np.asarray(want)

@@ -123,6 +123,27 @@ def test_fp8_quantizer_argument_errors(lib):
     assert _f(lib, M=0) == mx.MXFP4_OK
 
 
+def _fc(lib, x=A, y=A2, ys=A3, o=OFFS, G=1, M=4, K=128):
+    return lib.mxfp4_bf16_to_fp8_cols_ragged(x, y, ys, o, G, M, K, None)
+
+
+def test_fp8_column_quantizer_argument_errors(lib):
+    for kw in ("x", "y", "ys", "o"):
+        assert _fc(lib, **{kw: None}) == mx.MXFP4_ERR_NULL
+    assert _fc(lib, K=64) == mx.MXFP4_ERR_SHAPE
+    assert _fc(lib, K=0) == mx.MXFP4_ERR_SHAPE
+    assert _fc(lib, M=-1) == mx.MXFP4_ERR_SHAPE
+    assert _fc(lib, G=0) == mx.MXFP4_ERR_SHAPE
+    assert _fc(lib, M=(1 << 31), K=128) == mx.MXFP4_ERR_SHAPE
+    assert _fc(lib, M=1, K=(1 << 24) + 128) == mx.MXFP4_ERR_SHAPE      # documented K limit
+    assert _fc(lib, x=A + 2) == mx.MXFP4_ERR_ALIGN
+    assert _fc(lib, y=A2 + 1) == mx.MXFP4_ERR_ALIGN
+    assert _fc(lib, ys=A3 + 3) == mx.MXFP4_ERR_ALIGN
+    assert _fc(lib, o=OFFS + 1) == mx.MXFP4_ERR_ALIGN
+    assert _fc(lib, M=0) == mx.MXFP4_OK
+    assert _fc(lib, M=0, K=1 << 24) == mx.MXFP4_OK
+
+
 def test_validate_offsets_argument_errors(lib):
     assert lib.mxfp4_validate_offsets(None, 1, 4, None) == mx.MXFP4_ERR_NULL
     assert lib.mxfp4_validate_offsets(OFFS, 0, 4, None) == mx.MXFP4_ERR_SHAPE

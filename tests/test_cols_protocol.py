@@ -1,8 +1,9 @@
-"""CPU model of the column kernel's LDS progress-counter protocol.
+"""CPU model of the column kernels' LDS progress-counter protocol.
 
-The column kernel (csrc/cols.hip) splits each workgroup into 4 producer waves and 12
-consumer waves that share a four-slot LDS ring and synchronise only through monotonic
-counters: `published` (partial block-scale maxima), `produced` (strips converted) and
+The column kernels (csrc/cols.hip: 4 producer and 12 consumer waves; csrc/fp8q_cols.hip:
+8 producer and 8 consumer waves, two partial-maximum slots) split each workgroup into
+producer and consumer waves that share a four-slot LDS ring and synchronise only
+through monotonic counters: `published` (partial block-scale maxima), `produced` (strips converted) and
 `drained[slot]` (strips written out).  This model replays the kernel's waits, with the
 same targets, as agents under a deterministic random scheduler, and checks every
 shared access:
@@ -11,8 +12,8 @@ shared access:
     carry bytes of strip t - 1 (slot (t - 1) % 4) are still strip t - 1;
   * a producer overwrites ring slot t % 4 only after every consumer finished strip
     t - 4 (its own reader) and strip t - 3 (which reads strip t - 4 as carry);
-  * a producer reads the partial maxima of strip t only once all four waves published
-    them, and no wave overwrites them while another still needs them;
+  * a producer reads the partial maxima of strip t only once all producer waves
+    published them, and no wave overwrites them while another still needs them;
   * the slot's strip info (written by producer wave 0) is the strip a consumer expects.
 
 It checks the protocol design (the wait targets), not the compiled kernel; the GPU
@@ -22,20 +23,22 @@ import random
 
 import pytest
 
-SLOTS, PW, CW = 4, 4, 12
+SLOTS = 4
+# (producer waves, consumer waves, partial-maximum slots) of the kernels
+CONFIGS = [(4, 12, 4), (8, 8, 2), (8, 4, 2)]
 
 
 class Violation(AssertionError):
     pass
 
 
-def _run(n, seed, carry=True, drain_lag=3):
+def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4):
     rnd = random.Random(seed)
     cnt = {"published": 0, "produced": 0}
     for k in range(SLOTS):
         cnt[f"drained{k}"] = 0
     ring = [None] * SLOTS          # slot -> [strip, set of producer waves written]
-    pmax = [None] * SLOTS          # slot -> [strip, set of waves published]
+    pmax = [None] * PMAX           # slot -> [strip, set of waves published]
     info = [None] * SLOTS          # slot -> strip
     done_prod = [[False] * n for _ in range(PW)]       # producer w finished produce(t)
     done_cons = [[False] * n for _ in range(CW)]       # consumer v finished strip t
@@ -45,13 +48,13 @@ def _run(n, seed, carry=True, drain_lag=3):
             raise Violation(msg)
 
     def publish(w, t):
-        s = t % SLOTS
+        s = t % PMAX
         e = pmax[s]
         if e is not None and e[0] != t:
-            # the slot held strip t - 4: every producer must have read it (produce(t - 4))
-            need(e[0] == t - SLOTS, f"P{w} publishes {t} over pmax of strip {e[0]}")
-            need(all(done_prod[x][t - SLOTS] for x in range(PW)),
-                 f"P{w} publishes {t} while strip {t - SLOTS}'s maxima are still needed")
+            # the slot held strip t - PMAX: every producer must have read it
+            need(e[0] == t - PMAX, f"P{w} publishes {t} over pmax of strip {e[0]}")
+            need(all(done_prod[x][t - PMAX] for x in range(PW)),
+                 f"P{w} publishes {t} while strip {t - PMAX}'s maxima are still needed")
             e = None
         pmax[s] = [t, (e[1] if e else set()) | {w}]
 
@@ -66,9 +69,9 @@ def _run(n, seed, carry=True, drain_lag=3):
                     yield "wait"
             while cnt["published"] < PW * (t + 1):
                 yield "wait"
-            s = t % SLOTS
-            e = pmax[s]
+            e = pmax[t % PMAX]
             need(e is not None and e[0] == t and len(e[1]) == PW, f"P{w} reads pmax {e} for strip {t}")
+            s = t % SLOTS
             if w == 0:
                 info[s] = t
             e = ring[s]
@@ -131,10 +134,12 @@ def _run(n, seed, carry=True, drain_lag=3):
     return steps
 
 
+@pytest.mark.parametrize("cfg", CONFIGS)
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 9, 13])
-def test_protocol_random_schedules(n):
-    for seed in range(60):
-        _run(n, seed)
+def test_protocol_random_schedules(n, cfg):
+    pw, cw, pm = cfg
+    for seed in range(60 if cfg == CONFIGS[0] else 30):
+        _run(n, seed, PW=pw, CW=cw, PMAX=pm)
 
 
 def test_model_catches_a_weaker_wait():
@@ -150,3 +155,16 @@ def test_model_catches_a_weaker_wait():
                 caught = True
                 break
         assert caught, f"drain lag {lag} not caught"
+
+
+def test_model_catches_a_single_partial_maximum_slot():
+    """Two partial-maximum slots are the minimum: with one, a wave publishing strip
+    t + 1 overwrites strip t's maxima while another wave still quantizes strip t."""
+    caught = False
+    for seed in range(300):
+        try:
+            _run(9, seed, PW=8, CW=8, PMAX=1)
+        except Violation:
+            caught = True
+            break
+    assert caught
