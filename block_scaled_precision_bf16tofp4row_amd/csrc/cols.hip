@@ -338,8 +338,12 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     }
 
     // ================= consumers =================
-    consume_strips<kProducerWaves, kConsumerWaves>(
-        tile, info, &produced, drained, yT, ncols, n, wave - kProducerWaves, [&](uint32_t slot) {
+    // the producer waves run in lockstep (each waits for all partial maxima of a strip
+    // before converting it), so one summed counter shows that all of them wrote strip t
+    consume_strips<kConsumerWaves>(
+        tile, info, drained, yT, ncols, n, wave - kProducerWaves,
+        [&](uint32_t t) { return wait_at_least(&produced, kProducerWaves * (t + 1)); },
+        [&](uint32_t slot) {
             if (lane < 16 && 16 * lane < ncols) {
                 const uint32_t word = info[slot].S[lane >> 3];
                 const uint32_t w4 = ((word >> (8 * ((lane >> 1) & 3))) & 0xFFu) * 0x01010101u;

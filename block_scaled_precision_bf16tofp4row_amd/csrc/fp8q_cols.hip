@@ -13,20 +13,20 @@
 // consumer machinery are those of strips.h (same layout as the MXFP4 -> FP8 column
 // conversion).
 //
-// Producers (waves 0-7): wave w quantizes rows 16w..16w+15 of every strip.  Lane
-// (rq = lane >> 4, cc = lane & 15) holds rows 16w + 4rq .. + 3 of tile columns
-// 8cc..8cc+7 and 128+8cc..128+8cc+7: sixteen lanes read one row's two 256-byte halves,
-// so every load instruction reads whole 128-byte lines.  Loads run kQPrefetch strips
-// ahead.  The column amax is reduced over the lane's four rows (packed 16-bit max on
-// the magnitude bits), over the four row quads (lane shuffles), and over the eight
-// waves (each publishes its partial maxima in LDS, every lane then takes the max of
-// the eight for its sixteen columns).
+// Producers (waves 0-7): wave w quantizes tile columns 32w..32w+31 over all 128 rows
+// of every strip, so a column's amax never leaves its wave.  Lane (c = lane & 3,
+// rg = lane >> 2) holds rows 8rg..8rg+7 of columns 32w + 8c .. + 7 (one 16-byte chunk
+// per row; the lanes of a load instruction read 16 rows x 64 bytes).  Loads run
+// kQPrefetch strips ahead.  The column amax is reduced over the lane's eight rows
+// (packed 16-bit max on the magnitude bits) and over the sixteen row groups (two DPP
+// row rotations, then the gfx950 16- and 32-lane swaps); no cross-wave step, so each
+// producer wave runs its strips on its own and only the consumers wait for all of them.
 // The element convert, v_cvt_scalef32_pk_fp8_bf16, takes one scale for a pair of
 // BF16, and neighbouring columns have different scales, so a pair is two rows of one
-// column (one v_perm_b32): the two converts of a column's four rows then give the
-// column's ring dword directly, rows in order, with no byte transpose.  As in the row
-// quantizer, magnitudes are clamped to 448 * 2^(S-127) before the convert (it returns
-// NaN for quotients of 464 or more instead of saturating).
+// column (one v_perm_b32): the four converts of a column's eight rows give its eight
+// ring bytes, rows in order, with no byte transpose.  As in the row quantizer,
+// magnitudes are clamped to 448 * 2^(S-127) before the convert (it returns NaN for
+// quotients of 464 or more instead of saturating).
 // Consumers (waves 8-15): strips.h.
 #include "strips.h"
 
@@ -40,39 +40,44 @@ typedef __bf16 qbf16x2 __attribute__((ext_vector_type(2)));
 #ifndef MXFP4_FP8QC_PREFETCH
 #define MXFP4_FP8QC_PREFETCH 1
 #endif
-constexpr int kQProducerWaves = 8;                          // 16 rows each
+constexpr int kQProducerWaves = 8;                          // 32 columns each
 constexpr int kQConsumerWaves = MXFP4_FP8QC_CONSUMERS;
 constexpr int kQPrefetch = MXFP4_FP8QC_PREFETCH;            // strips of loads in flight
 constexpr int kQThreads = 64 * (kQProducerWaves + kQConsumerWaves);
-constexpr int kPmaxSlots = 2;                               // partial maxima: strips t and t + 1
-static_assert(kStripRows == 16 * kQProducerWaves, "a producer wave quantizes 16 rows");
-static_assert(kTileCols == 256, "a producer lane holds columns 8cc.. and 128 + 8cc..");
+static_assert(kTileCols == 32 * kQProducerWaves, "a producer wave quantizes 32 columns");
+static_assert(kStripRows == 128, "sixteen row groups of eight rows");
 static_assert((kRing & (kRing - 1)) == 0, "the ring position wraps with a mask");
 
 namespace {
 
-// A lane's four rows of a strip, two 16-byte chunks (8 BF16) per row: v[i][h] holds
-// tile columns 128h + 8cc .. + 7 of row 4rq + i of the wave's rows.
+// A lane's eight rows of a strip: v[i] holds 8 BF16 (columns 32w + 8c .. + 7) of row
+// 8rg + i.
 struct QRows {
-    u32x4 v[4][2];
+    u32x4 v[8];
 };
 
-// Loads are unconditional (rows past the strip repeat its last row, which leaves the
-// column amax unchanged; their converted bytes are never written out), so every strip
-// issues the same straight-line sequence of loads.  Row offsets within a strip fit in
-// 32 bits (128 rows x 2K bytes with K <= 2^24).
+// Loads are buffer loads: the strip's base address and byte range (its rows that
+// exist) go into the scalar buffer resource, and the lane's byte offsets (row * 2K +
+// column byte) are the same for every strip, computed once (`off`).  Rows past a
+// partial strip (an expert's last) lie past the range and read as zero, which leaves
+// the column amax unchanged; their converted bytes are never written out.  So every
+// strip issues the same straight-line loads with no vector arithmetic in front of
+// them (temporaries there would make the compiler wait for the loads still in flight
+// before it reuses their registers).  Offsets fit in 32 bits (128 rows x 2K bytes with
+// K <= 2^24; the range is capped at 2^32 - 1, far above the last valid offset).
+constexpr int kBufferWord3 = 0x00020000;          // gfx9 buffer resource word 3 (32-bit data)
+
 __device__ __forceinline__ QRows load_rows(const uint8_t* __restrict__ x, int64_t K, const StripInfo& st,
-                                           int row_q, uint32_t cbyte0, uint32_t cbyte1, uint32_t kt)
+                                           uint32_t kt, const uint32_t (&off)[8])
 {
     QRows in;
     const uint8_t* const xb = x + (st.row0 + st.r_lo) * (2 * K) + 512 * (int64_t)kt;
-    const uint32_t rb = (uint32_t)(2 * K);
+    const uint64_t range = (uint64_t)st.nrows * (uint64_t)(2 * K);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)xb, (short)0, (int)(range > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)range), kBufferWord3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t r = (uint32_t)min(row_q + i, st.nrows - 1);
-        in.v[i][0] = *reinterpret_cast<const u32x4*>(xb + (r * rb + cbyte0));
-        in.v[i][1] = *reinterpret_cast<const u32x4*>(xb + (r * rb + cbyte1));
-    }
+    for (int i = 0; i < 8; ++i)
+        in.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off[i], 0, 0));
     return in;
 }
 
@@ -80,6 +85,20 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
 {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
                                                                   __builtin_bit_cast(u16x2, b)));
+}
+
+// Packed 16-bit max over the lanes that share lane & 3 (the sixteen row groups): DPP
+// row rotations by 4 and 8 inside each 16-lane row, then the gfx950 swaps of 16-lane
+// rows and 32-lane halves (the max of both swap outputs holds the partner's value
+// whichever way the swap pairs the lanes).
+__device__ __forceinline__ uint32_t rowgroup_max(uint32_t m)
+{
+    m = pk_max_u16(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x124, 0xF, 0xF, false));   // row_ror:4
+    m = pk_max_u16(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x128, 0xF, 0xF, false));   // row_ror:8
+    const auto a = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+    m = pk_max_u16(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    return pk_max_u16(b[0], b[1]);
 }
 
 __device__ __forceinline__ qbf16x2 as_qbf16x2(uint32_t u)
@@ -113,10 +132,11 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     __shared__ __attribute__((aligned(16))) SlotInfo info[kSlots];
     // per ring slot: the block scale byte of each tile column
     __shared__ __attribute__((aligned(16))) uint8_t sbytes[kSlots][kTileCols];
-    // per strip parity, per producer wave: the largest BF16 magnitude field of each
-    // tile column over the wave's 16 rows
-    __shared__ __attribute__((aligned(16))) uint16_t pmax[kPmaxSlots][kQProducerWaves][kTileCols];
-    __shared__ uint32_t produced, published, drained[kSlots];
+    // strips finished, one counter per producer wave (the producer waves do not run in
+    // lockstep, so a summed count would not show that all of them wrote strip t), and
+    // per ring slot the strips drained by the consumer waves (all monotonic)
+    __shared__ __attribute__((aligned(16))) uint32_t produced[kQProducerWaves];
+    __shared__ uint32_t drained[kSlots];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -142,8 +162,8 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     const uint32_t n = s1 - s0 + lead;
 
     if (tid == 0) {
-        produced = 0;
-        published = 0;
+        for (int k = 0; k < kQProducerWaves; ++k)
+            produced[k] = 0;
         for (int k = 0; k < kSlots; ++k)
             drained[k] = 0;
     }
@@ -151,116 +171,75 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
 
     if (wave < kQProducerWaves) {
         // ================= producers =================
-        const int cc = lane & 15;
-        const int rq = lane >> 4;
-        const int row_q = 16 * wave + 4 * rq;     // first of the lane's four rows
-        // the narrow last tile (128 columns) has no second half: those lanes repeat the
-        // first half (their columns are never written out)
-        const uint32_t cbyte0 = 16 * (uint32_t)cc;
-        const uint32_t cbyte1 = ncols > 128 ? 256 + cbyte0 : cbyte0;
-        // tile column 128h + 8cc + j sits at LDS byte lds_col(128h + 8cc) + 544 j
-        const uint32_t wbase0 = lds_col(8 * cc) + row_q;
-        const uint32_t wbase1 = lds_col(128 + 8 * cc) + row_q;
+        const int c = lane & 3;
+        const int rg = lane >> 2;
+        const int row_g = 8 * rg;                 // first of the lane's eight rows
+        // the narrow last tile (128 columns) has waves 0-3 only: waves 4-7 repeat the
+        // columns of wave w - 4 (their ring columns are never written out)
+        const uint32_t wcol = ncols > 128 ? (uint32_t)wave : (uint32_t)(wave & 3);
+        const uint32_t cbyte = 64 * wcol + 16 * (uint32_t)c;
+        uint32_t off[8];                          // byte offsets of the lane's rows in a strip
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            off[i] = (uint32_t)(row_g + i) * (uint32_t)(2 * K) + cbyte;
+        // tile column 32w + 8c + j sits at LDS byte lds_col(32w + 8c) + 544 j
+        const uint32_t wbase = lds_col(32 * wave + 8 * c) + row_g;
 
-        // this wave's partial maxima of strip `st` (its 16 rows) into pmax[ps]
-        auto publish_max = [&](const QRows& in, uint32_t ps) {
-            uint32_t m[2][4];
+        auto produce = [&](const StripInfo& st, const QRows& in, uint32_t slot, uint32_t flags) {
+            // column maxima over the strip (pairs of columns 8c + 2d, 8c + 2d + 1)
+            uint32_t M[4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const u32x4 a = in.v[0][h], b = in.v[1][h], c = in.v[2][h], d = in.v[3][h];
-                m[h][0] = pk_max_u16(pk_max_u16(a.x & 0x7FFF7FFFu, b.x & 0x7FFF7FFFu),
-                                     pk_max_u16(c.x & 0x7FFF7FFFu, d.x & 0x7FFF7FFFu));
-                m[h][1] = pk_max_u16(pk_max_u16(a.y & 0x7FFF7FFFu, b.y & 0x7FFF7FFFu),
-                                     pk_max_u16(c.y & 0x7FFF7FFFu, d.y & 0x7FFF7FFFu));
-                m[h][2] = pk_max_u16(pk_max_u16(a.z & 0x7FFF7FFFu, b.z & 0x7FFF7FFFu),
-                                     pk_max_u16(c.z & 0x7FFF7FFFu, d.z & 0x7FFF7FFFu));
-                m[h][3] = pk_max_u16(pk_max_u16(a.w & 0x7FFF7FFFu, b.w & 0x7FFF7FFFu),
-                                     pk_max_u16(c.w & 0x7FFF7FFFu, d.w & 0x7FFF7FFFu));
+            for (int d = 0; d < 4; ++d) {
+                uint32_t m = in.v[0][d] & 0x7FFF7FFFu;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    m[h][q] = pk_max_u16(m[h][q], (uint32_t)__shfl_xor((int)m[h][q], 16, 64));
-                    m[h][q] = pk_max_u16(m[h][q], (uint32_t)__shfl_xor((int)m[h][q], 32, 64));
-                }
-            }
-            if (rq == 0) {
-                *reinterpret_cast<u32x4*>(&pmax[ps][wave][8 * cc]) = u32x4{m[0][0], m[0][1], m[0][2], m[0][3]};
-                *reinterpret_cast<u32x4*>(&pmax[ps][wave][128 + 8 * cc]) =
-                    u32x4{m[1][0], m[1][1], m[1][2], m[1][3]};
-            }
-        };
-
-        auto produce = [&](const StripInfo& st, const QRows& in, uint32_t slot, uint32_t ps, uint32_t flags) {
-            // column maxima over the strip: max of the eight waves' partial maxima
-            uint32_t M[2][4];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                u32x4 acc = *reinterpret_cast<const u32x4*>(&pmax[ps][0][128 * h + 8 * cc]);
-#pragma unroll
-                for (int w = 1; w < kQProducerWaves; ++w) {
-                    const u32x4 o = *reinterpret_cast<const u32x4*>(&pmax[ps][w][128 * h + 8 * cc]);
-                    acc = u32x4{pk_max_u16(acc.x, o.x), pk_max_u16(acc.y, o.y), pk_max_u16(acc.z, o.z),
-                                pk_max_u16(acc.w, o.w)};
-                }
-                M[h][0] = acc.x;
-                M[h][1] = acc.y;
-                M[h][2] = acc.z;
-                M[h][3] = acc.w;
+                for (int i = 1; i < 8; ++i)
+                    m = pk_max_u16(m, in.v[i][d] & 0x7FFF7FFFu);
+                M[d] = rowgroup_max(m);
             }
             // scale bytes: biased exponent field of the column max minus 8, at least 0
-            uint32_t Sb[2][2];            // [h][columns 0..3 / 4..7] as bytes
+            uint32_t S2[4];               // S of columns 2d (low half) and 2d + 1 (high half)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    const u16x2 e0 = __builtin_bit_cast(u16x2, M[h][2 * p]) >> (unsigned short)7;
-                    const u16x2 e1 = __builtin_bit_cast(u16x2, M[h][2 * p + 1]) >> (unsigned short)7;
-                    const u16x2 eight = {8, 8};
-                    const u16x2 s0v = __builtin_elementwise_sub_sat(e0, eight);
-                    const u16x2 s1v = __builtin_elementwise_sub_sat(e1, eight);
-                    Sb[h][p] = (uint32_t)s0v.x | ((uint32_t)s0v.y << 8) | ((uint32_t)s1v.x << 16) |
-                               ((uint32_t)s1v.y << 24);
-                }
+            for (int d = 0; d < 4; ++d) {
+                const u16x2 e = __builtin_bit_cast(u16x2, M[d]) >> (unsigned short)7;
+                const u16x2 eight = {8, 8};
+                S2[d] = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(e, eight));
             }
-            if (wave == 0) {
-                if (rq == 0) {
-                    *reinterpret_cast<u32x2*>(&sbytes[slot][8 * cc]) = u32x2{Sb[0][0], Sb[0][1]};
-                    *reinterpret_cast<u32x2*>(&sbytes[slot][128 + 8 * cc]) = u32x2{Sb[1][0], Sb[1][1]};
-                }
-                if (lane == 0) {
-                    info[slot].A0 = K * st.row0 + st.r_lo + (int64_t)kTileCols * kt * st.mg;
-                    info[slot].mg = (int32_t)st.mg;
-                    info[slot].nrows = st.nrows;
-                    info[slot].blk = st.s;
-                    info[slot].flags = flags;
-                }
+            if (rg == 0)
+                *reinterpret_cast<u32x2*>(&sbytes[slot][32 * wave + 8 * c]) =
+                    u32x2{perm(S2[1], S2[0], 0x06040200u), perm(S2[3], S2[2], 0x06040200u)};
+            if (wave == 0 && lane == 0) {
+                info[slot].A0 = K * st.row0 + st.r_lo + (int64_t)kTileCols * kt * st.mg;
+                info[slot].mg = (int32_t)st.mg;
+                info[slot].nrows = st.nrows;
+                info[slot].blk = st.s;
+                info[slot].flags = flags;
             }
-            // quantize column by column: rows (0, 1) and (2, 3) of the lane's four rows
-            // form the two pairs of one convert each; the result dword is the column's
-            // four ring bytes in row order
-            const uint32_t sl = kStripRows * slot;
+            // quantize column by column: rows (0, 1), (2, 3), (4, 5), (6, 7) form the
+            // four pairs; the two result dwords are the column's eight ring bytes
+            uint8_t* const w = tile + wbase + kStripRows * slot;
+            u32x2 T[8];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint8_t* const w = tile + (h ? wbase1 : wbase0) + sl;
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t S = (S2[j >> 1] >> (16 * (j & 1))) & 0xFFu;
+                const uint32_t clamp = ((S + 8) << 7) | 0x60u;
+                const uint32_t clamp2 = clamp * 0x00010001u;
+                const float scale = __uint_as_float(max(S << 23, 0x00400000u));   // S = 0: 2^-127
+                const int d = j >> 1;
+                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                u16x2 lo = {0, 0}, hi = {0, 0};
+                lo = cvt_pair<false>(lo, perm(in.v[1][d], in.v[0][d], sel), clamp2, scale);
+                lo = cvt_pair<true>(lo, perm(in.v[3][d], in.v[2][d], sel), clamp2, scale);
+                hi = cvt_pair<false>(hi, perm(in.v[5][d], in.v[4][d], sel), clamp2, scale);
+                hi = cvt_pair<true>(hi, perm(in.v[7][d], in.v[6][d], sel), clamp2, scale);
+                T[j] = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+                *reinterpret_cast<u32x2*>(w + kColBytes * j) = T[j];
+            }
+            // ring bytes 0..31 (rows 0..31 of slot 0: row groups 0-3) are repeated after
+            // the ring, so a 32-byte read window never wraps
+            if (slot == 0 && rg < 4) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t S = (Sb[h][j >> 2] >> (8 * (j & 3))) & 0xFFu;
-                    const uint32_t clamp = ((S + 8) << 7) | 0x60u;
-                    const uint32_t clamp2 = clamp * 0x00010001u;
-                    const float scale = __uint_as_float(S == 0 ? 0x00400000u : S << 23);
-                    const int q = j >> 1;
-                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                    const uint32_t r01 = perm(in.v[1][h][q], in.v[0][h][q], sel);
-                    const uint32_t r23 = perm(in.v[3][h][q], in.v[2][h][q], sel);
-                    u16x2 acc = {0, 0};
-                    acc = cvt_pair<false>(acc, r01, clamp2, scale);
-                    acc = cvt_pair<true>(acc, r23, clamp2, scale);
-                    const uint32_t T = __builtin_bit_cast(uint32_t, acc);
-                    *reinterpret_cast<uint32_t*>(w + kColBytes * j) = T;
-                    // ring bytes 0..31 (rows 0..31 of slot 0, waves 0 and 1) are repeated
-                    // after the ring, so a 32-byte read window never wraps
-                    if (slot == 0 && wave < 2)
-                        *reinterpret_cast<uint32_t*>(w + kRing + kColBytes * j) = T;
-                }
+                for (int j = 0; j < 8; ++j)
+                    *reinterpret_cast<u32x2*>(w + kRing + kColBytes * j) = T[j];
             }
         };
         auto flags_of = [](uint32_t prev_sb, const StripInfo& cur, bool lead_in) {
@@ -268,10 +247,9 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
         };
 
         // Step t waits until the consumers have drained strip t - 3 (whose slot carries
-        // into strip t - 2, the last reader of slot t % 4) and until all producer waves
-        // have published their partial maxima of strip t, quantizes strip t, signals it,
-        // and publishes its own partial maxima of strip t + 1.  Register sets rotate over
-        // kQPrefetch + 1 strips; the loop is unrolled by that much so each set keeps
+        // into strip t - 2, the last reader of slot t % 4), quantizes strip t and
+        // signals it.  Loads run kQPrefetch strips ahead; register sets rotate over
+        // kQPrefetch + 1 strips and the loop is unrolled by that much so each set keeps
         // fixed registers.
         constexpr int kSets = kQPrefetch + 1;
         uint32_t prev_sb = 0xFFFFFFFFu;
@@ -285,9 +263,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
             I[u] = (uint32_t)u < n ? next_strip(offs, G, I[u - 1]) : I[u - 1];
 #pragma unroll
         for (int u = 0; u < kQPrefetch; ++u)
-            R[u] = load_rows(x, K, I[u], row_q, cbyte0, cbyte1, kt);
-        publish_max(R[0], 0);
-        signal(&published);
+            R[u] = load_rows(x, K, I[u], kt, off);
         for (uint32_t t = 0;; t += kSets) {
 #pragma unroll
             for (int u = 0; u < kSets; ++u) {
@@ -295,27 +271,24 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                 const int ld = (u + kQPrefetch) % kSets;          // set receiving strip tt + kQPrefetch
                 const int pv = (u + kQPrefetch - 1) % kSets;      // set of strip tt + kQPrefetch - 1
                 I[ld] = tt + kQPrefetch < n ? next_strip(offs, G, I[pv]) : I[pv];
-                R[ld] = load_rows(x, K, I[ld], row_q, cbyte0, cbyte1, kt);
-                const int nx = (u + 1) % kSets;                   // set of strip tt + 1
+                R[ld] = load_rows(x, K, I[ld], kt, off);
                 if (tt >= 3 && !wait_at_least(&drained[(tt - 3) % kSlots],
                                               kQConsumerWaves * ((tt - 3) / kSlots + 1)))
                     return;
-                if (!wait_at_least(&published, kQProducerWaves * (tt + 1)))
-                    return;
-                produce(I[u], R[u], tt % kSlots, tt % kPmaxSlots, flags_of(prev_sb, I[u], tt == 0 && lead != 0));
+                produce(I[u], R[u], tt % kSlots, flags_of(prev_sb, I[u], tt == 0 && lead != 0));
                 prev_sb = I[u].sb;
-                signal(&produced);
+                signal(&produced[wave]);
                 if (tt + 1 >= n)
                     return;
-                publish_max(R[nx], (tt + 1) % kPmaxSlots);
-                signal(&published);
             }
         }
     }
 
     // ================= consumers =================
-    consume_strips<kQProducerWaves, kQConsumerWaves>(
-        tile, info, &produced, drained, yT, ncols, n, wave - kQProducerWaves, [&](uint32_t slot) {
+    consume_strips<kQConsumerWaves>(
+        tile, info, drained, yT, ncols, n, wave - kQProducerWaves,
+        [&](uint32_t t) { return wait_all_at_least<kQProducerWaves>(produced, t + 1); },
+        [&](uint32_t slot) {
             if (lane < 16 && 16 * lane < ncols)
                 *reinterpret_cast<u32x4*>(yT_scales + K * (int64_t)uniform(info[slot].blk) +
                                           kTileCols * (int64_t)kt + 16 * lane) =

@@ -80,6 +80,22 @@ __device__ __forceinline__ bool wait_at_least(uint32_t* ctr, uint32_t target)
     return false;
 }
 
+// Wait (wave-uniformly) until each of the N counters ctr[0..N-1] is >= target.
+template <int N>
+__device__ __forceinline__ bool wait_all_at_least(uint32_t* ctr, uint32_t target)
+{
+    for (uint32_t i = 0; i < kSpinLimit; ++i) {
+        uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            m = min(m, __hip_atomic_load(ctr + k, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (uniform(m) >= target)
+            return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
 // Count this wave's step as done: the release waits for the wave's own LDS accesses
 // (writes it publishes, reads of a slot it frees) before the increment.
 __device__ __forceinline__ void signal(uint32_t* ctr)
@@ -231,13 +247,14 @@ struct ColState {
 
 // The consumer waves' loop, shared by the column kernels: wave v (0 .. kConsumerWaves - 1
 // of the consumers) writes store instructions v, v + kConsumerWaves, ... (< 32) of every
-// strip the workgroup converts, once the kProducerWaves producer waves have counted the
-// strip in `produced`, and counts the slot in `drained[slot]` when done.  Consumer wave
-// 0 also calls write_scales(slot) for every strip that is not a lead-in strip.
-template <int kProducerWaves, int kConsumerWaves, typename WriteScales>
-__device__ __forceinline__ void consume_strips(uint8_t* tile, const SlotInfo* info, uint32_t* produced,
-                                               uint32_t* drained, uint8_t* __restrict__ yT, int ncols,
-                                               uint32_t n, int v, WriteScales write_scales)
+// strip the workgroup converts, once wait_produced(t) has seen every producer wave
+// finish strip t (false: the wait gave up, leave), and counts the slot in
+// `drained[slot]` when done.  Consumer wave 0 also calls write_scales(slot) for every
+// strip that is not a lead-in strip.
+template <int kConsumerWaves, typename WaitProduced, typename WriteScales>
+__device__ __forceinline__ void consume_strips(uint8_t* tile, const SlotInfo* info, uint32_t* drained,
+                                               uint8_t* __restrict__ yT, int ncols, uint32_t n, int v,
+                                               WaitProduced wait_produced, WriteScales write_scales)
 {
     constexpr int kMaxIts = (32 + kConsumerWaves - 1) / kConsumerWaves;
     const int lane = threadIdx.x & 63;
@@ -248,7 +265,7 @@ __device__ __forceinline__ void consume_strips(uint8_t* tile, const SlotInfo* in
     auto col_of = [&](int g) { return (uint32_t)(2 * (g >> 2) + ((g & 3) >> 1) + 16 * mc + 128 * (g & 1)); };
     ColState<kMaxIts> cs;
     for (uint32_t t = 0; t < n; ++t) {
-        if (!wait_at_least(produced, kProducerWaves * (t + 1)))
+        if (!wait_produced(t))
             return;
         const uint32_t slot = t % kSlots;
         const int64_t A0 = uniform(info[slot].A0);

@@ -1,10 +1,12 @@
 """CPU model of the column kernels' LDS progress-counter protocol.
 
-The column kernels (csrc/cols.hip: 4 producer and 12 consumer waves; csrc/fp8q_cols.hip:
-8 producer and 8 consumer waves, two partial-maximum slots) split each workgroup into
-producer and consumer waves that share a four-slot LDS ring and synchronise only
-through monotonic counters: `published` (partial block-scale maxima), `produced` (strips converted) and
-`drained[slot]` (strips written out).  This model replays the kernel's waits, with the
+The column kernels (csrc/cols.hip: 4 producer and 12 consumer waves that also exchange
+partial block-scale maxima; csrc/fp8q_cols.hip: 8 producer and 8 consumer waves, each
+producer wave owning whole columns, so no partial maxima, and one `produced` counter per
+producer wave) split each workgroup into producer and consumer waves that share a
+four-slot LDS ring and synchronise only through monotonic counters: `published`
+(partial block-scale maxima), `produced` (strips converted) and `drained[slot]`
+(strips written out).  This model replays the kernel's waits, with the
 same targets, as agents under a deterministic random scheduler, and checks every
 shared access:
 
@@ -24,21 +26,27 @@ import random
 import pytest
 
 SLOTS = 4
-# (producer waves, consumer waves, partial-maximum slots) of the kernels
-CONFIGS = [(4, 12, 4), (8, 8, 2), (8, 4, 2)]
+# (producer waves, consumer waves, partial-maximum slots or None) of the kernels
+CONFIGS = [(4, 12, 4), (8, 8, None)]
 
 
 class Violation(AssertionError):
     pass
 
 
-def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4):
+def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None):
+    """PMAX None: no partial maxima.  per_wave (default: PMAX is None): one produced
+    counter per producer wave, the consumers wait for the smallest."""
+    if per_wave is None:
+        per_wave = PMAX is None
     rnd = random.Random(seed)
     cnt = {"published": 0, "produced": 0}
+    for w in range(PW):
+        cnt[f"produced{w}"] = 0
     for k in range(SLOTS):
         cnt[f"drained{k}"] = 0
     ring = [None] * SLOTS          # slot -> [strip, set of producer waves written]
-    pmax = [None] * PMAX           # slot -> [strip, set of waves published]
+    pmax = [None] * (PMAX or 1)    # slot -> [strip, set of waves published]
     info = [None] * SLOTS          # slot -> strip
     done_prod = [[False] * n for _ in range(PW)]       # producer w finished produce(t)
     done_cons = [[False] * n for _ in range(CW)]       # consumer v finished strip t
@@ -59,18 +67,20 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4):
         pmax[s] = [t, (e[1] if e else set()) | {w}]
 
     def producer(w):
-        publish(w, 0)
-        cnt["published"] += 1
+        if PMAX:
+            publish(w, 0)
+            cnt["published"] += 1
         yield None
         for t in range(n):
             # the kernel waits until strip t - 3 is drained (drain_lag = 3)
             if t >= drain_lag:
                 while cnt[f"drained{(t - drain_lag) % SLOTS}"] < CW * ((t - drain_lag) // SLOTS + 1):
                     yield "wait"
-            while cnt["published"] < PW * (t + 1):
-                yield "wait"
-            e = pmax[t % PMAX]
-            need(e is not None and e[0] == t and len(e[1]) == PW, f"P{w} reads pmax {e} for strip {t}")
+            if PMAX:
+                while cnt["published"] < PW * (t + 1):
+                    yield "wait"
+                e = pmax[t % PMAX]
+                need(e is not None and e[0] == t and len(e[1]) == PW, f"P{w} reads pmax {e} for strip {t}")
             s = t % SLOTS
             if w == 0:
                 info[s] = t
@@ -87,17 +97,23 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4):
             done_prod[w][t] = True
             yield None
             cnt["produced"] += 1
+            cnt[f"produced{w}"] += 1
             if t + 1 >= n:
                 return
-            yield None
-            publish(w, t + 1)
-            yield None
-            cnt["published"] += 1
+            if PMAX:
+                yield None
+                publish(w, t + 1)
+                yield None
+                cnt["published"] += 1
 
     def consumer(v):
         for t in range(n):
-            while cnt["produced"] < PW * (t + 1):
-                yield "wait"
+            if per_wave:
+                while min(cnt[f"produced{w}"] for w in range(PW)) < t + 1:
+                    yield "wait"
+            else:
+                while cnt["produced"] < PW * (t + 1):
+                    yield "wait"
             s = t % SLOTS
             need(info[s] == t, f"C{v} expects strip {t}, slot info says {info[s]}")
             e = ring[s]
@@ -157,13 +173,26 @@ def test_model_catches_a_weaker_wait():
         assert caught, f"drain lag {lag} not caught"
 
 
-def test_model_catches_a_single_partial_maximum_slot():
-    """Two partial-maximum slots are the minimum: with one, a wave publishing strip
-    t + 1 overwrites strip t's maxima while another wave still quantizes strip t."""
+def test_model_catches_a_summed_produced_counter_without_lockstep():
+    """Without the partial-maximum exchange, producer waves drift apart, so a single
+    summed `produced` counter no longer shows that every wave wrote strip t."""
     caught = False
     for seed in range(300):
         try:
-            _run(9, seed, PW=8, CW=8, PMAX=1)
+            _run(9, seed, PW=8, CW=8, PMAX=None, per_wave=False)
+        except Violation:
+            caught = True
+            break
+    assert caught
+
+
+def test_model_catches_a_single_partial_maximum_slot():
+    """The partial-maximum check is not vacuous: with one slot, a wave publishing strip
+    t + 1 overwrites strip t's maxima while another wave still converts strip t."""
+    caught = False
+    for seed in range(300):
+        try:
+            _run(9, seed, PW=4, CW=12, PMAX=1)
         except Violation:
             caught = True
             break
