@@ -18,8 +18,8 @@ with HIP events on the launch stream inside the timed region, against the
 forward chain, every launch's median over 20 launches each preceded by a 512 MB
 scrub read (so inputs come from HBM, not the caches), next to a device copy
 moving the same bytes.  ``backward`` times the FP8 gradient quantizer
-(mxfp4_bf16_to_fp8_rows) on the same segments, outside ``value``; the scrubbed
-medians include it.  ``cpu_baseline`` times the CPU oracle on a bounded
+(mxfp4_bf16_to_fp8_rows and mxfp4_bf16_to_fp8_cols_ragged) on the same segments,
+outside ``value``; the scrubbed medians include it.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same workload on this host (all allowed threads, and one thread).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload config5] [--no-scrubbed]
@@ -47,8 +47,9 @@ CSRC = os.path.join(ROOT, "block_scaled_precision_bf16tofp4row_amd", "csrc")
 KERNEL_SOURCES = {
     "quantize": ["quantize.hip", "common.h"],
     "rows": ["rows.hip", "common.h"],
-    "cols": ["cols.hip", "common.h"],
+    "cols": ["cols.hip", "strips.h", "common.h"],
     "fp8q_rows": ["fp8q.hip", "common.h"],
+    "fp8q_cols": ["fp8q_cols.hip", "strips.h", "common.h"],
 }
 
 
@@ -67,6 +68,8 @@ def alg_bytes(kernel: str, M_tot: int, K: int, col_scale_bytes: int = 0) -> int:
         return n // 2 + n // 32 + n + col_scale_bytes
     if kernel == "fp8q_rows":           # 2 B in, 1 + 1/128 B out
         return 2 * n + n + n // 128
+    if kernel == "fp8q_cols":           # 2 B in, 1 B out + one scale byte per (block, k)
+        return 2 * n + n + col_scale_bytes
     raise ValueError(kernel)
 
 
@@ -169,11 +172,16 @@ def build_launches(mx, workload, dev, torch, backward: bool = False):
             x = torch.from_numpy(seg.x_bits.view(np.int16)).to(dev)
             offs = torch.from_numpy(seg.offs).to(dev)
             y, ys = mx.alloc_fp8q_rows_outputs(seg.M_cap, seg.K, dev)
-            d = {"seg": seg, "x": x, "offs": offs, "y": y, "ys": ys}
+            yT, ysT = mx.alloc_cols_outputs(seg.M_cap, seg.K, seg.G, dev)
+            nb = (np.diff(seg.offs.astype(np.int64)) + 127) // 128
+            d = {"seg": seg, "x": x, "offs": offs, "y": y, "ys": ys, "yT": yT, "ysT": ysT}
             segs.append(d)
             launches.append(("fp8q_rows", seg.name,
                              lambda d=d: mx.mxfp4_bf16_to_fp8_rows(d["x"], d["y"], d["ys"], d["offs"]),
                              alg_bytes("fp8q_rows", seg.M_tot, seg.K)))
+            launches.append(("fp8q_cols", seg.name,
+                             lambda d=d: mx.mxfp4_bf16_to_fp8_cols_ragged(d["x"], d["yT"], d["ysT"], d["offs"]),
+                             alg_bytes("fp8q_cols", seg.M_tot, seg.K, int(nb.sum()) * seg.K)))
         return segs, launches
     for seg in workload.segments:
         x = torch.from_numpy(seg.x_bits.view(np.int16)).to(dev)
@@ -365,7 +373,8 @@ def main():
         })
     b_step_bytes = sum(l[3] for l in blaunches)
     backward = {
-        "what": "backward FP8 gradient quantizer (BF16 -> E4M3, 1x128 blocks) per segment",
+        "what": "backward FP8 gradient quantizer (BF16 -> E4M3, 1x128 blocks), row and transposed "
+                "column layout, per segment",
         "alg_bytes_per_step": b_step_bytes,
         "ms_per_step": round(b_ms_per_step, 4),
         "GBps": round(b_step_bytes / (b_ms_per_step / 1000.0) / 1e9, 1),
