@@ -92,8 +92,10 @@ __device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t 
 // A lane's four rows of a strip: eight consecutive lanes read one row's whole 128-byte
 // line of codes, so a load instruction touches 8 lines.  Scales are loaded as whole
 // dwords (a byte load would be zero-extended where the loop carries it, which makes the
-// compiler wait for the prefetched loads early); the byte is extracted at use.  Row
-// offsets within a strip fit in 32 bits (128 rows x K/2 bytes with K <= 2^24).
+// compiler wait for the prefetched loads early); the byte is extracted at use.  Loads go
+// through strip_rsrc (strips.h): rows past a partial strip read as zero codes with scale
+// byte 0, which leaves the block scale unchanged; their bytes are never written out.
+// Lane offsets within a strip fit in 32 bits (128 rows x K/2 bytes with K <= 2^24).
 struct Codes {
     u32x4 c[4];                // 32 codes of the lane's group for each of its four rows
 };
@@ -101,20 +103,15 @@ struct Scales {
     uint32_t s;                // lane L: dword L & 1 of the 8 scale bytes of wave row L >> 1
 };
 
-// Loads are unconditional (rows past the strip are clamped to its last row and masked
-// at use), so every strip issues the same straight-line sequence of loads and the
-// compiler can wait for exactly the loads it needs.
 __device__ __forceinline__ Codes load_codes(const uint8_t* __restrict__ codes, int64_t K,
-                                            const StripInfo& st, int row_q, uint32_t cbyte, uint32_t kt)
+                                            const StripInfo& st, uint32_t kt, const uint32_t (&off)[4])
 {
     Codes in;
-    const uint8_t* const cb = codes + (st.row0 + st.r_lo) * (K / 2) + 128 * (int64_t)kt;
-    const uint32_t kc = (uint32_t)(K / 2);
+    const __amdgpu_buffer_rsrc_t rsrc = strip_rsrc(codes + (st.row0 + st.r_lo) * (K / 2) + 128 * (int64_t)kt,
+                                                   (uint64_t)st.nrows * (uint64_t)(K / 2));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t r = (uint32_t)min(row_q + i, st.nrows - 1);
-        in.c[i] = *reinterpret_cast<const u32x4*>(cb + (r * kc + cbyte));
-    }
+    for (int i = 0; i < 4; ++i)
+        in.c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off[i], 0, 0));
     return in;
 }
 
@@ -122,15 +119,12 @@ __device__ __forceinline__ Codes load_codes(const uint8_t* __restrict__ codes, i
 // a single load instruction per strip; lanes fetch their own rows' bytes with
 // ds_bpermute at use.  The narrow last tile has groups 0..3 only (one dword per row).
 __device__ __forceinline__ Scales load_scales(const uint8_t* __restrict__ scales, int64_t K,
-                                              const StripInfo& st, int wave_row0, bool narrow,
-                                              uint32_t kt)
+                                              const StripInfo& st, uint32_t kt, uint32_t off)
 {
     Scales in;
-    const uint8_t* const sb = scales + (st.row0 + st.r_lo) * (K / 32) + 8 * (int64_t)kt;
-    const int lane = threadIdx.x & 63;
-    const uint32_t r = (uint32_t)min(wave_row0 + (lane >> 1), st.nrows - 1);
-    const uint32_t dw = narrow ? 0u : (uint32_t)(lane & 1);
-    in.s = *reinterpret_cast<const uint32_t*>(sb + (r * (uint32_t)(K / 32) + 4 * dw));
+    const __amdgpu_buffer_rsrc_t rsrc = strip_rsrc(scales + (st.row0 + st.r_lo) * (K / 32) + 8 * (int64_t)kt,
+                                                   (uint64_t)st.nrows * (uint64_t)(K / 32));
+    in.s = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)off, 0, 0);
     return in;
 }
 
@@ -202,12 +196,19 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
         const uint32_t sshift = 8 * (cl & 3);
         // column 32c + j of the tile sits at LDS byte lds_col(32c) + 544 j
         const uint32_t wbase = lds_col(32 * c) + row_q;
+        // byte offsets within a strip of the lane's four code chunks and of its scale dword
+        uint32_t coff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            coff[i] = (uint32_t)(row_q + i) * (uint32_t)(K / 2) + cbyte;
+        const uint32_t soff = (uint32_t)(32 * wave + (lane >> 1)) * (uint32_t)(K / 32) +
+                              4 * (ncols <= 128 ? 0u : (uint32_t)(lane & 1));
 
-        // the lane's four MX scale bytes (zero for rows past the strip)
+        // the lane's four MX scale bytes (zero for rows past the strip: those read as zero)
         struct RowScales {
             uint32_t b[4];
         };
-        auto row_scales = [&](const StripInfo& st, const Scales& in) {
+        auto row_scales = [&](const Scales& in) {
             RowScales sc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -215,8 +216,6 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                 const int src = 2 * (4 * rq + i) + (int)(cl >> 2);
                 const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src, (int)in.s);
                 sc.b[i] = __builtin_amdgcn_ubfe(w, sshift, 8);
-                if (st.nrows < kStripRows)
-                    sc.b[i] = row_q + i < st.nrows ? sc.b[i] : 0u;
             }
             return sc;
         };
@@ -305,10 +304,10 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
             I[u] = (uint32_t)u < n ? next_strip(offs, G, I[u - 1]) : I[u - 1];
 #pragma unroll
         for (int u = 0; u < kPrefetch; ++u) {
-            Sc[u] = load_scales(scales, K, I[u], 32 * wave, ncols <= 128, kt);
-            C[u] = load_codes(codes, K, I[u], row_q, cbyte, kt);
+            Sc[u] = load_scales(scales, K, I[u], kt, soff);
+            C[u] = load_codes(codes, K, I[u], kt, coff);
         }
-        RowScales sc = row_scales(I[0], Sc[0]);   // strip t
+        RowScales sc = row_scales(Sc[0]);   // strip t
         publish_max(sc, 0);
         signal(&published);
         for (uint32_t t = 0;; t += kSets) {
@@ -318,8 +317,8 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                 const int ld = (u + kPrefetch) % kSets;          // set receiving strip tt + kPrefetch
                 const int pv = (u + kPrefetch - 1) % kSets;      // set of strip tt + kPrefetch - 1
                 I[ld] = tt + kPrefetch < n ? next_strip(offs, G, I[pv]) : I[pv];
-                Sc[ld] = load_scales(scales, K, I[ld], 32 * wave, ncols <= 128, kt);
-                C[ld] = load_codes(codes, K, I[ld], row_q, cbyte, kt);
+                Sc[ld] = load_scales(scales, K, I[ld], kt, soff);
+                C[ld] = load_codes(codes, K, I[ld], kt, coff);
                 const int nx = (u + 1) % kSets;                  // set of strip tt + 1
                 if (tt >= 3 && !wait_at_least(&drained[(tt - 3) % kSlots], kConsumerWaves * ((tt - 3) / kSlots + 1)))
                     return;
@@ -330,7 +329,7 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                 signal(&produced);
                 if (tt + 1 >= n)
                     return;
-                sc = row_scales(I[nx], Sc[nx]);
+                sc = row_scales(Sc[nx]);
                 publish_max(sc, (tt + 1) % kSlots);
                 signal(&published);
             }

@@ -56,25 +56,16 @@ struct QRows {
     u32x4 v[8];
 };
 
-// Loads are buffer loads: the strip's base address and byte range (its rows that
-// exist) go into the scalar buffer resource, and the lane's byte offsets (row * 2K +
-// column byte) are the same for every strip, computed once (`off`).  Rows past a
-// partial strip (an expert's last) lie past the range and read as zero, which leaves
-// the column amax unchanged; their converted bytes are never written out.  So every
-// strip issues the same straight-line loads with no vector arithmetic in front of
-// them (temporaries there would make the compiler wait for the loads still in flight
-// before it reuses their registers).  Offsets fit in 32 bits (128 rows x 2K bytes with
+// Loads go through strip_rsrc (strips.h): rows past a partial strip read as zero, which
+// leaves the column amax unchanged; their converted bytes are never written out.  The
+// lane's byte offsets (row * 2K + column byte) fit in 32 bits (128 rows x 2K bytes with
 // K <= 2^24; the range is capped at 2^32 - 1, far above the last valid offset).
-constexpr int kBufferWord3 = 0x00020000;          // gfx9 buffer resource word 3 (32-bit data)
-
 __device__ __forceinline__ QRows load_rows(const uint8_t* __restrict__ x, int64_t K, const StripInfo& st,
                                            uint32_t kt, const uint32_t (&off)[8])
 {
     QRows in;
-    const uint8_t* const xb = x + (st.row0 + st.r_lo) * (2 * K) + 512 * (int64_t)kt;
-    const uint64_t range = (uint64_t)st.nrows * (uint64_t)(2 * K);
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)xb, (short)0, (int)(range > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)range), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsrc = strip_rsrc(x + (st.row0 + st.r_lo) * (2 * K) + 512 * (int64_t)kt,
+                                                   (uint64_t)st.nrows * (uint64_t)(2 * K));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         in.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off[i], 0, 0));

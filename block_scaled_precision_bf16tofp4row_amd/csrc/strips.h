@@ -62,6 +62,24 @@ __device__ __forceinline__ uint32_t lds_col(uint32_t kk)
     return kColBytes * kk + 32 * (kk >> 5);
 }
 
+// ---- strip loads ---------------------------------------------------------------------
+
+// Producers read a strip through a buffer resource whose base is the strip's first row
+// and whose range is its rows that exist: a load past the range (a row past a partial
+// strip, the last of an expert) returns zero instead of touching memory.  Lane offsets
+// within a strip are then the same for every strip (computed once), so a strip's loads
+// are issued with no vector arithmetic in front of them; temporaries there make the
+// compiler wait for loads still in flight before it reuses their registers, which
+// empties the prefetch.
+constexpr int kBufferWord3 = 0x00020000;          // gfx9 buffer resource word 3 (32-bit data)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t strip_rsrc(const void* base, uint64_t range)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             (int)(range > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)range),
+                                             kBufferWord3);
+}
+
 // ---- progress counters in LDS --------------------------------------------------------
 
 // Polls of a counter before a wave gives up (about a second): only a broken protocol
