@@ -70,6 +70,11 @@ def _load():
     lib.oracle_fp8q_block.argtypes = [P, P, P]
     lib.oracle_fp8q_rows.argtypes = [P, I64, I64, I64, P, P]
     lib.oracle_fp8q_cols.argtypes = [P, P, ctypes.c_int32, I64, I64, I64, P, P]
+    lib.oracle_fp8_gemm_at.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, P, P, I64, P, P, P]
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_bf16_round.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_round.restype = ctypes.c_uint16
     lib.oracle_scale_for_amax_e4m3.argtypes = [ctypes.c_double]
     lib.oracle_scale_for_amax_e4m3.restype = ctypes.c_int
     lib.oracle_fp8_of_code.restype = ctypes.c_uint8
@@ -295,3 +300,52 @@ def fp8q_cols(x_bits: np.ndarray, offs: np.ndarray, threads: int = 1,
 
     _run_ranges(run, work, threads)
     return yT, yT_scales
+
+
+# ---- FP8 grouped GEMM (forward, row layout) -----------------------------------------
+
+def e4m3_value(b: int) -> float:
+    return _load().oracle_e4m3_value(int(b))
+
+
+def bf16_round(v: float) -> int:
+    return int(_load().oracle_bf16_round(float(v)))
+
+
+def fp8_gemm_at(a, sa, w, sw, offs, ms, ns, threads: int = 1):
+    """The expert-grouped FP8 GEMM at the points (ms[i], ns[i]).
+
+    a [M, K] E4M3 bytes, sa [M, K/128] UE8M0, w [G, N, K] E4M3, sw [G, N, K/128] UE8M0,
+    offs [G+1] int32.  Returns (exact fp64 values, BF16 bits, sum of |terms|)."""
+    lib = _load()
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    sw = np.ascontiguousarray(sw, dtype=np.uint8)
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    G, N, K = w.shape
+    assert K % 128 == 0 and a.shape[1] == K and ms.shape == ns.shape
+    cnt = ms.size
+    exact = np.zeros(cnt, np.float64)
+    ybf = np.zeros(cnt, np.uint16)
+    absum = np.zeros(cnt, np.float64)
+
+    def run(r):
+        lo, hi = r
+        lib.oracle_fp8_gemm_at(_ptr(a), _ptr(sa), _ptr(w), _ptr(sw), _ptr(offs), G, N, K,
+                               _ptr(ms[lo:]), _ptr(ns[lo:]), hi - lo,
+                               _ptr(exact[lo:]), _ptr(ybf[lo:]), _ptr(absum[lo:]))
+
+    _run_ranges(run, _ranges(cnt, threads * 4), threads)
+    return exact, ybf, absum
+
+
+def fp8_gemm(a, sa, w, sw, offs, threads: int = 1):
+    """Every output of the GEMM: (exact [M_tot, N] fp64, BF16 bits [M_tot, N], absum)."""
+    G, N, K = np.asarray(w).shape
+    M_tot = int(np.asarray(offs)[-1])
+    mm, nn = np.meshgrid(np.arange(M_tot, dtype=np.int64), np.arange(N, dtype=np.int64), indexing="ij")
+    e, y, t = fp8_gemm_at(a, sa, w, sw, offs, mm.reshape(-1), nn.reshape(-1), threads)
+    return e.reshape(M_tot, N), y.reshape(M_tot, N), t.reshape(M_tot, N)

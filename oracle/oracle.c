@@ -338,6 +338,94 @@ void oracle_fp8q_cols(const uint16_t *x, const int32_t *offs, int32_t g, int64_t
     }
 }
 
+/* ---- FP8 grouped GEMM, forward (row layout) ---------------------------- */
+/* Technical summary, section 2: the GEMMs stay in FP8 on the standard block-scaled
+ * pipeline (item 1: E4M3 with 128-element blocks; the precision-decoupling framing:
+ * compute in FP8, store and communicate in FP4); the forward expert GEMM consumes the
+ * row-layout FP8 activations.  Reading (the page fixes no GEMM formula): each expert g
+ * owns rows [offs[g], offs[g+1]) of A and a weight W_g [N, K] in the same format as the
+ * activations (E4M3 with one UE8M0 scale per 1x128 block along K, per output feature;
+ * a 128x128-block weight scale is the case where 128 consecutive features repeat it),
+ * and
+ *     y[m, n] = bf16( sum_k A[m,k] 2^(sA[m,k/128]-127) * W_g[n,k] 2^(sW_g[n,k/128]-127) )
+ * with the sum taken exactly (here: fp64, whose rounding over K <= 2^16 terms is far
+ * below the BF16 step) and one round-to-nearest-even to BF16 at the end. */
+
+/* E4M3FN byte -> exact double: bias 7, exponent field 0 is subnormal (m * 2^-9).
+ * The NaN bytes 0x7F / 0xFF are not valid inputs. */
+static double e4m3_value(uint8_t b)
+{
+    int e = (b >> 3) & 0xF, m = b & 7;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return (b & 0x80) ? -v : v;
+}
+
+/* Round half to even at integer granularity (q >= 0). */
+static double round_half_even(double q)
+{
+    double f = floor(q), r = q - f;
+    if (r > 0.5 || (r == 0.5 && fmod(f, 2.0) != 0.0))
+        f += 1.0;
+    return f;
+}
+
+/* double -> BF16 bits, one rounding to nearest even from the exact value (no binary32
+ * intermediate): 8 significant bits for normals (exponent field 1..254), steps of
+ * 2^-133 below 2^-126 (subnormals), Inf above the largest finite value. */
+static uint16_t bf16_round(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    int e;
+    double f = frexp(a, &e);            /* a = f 2^e, f in [0.5, 1) */
+    int E = e - 1 + 127;                /* biased exponent of a */
+    if (E <= 0) {                       /* subnormal range: units of 2^-133 */
+        double q = round_half_even(ldexp(a, 133));
+        return (uint16_t)(sign | (uint16_t)q);          /* q = 128 is the smallest normal */
+    }
+    double q = round_half_even(f * 256.0);              /* 128 .. 256 */
+    if (q == 256.0) {
+        q = 128.0;
+        ++E;
+    }
+    if (E >= 255)
+        return (uint16_t)(sign | 0x7F80);
+    return (uint16_t)(sign | (uint16_t)(E << 7) | (uint16_t)(q - 128.0));
+}
+
+/* y = the GEMM above at `count` points (ms[i], ns[i]); exact[i] gets the fp64 sum,
+ * y_bf16[i] its BF16 rounding, absum[i] = sum_k |term| (for error bounds).  A [*, K],
+ * sA [*, K/128], W [G, N, K], sW [G, N, K/128] row-major.  Rows must lie in
+ * [0, offs[G]). */
+void oracle_fp8_gemm_at(const uint8_t *a, const uint8_t *sa, const uint8_t *w, const uint8_t *sw,
+                        const int32_t *offs, int32_t G, int64_t N, int64_t K,
+                        const int64_t *ms, const int64_t *ns, int64_t count,
+                        double *exact, uint16_t *y_bf16, double *absum)
+{
+    int64_t kb = K / 128;
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        int32_t g = 0;
+        while (g + 1 < G && (int64_t)offs[g + 1] <= m)
+            ++g;
+        const uint8_t *ar = a + m * K, *sar = sa + m * kb;
+        const uint8_t *wr = w + ((int64_t)g * N + n) * K, *swr = sw + ((int64_t)g * N + n) * kb;
+        double s = 0.0, t = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double x = ldexp(e4m3_value(ar[k]), (int)sar[k / 128] - 127);
+            double y = ldexp(e4m3_value(wr[k]), (int)swr[k / 128] - 127);
+            s += x * y;
+            t += fabs(x * y);
+        }
+        exact[i] = s;
+        y_bf16[i] = bf16_round(s);
+        if (absum)
+            absum[i] = t;
+    }
+}
+
 /* ---- small helpers exported for the pins ------------------------------- */
 
 int oracle_e2m1_encode(double y) { return e2m1_encode(y); }
@@ -347,3 +435,5 @@ double oracle_bf16_value(uint16_t b) { return bf16_value(b); }
 int oracle_scale_for_amax(double amax) { return ue8m0_scale_for_amax(amax); }
 uint8_t oracle_fp8_of_code(int c, int s, int S) { return fp8_of_code(c, s, S); }
 int oracle_scale_for_amax_e4m3(double amax) { return ue8m0_scale_for_amax_e4m3(amax); }
+double oracle_e4m3_value(uint8_t b) { return e4m3_value(b); }
+uint16_t oracle_bf16_round(double v) { return bf16_round(v); }

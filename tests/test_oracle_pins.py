@@ -553,3 +553,171 @@ def test_fp8q_cols_threaded_and_grouped_drivers_agree():
     for got in (b, (yT, ys)):
         np.testing.assert_array_equal(a[0], got[0])
         np.testing.assert_array_equal(a[1], got[1])
+
+
+# ---- FP8 grouped GEMM (forward, row layout) -------------------------------------------
+
+def _e4m3_codes(rng, shape, lo_exp=0, hi_exp=15):
+    """Random E4M3FN bytes (no NaN), exponent fields in [lo_exp, hi_exp]."""
+    e = rng.integers(lo_exp, hi_exp + 1, size=shape)
+    m = rng.integers(0, 8, size=shape)
+    s = rng.integers(0, 2, size=shape)
+    b = (s << 7) | (e << 3) | m
+    b = np.where((b & 0x7F) == 0x7F, b - 1, b)
+    return b.astype(np.uint8)
+
+
+def _decode_e4m3(b):
+    return torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_value_every_code_matches_torch():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    want = _decode_e4m3(codes)
+    got = np.array([oracle.e4m3_value(int(c)) for c in codes])
+    np.testing.assert_array_equal(got, want)
+
+
+def _bf16_grid_round(x: Fraction) -> int:
+    """Nearest BF16 (ties to the even code) by search over the representable values
+    around x; finite range only."""
+    sign = 0x8000 if x < 0 else 0
+    ax = abs(x)
+    if ax == 0:
+        return sign
+    best = None
+    # candidates: the two BF16 magnitudes bracketing ax (found by binary search on bits)
+    lo, hi = 0, 0x7F7F
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if exact_ref.bf16_to_fraction(mid) <= ax:
+            lo = mid
+        else:
+            hi = mid - 1
+    cands = [lo, min(lo + 1, 0x7F7F)]
+    for c in cands:
+        d = abs(exact_ref.bf16_to_fraction(c) - ax)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return sign | best[1]
+
+
+def test_bf16_round_exact_values_and_ties():
+    # every finite BF16 value is returned unchanged
+    for b in list(range(0, 0x7F80, 37)) + [0x0001, 0x007F, 0x0080, 0x7F7F]:
+        v = struct.unpack("<f", struct.pack("<I", b << 16))[0]
+        assert oracle.bf16_round(v) == b
+        assert oracle.bf16_round(-v) == b | 0x8000
+    # midpoints between neighbours go to the even code (normals and subnormals)
+    for b in list(range(1, 0x7F7F, 53)) + [0x007F, 0x0080, 0x0001]:
+        lo = exact_ref.bf16_to_fraction(b)
+        hi = exact_ref.bf16_to_fraction(b + 1)
+        mid = float((lo + hi) / 2)          # exact in double (BF16 has 8 bits)
+        assert oracle.bf16_round(mid) == (b if b % 2 == 0 else b + 1)
+    # above the largest finite value by half a step or more: Inf
+    top = exact_ref.bf16_to_fraction(0x7F7F)
+    step = top - exact_ref.bf16_to_fraction(0x7F7E)
+    assert oracle.bf16_round(float(top + step / 2)) == 0x7F80
+    assert oracle.bf16_round(float(top + step / 4)) == 0x7F7F
+
+
+def test_bf16_round_random_doubles_match_grid_search():
+    rng = np.random.default_rng(41)
+    vals = np.concatenate([rng.standard_normal(400) * 10.0 ** rng.integers(-30, 30, 400),
+                           rng.standard_normal(100) * 2.0 ** -128,      # BF16 subnormal range
+                           rng.standard_normal(50) * 2.0 ** -134])
+    for v in vals:
+        assert oracle.bf16_round(float(v)) == _bf16_grid_round(Fraction(float(v))), v
+
+
+def _gemm_case(rng, counts, N, K, lo_exp=0, hi_exp=15, s_lo=118, s_hi=136):
+    G = len(counts)
+    M = sum(counts)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = _e4m3_codes(rng, (M, K), lo_exp, hi_exp)
+    sa = rng.integers(s_lo, s_hi, size=(M, K // 128)).astype(np.uint8)
+    w = _e4m3_codes(rng, (G, N, K), lo_exp, hi_exp)
+    sw = rng.integers(s_lo, s_hi, size=(G, N, K // 128)).astype(np.uint8)
+    return a, sa, w, sw, offs
+
+
+def _gemm_numpy(a, sa, w, sw, offs):
+    """Decoded operands (torch's E4M3 decode, scales as powers of two) and one float64
+    matmul per expert (numpy)."""
+    A = _decode_e4m3(a) * np.repeat(2.0 ** (sa.astype(np.float64) - 127), 128, axis=1)
+    out = []
+    for g in range(len(offs) - 1):
+        W = _decode_e4m3(w[g]) * np.repeat(2.0 ** (sw[g].astype(np.float64) - 127), 128, axis=1)
+        out.append(A[offs[g]:offs[g + 1]] @ W.T)
+    return np.concatenate(out) if out else np.zeros((0, w.shape[1]))
+
+
+def test_fp8_gemm_matches_numpy_matmul_per_expert():
+    rng = np.random.default_rng(42)
+    a, sa, w, sw, offs = _gemm_case(rng, [5, 0, 9, 1], N=24, K=384)
+    exact, ybf, absum = oracle.fp8_gemm(a, sa, w, sw, offs, threads=2)
+    ref = _gemm_numpy(a, sa, w, sw, offs)
+    np.testing.assert_allclose(exact, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+    # BF16 bits: an independent nearest-even search on the BF16 grid, where the value is
+    # not within a hair of a midpoint (the two fp64 sums may differ in the last bits)
+    ok = 0
+    for (m, n), v in np.ndenumerate(ref):
+        x = Fraction(float(v))
+        yb = _bf16_grid_round(x)
+        lo = exact_ref.bf16_to_fraction(yb & 0x7FFF)
+        if abs(abs(x) - lo) < Fraction(1, 10 ** 9) * abs(x) + Fraction(1, 10 ** 300):
+            continue
+        assert ybf[m, n] == yb
+        ok += 1
+    assert ok > 0.9 * ref.size
+    # the sum of |terms| is |A| |W|^T per expert
+    abs_ref = _gemm_numpy(a & 0x7F, sa, w & 0x7F, sw, offs)
+    np.testing.assert_allclose(absum, abs_ref, rtol=1e-12, atol=0)
+    assert np.all(absum >= np.abs(exact))
+
+
+def test_fp8_gemm_brute_force_rational_tiny():
+    rng = np.random.default_rng(43)
+    a, sa, w, sw, offs = _gemm_case(rng, [2, 3], N=3, K=128, lo_exp=0, hi_exp=15, s_lo=120, s_hi=134)
+    exact, ybf, _ = oracle.fp8_gemm(a, sa, w, sw, offs)
+    vals = {c: Fraction(0) if (c & 0x7F) == 0 else None for c in range(256)}
+    for c in range(256):
+        if (c & 0x7F) == 0x7F:
+            continue
+        e, m = (c >> 3) & 15, c & 7
+        v = Fraction(m, 2 ** 9) if e == 0 else Fraction(8 + m) * Fraction(2) ** (e - 10)
+        vals[c] = -v if c & 0x80 else v
+    for mrow in range(int(offs[-1])):
+        g = 0 if mrow < offs[1] else 1
+        for n in range(3):
+            tot = Fraction(0)
+            for k in range(128):
+                tot += (vals[int(a[mrow, k])] * Fraction(2) ** (int(sa[mrow, 0]) - 127) *
+                        vals[int(w[g, n, k])] * Fraction(2) ** (int(sw[g, n, 0]) - 127))
+            assert abs(Fraction(exact[mrow, n]) - tot) <= abs(tot) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
+            assert ybf[mrow, n] == _bf16_grid_round(tot)
+
+
+def test_fp8_gemm_routes_rows_to_their_expert_and_scales_exactly():
+    rng = np.random.default_rng(44)
+    counts = [3, 0, 4, 2]
+    N, K = 8, 256
+    a, sa, w, sw, offs = _gemm_case(rng, counts, N, K, lo_exp=5, hi_exp=9)
+    # expert g's weight is the constant 1.0 (0x38) times 2^g: y[m, n] = 2^g * sum_k A[m,k]
+    for g in range(len(counts)):
+        w[g] = 0x38
+        sw[g] = 127 + g
+    exact, _, _ = oracle.fp8_gemm(a, sa, w, sw, offs)
+    A = _decode_e4m3(a) * np.repeat(2.0 ** (sa.astype(np.float64) - 127), 128, axis=1)
+    for g in range(len(counts)):
+        rows = slice(offs[g], offs[g + 1])
+        np.testing.assert_array_equal(exact[rows], np.repeat(A[rows].sum(axis=1, keepdims=True) * 2.0 ** g, N, axis=1))
+    # raising one activation block scale by one doubles exactly that block's share
+    a2, sa2 = a.copy(), sa.copy()
+    sa2[:, 1] += 1
+    e2, _, _ = oracle.fp8_gemm(a2, sa2, w, sw, offs)
+    blk = np.zeros_like(exact)
+    for g in range(len(counts)):
+        rows = slice(offs[g], offs[g + 1])
+        blk[rows] = np.repeat(A[rows, 128:256].sum(axis=1, keepdims=True) * 2.0 ** g, N, axis=1)
+    np.testing.assert_allclose(e2 - exact, blk, rtol=1e-12, atol=0)
