@@ -14,6 +14,7 @@ The binding has the same names as the C ABI:
 * ``mxfp4_to_fp8_cols_ragged(codes, scales, yT, yT_scales, offs, ...)``
 * ``mxfp4_bf16_to_fp8_rows(x, y, y_scales, offs, ...)`` and
   ``mxfp4_bf16_to_fp8_cols_ragged(x, yT, yT_scales, offs, ...)`` (backward FP8 quantizer)
+* ``mxfp4_fp8_grouped_gemm(a, a_scales, w, w_scales, y, offs, ...)`` (FP8 expert GEMM)
 * ``mxfp4_cols_scale_capacity(M_cap, K, G)``, ``mxfp4_validate_offsets(offs, ...)``,
   ``mxfp4_status_string(status)``
 
@@ -45,6 +46,7 @@ EXPORTED = (
     "mxfp4_to_fp8_cols_ragged",
     "mxfp4_bf16_to_fp8_rows",
     "mxfp4_bf16_to_fp8_cols_ragged",
+    "mxfp4_fp8_grouped_gemm",
     "mxfp4_cols_scale_capacity",
     "mxfp4_validate_offsets",
     "mxfp4_status_string",
@@ -81,6 +83,8 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_bf16_to_fp8_rows.restype = st
     lib.mxfp4_bf16_to_fp8_cols_ragged.argtypes = [P, P, P, P, I32, I64, I64, P]
     lib.mxfp4_bf16_to_fp8_cols_ragged.restype = st
+    lib.mxfp4_fp8_grouped_gemm.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
+    lib.mxfp4_fp8_grouped_gemm.restype = st
     lib.mxfp4_cols_scale_capacity.argtypes = [I64, I64, I32]
     lib.mxfp4_cols_scale_capacity.restype = I64
     lib.mxfp4_validate_offsets.argtypes = [P, I32, I64, P]
@@ -223,6 +227,30 @@ def mxfp4_bf16_to_fp8_cols_ragged(x, yT, yT_scales, offs, G=None, M_cap=None, K=
     lib = load_library()
     _check(lib.mxfp4_bf16_to_fp8_cols_ragged(_ptr(x), _ptr(yT), _ptr(yT_scales), _ptr(offs), G, M_cap, K,
                                              _stream(stream)), "mxfp4_bf16_to_fp8_cols_ragged")
+
+
+def mxfp4_fp8_grouped_gemm(a, a_scales, w, w_scales, y, offs, G=None, M_cap=None, N=None, K=None,
+                           stream=None):
+    """E4M3 a [M_cap, K] (+ UE8M0 [M_cap, K/128]) x per-expert E4M3 w [G, N, K]
+    (+ [G, N, K/128]) -> BF16 y [M_cap, N] (see the header)."""
+    if G is None:
+        G = offs.numel() - 1
+    if M_cap is None:
+        M_cap = a.shape[0]
+    if K is None:
+        K = a.shape[1]
+    if N is None:
+        N = w.shape[1]
+    G, M_cap, N, K = int(G), int(M_cap), int(N), int(K)
+    m, k = max(M_cap, 0), max(K, 0)
+    _need("mxfp4_fp8_grouped_gemm", [(a, m * k, "a", _FP8), (a_scales, m * k // 128, "a_scales", _U8),
+                                     (w, max(G, 0) * max(N, 0) * k, "w", _FP8),
+                                     (w_scales, max(G, 0) * max(N, 0) * k // 128, "w_scales", _U8),
+                                     (y, 2 * m * max(N, 0), "y", ("bfloat16", "int16", "uint16")),
+                                     (offs, 4 * (G + 1), "group_offsets", ("int32",))])
+    lib = load_library()
+    _check(lib.mxfp4_fp8_grouped_gemm(_ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scales), _ptr(y), _ptr(offs),
+                                      G, M_cap, N, K, _stream(stream)), "mxfp4_fp8_grouped_gemm")
 
 
 def mxfp4_validate_offsets(offs, G=None, M_cap=None, stream=None) -> bool:

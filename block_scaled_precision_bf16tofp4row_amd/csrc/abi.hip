@@ -14,6 +14,8 @@ hipError_t launch_fp8_rows(const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, c
 hipError_t launch_fp8_cols(const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, const int32_t*,
                            int32_t, int64_t, int64_t, hipStream_t);
 int64_t cols_block_capacity(int64_t M_cap, int32_t G);
+hipError_t launch_fp8_gemm(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*,
+                           const int32_t*, int32_t, int64_t, int64_t, int64_t, hipStream_t);
 hipError_t launch_fp8q_cols(const uint16_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
                             int64_t, hipStream_t);
 hipError_t launch_fp8q_rows(const uint16_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
@@ -28,6 +30,8 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 constexpr int64_t kMaxElems = (int64_t)1 << 50;
 // Largest K of the column conversion.
 constexpr int64_t kMaxColsK = (int64_t)1 << 24;
+// Largest N and K of the GEMM (its per-tile byte offsets are 32-bit).
+constexpr int64_t kMaxGemmDim = (int64_t)1 << 20;
 
 mxfp4_status check_shape(int32_t G, int64_t M_cap, int64_t K, int64_t k_multiple)
 {
@@ -140,6 +144,31 @@ mxfp4_status mxfp4_bf16_to_fp8_cols_ragged(const uint16_t* x_bf16, uint8_t* yT_e
         return MXFP4_OK;
     return from_hip(mxfp4::launch_fp8q_cols(x_bf16, yT_e4m3, yT_scales, group_offsets, G, M_cap,
                                             K, stream));
+}
+
+mxfp4_status mxfp4_fp8_grouped_gemm(const uint8_t* a_e4m3, const uint8_t* a_scales,
+                                    const uint8_t* w_e4m3, const uint8_t* w_scales,
+                                    uint16_t* y_bf16, const int32_t* group_offsets, int32_t G,
+                                    int64_t M_cap, int64_t N, int64_t K, hipStream_t stream)
+{
+    if (!a_e4m3 || !a_scales || !w_e4m3 || !w_scales || !y_bf16 || !group_offsets)
+        return MXFP4_ERR_NULL;
+    mxfp4_status st = check_shape(G, M_cap, K, 128);
+    if (st != MXFP4_OK)
+        return st;
+    if (K > kMaxGemmDim || N <= 0 || N % 256 != 0 || N > kMaxGemmDim)
+        return MXFP4_ERR_SHAPE;
+    if (M_cap > 0 && N > kMaxElems / M_cap)          // output elements
+        return MXFP4_ERR_SHAPE;
+    if ((int64_t)G > kMaxElems / (N * K))             // weight elements
+        return MXFP4_ERR_SHAPE;
+    if (!aligned(a_e4m3, 16) || !aligned(a_scales, 16) || !aligned(w_e4m3, 16) ||
+        !aligned(w_scales, 16) || !aligned(y_bf16, 16) || !aligned(group_offsets, 4))
+        return MXFP4_ERR_ALIGN;
+    if (M_cap == 0)
+        return MXFP4_OK;
+    return from_hip(mxfp4::launch_fp8_gemm(a_e4m3, a_scales, w_e4m3, w_scales, y_bf16, group_offsets,
+                                           G, M_cap, N, K, stream));
 }
 
 int64_t mxfp4_cols_scale_capacity(int64_t M_cap, int64_t K, int32_t G)

@@ -1,0 +1,260 @@
+// gemm.hip -- expert-grouped FP8 GEMM, forward (row layout): the FP8 compute step that
+// consumes the converted activations.
+//
+// Method: "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs", technical
+// summary section 2: GEMMs run in FP8 on the standard block-scaled pipeline (item 1:
+// E4M3 with 128-element blocks; storage and communication are FP4, compute is FP8); the
+// forward expert GEMM takes the row-layout FP8 activations produced by the direct
+// FP4 -> FP8 conversion.  For the expert g that owns row m (offs[g] <= m < offs[g+1]):
+//     y[m, n] = bf16( sum_k A[m,k] 2^(sA[m,k/128]-127) * W_g[n,k] 2^(sW_g[n,k/128]-127) )
+// A [M, K] and W_g [N, K] are E4M3 with one UE8M0 scale per 1x128 block along K.
+//
+// gfx950 mapping: v_mfma_scale_f32_32x32x64_f8f6f4 multiplies a 32x64 by a 64x32 E4M3
+// block and applies one E8M0 scale per 32 K-elements of each operand row in the
+// hardware, so the 1x128 block scales cost nothing: a lane passes the scale of its
+// row's current 128-block.  Operand layout (measured on MI355X with an in-bounds probe):
+// lane l supplies row l % 32; bytes 0-15 of its 32 are K-block 0 (k < 32) and bytes
+// 16-31 K-block 1; which k within a block a byte is does not matter as long as both
+// operands agree, so lane (r, h = l / 32) takes k in [16h, 16h + 16) and
+// [32 + 16h, 32 + 16h + 16); its scale byte applies to (row r, K-block h).  Result
+// value i of lane l is row (i / 4) * 8 + (l / 32) * 4 + i % 4, column l % 32.  With the
+// weights as the first operand and the tokens as the second, a lane's results are 4
+// consecutive output features of one token (one 8-byte store).
+//
+// Work: a workgroup (4 waves) owns a 256-token x 256-feature tile of one expert and
+// walks K in steps of 128 (one scale block); wave (wm, wn) computes tokens
+// 128 wm .. + 127 x features 128 wn .. + 127 as 4 x 4 MFMA tiles (256 fp32 accumulators
+// per lane).  Tiles of both operands are double-buffered in LDS (2 x 64 KB): every
+// thread loads eight 16-byte chunks of each operand per step (eight lanes per 128-byte
+// row, whole lines), held in registers while the current step computes, then written
+// to the other buffer.  LDS rows are 128 bytes with the 16-byte chunk c of row r stored
+// at chunk c ^ (r & 7), so the fragment reads of 8 consecutive rows hit distinct banks.
+// Operand and scale loads are buffer loads whose range is the tile's rows that exist:
+// rows past the last partial tile of an expert read as zero (they add nothing and are
+// not stored).  The tile -> (expert, token tile) map is found on the device from the
+// offsets; output rows past offs[G] are never written.
+#include "strips.h"
+
+namespace mxfp4 {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_g __attribute__((ext_vector_type(2)));
+
+constexpr int kGemmThreads = 256;                 // 4 waves
+constexpr int kTM = 256;                          // tokens per workgroup tile
+constexpr int kTN = 256;                          // output features per workgroup tile
+constexpr int kTK = 128;                          // K per step (one scale block)
+constexpr int kStage = (kTM + kTN) * kTK;         // bytes of one LDS buffer (64 KB)
+
+namespace {
+
+// Token tile `mtile` (in expert order) -> expert, its first row and the tile's rows.
+// False if the tile does not exist.  Experts are scanned 64 at a time, one per lane.
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offs, int G, uint32_t mtile,
+                                          int& g_out, int64_t& row0, int& rows)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t run = 0;
+    for (int g0 = 0; g0 < G; g0 += 64) {
+        const int h = g0 + lane;
+        const int32_t r0 = h < G ? offs[h] : 0;
+        const int32_t mg = h < G ? offs[h + 1] - r0 : 0;
+        const uint32_t nt = (uint32_t)(mg + kTM - 1) / kTM;
+        uint32_t incl = nt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t o = __shfl_up(incl, d, 64);
+            if (lane >= d)
+                incl += o;
+        }
+        const uint32_t first = run + incl - nt;
+        const uint64_t mask = __ballot(nt > 0 && mtile >= first && mtile < first + nt);
+        if (mask) {
+            const int src = __builtin_ctzll(mask);
+            const uint32_t j = mtile - (uint32_t)__builtin_amdgcn_readlane((int)first, src);
+            const int32_t base = __builtin_amdgcn_readlane(r0, src);
+            const int32_t m = __builtin_amdgcn_readlane(mg, src);
+            g_out = g0 + src;
+            row0 = (int64_t)base + (int64_t)kTM * j;
+            rows = min(kTM, m - kTM * (int)j);
+            return true;
+        }
+        run = uniform(run + (uint32_t)__shfl(incl, 63, 64));
+    }
+    return false;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
+    const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ w,
+    const uint8_t* __restrict__ sw, uint16_t* __restrict__ y, const int32_t* __restrict__ offs, int G,
+    int64_t N, int64_t K)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t ntn = (uint32_t)(N / kTN);
+    const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t mtile = lin / ntn, ntile = lin % ntn;
+    int g;
+    int64_t row0;
+    int rows;
+    if (!find_tile(offs, G, mtile, g, row0, rows))
+        return;                                   // uniform over the workgroup
+    const int64_t n0 = (int64_t)kTN * ntile;
+    const uint32_t kb_n = (uint32_t)(K / kTK);    // scale blocks along K
+
+    // operand tiles: tokens (rows row0 ..) of A and features (rows n0 ..) of W_g
+    const __amdgpu_buffer_rsrc_t ra = strip_rsrc(a + row0 * K, (uint64_t)rows * (uint64_t)K);
+    const __amdgpu_buffer_rsrc_t rw = strip_rsrc(w + ((int64_t)g * N + n0) * K, (uint64_t)kTN * (uint64_t)K);
+    const __amdgpu_buffer_rsrc_t rsa = strip_rsrc(sa + row0 * kb_n, (uint64_t)rows * kb_n);
+    const __amdgpu_buffer_rsrc_t rsw = strip_rsrc(sw + ((int64_t)g * N + n0) * kb_n, (uint64_t)kTN * kb_n);
+
+    // loader role: thread t loads chunk c = t & 7 of rows 32 i + (t >> 3), i = 0..7
+    const uint32_t lrow = (uint32_t)(tid >> 3), lchunk = (uint32_t)(tid & 7);
+    const uint32_t loff = lrow * (uint32_t)K + 16 * lchunk;           // + 32 i K
+    const uint32_t lds_w = lrow * kTK + 16 * (lchunk ^ (lrow & 7));   // + 32 i kTK
+    // compute role: wave (wm, wn), lane (r, h)
+    const int wm = wave & 1, wn = wave >> 1;
+    const uint32_t r = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+    const uint32_t sw8 = r & 7;                                        // the swizzle of rows r + 32 x
+    // scale byte offsets of the lane's rows (features 128 wn + 32 nt + r, tokens 128 wm + 32 mt + r)
+    uint32_t soff_w[4], soff_a[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        soff_w[t] = (uint32_t)(128 * wn + 32 * t + r) * kb_n;
+        soff_a[t] = (uint32_t)(128 * wm + 32 * t + r) * kb_n;
+    }
+
+    u32x4 ra_reg[8], rw_reg[8];
+    auto load_tiles = [&](uint32_t kb) {
+        const int koff = (int)(kb * kTK);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ra_reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      ra, (int)(loff + 32u * i * (uint32_t)K), koff, 0));
+            rw_reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rw, (int)(loff + 32u * i * (uint32_t)K), koff, 0));
+        }
+    };
+    auto store_tiles = [&](uint32_t stage) {
+        uint8_t* const sa_l = lds + stage * kStage;          // tokens: bytes [0, 32 KB)
+        uint8_t* const sw_l = sa_l + kTM * kTK;              // features: bytes [32 KB, 64 KB)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            *reinterpret_cast<u32x4*>(sa_l + lds_w + 32 * i * kTK) = ra_reg[i];
+            *reinterpret_cast<u32x4*>(sw_l + lds_w + 32 * i * kTK) = rw_reg[i];
+        }
+    };
+    uint32_t sc_w[4], sc_a[4];                    // current step's scale bytes
+    uint32_t nx_w[4], nx_a[4];
+    auto load_scales = [&](uint32_t kb, uint32_t (&dw)[4], uint32_t (&da)[4]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            dw[t] = __builtin_amdgcn_raw_buffer_load_b8(rsw, (int)soff_w[t], (int)kb, 0);
+            da[t] = __builtin_amdgcn_raw_buffer_load_b8(rsa, (int)soff_a[t], (int)kb, 0);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+            acc[mt][nt] = f32x16{};
+
+    load_tiles(0);
+    load_scales(0, sc_w, sc_a);
+    store_tiles(0);
+    __syncthreads();
+
+    for (uint32_t kb = 0; kb < kb_n; ++kb) {
+        const uint32_t cur = kb & 1;
+        const bool more = kb + 1 < kb_n;
+        if (more) {
+            load_tiles(kb + 1);
+            load_scales(kb + 1, nx_w, nx_a);
+        }
+        const uint8_t* const ta = lds + cur * kStage + (128 * wm) * kTK;
+        const uint8_t* const tw = lds + cur * kStage + kTM * kTK + (128 * wn) * kTK;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            const uint32_t c0 = 16 * ((4 * kh + h) ^ sw8), c1 = 16 * ((4 * kh + 2 + h) ^ sw8);
+            i32x8 fw[4], fa[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint8_t* const rowp_w = tw + (32 * t + r) * kTK;
+                const uint8_t* const rowp_a = ta + (32 * t + r) * kTK;
+                const u32x4 w0 = *reinterpret_cast<const u32x4*>(rowp_w + c0);
+                const u32x4 w1 = *reinterpret_cast<const u32x4*>(rowp_w + c1);
+                const u32x4 a0 = *reinterpret_cast<const u32x4*>(rowp_a + c0);
+                const u32x4 a1 = *reinterpret_cast<const u32x4*>(rowp_a + c1);
+                fw[t] = i32x8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+                fa[t] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fw[nt], fa[mt], acc[mt][nt], 0, 0, 0, (int)sc_w[nt], 0, (int)sc_a[mt]);
+        }
+        if (more) {
+            store_tiles(cur ^ 1);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                sc_w[t] = nx_w[t];
+                sc_a[t] = nx_a[t];
+            }
+        }
+        __syncthreads();
+    }
+
+    // epilogue: lane (r, h) of MFMA tile (mt, nt) holds token 128 wm + 32 mt + r and
+    // features 128 wn + 32 nt + 8 q + 4 h + (0..3) in values 4q .. 4q + 3
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int mloc = 128 * wm + 32 * mt + (int)r;
+        if (mloc >= rows)
+            continue;
+        uint16_t* const yrow = y + (row0 + mloc) * N + n0 + 128 * wn + 4 * h;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x16& v = acc[mt][nt];
+                const bf16x2_g p0 = {(__bf16)v[4 * q + 0], (__bf16)v[4 * q + 1]};
+                const bf16x2_g p1 = {(__bf16)v[4 * q + 2], (__bf16)v[4 * q + 3]};
+                *reinterpret_cast<u32x2*>(yrow + 32 * nt + 8 * q) =
+                    u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+            }
+    }
+}
+
+int64_t gemm_tile_capacity(int64_t M_cap, int32_t G)
+{
+    return (M_cap + kTM - 1) / kTM + G;
+}
+
+hipError_t launch_fp8_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* w, const uint8_t* sw,
+                           uint16_t* y, const int32_t* offs, int32_t G, int64_t M_cap, int64_t N, int64_t K,
+                           hipStream_t stream)
+{
+    if (M_cap == 0)
+        return hipSuccess;
+    const int64_t grid = gemm_tile_capacity(M_cap, G) * (N / kTN);
+    if (grid > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    int g = G;
+    int64_t n = N, k = K;
+    void* args[] = {(void*)&a, (void*)&sa, (void*)&w, (void*)&sw, (void*)&y, (void*)&offs, (void*)&g,
+                    (void*)&n, (void*)&k};
+    return hipLaunchKernel((const void*)fp8_gemm_kernel, dim3((unsigned)grid), dim3(kGemmThreads), args, 0,
+                           stream);
+}
+
+}  // namespace mxfp4

@@ -130,6 +130,25 @@ mxfp4_status mxfp4_bf16_to_fp8_cols_ragged(const uint16_t* x_bf16, uint8_t* yT_e
                                            int32_t G, int64_t M_cap, int64_t K,
                                            hipStream_t stream);
 
+/* Expert-grouped FP8 GEMM, forward (technical summary section 2: compute stays FP8 on
+ * the block-scaled pipeline, E4M3 with 128-element blocks, item 1; it consumes the row
+ * layout FP8 activations).  For the expert g owning row m (offs[g] <= m < offs[g+1]):
+ *   y[m, n] = bf16( sum_k A[m,k] 2^(sA[m,k/128]-127) * W[g,n,k] 2^(sW[g,n,k/128]-127) )
+ *   a_e4m3    [M_cap, K]     E4M3FN activations (e.g. mxfp4_to_fp8_rows output).
+ *   a_scales  [M_cap, K/128] UE8M0.
+ *   w_e4m3    [G, N, K]      E4M3FN weights, one [N, K] matrix per expert.
+ *   w_scales  [G, N, K/128]  UE8M0 (a 128x128-block weight scale is this format with
+ *             the scale repeated over its 128 rows).
+ *   y_bf16    [M_cap, N]     BF16 bits; rows [offs[G], M_cap) are not written.
+ *   The sum is accumulated in fp32 by the matrix cores (the precision of each 64-term
+ *   dot product inside them is the hardware's) and rounded once to BF16 (nearest even).
+ *   K must be a multiple of 128 and at most 2^20, N a multiple of 256 and at most 2^20
+ *   (else MXFP4_ERR_SHAPE).  No NaN bytes (0x7F / 0xFF) in the operands. */
+mxfp4_status mxfp4_fp8_grouped_gemm(const uint8_t* a_e4m3, const uint8_t* a_scales,
+                                    const uint8_t* w_e4m3, const uint8_t* w_scales,
+                                    uint16_t* y_bf16, const int32_t* group_offsets, int32_t G,
+                                    int64_t M_cap, int64_t N, int64_t K, hipStream_t stream);
+
 /* Bytes the column-layout scale buffer needs for any offsets with offs[G] <= M_cap:
  * K * (ceil(M_cap / 128) + G).  Returns -1 for invalid sizes. */
 int64_t mxfp4_cols_scale_capacity(int64_t M_cap, int64_t K, int32_t G);

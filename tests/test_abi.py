@@ -144,6 +144,27 @@ def test_fp8_column_quantizer_argument_errors(lib):
     assert _fc(lib, M=0, K=1 << 24) == mx.MXFP4_OK
 
 
+def _gm(lib, a=A, sa=A2, w=A3, sw=A4, y=A, o=OFFS, G=1, M=4, N=256, K=128):
+    return lib.mxfp4_fp8_grouped_gemm(a, sa, w, sw, y, o, G, M, N, K, None)
+
+
+def test_grouped_gemm_argument_errors(lib):
+    for kw in ("a", "sa", "w", "sw", "y", "o"):
+        assert _gm(lib, **{kw: None}) == mx.MXFP4_ERR_NULL
+    assert _gm(lib, K=64) == mx.MXFP4_ERR_SHAPE           # K % 128
+    assert _gm(lib, N=128) == mx.MXFP4_ERR_SHAPE          # N % 256
+    assert _gm(lib, N=0) == mx.MXFP4_ERR_SHAPE
+    assert _gm(lib, K=(1 << 20) + 128) == mx.MXFP4_ERR_SHAPE
+    assert _gm(lib, N=(1 << 20) + 256) == mx.MXFP4_ERR_SHAPE
+    assert _gm(lib, G=0) == mx.MXFP4_ERR_SHAPE
+    assert _gm(lib, M=-1) == mx.MXFP4_ERR_SHAPE
+    assert _gm(lib, a=A + 4) == mx.MXFP4_ERR_ALIGN
+    assert _gm(lib, y=A + 2) == mx.MXFP4_ERR_ALIGN
+    assert _gm(lib, sw=A4 + 1) == mx.MXFP4_ERR_ALIGN
+    assert _gm(lib, o=OFFS + 2) == mx.MXFP4_ERR_ALIGN
+    assert _gm(lib, M=0) == mx.MXFP4_OK
+
+
 def test_validate_offsets_argument_errors(lib):
     assert lib.mxfp4_validate_offsets(None, 1, 4, None) == mx.MXFP4_ERR_NULL
     assert lib.mxfp4_validate_offsets(OFFS, 0, 4, None) == mx.MXFP4_ERR_SHAPE
