@@ -21,18 +21,30 @@
 // weights as the first operand and the tokens as the second, a lane's results are 4
 // consecutive output features of one token (one 8-byte store).
 //
-// Work: a workgroup (4 waves) owns a 256-token x 256-feature tile of one expert and
-// walks K in steps of 128 (one scale block); wave (wm, wn) computes tokens
-// 128 wm .. + 127 x features 128 wn .. + 127 as 4 x 4 MFMA tiles (256 fp32 accumulators
-// per lane).  Tiles of both operands are double-buffered in LDS (2 x 64 KB): every
-// thread loads eight 16-byte chunks of each operand per step (eight lanes per 128-byte
-// row, whole lines), held in registers while the current step computes, then written
-// to the other buffer.  LDS rows are 128 bytes with the 16-byte chunk c of row r stored
-// at chunk c ^ (r & 7), so the fragment reads of 8 consecutive rows hit distinct banks.
-// Operand and scale loads are buffer loads whose range is the tile's rows that exist:
-// rows past the last partial tile of an expert read as zero (they add nothing and are
-// not stored).  The tile -> (expert, token tile) map is found on the device from the
-// offsets; output rows past offs[G] are never written.
+// Work (K a multiple of 256 up to 7168, the fast path): a workgroup (4 waves) owns a 256-token x 256-feature
+// tile of one expert and walks K in stages of 64; wave (wm, wn) computes tokens 128 wm .. + 127 x features
+// 128 wn .. + 127 as 4 x 4 MFMA tiles (256 fp32 accumulators per lane).  Operand tiles
+// go straight from memory to LDS (buffer_load ... lds: lane L's 16 bytes land at the
+// instruction's LDS base + 16 L) through a ring of 4 stages (4 x 32 KB), issued 3 stages
+// ahead, so the loads have three stages of matrix work to arrive and use no registers.
+// Each wave loads 64 rows of each operand per stage, 16 rows x 64 bytes per
+// instruction; LDS rows are 64 bytes with the 16-byte chunk c of row r stored at chunk
+// c ^ ((r >> 2) & 3), so the fragment reads of 16 consecutive rows (one LDS cycle of a
+// 16-byte read) hit distinct banks
+// (a lane of the load picks the global chunk that belongs in its LDS slot).  The
+// compiler does not see that the fragment reads depend on these loads, so a stage is
+// awaited explicitly: every step issues the same 8 LDS loads per lane, and before stage
+// t's barrier a lane waits until at most the younger stages' loads remain in flight.
+// The tile's block scales (256 rows x K/128 bytes per operand) are staged in LDS once,
+// laid out so that one 4-byte read gives a lane the scales of its four MFMA tiles; they
+// take no registers across stages and no place in the memory-operation count.  Operand and scale loads are buffer
+// loads whose range is the tile's rows that exist: rows past the last partial tile of
+// an expert read as zero (they add nothing and are not stored).  The tile ->
+// (expert, token tile) map is found on the device from the offsets; output rows past
+// offs[G] are never written.
+// For other K (above 7168 the scales do not fit in LDS beside the ring) a general
+// kernel keeps the same tiles with two 128-K register-staged LDS buffers and per-step
+// scale loads.
 #include "strips.h"
 
 namespace mxfp4 {
@@ -44,8 +56,18 @@ typedef __bf16 bf16x2_g __attribute__((ext_vector_type(2)));
 constexpr int kGemmThreads = 256;                 // 4 waves
 constexpr int kTM = 256;                          // tokens per workgroup tile
 constexpr int kTN = 256;                          // output features per workgroup tile
-constexpr int kTK = 128;                          // K per step (one scale block)
-constexpr int kStage = (kTM + kTN) * kTK;         // bytes of one LDS buffer (64 KB)
+// fast path
+constexpr int kTK = 64;                           // K per stage (half a scale block)
+constexpr int kStages = 4;                        // LDS ring depth; loads run kStages - 1 ahead
+constexpr int kStage = (kTM + kTN) * kTK;         // bytes of one LDS stage (32 KB)
+constexpr int kLoadsPerStep = 8;                  // LDS loads a lane issues per stage
+constexpr int kMaxFastBlocks = 56;                // scale blocks staged in LDS (K <= 7168)
+// general path
+constexpr int kTK1 = 128;
+constexpr int kStage1 = (kTM + kTN) * kTK1;       // 64 KB
+
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n and nothing else.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 namespace {
 
@@ -87,12 +109,12 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offs, int 
 
 }  // namespace
 
-__global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
+__global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_general_kernel(
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ sw, uint16_t* __restrict__ y, const int32_t* __restrict__ offs, int G,
     int64_t N, int64_t K)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -106,7 +128,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
     if (!find_tile(offs, G, mtile, g, row0, rows))
         return;                                   // uniform over the workgroup
     const int64_t n0 = (int64_t)kTN * ntile;
-    const uint32_t kb_n = (uint32_t)(K / kTK);    // scale blocks along K
+    const uint32_t kb_n = (uint32_t)(K / kTK1);    // scale blocks along K
 
     // operand tiles: tokens (rows row0 ..) of A and features (rows n0 ..) of W_g
     const __amdgpu_buffer_rsrc_t ra = strip_rsrc(a + row0 * K, (uint64_t)rows * (uint64_t)K);
@@ -117,11 +139,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
     // loader role: thread t loads chunk c = t & 7 of rows 32 i + (t >> 3), i = 0..7
     const uint32_t lrow = (uint32_t)(tid >> 3), lchunk = (uint32_t)(tid & 7);
     const uint32_t loff = lrow * (uint32_t)K + 16 * lchunk;           // + 32 i K
-    const uint32_t lds_w = lrow * kTK + 16 * (lchunk ^ (lrow & 7));   // + 32 i kTK
+    const uint32_t lds_w = lrow * kTK1 + 16 * (lchunk ^ ((lrow >> 1) & 7));   // + 32 i kTK1
     // compute role: wave (wm, wn), lane (r, h)
     const int wm = wave & 1, wn = wave >> 1;
     const uint32_t r = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
-    const uint32_t sw8 = r & 7;                                        // the swizzle of rows r + 32 x
+    const uint32_t sw8 = (r >> 1) & 7;                                 // the swizzle of rows r + 32 x
     // scale byte offsets of the lane's rows (features 128 wn + 32 nt + r, tokens 128 wm + 32 mt + r)
     uint32_t soff_w[4], soff_a[4];
 #pragma unroll
@@ -132,7 +154,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
 
     u32x4 ra_reg[8], rw_reg[8];
     auto load_tiles = [&](uint32_t kb) {
-        const int koff = (int)(kb * kTK);
+        const int koff = (int)(kb * kTK1);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             ra_reg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -142,12 +164,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
         }
     };
     auto store_tiles = [&](uint32_t stage) {
-        uint8_t* const sa_l = lds + stage * kStage;          // tokens: bytes [0, 32 KB)
-        uint8_t* const sw_l = sa_l + kTM * kTK;              // features: bytes [32 KB, 64 KB)
+        uint8_t* const sa_l = lds + stage * kStage1;          // tokens: bytes [0, 32 KB)
+        uint8_t* const sw_l = sa_l + kTM * kTK1;              // features: bytes [32 KB, 64 KB)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            *reinterpret_cast<u32x4*>(sa_l + lds_w + 32 * i * kTK) = ra_reg[i];
-            *reinterpret_cast<u32x4*>(sw_l + lds_w + 32 * i * kTK) = rw_reg[i];
+            *reinterpret_cast<u32x4*>(sa_l + lds_w + 32 * i * kTK1) = ra_reg[i];
+            *reinterpret_cast<u32x4*>(sw_l + lds_w + 32 * i * kTK1) = rw_reg[i];
         }
     };
     uint32_t sc_w[4], sc_a[4];                    // current step's scale bytes
@@ -179,16 +201,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
             load_tiles(kb + 1);
             load_scales(kb + 1, nx_w, nx_a);
         }
-        const uint8_t* const ta = lds + cur * kStage + (128 * wm) * kTK;
-        const uint8_t* const tw = lds + cur * kStage + kTM * kTK + (128 * wn) * kTK;
+        const uint8_t* const ta = lds + cur * kStage1 + (128 * wm) * kTK1;
+        const uint8_t* const tw = lds + cur * kStage1 + kTM * kTK1 + (128 * wn) * kTK1;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
             const uint32_t c0 = 16 * ((4 * kh + h) ^ sw8), c1 = 16 * ((4 * kh + 2 + h) ^ sw8);
             i32x8 fw[4], fa[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const uint8_t* const rowp_w = tw + (32 * t + r) * kTK;
-                const uint8_t* const rowp_a = ta + (32 * t + r) * kTK;
+                const uint8_t* const rowp_w = tw + (32 * t + r) * kTK1;
+                const uint8_t* const rowp_a = ta + (32 * t + r) * kTK1;
                 const u32x4 w0 = *reinterpret_cast<const u32x4*>(rowp_w + c0);
                 const u32x4 w1 = *reinterpret_cast<const u32x4*>(rowp_w + c1);
                 const u32x4 a0 = *reinterpret_cast<const u32x4*>(rowp_a + c0);
@@ -235,6 +257,160 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
     }
 }
 
+__global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
+    const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ w,
+    const uint8_t* __restrict__ sw, uint16_t* __restrict__ y, const int32_t* __restrict__ offs, int G,
+    int64_t N, int64_t K)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t lds2[kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t lds3[kStage];
+    // block scales: [block][half][row 0..31][tile 0..3] per operand
+    __shared__ __attribute__((aligned(16))) uint8_t scl_a[kMaxFastBlocks * kTM];
+    __shared__ __attribute__((aligned(16))) uint8_t scl_w[kMaxFastBlocks * kTN];
+    auto stage_ptr = [&](int b) -> uint8_t* { return b == 0 ? lds0 : b == 1 ? lds1 : b == 2 ? lds2 : lds3; };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t ntn = (uint32_t)(N / kTN);
+    const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t mtile = lin / ntn, ntile = lin % ntn;
+    int g;
+    int64_t row0;
+    int rows;
+    if (!find_tile(offs, G, mtile, g, row0, rows))
+        return;                                   // uniform over the workgroup
+    const int64_t n0 = (int64_t)kTN * ntile;
+    const uint32_t kb_n = (uint32_t)(K / 128);    // scale blocks along K
+    const uint32_t T = (uint32_t)(K / kTK);       // stages
+
+    // operand tiles: tokens (rows row0 ..) of A and features (rows n0 ..) of W_g
+    const __amdgpu_buffer_rsrc_t ra = strip_rsrc(a + row0 * K, (uint64_t)rows * (uint64_t)K);
+    const __amdgpu_buffer_rsrc_t rw = strip_rsrc(w + ((int64_t)g * N + n0) * K, (uint64_t)kTN * (uint64_t)K);
+    const __amdgpu_buffer_rsrc_t rsa = strip_rsrc(sa + row0 * kb_n, (uint64_t)rows * kb_n);
+    const __amdgpu_buffer_rsrc_t rsw = strip_rsrc(sw + ((int64_t)g * N + n0) * kb_n, (uint64_t)kTN * kb_n);
+
+    // loader role: instruction i of wave w fills LDS rows 64 w + 16 i .. + 15; lane L takes
+    // row 64 w + 16 i + L / 4, LDS chunk L % 4, i.e. global chunk (L % 4) ^ ((row >> 2) & 3)
+    const uint32_t lrow = (uint32_t)(64 * wave + (lane >> 2));        // + 16 i
+    const uint32_t lchunk = (uint32_t)(lane & 3) ^ ((lrow >> 2) & 3);  // ((lrow + 16 i) >> 2) & 3 is the same
+    uint32_t loff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        loff[i] = (lrow + 16 * i) * (uint32_t)K + 16 * lchunk;
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    // compute role: wave (wm, wn), lane (r, h)
+    const int wm = wave & 1, wn = wave >> 1;
+    const uint32_t r = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+    const uint32_t sw8 = (r >> 2) & 3;                                 // the swizzle of rows r + 32 x
+    // stage the tile's block scales: thread t owns row t (row 128 x + 32 q + y goes to
+    // byte [block][x][y][q]); rows past the tile read as zero
+    {
+        const uint32_t x = (uint32_t)tid >> 7, q = ((uint32_t)tid >> 5) & 3, yy = (uint32_t)tid & 31;
+        const uint32_t dst = x * 128 + yy * 4 + q;
+        for (uint32_t b = 0; b < kb_n; ++b) {
+            scl_a[b * kTM + dst] = (uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rsa, (int)((uint32_t)tid * kb_n + b), 0, 0);
+            scl_w[b * kTN + dst] = (uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rsw, (int)((uint32_t)tid * kb_n + b), 0, 0);
+        }
+    }
+    // the scale loads above are awaited here, before any LDS load is in flight
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+    // the 8 LDS loads of stage s into buffer buf
+    auto issue = [&](uint32_t s, int buf) {
+        const int koff = (int)(s * kTK);
+        lds_u8* const st = (lds_u8*)stage_ptr(buf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, st + (64 * wave + 16 * i) * kTK, 16, loff[i], koff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, st + kTM * kTK + (64 * wave + 16 * i) * kTK, 16, loff[i],
+                                                     koff, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+            acc[mt][nt] = f32x16{};
+
+    __syncthreads();                              // scales staged
+#pragma unroll
+    for (int u = 0; u < kStages - 1; ++u)
+        if ((uint32_t)u < T)
+            issue((uint32_t)u, u);
+
+    // T is a multiple of 4 (K is a multiple of 256 on this path): stages run in groups
+    // of 4, one per LDS buffer
+    for (uint32_t t0 = 0; t0 < T; t0 += kStages) {
+#pragma unroll
+        for (int u = 0; u < kStages; ++u) {
+            const uint32_t t = t0 + u;
+            // stage t is this lane's; the younger stages' loads may stay in flight
+            const uint32_t younger = min(T - 1 - t, (uint32_t)(kStages - 2));
+            if (younger >= 2)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStep));
+            else if (younger == 1)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerStep));
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __syncthreads();                      // every lane's part of stage t is in LDS,
+                                                  // and every wave is done with stage t - 1
+            if (t + kStages - 1 < T)
+                issue(t + kStages - 1, (u + kStages - 1) % kStages);
+            const uint8_t* const ta = stage_ptr(u) + (128 * wm) * kTK;
+            const uint8_t* const tw = stage_ptr(u) + kTM * kTK + (128 * wn) * kTK;
+            const uint32_t sca4 = *reinterpret_cast<const uint32_t*>(scl_a + (t >> 1) * kTM + wm * 128 + r * 4);
+            const uint32_t scw4 = *reinterpret_cast<const uint32_t*>(scl_w + (t >> 1) * kTN + wn * 128 + r * 4);
+            const uint32_t c0 = 16 * (h ^ sw8), c1 = 16 * ((2 + h) ^ sw8);
+            i32x8 fw[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint8_t* const rowp_w = tw + (32 * q + r) * kTK;
+                const u32x4 w0 = *reinterpret_cast<const u32x4*>(rowp_w + c0);
+                const u32x4 w1 = *reinterpret_cast<const u32x4*>(rowp_w + c1);
+                fw[q] = i32x8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const uint8_t* const rowp_a = ta + (32 * mt + r) * kTK;
+                const u32x4 a0 = *reinterpret_cast<const u32x4*>(rowp_a + c0);
+                const u32x4 a1 = *reinterpret_cast<const u32x4*>(rowp_a + c1);
+                const i32x8 fa = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fw[nt], fa, acc[mt][nt], 0, 0, 0, (int)((scw4 >> (8 * nt)) & 0xFF), 0,
+                        (int)((sca4 >> (8 * mt)) & 0xFF));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // epilogue: lane (r, h) of MFMA tile (mt, nt) holds token 128 wm + 32 mt + r and
+    // features 128 wn + 32 nt + 8 q + 4 h + (0..3) in values 4q .. 4q + 3
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int mloc = 128 * wm + 32 * mt + (int)r;
+        if (mloc >= rows)
+            continue;
+        uint16_t* const yrow = y + (row0 + mloc) * N + n0 + 128 * wn + 4 * h;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x16& v = acc[mt][nt];
+                const bf16x2_g p0 = {(__bf16)v[4 * q + 0], (__bf16)v[4 * q + 1]};
+                const bf16x2_g p1 = {(__bf16)v[4 * q + 2], (__bf16)v[4 * q + 3]};
+                *reinterpret_cast<u32x2*>(yrow + 32 * nt + 8 * q) =
+                    u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+            }
+    }
+}
+
 int64_t gemm_tile_capacity(int64_t M_cap, int32_t G)
 {
     return (M_cap + kTM - 1) / kTM + G;
@@ -253,8 +429,9 @@ hipError_t launch_fp8_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* w
     int64_t n = N, k = K;
     void* args[] = {(void*)&a, (void*)&sa, (void*)&w, (void*)&sw, (void*)&y, (void*)&offs, (void*)&g,
                     (void*)&n, (void*)&k};
-    return hipLaunchKernel((const void*)fp8_gemm_kernel, dim3((unsigned)grid), dim3(kGemmThreads), args, 0,
-                           stream);
+    const bool fast = K <= 128 * kMaxFastBlocks && K % (kTK * kStages) == 0;
+    const void* kern = fast ? (const void*)fp8_gemm_kernel : (const void*)fp8_gemm_general_kernel;
+    return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kGemmThreads), args, 0, stream);
 }
 
 }  // namespace mxfp4
