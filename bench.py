@@ -19,7 +19,9 @@ forward chain, every launch's median over 20 launches each preceded by a 512 MB
 scrub read (so inputs come from HBM, not the caches), next to a device copy
 moving the same bytes.  ``backward`` times the FP8 gradient quantizer
 (mxfp4_bf16_to_fp8_rows and mxfp4_bf16_to_fp8_cols_ragged) on the same segments,
-outside ``value``; the scrubbed medians include it.  ``cpu_baseline`` times the CPU oracle on a bounded
+outside ``value``; the scrubbed medians include it.  ``gemm`` times the forward expert
+GEMM (mxfp4_fp8_grouped_gemm) on the hidden segment's FP8 row output against
+per-expert E4M3 weights ([8, 4096, 7168], synthetic), with its MFMA roofline.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same workload on this host (all allowed threads, and one thread).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload config5] [--no-scrubbed]
@@ -50,7 +52,9 @@ KERNEL_SOURCES = {
     "cols": ["cols.hip", "strips.h", "common.h"],
     "fp8q_rows": ["fp8q.hip", "common.h"],
     "fp8q_cols": ["fp8q_cols.hip", "strips.h", "common.h"],
+    "gemm": ["gemm.hip", "strips.h", "common.h"],
 }
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix throughput, vendor datasheet
 
 
 def log(msg):
@@ -282,6 +286,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
+    ap.add_argument("--gemm-n", type=int, default=4096,
+                    help="output features of the expert GEMM timed on the hidden segment (0: skip)")
     ap.add_argument("--no-scrubbed", action="store_true",
                     help="skip the per-kernel scrubbed medians of configs 2, 4 and 5")
     args = ap.parse_args()
@@ -344,6 +350,45 @@ def main():
     dom = max(per_kernel, key=lambda p: p["mean_us"])
     achieved = dom["GBps"]
     traffic = read_traffic(dom["kernel"], w.name, dom["segment"])
+
+    # the forward expert GEMM on the hidden segment's FP8 row output (not in `value`)
+    gemm = None
+    if args.gemm_n > 0 and "y" in segs[0]:
+        seg0 = segs[0]
+        sg = seg0["seg"]
+        Ng, Kg, Gg = int(args.gemm_n), sg.K, sg.G
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0)
+        wq = torch.randint(0, 256, (Gg, Ng, Kg), device=dev, dtype=torch.int32, generator=gen)
+        wq = torch.where((wq & 0x7F) == 0x7F, wq - 1, wq).to(torch.uint8)        # no NaN bytes
+        wqs = torch.randint(118, 136, (Gg, Ng, Kg // 128), device=dev, dtype=torch.int32, generator=gen).to(torch.uint8)
+        yg = torch.empty((sg.M_cap, Ng), dtype=torch.int16, device=dev)
+        gfn = lambda: mx.mxfp4_fp8_grouped_gemm(seg0["y"], seg0["ys"], wq, wqs, yg, seg0["offs"])
+        for _ in range(max(1, args.warmup)):
+            gfn()
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a_, b_ in gev:
+            a_.record()
+            gfn()
+            b_.record()
+        torch.cuda.synchronize()
+        gms = [a_.elapsed_time(b_) for a_, b_ in gev]
+        flop = 2.0 * sg.M_tot * Ng * Kg
+        g_us = float(np.mean(gms)) * 1000.0
+        tflops = flop / (g_us * 1e-6) / 1e12
+        gemm = {
+            "what": "forward expert GEMM: hidden-segment FP8 row output x per-expert E4M3 weights -> BF16",
+            "shape": {"M_tot": sg.M_tot, "K": Kg, "N": Ng, "G": Gg},
+            "flop_per_launch": flop,
+            "mean_us": round(g_us, 2), "median_us": round(float(np.median(gms)) * 1000.0, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP8_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / FP8_MFMA_PEAK_TFLOPS, 4)},
+        }
+        log(f"[bench] expert GEMM {sg.M_tot} x {Kg} x {Ng} over {Gg} experts: {g_us:.1f} us, "
+            f"{tflops:.0f} TFLOP/s ({tflops / FP8_MFMA_PEAK_TFLOPS:.1%} of the FP8 peak)")
+        del wq, wqs, yg
 
     # the backward FP8 quantizer on the same segments, timed the same way (not in `value`)
     bsegs, blaunches = build_launches(mx, w, dev, torch, backward=True)
@@ -430,6 +475,7 @@ def main():
         },
         "per_kernel": per_kernel,
         "backward": backward,
+        "gemm": gemm,
         "per_config_scrubbed": None,
         "cpu_baseline": None,
     }
