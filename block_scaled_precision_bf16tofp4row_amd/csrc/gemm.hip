@@ -21,30 +21,34 @@
 // weights as the first operand and the tokens as the second, a lane's results are 4
 // consecutive output features of one token (one 8-byte store).
 //
-// Work (K a multiple of 256 up to 7168, the fast path): a workgroup (4 waves) owns a 256-token x 256-feature
-// tile of one expert and walks K in stages of 64; wave (wm, wn) computes tokens 128 wm .. + 127 x features
-// 128 wn .. + 127 as 4 x 4 MFMA tiles (256 fp32 accumulators per lane).  Operand tiles
-// go straight from memory to LDS (buffer_load ... lds: lane L's 16 bytes land at the
-// instruction's LDS base + 16 L) through a ring of 4 stages (4 x 32 KB), issued 3 stages
-// ahead, so the loads have three stages of matrix work to arrive and use no registers.
-// Each wave loads 64 rows of each operand per stage, 16 rows x 64 bytes per
-// instruction; LDS rows are 64 bytes with the 16-byte chunk c of row r stored at chunk
-// c ^ ((r >> 2) & 3), so the fragment reads of 16 consecutive rows (one LDS cycle of a
-// 16-byte read) hit distinct banks
-// (a lane of the load picks the global chunk that belongs in its LDS slot).  The
-// compiler does not see that the fragment reads depend on these loads, so a stage is
-// awaited explicitly: every step issues the same 8 LDS loads per lane, and before stage
-// t's barrier a lane waits until at most the younger stages' loads remain in flight.
+// Work (K a multiple of 256 up to 7168, the fast path): a workgroup of 8 waves (two
+// per SIMD, so one wave's matrix work hides the other's LDS reads) owns a 256-token x
+// 256-feature tile of one expert and walks K in stages of 64; wave (wm, wn) computes
+// tokens 128 wm .. + 127 x features 64 wn .. + 63 as 4 x 2 MFMA tiles (128 fp32
+// accumulators per lane).  Operand tiles go straight from memory to LDS (buffer_load
+// ... lds: lane L's 16 bytes land at the instruction's LDS base + 16 L) through a ring
+// of 4 stages (4 x 32 KB), issued 3 stages ahead, so the loads have three stages of
+// matrix work to arrive and use no registers.  Each wave loads 32 rows of each operand
+// per stage, 16 rows x 64 bytes per instruction; LDS rows are 64 bytes with the 16-byte
+// chunk c of row r stored at chunk c ^ ((r >> 2) & 3), so the fragment reads of 16
+// consecutive rows (one LDS cycle of a 16-byte read) hit distinct banks (a lane of the
+// load picks the global chunk that belongs in its LDS slot).  The compiler does not see
+// that the fragment reads depend on these loads, so a stage is awaited explicitly:
+// every stage issues the same 4 LDS loads per lane, and before stage t's barrier a lane
+// waits until at most the younger stages' loads remain in flight.  Stages run in groups
+// of four (one per ring buffer) whose waits and load issues are fixed at compile time,
+// the last group peeled, so that a group is one basic block and the compiler keeps each
+// stage's matrix work in its stage instead of sinking it towards the stores.
 // The tile's block scales (256 rows x K/128 bytes per operand) are staged in LDS once,
 // laid out so that one 4-byte read gives a lane the scales of its four MFMA tiles; they
-// take no registers across stages and no place in the memory-operation count.  Operand and scale loads are buffer
-// loads whose range is the tile's rows that exist: rows past the last partial tile of
-// an expert read as zero (they add nothing and are not stored).  The tile ->
-// (expert, token tile) map is found on the device from the offsets; output rows past
-// offs[G] are never written.
+// take no registers across stages and no place in the memory-operation count.  Operand
+// and scale loads are buffer loads whose range is the tile's rows that exist: rows past
+// the last partial tile of an expert read as zero (they add nothing), and the output
+// stores go through a resource of the same rows, so those rows are never written.  The
+// tile -> (expert, token tile) map is found on the device from the offsets.
 // For other K (above 7168 the scales do not fit in LDS beside the ring) a general
-// kernel keeps the same tiles with two 128-K register-staged LDS buffers and per-step
-// scale loads.
+// kernel of 4 waves keeps the same workgroup tiles (128 x 128 per wave) with two 128-K
+// register-staged LDS buffers and per-step scale loads.
 #include "strips.h"
 
 namespace mxfp4 {
@@ -53,14 +57,15 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_g __attribute__((ext_vector_type(2)));
 
-constexpr int kGemmThreads = 256;                 // 4 waves
+constexpr int kGemmThreads = 256;                 // 4 waves (general path)
 constexpr int kTM = 256;                          // tokens per workgroup tile
 constexpr int kTN = 256;                          // output features per workgroup tile
 // fast path
 constexpr int kTK = 64;                           // K per stage (half a scale block)
 constexpr int kStages = 4;                        // LDS ring depth; loads run kStages - 1 ahead
 constexpr int kStage = (kTM + kTN) * kTK;         // bytes of one LDS stage (32 KB)
-constexpr int kLoadsPerStep = 8;                  // LDS loads a lane issues per stage
+constexpr int kFastThreads = 512;                 // 8 waves, two per SIMD
+constexpr int kFastLoadsPerStep = 4;              // LDS loads a lane issues per stage
 constexpr int kMaxFastBlocks = 56;                // scale blocks staged in LDS (K <= 7168)
 // general path
 constexpr int kTK1 = 128;
@@ -107,6 +112,22 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offs, int 
     return false;
 }
 
+// Workgroup -> (token tile, feature tile).  The tiles of one XCD run in this order:
+// groups of kGroupM token tiles, every feature tile of a group before the next group,
+// the group's token tiles innermost, so the workgroups one XCD holds at a time share a
+// few operand tiles of each kind in its L2.
+constexpr uint32_t kGroupM = 4;
+__device__ __forceinline__ void tile_of(uint32_t lin, uint32_t nblocks, uint32_t ntn, uint32_t& mtile,
+                                        uint32_t& ntile)
+{
+    const uint32_t ntm = nblocks / ntn;
+    const uint32_t grp = lin / (kGroupM * ntn);
+    const uint32_t gm = min(kGroupM, ntm - grp * kGroupM);
+    const uint32_t idx = lin - grp * kGroupM * ntn;
+    mtile = grp * kGroupM + idx % gm;
+    ntile = idx / gm;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_general_kernel(
@@ -119,9 +140,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_general_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t ntn = (uint32_t)(N / kTN);
-    const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
-    const uint32_t mtile = lin / ntn, ntile = lin % ntn;
+    uint32_t mtile, ntile;
+    tile_of(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, (uint32_t)(N / kTN), mtile, ntile);
     int g;
     int64_t row0;
     int rows;
@@ -257,7 +277,87 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_general_kernel(
     }
 }
 
-__global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
+// What a wave of the fast kernel needs in its stage loop.
+struct FastCtx {
+    uint8_t* stage[kStages];                      // the LDS ring
+    const uint8_t* scl_a;                         // staged block scales
+    const uint8_t* scl_w;
+    __amdgpu_buffer_rsrc_t ra, rw;                // token and feature rows of the tile
+    uint32_t loff[2];                             // the lane's loader offsets
+    int wave, wm, wn;
+    uint32_t r, h;
+};
+
+// The LDS loads of stage s into ring buffer buf: instruction i of wave w fills LDS rows
+// 32 w + 16 i .. + 15 of each operand.
+__device__ __forceinline__ void fast_issue(const FastCtx& cx, uint32_t s, int buf)
+{
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    const int koff = (int)(s * kTK);
+    lds_u8* const st = (lds_u8*)cx.stage[buf];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(cx.ra, st + (32 * cx.wave + 16 * i) * kTK, 16, cx.loff[i], koff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(cx.rw, st + kTM * kTK + (32 * cx.wave + 16 * i) * kTK, 16,
+                                                 cx.loff[i], koff, 0, 0);
+    }
+}
+
+// Stages t0 .. t0 + 3 (ring buffers 0 .. 3).  Before stage t's barrier a lane waits
+// until only the younger stages' loads (at most two stages) remain in flight; after it,
+// the lane issues stage t + 3 into the buffer stage t - 1 used.  kLast: t0 + 4 == T.
+template <bool kLast>
+__device__ __forceinline__ void fast_group(const FastCtx& cx, uint32_t t0, f32x16 (&acc)[4][2])
+{
+    const uint32_t sw8 = (cx.r >> 2) & 3;                              // the swizzle of rows r + 32 x
+    const uint32_t c0 = 16 * (cx.h ^ sw8), c1 = 16 * ((2 + cx.h) ^ sw8);
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+        const uint32_t t = t0 + u;
+        constexpr int kFull = kStages - 2;
+        const int younger = kLast ? min(kStages - 1 - u, kFull) : kFull;
+        if (younger == 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kFastLoadsPerStep));
+        else if (younger == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kFastLoadsPerStep));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();                          // every lane's part of stage t is in LDS,
+                                                  // and every wave is done with stage t - 1
+        if (!kLast || u == 0)
+            fast_issue(cx, t + kStages - 1, (u + kStages - 1) % kStages);
+        const uint8_t* const ta = cx.stage[u] + (128 * cx.wm) * kTK;
+        const uint8_t* const tw = cx.stage[u] + kTM * kTK + (64 * cx.wn) * kTK;
+        const uint32_t sca4 = *reinterpret_cast<const uint32_t*>(cx.scl_a + (t >> 1) * kTM + cx.wm * 128 + cx.r * 4);
+        // features 64 wn + 32 nt + r are scale row 128 (wn / 2) + 32 (2 (wn % 2) + nt) + r
+        const uint32_t scw4 =
+            *reinterpret_cast<const uint32_t*>(cx.scl_w + (t >> 1) * kTN + (cx.wn >> 1) * 128 + cx.r * 4) >>
+            (16 * (cx.wn & 1));
+        i32x8 fw[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint8_t* const rowp_w = tw + (32 * q + cx.r) * kTK;
+            const u32x4 w0 = *reinterpret_cast<const u32x4*>(rowp_w + c0);
+            const u32x4 w1 = *reinterpret_cast<const u32x4*>(rowp_w + c1);
+            fw[q] = i32x8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const uint8_t* const rowp_a = ta + (32 * mt + cx.r) * kTK;
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(rowp_a + c0);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(rowp_a + c1);
+            const i32x8 fa = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    fw[nt], fa, acc[mt][nt], 0, 0, 0, (int)((scw4 >> (8 * nt)) & 0xFF), 0,
+                    (int)((sca4 >> (8 * mt)) & 0xFF));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+__global__ __launch_bounds__(kFastThreads, 1) void fp8_gemm_kernel(
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ sw, uint16_t* __restrict__ y, const int32_t* __restrict__ offs, int G,
     int64_t N, int64_t K)
@@ -269,14 +369,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
     // block scales: [block][half][row 0..31][tile 0..3] per operand
     __shared__ __attribute__((aligned(16))) uint8_t scl_a[kMaxFastBlocks * kTM];
     __shared__ __attribute__((aligned(16))) uint8_t scl_w[kMaxFastBlocks * kTN];
-    auto stage_ptr = [&](int b) -> uint8_t* { return b == 0 ? lds0 : b == 1 ? lds1 : b == 2 ? lds2 : lds3; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t ntn = (uint32_t)(N / kTN);
-    const uint32_t lin = xcd_remap(blockIdx.x, gridDim.x);
-    const uint32_t mtile = lin / ntn, ntile = lin % ntn;
+    uint32_t mtile, ntile;
+    tile_of(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, (uint32_t)(N / kTN), mtile, ntile);
     int g;
     int64_t row0;
     int rows;
@@ -292,121 +390,73 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_kernel(
     const __amdgpu_buffer_rsrc_t rsa = strip_rsrc(sa + row0 * kb_n, (uint64_t)rows * kb_n);
     const __amdgpu_buffer_rsrc_t rsw = strip_rsrc(sw + ((int64_t)g * N + n0) * kb_n, (uint64_t)kTN * kb_n);
 
-    // loader role: instruction i of wave w fills LDS rows 64 w + 16 i .. + 15; lane L takes
-    // row 64 w + 16 i + L / 4, LDS chunk L % 4, i.e. global chunk (L % 4) ^ ((row >> 2) & 3)
-    const uint32_t lrow = (uint32_t)(64 * wave + (lane >> 2));        // + 16 i
+    // loader role: instruction i of wave w fills LDS rows 32 w + 16 i .. + 15 of each
+    // operand; lane L takes row 32 w + 16 i + L / 4, LDS chunk L % 4, i.e. global chunk
+    // (L % 4) ^ ((row >> 2) & 3)
+    const uint32_t lrow = (uint32_t)(32 * wave + (lane >> 2));        // + 16 i
     const uint32_t lchunk = (uint32_t)(lane & 3) ^ ((lrow >> 2) & 3);  // ((lrow + 16 i) >> 2) & 3 is the same
-    uint32_t loff[4];
+    uint32_t loff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
         loff[i] = (lrow + 16 * i) * (uint32_t)K + 16 * lchunk;
-    typedef __attribute__((address_space(3))) uint8_t lds_u8;
-    // compute role: wave (wm, wn), lane (r, h)
+    // compute role: wave (wm, wn) owns tokens 128 wm .. + 127 and features 64 wn .. + 63;
+    // lane (r, h)
     const int wm = wave & 1, wn = wave >> 1;
     const uint32_t r = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
-    const uint32_t sw8 = (r >> 2) & 3;                                 // the swizzle of rows r + 32 x
-    // stage the tile's block scales: thread t owns row t (row 128 x + 32 q + y goes to
-    // byte [block][x][y][q]); rows past the tile read as zero
+    // stage the tile's block scales: thread t < 256 owns token row t, thread 256 + t
+    // feature row t (row 128 x + 32 q + y goes to byte [block][x][y][q]); rows past the
+    // tile read as zero
     {
-        const uint32_t x = (uint32_t)tid >> 7, q = ((uint32_t)tid >> 5) & 3, yy = (uint32_t)tid & 31;
+        const uint32_t t8 = (uint32_t)tid & 255;
+        const uint32_t x = t8 >> 7, q = (t8 >> 5) & 3, yy = t8 & 31;
         const uint32_t dst = x * 128 + yy * 4 + q;
-        for (uint32_t b = 0; b < kb_n; ++b) {
-            scl_a[b * kTM + dst] = (uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rsa, (int)((uint32_t)tid * kb_n + b), 0, 0);
-            scl_w[b * kTN + dst] = (uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rsw, (int)((uint32_t)tid * kb_n + b), 0, 0);
-        }
+        const __amdgpu_buffer_rsrc_t rs = wave < 4 ? rsa : rsw;
+        uint8_t* const scl = wave < 4 ? scl_a : scl_w;
+        for (uint32_t b = 0; b < kb_n; ++b)
+            scl[b * kTM + dst] = (uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)(t8 * kb_n + b), 0, 0);
     }
     // the scale loads above are awaited here, before any LDS load is in flight
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-    // the 8 LDS loads of stage s into buffer buf
-    auto issue = [&](uint32_t s, int buf) {
-        const int koff = (int)(s * kTK);
-        lds_u8* const st = (lds_u8*)stage_ptr(buf);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, st + (64 * wave + 16 * i) * kTK, 16, loff[i], koff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, st + kTM * kTK + (64 * wave + 16 * i) * kTK, 16, loff[i],
-                                                     koff, 0, 0);
-        }
-    };
-
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 2; ++nt)
             acc[mt][nt] = f32x16{};
 
+    const FastCtx cx{{lds0, lds1, lds2, lds3}, scl_a, scl_w, ra, rw, {loff[0], loff[1]}, wave, wm, wn, r, h};
     __syncthreads();                              // scales staged
 #pragma unroll
-    for (int u = 0; u < kStages - 1; ++u)
-        if ((uint32_t)u < T)
-            issue((uint32_t)u, u);
-
+    for (int u = 0; u < kStages - 1; ++u)         // T >= 4 on this path
+        fast_issue(cx, (uint32_t)u, u);
     // T is a multiple of 4 (K is a multiple of 256 on this path): stages run in groups
-    // of 4, one per LDS buffer
-    for (uint32_t t0 = 0; t0 < T; t0 += kStages) {
-#pragma unroll
-        for (int u = 0; u < kStages; ++u) {
-            const uint32_t t = t0 + u;
-            // stage t is this lane's; the younger stages' loads may stay in flight
-            const uint32_t younger = min(T - 1 - t, (uint32_t)(kStages - 2));
-            if (younger >= 2)
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStep));
-            else if (younger == 1)
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerStep));
-            else
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-            __syncthreads();                      // every lane's part of stage t is in LDS,
-                                                  // and every wave is done with stage t - 1
-            if (t + kStages - 1 < T)
-                issue(t + kStages - 1, (u + kStages - 1) % kStages);
-            const uint8_t* const ta = stage_ptr(u) + (128 * wm) * kTK;
-            const uint8_t* const tw = stage_ptr(u) + kTM * kTK + (128 * wn) * kTK;
-            const uint32_t sca4 = *reinterpret_cast<const uint32_t*>(scl_a + (t >> 1) * kTM + wm * 128 + r * 4);
-            const uint32_t scw4 = *reinterpret_cast<const uint32_t*>(scl_w + (t >> 1) * kTN + wn * 128 + r * 4);
-            const uint32_t c0 = 16 * (h ^ sw8), c1 = 16 * ((2 + h) ^ sw8);
-            i32x8 fw[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint8_t* const rowp_w = tw + (32 * q + r) * kTK;
-                const u32x4 w0 = *reinterpret_cast<const u32x4*>(rowp_w + c0);
-                const u32x4 w1 = *reinterpret_cast<const u32x4*>(rowp_w + c1);
-                fw[q] = i32x8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
-            }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const uint8_t* const rowp_a = ta + (32 * mt + r) * kTK;
-                const u32x4 a0 = *reinterpret_cast<const u32x4*>(rowp_a + c0);
-                const u32x4 a1 = *reinterpret_cast<const u32x4*>(rowp_a + c1);
-                const i32x8 fa = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fw[nt], fa, acc[mt][nt], 0, 0, 0, (int)((scw4 >> (8 * nt)) & 0xFF), 0,
-                        (int)((sca4 >> (8 * mt)) & 0xFF));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
+    // of 4, one per LDS buffer; the last group is peeled so that every wait and every
+    // load issue in a group is fixed at compile time and a group is one basic block
+    uint32_t t0 = 0;
+    for (; t0 + kStages < T; t0 += kStages)
+        fast_group<false>(cx, t0, acc);
+    fast_group<true>(cx, t0, acc);
 
     // epilogue: lane (r, h) of MFMA tile (mt, nt) holds token 128 wm + 32 mt + r and
-    // features 128 wn + 32 nt + 8 q + 4 h + (0..3) in values 4q .. 4q + 3
+    // features 64 wn + 32 nt + 8 q + 4 h + (0..3) in values 4q .. 4q + 3.  The stores
+    // go through a buffer resource whose range is the tile's existing rows, so stores
+    // of rows past them are dropped without a branch.
+    const __amdgpu_buffer_rsrc_t ry = strip_rsrc(y + row0 * N, (uint64_t)rows * (uint64_t)N * 2);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        const int mloc = 128 * wm + 32 * mt + (int)r;
-        if (mloc >= rows)
-            continue;
-        uint16_t* const yrow = y + (row0 + mloc) * N + n0 + 128 * wn + 4 * h;
+        const uint32_t mloc = 128 * wm + 32 * mt + r;
+        const uint32_t yoff = (mloc * (uint32_t)N + (uint32_t)n0 + 64 * wn + 4 * h) * 2;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x16& v = acc[mt][nt];
                 const bf16x2_g p0 = {(__bf16)v[4 * q + 0], (__bf16)v[4 * q + 1]};
                 const bf16x2_g p1 = {(__bf16)v[4 * q + 2], (__bf16)v[4 * q + 3]};
-                *reinterpret_cast<u32x2*>(yrow + 32 * nt + 8 * q) =
-                    u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)}, ry,
+                    (int)(yoff + 2 * (32 * nt + 8 * q)), 0, 0);
             }
     }
 }
@@ -431,7 +481,7 @@ hipError_t launch_fp8_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* w
                     (void*)&n, (void*)&k};
     const bool fast = K <= 128 * kMaxFastBlocks && K % (kTK * kStages) == 0;
     const void* kern = fast ? (const void*)fp8_gemm_kernel : (const void*)fp8_gemm_general_kernel;
-    return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kGemmThreads), args, 0, stream);
+    return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(fast ? kFastThreads : kGemmThreads), args, 0, stream);
 }
 
 }  // namespace mxfp4
