@@ -23,22 +23,22 @@
 //
 // Work (K a multiple of 256 up to 7168, the fast path): a workgroup of 8 waves (two
 // per SIMD, so one wave's matrix work hides the other's LDS reads) owns a 256-token x
-// 256-feature tile of one expert and walks K in stages of 64; wave (wm, wn) computes
-// tokens 128 wm .. + 127 x features 64 wn .. + 63 as 4 x 2 MFMA tiles (128 fp32
-// accumulators per lane).  Operand tiles go straight from memory to LDS (buffer_load
-// ... lds: lane L's 16 bytes land at the instruction's LDS base + 16 L) through a ring
-// of 4 stages (4 x 32 KB), issued 3 stages ahead, so the loads have three stages of
-// matrix work to arrive and use no registers.  Each wave loads 32 rows of each operand
-// per stage, 16 rows x 64 bytes per instruction; LDS rows are 64 bytes with the 16-byte
-// chunk c of row r stored at chunk c ^ ((r >> 2) & 3), so the fragment reads of 16
-// consecutive rows (one LDS cycle of a 16-byte read) hit distinct banks (a lane of the
-// load picks the global chunk that belongs in its LDS slot).  The compiler does not see
-// that the fragment reads depend on these loads, so a stage is awaited explicitly:
-// every stage issues the same 4 LDS loads per lane, and before stage t's barrier a lane
-// waits until at most the younger stages' loads remain in flight.  Stages run in groups
-// of four (one per ring buffer) whose waits and load issues are fixed at compile time,
-// the last group peeled, so that a group is one basic block and the compiler keeps each
-// stage's matrix work in its stage instead of sinking it towards the stores.
+// 256-feature tile of one expert and walks K in stages of 128 (one scale block);
+// wave (wm, wn) computes tokens 128 wm .. + 127 x features 64 wn .. + 63 as 4 x 2
+// MFMA tiles (128 fp32 accumulators per lane), two MFMA K-steps per stage.  Operand
+// tiles go straight from memory to LDS (buffer_load ... lds: lane L's 16 bytes land at
+// the instruction's LDS base + 16 L) into two 64 KB buffers, the next stage's loads
+// running during the current stage's matrix work, with no registers held for them.
+// Each wave loads 32 rows of each operand per stage, 8 rows x 128 bytes (whole cache
+// lines) per instruction; LDS rows are 128 bytes with the 16-byte chunk c of row r
+// stored at chunk c ^ ((r >> 1) & 7), so the fragment reads of 16 consecutive rows
+// (one LDS cycle of a 16-byte read) hit distinct banks (a lane of the load picks the
+// global chunk that belongs in its LDS slot).  The compiler does not see that the
+// fragment reads depend on these loads, so a stage is awaited explicitly: before stage
+// t's barrier a lane waits for its own loads of stage t.  Stages run in pairs (one per
+// buffer) whose load issues are fixed at compile time, the last pair peeled, so that a
+// pair is one basic block and the compiler keeps each stage's matrix work in its stage
+// instead of sinking it towards the stores.
 // The tile's block scales (256 rows x K/128 bytes per operand) are staged in LDS once,
 // laid out so that one 4-byte read gives a lane the scales of its four MFMA tiles; they
 // take no registers across stages and no place in the memory-operation count.  Operand
@@ -46,7 +46,7 @@
 // the last partial tile of an expert read as zero (they add nothing), and the output
 // stores go through a resource of the same rows, so those rows are never written.  The
 // tile -> (expert, token tile) map is found on the device from the offsets.
-// For other K (above 7168 the scales do not fit in LDS beside the ring) a general
+// For other K (above 7168 the scales do not fit in LDS beside the buffers) a general
 // kernel of 4 waves keeps the same workgroup tiles (128 x 128 per wave) with two 128-K
 // register-staged LDS buffers and per-step scale loads.
 #include "strips.h"
@@ -61,11 +61,11 @@ constexpr int kGemmThreads = 256;                 // 4 waves (general path)
 constexpr int kTM = 256;                          // tokens per workgroup tile
 constexpr int kTN = 256;                          // output features per workgroup tile
 // fast path
-constexpr int kTK = 64;                           // K per stage (half a scale block)
-constexpr int kStages = 4;                        // LDS ring depth; loads run kStages - 1 ahead
-constexpr int kStage = (kTM + kTN) * kTK;         // bytes of one LDS stage (32 KB)
+constexpr int kTK = 128;                          // K per stage (one scale block, whole 128-B lines)
+constexpr int kStages = 2;                        // LDS buffers; loads run one stage ahead
+constexpr int kStage = (kTM + kTN) * kTK;         // bytes of one LDS stage (64 KB)
 constexpr int kFastThreads = 512;                 // 8 waves, two per SIMD
-constexpr int kFastLoadsPerStep = 4;              // LDS loads a lane issues per stage
+constexpr int kFastLoadsPerStep = 8;              // LDS loads a lane issues per stage
 constexpr int kMaxFastBlocks = 56;                // scale blocks staged in LDS (K <= 7168)
 // general path
 constexpr int kTK1 = 128;
@@ -279,79 +279,75 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_general_kernel(
 
 // What a wave of the fast kernel needs in its stage loop.
 struct FastCtx {
-    uint8_t* stage[kStages];                      // the LDS ring
+    uint8_t* stage[kStages];                      // the LDS buffers
     const uint8_t* scl_a;                         // staged block scales
     const uint8_t* scl_w;
     __amdgpu_buffer_rsrc_t ra, rw;                // token and feature rows of the tile
-    uint32_t loff[2];                             // the lane's loader offsets
+    uint32_t loff[4];                             // the lane's loader offsets
     int wave, wm, wn;
     uint32_t r, h;
 };
 
-// The LDS loads of stage s into ring buffer buf: instruction i of wave w fills LDS rows
-// 32 w + 16 i .. + 15 of each operand.
+// The LDS loads of stage s into buffer buf: instruction i of wave w fills LDS rows
+// 32 w + 8 i .. + 7 of each operand (8 rows x 128 bytes).
 __device__ __forceinline__ void fast_issue(const FastCtx& cx, uint32_t s, int buf)
 {
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
     const int koff = (int)(s * kTK);
     lds_u8* const st = (lds_u8*)cx.stage[buf];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(cx.ra, st + (32 * cx.wave + 16 * i) * kTK, 16, cx.loff[i], koff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(cx.rw, st + kTM * kTK + (32 * cx.wave + 16 * i) * kTK, 16,
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(cx.ra, st + (32 * cx.wave + 8 * i) * kTK, 16, cx.loff[i], koff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(cx.rw, st + kTM * kTK + (32 * cx.wave + 8 * i) * kTK, 16,
                                                  cx.loff[i], koff, 0, 0);
     }
 }
 
-// Stages t0 .. t0 + 3 (ring buffers 0 .. 3).  Before stage t's barrier a lane waits
-// until only the younger stages' loads (at most two stages) remain in flight; after it,
-// the lane issues stage t + 3 into the buffer stage t - 1 used.  kLast: t0 + 4 == T.
+// Stages t0 and t0 + 1 (buffers 0 and 1).  Before stage t's barrier a lane waits for
+// its loads of stage t; after it (every wave is done with stage t - 1), the lane issues
+// stage t + 1 into the other buffer.  kLast: t0 + 2 == T.
 template <bool kLast>
 __device__ __forceinline__ void fast_group(const FastCtx& cx, uint32_t t0, f32x16 (&acc)[4][2])
 {
-    const uint32_t sw8 = (cx.r >> 2) & 3;                              // the swizzle of rows r + 32 x
-    const uint32_t c0 = 16 * (cx.h ^ sw8), c1 = 16 * ((2 + cx.h) ^ sw8);
+    const uint32_t sw8 = (cx.r >> 1) & 7;                              // the swizzle of rows r + 32 x
 #pragma unroll
     for (int u = 0; u < kStages; ++u) {
         const uint32_t t = t0 + u;
-        constexpr int kFull = kStages - 2;
-        const int younger = kLast ? min(kStages - 1 - u, kFull) : kFull;
-        if (younger == 2)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kFastLoadsPerStep));
-        else if (younger == 1)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kFastLoadsPerStep));
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();                          // every lane's part of stage t is in LDS,
                                                   // and every wave is done with stage t - 1
         if (!kLast || u == 0)
-            fast_issue(cx, t + kStages - 1, (u + kStages - 1) % kStages);
+            fast_issue(cx, t + 1, u ^ 1);
         const uint8_t* const ta = cx.stage[u] + (128 * cx.wm) * kTK;
         const uint8_t* const tw = cx.stage[u] + kTM * kTK + (64 * cx.wn) * kTK;
-        const uint32_t sca4 = *reinterpret_cast<const uint32_t*>(cx.scl_a + (t >> 1) * kTM + cx.wm * 128 + cx.r * 4);
+        const uint32_t sca4 = *reinterpret_cast<const uint32_t*>(cx.scl_a + t * kTM + cx.wm * 128 + cx.r * 4);
         // features 64 wn + 32 nt + r are scale row 128 (wn / 2) + 32 (2 (wn % 2) + nt) + r
         const uint32_t scw4 =
-            *reinterpret_cast<const uint32_t*>(cx.scl_w + (t >> 1) * kTN + (cx.wn >> 1) * 128 + cx.r * 4) >>
+            *reinterpret_cast<const uint32_t*>(cx.scl_w + t * kTN + (cx.wn >> 1) * 128 + cx.r * 4) >>
             (16 * (cx.wn & 1));
-        i32x8 fw[2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const uint8_t* const rowp_w = tw + (32 * q + cx.r) * kTK;
-            const u32x4 w0 = *reinterpret_cast<const u32x4*>(rowp_w + c0);
-            const u32x4 w1 = *reinterpret_cast<const u32x4*>(rowp_w + c1);
-            fw[q] = i32x8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
-        }
+        for (int j = 0; j < 2; ++j) {             // the stage's two MFMA K-steps of 64
+            const uint32_t c0 = 16 * ((4 * j + cx.h) ^ sw8), c1 = 16 * ((4 * j + 2 + cx.h) ^ sw8);
+            i32x8 fw[2];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const uint8_t* const rowp_a = ta + (32 * mt + cx.r) * kTK;
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(rowp_a + c0);
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(rowp_a + c1);
-            const i32x8 fa = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            for (int q = 0; q < 2; ++q) {
+                const uint8_t* const rowp_w = tw + (32 * q + cx.r) * kTK;
+                const u32x4 w0 = *reinterpret_cast<const u32x4*>(rowp_w + c0);
+                const u32x4 w1 = *reinterpret_cast<const u32x4*>(rowp_w + c1);
+                fw[q] = i32x8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+            }
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    fw[nt], fa, acc[mt][nt], 0, 0, 0, (int)((scw4 >> (8 * nt)) & 0xFF), 0,
-                    (int)((sca4 >> (8 * mt)) & 0xFF));
+            for (int mt = 0; mt < 4; ++mt) {
+                const uint8_t* const rowp_a = ta + (32 * mt + cx.r) * kTK;
+                const u32x4 a0 = *reinterpret_cast<const u32x4*>(rowp_a + c0);
+                const u32x4 a1 = *reinterpret_cast<const u32x4*>(rowp_a + c1);
+                const i32x8 fa = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fw[nt], fa, acc[mt][nt], 0, 0, 0, (int)((scw4 >> (8 * nt)) & 0xFF), 0,
+                        (int)((sca4 >> (8 * mt)) & 0xFF));
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -364,8 +360,6 @@ __global__ __launch_bounds__(kFastThreads, 1) void fp8_gemm_kernel(
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[kStage];
-    __shared__ __attribute__((aligned(16))) uint8_t lds2[kStage];
-    __shared__ __attribute__((aligned(16))) uint8_t lds3[kStage];
     // block scales: [block][half][row 0..31][tile 0..3] per operand
     __shared__ __attribute__((aligned(16))) uint8_t scl_a[kMaxFastBlocks * kTM];
     __shared__ __attribute__((aligned(16))) uint8_t scl_w[kMaxFastBlocks * kTN];
@@ -390,15 +384,15 @@ __global__ __launch_bounds__(kFastThreads, 1) void fp8_gemm_kernel(
     const __amdgpu_buffer_rsrc_t rsa = strip_rsrc(sa + row0 * kb_n, (uint64_t)rows * kb_n);
     const __amdgpu_buffer_rsrc_t rsw = strip_rsrc(sw + ((int64_t)g * N + n0) * kb_n, (uint64_t)kTN * kb_n);
 
-    // loader role: instruction i of wave w fills LDS rows 32 w + 16 i .. + 15 of each
-    // operand; lane L takes row 32 w + 16 i + L / 4, LDS chunk L % 4, i.e. global chunk
-    // (L % 4) ^ ((row >> 2) & 3)
-    const uint32_t lrow = (uint32_t)(32 * wave + (lane >> 2));        // + 16 i
-    const uint32_t lchunk = (uint32_t)(lane & 3) ^ ((lrow >> 2) & 3);  // ((lrow + 16 i) >> 2) & 3 is the same
-    uint32_t loff[2];
+    // loader role: instruction i of wave w fills LDS rows 32 w + 8 i .. + 7 of each
+    // operand; lane L takes row 32 w + 8 i + L / 8, LDS chunk L % 8, i.e. global chunk
+    // (L % 8) ^ ((row >> 1) & 7)
+    uint32_t loff[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-        loff[i] = (lrow + 16 * i) * (uint32_t)K + 16 * lchunk;
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lrow = (uint32_t)(32 * wave + 8 * i + (lane >> 3));
+        loff[i] = lrow * (uint32_t)K + 16 * ((uint32_t)(lane & 7) ^ ((lrow >> 1) & 7));
+    }
     // compute role: wave (wm, wn) owns tokens 128 wm .. + 127 and features 64 wn .. + 63;
     // lane (r, h)
     const int wm = wave & 1, wn = wave >> 1;
@@ -425,14 +419,12 @@ __global__ __launch_bounds__(kFastThreads, 1) void fp8_gemm_kernel(
         for (int nt = 0; nt < 2; ++nt)
             acc[mt][nt] = f32x16{};
 
-    const FastCtx cx{{lds0, lds1, lds2, lds3}, scl_a, scl_w, ra, rw, {loff[0], loff[1]}, wave, wm, wn, r, h};
+    const FastCtx cx{{lds0, lds1}, scl_a, scl_w, ra, rw, {loff[0], loff[1], loff[2], loff[3]}, wave, wm, wn, r, h};
     __syncthreads();                              // scales staged
-#pragma unroll
-    for (int u = 0; u < kStages - 1; ++u)         // T >= 4 on this path
-        fast_issue(cx, (uint32_t)u, u);
-    // T is a multiple of 4 (K is a multiple of 256 on this path): stages run in groups
-    // of 4, one per LDS buffer; the last group is peeled so that every wait and every
-    // load issue in a group is fixed at compile time and a group is one basic block
+    fast_issue(cx, 0, 0);
+    // T is even (K is a multiple of 256 on this path): stages run in pairs, one per LDS
+    // buffer; the last pair is peeled so that every load issue in a pair is fixed at
+    // compile time and a pair is one basic block
     uint32_t t0 = 0;
     for (; t0 + kStages < T; t0 += kStages)
         fast_group<false>(cx, t0, acc);
