@@ -71,6 +71,7 @@ def _load():
     lib.oracle_fp8q_rows.argtypes = [P, I64, I64, I64, P, P]
     lib.oracle_fp8q_cols.argtypes = [P, P, ctypes.c_int32, I64, I64, I64, P, P]
     lib.oracle_fp8_gemm_at.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, P, P, I64, P, P, P]
+    lib.oracle_fp8_wgrad_at.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, P, P, P, I64, P, P, P]
     lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_value.restype = ctypes.c_double
     lib.oracle_bf16_round.argtypes = [ctypes.c_double]
@@ -340,6 +341,50 @@ def fp8_gemm_at(a, sa, w, sw, offs, ms, ns, threads: int = 1):
 
     _run_ranges(run, _ranges(cnt, threads * 4), threads)
     return exact, ybf, absum
+
+
+def fp8_wgrad_at(dyT, dyT_scales, xT, xT_scales, offs, N, K, gs, ns, ks, threads: int = 1):
+    """The weight-gradient GEMM over the column layouts at the points (gs[i], ns[i], ks[i]):
+    dW[g, n, k] = sum over expert g's tokens of dY_g[m, n] X_g[m, k].  dyT / xT are the
+    column-layout outputs for widths N / K (oracle.fp8q_cols / oracle.fp8_cols).
+    Returns (exact fp64 values, BF16 bits, sum of |terms|)."""
+    lib = _load()
+    dyT = np.ascontiguousarray(dyT, dtype=np.uint8)
+    dyT_scales = np.ascontiguousarray(dyT_scales, dtype=np.uint8)
+    xT = np.ascontiguousarray(xT, dtype=np.uint8)
+    xT_scales = np.ascontiguousarray(xT_scales, dtype=np.uint8)
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    gs = np.ascontiguousarray(gs, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    ks = np.ascontiguousarray(ks, dtype=np.int64)
+    G = offs.size - 1
+    assert gs.shape == ns.shape == ks.shape
+    assert dyT.size >= N * int(offs[-1]) and xT.size >= K * int(offs[-1])
+    assert dyT_scales.size >= cols_scale_size(offs, N) and xT_scales.size >= cols_scale_size(offs, K)
+    assert np.all((gs >= 0) & (gs < G) & (ns >= 0) & (ns < N) & (ks >= 0) & (ks < K))
+    cnt = gs.size
+    exact = np.zeros(cnt, np.float64)
+    ybf = np.zeros(cnt, np.uint16)
+    absum = np.zeros(cnt, np.float64)
+
+    def run(r):
+        lo, hi = r
+        lib.oracle_fp8_wgrad_at(_ptr(dyT), _ptr(dyT_scales), _ptr(xT), _ptr(xT_scales), _ptr(offs), G, N, K,
+                                _ptr(gs[lo:]), _ptr(ns[lo:]), _ptr(ks[lo:]), hi - lo,
+                                _ptr(exact[lo:]), _ptr(ybf[lo:]), _ptr(absum[lo:]))
+
+    _run_ranges(run, _ranges(cnt, threads * 4), threads)
+    return exact, ybf, absum
+
+
+def fp8_wgrad(dyT, dyT_scales, xT, xT_scales, offs, N, K, threads: int = 1):
+    """Every output of the weight-gradient GEMM: (exact [G, N, K] fp64, BF16 bits, absum)."""
+    G = np.asarray(offs).size - 1
+    gg, nn, kk = np.meshgrid(np.arange(G, dtype=np.int64), np.arange(N, dtype=np.int64),
+                             np.arange(K, dtype=np.int64), indexing="ij")
+    e, y, t = fp8_wgrad_at(dyT, dyT_scales, xT, xT_scales, offs, N, K, gg.reshape(-1), nn.reshape(-1),
+                           kk.reshape(-1), threads)
+    return e.reshape(G, N, K), y.reshape(G, N, K), t.reshape(G, N, K)
 
 
 def fp8_gemm(a, sa, w, sw, offs, threads: int = 1):

@@ -426,6 +426,57 @@ void oracle_fp8_gemm_at(const uint8_t *a, const uint8_t *sa, const uint8_t *w, c
     }
 }
 
+/* ---- FP8 grouped GEMM, weight gradient (column layouts) ---------------- */
+/* Technical summary, section 2: the GEMMs stay in FP8 (item 1), and the column
+ * conversion (item 3: the transpose fused into the Wgrad conversion, ragged experts)
+ * produces the weight-gradient GEMM's operands.  Reading: for expert g with M_g tokens,
+ * the weight gradient contracts over the expert's tokens,
+ *     dW[g, n, k] = bf16( sum_{m < M_g} dY_g[m, n] X_g[m, k] )
+ * where both operands come in the column layout of oracle_fp8_cols / oracle_fp8q_cols:
+ * dyT holds expert g as [N, M_g] at byte N*offs[g] with scales [nb_g, N] at byte N*B_g
+ * (entry (b, n) scales tokens 128b .. 128b+127 of row n), and xT likewise with K.
+ * B_g is the number of 128-token blocks of the experts before g; a partial last block
+ * scales only the tokens it has.  An expert with no tokens has dW_g = 0.  The sum is
+ * taken in fp64 and rounded once to BF16 (nearest even), as for the forward GEMM. */
+
+/* 128-token blocks of the experts before g. */
+static int64_t blocks_before(const int32_t *offs, int32_t g)
+{
+    int64_t b = 0;
+    for (int32_t e = 0; e < g; ++e)
+        b += ((int64_t)offs[e + 1] - offs[e] + 127) / 128;
+    return b;
+}
+
+/* dW at `count` points (gs[i], ns[i], ks[i]); exact / y_bf16 / absum as in
+ * oracle_fp8_gemm_at (absum = sum_m |term|). */
+void oracle_fp8_wgrad_at(const uint8_t *dyT, const uint8_t *dyT_scales, const uint8_t *xT,
+                         const uint8_t *xT_scales, const int32_t *offs, int32_t G, int64_t N,
+                         int64_t K, const int64_t *gs, const int64_t *ns, const int64_t *ks,
+                         int64_t count, double *exact, uint16_t *y_bf16, double *absum)
+{
+    (void)G;
+    for (int64_t i = 0; i < count; ++i) {
+        int32_t g = (int32_t)gs[i];
+        int64_t n = ns[i], k = ks[i];
+        int64_t m0 = offs[g], Mg = (int64_t)offs[g + 1] - offs[g], Bg = blocks_before(offs, g);
+        const uint8_t *dy = dyT + N * m0 + n * Mg;          /* row n of expert g's [N, M_g] */
+        const uint8_t *xx = xT + K * m0 + k * Mg;           /* row k of expert g's [K, M_g] */
+        double s = 0.0, t = 0.0;
+        for (int64_t m = 0; m < Mg; ++m) {
+            int64_t b = m / 128;
+            double u = ldexp(e4m3_value(dy[m]), (int)dyT_scales[N * (Bg + b) + n] - 127);
+            double v = ldexp(e4m3_value(xx[m]), (int)xT_scales[K * (Bg + b) + k] - 127);
+            s += u * v;
+            t += fabs(u * v);
+        }
+        exact[i] = s;
+        y_bf16[i] = bf16_round(s);
+        if (absum)
+            absum[i] = t;
+    }
+}
+
 /* ---- small helpers exported for the pins ------------------------------- */
 
 int oracle_e2m1_encode(double y) { return e2m1_encode(y); }

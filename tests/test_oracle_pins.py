@@ -721,3 +721,122 @@ def test_fp8_gemm_routes_rows_to_their_expert_and_scales_exactly():
         rows = slice(offs[g], offs[g + 1])
         blk[rows] = np.repeat(A[rows, 128:256].sum(axis=1, keepdims=True) * 2.0 ** g, N, axis=1)
     np.testing.assert_allclose(e2 - exact, blk, rtol=1e-12, atol=0)
+
+
+# ---- weight-gradient GEMM over the column layouts ---------------------------------
+
+def _wgrad_case(rng, counts, N, K, lo_exp=0, hi_exp=15, s_lo=118, s_hi=136):
+    """Random column-layout operands: dyT / xT bytes for every expert's [N, M_g] /
+    [K, M_g] and scales for every (128-token block, row)."""
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offs[-1])
+    nb = int(sum((c + 127) // 128 for c in counts))
+    dyT = _e4m3_codes(rng, (N * M,), lo_exp, hi_exp)
+    xT = _e4m3_codes(rng, (K * M,), lo_exp, hi_exp)
+    sdy = rng.integers(s_lo, s_hi, size=(nb * N,)).astype(np.uint8)
+    sx = rng.integers(s_lo, s_hi, size=(nb * K,)).astype(np.uint8)
+    return dyT, sdy, xT, sx, offs
+
+
+def _wgrad_expert_operands(dyT, sdy, xT, sx, offs, N, K, g):
+    """Expert g's operands as plain matrices: DY [N, M_g] and X [K, M_g] (bytes) with
+    per-element scale exponents, read from the layout by index arithmetic."""
+    m0, Mg = int(offs[g]), int(offs[g + 1] - offs[g])
+    Bg = int(sum((int(offs[e + 1] - offs[e]) + 127) // 128 for e in range(g)))
+    DY = dyT[N * m0: N * (m0 + Mg)].reshape(N, Mg)
+    X = xT[K * m0: K * (m0 + Mg)].reshape(K, Mg)
+    nb = (Mg + 127) // 128
+    Sdy = sdy[N * Bg: N * (Bg + nb)].reshape(nb, N).T          # [N, nb]
+    Sx = sx[K * Bg: K * (Bg + nb)].reshape(nb, K).T            # [K, nb]
+    return DY, Sdy, X, Sx, Mg, nb
+
+
+def test_fp8_wgrad_equals_forward_oracle_on_padded_transposes():
+    """dW_g = DY_g X_g^T over tokens is the pinned forward GEMM with A = DY_g (rows n,
+    K-dim = tokens zero-padded to whole blocks) and one expert whose weight is X_g."""
+    rng = np.random.default_rng(51)
+    counts = [130, 0, 3, 256, 1]
+    N, K = 8, 12
+    dyT, sdy, xT, sx, offs = _wgrad_case(rng, counts, N, K)
+    exact, ybf, absum = oracle.fp8_wgrad(dyT, sdy, xT, sx, offs, N, K, threads=2)
+    for g in range(len(counts)):
+        DY, Sdy, X, Sx, Mg, nb = _wgrad_expert_operands(dyT, sdy, xT, sx, offs, N, K, g)
+        if Mg == 0:
+            assert np.all(exact[g] == 0) and np.all(ybf[g] == 0) and np.all(absum[g] == 0)
+            continue
+        A = np.zeros((N, 128 * nb), np.uint8)
+        A[:, :Mg] = DY
+        W = np.zeros((1, K, 128 * nb), np.uint8)
+        W[0, :, :Mg] = X
+        e_f, y_f, t_f = oracle.fp8_gemm(A, np.ascontiguousarray(Sdy), W, np.ascontiguousarray(Sx)[None],
+                                        np.array([0, N], np.int32))
+        np.testing.assert_array_equal(exact[g], e_f)
+        np.testing.assert_array_equal(ybf[g], y_f)
+        np.testing.assert_array_equal(absum[g], t_f)
+
+
+def test_fp8_wgrad_matches_numpy_matmul_per_expert():
+    rng = np.random.default_rng(52)
+    counts = [5, 200, 0, 129]
+    N, K = 16, 24
+    dyT, sdy, xT, sx, offs = _wgrad_case(rng, counts, N, K)
+    exact, _, absum = oracle.fp8_wgrad(dyT, sdy, xT, sx, offs, N, K)
+    for g in range(len(counts)):
+        DY, Sdy, X, Sx, Mg, nb = _wgrad_expert_operands(dyT, sdy, xT, sx, offs, N, K, g)
+        blk = np.arange(Mg) // 128
+        D = _decode_e4m3(DY) * 2.0 ** (Sdy[:, blk].astype(np.float64) - 127)
+        Xv = _decode_e4m3(X) * 2.0 ** (Sx[:, blk].astype(np.float64) - 127)
+        ref = D @ Xv.T
+        np.testing.assert_allclose(exact[g], ref, rtol=0, atol=1e-12 * max(np.abs(ref).max(), 1e-300))
+        np.testing.assert_allclose(absum[g], np.abs(D) @ np.abs(Xv).T, rtol=1e-12, atol=0)
+
+
+def test_fp8_wgrad_brute_force_rational_tiny():
+    rng = np.random.default_rng(53)
+    counts = [3, 0, 130]
+    N, K = 2, 3
+    dyT, sdy, xT, sx, offs = _wgrad_case(rng, counts, N, K, s_lo=120, s_hi=134)
+    exact, ybf, _ = oracle.fp8_wgrad(dyT, sdy, xT, sx, offs, N, K)
+
+    def val(c):
+        e, m = (c >> 3) & 15, c & 7
+        v = Fraction(m, 2 ** 9) if e == 0 else Fraction(8 + m) * Fraction(2) ** (e - 10)
+        return -v if c & 0x80 else v
+
+    B = 0
+    for g, Mg in enumerate(counts):
+        m0 = int(offs[g])
+        for n in range(N):
+            for k in range(K):
+                tot = Fraction(0)
+                for m in range(Mg):
+                    b = B + m // 128
+                    tot += (val(int(dyT[N * m0 + n * Mg + m])) * Fraction(2) ** (int(sdy[N * b + n]) - 127) *
+                            val(int(xT[K * m0 + k * Mg + m])) * Fraction(2) ** (int(sx[K * b + k]) - 127))
+                assert abs(Fraction(exact[g, n, k]) - tot) <= abs(tot) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
+                assert ybf[g, n, k] == _bf16_grid_round(tot)
+        B += (Mg + 127) // 128
+
+
+def test_fp8_wgrad_block_scale_moves_only_its_block():
+    """Raising the scale of (block 1, row n) of expert 0's dY by one adds exactly that
+    block's share of row n again; other rows and experts are unchanged."""
+    rng = np.random.default_rng(54)
+    counts = [300, 7]
+    N, K = 4, 5
+    dyT, sdy, xT, sx, offs = _wgrad_case(rng, counts, N, K, lo_exp=4, hi_exp=10)
+    e0, _, _ = oracle.fp8_wgrad(dyT, sdy, xT, sx, offs, N, K)
+    n = 2
+    sdy2 = sdy.copy()
+    sdy2[N * 1 + n] += 1                                   # expert 0, block 1, row n
+    e1, _, _ = oracle.fp8_wgrad(dyT, sdy2, xT, sx, offs, N, K)
+    DY, Sdy, X, Sx, Mg, nb = _wgrad_expert_operands(dyT, sdy, xT, sx, offs, N, K, 0)
+    blk = np.arange(Mg) // 128
+    D = _decode_e4m3(DY) * 2.0 ** (Sdy[:, blk].astype(np.float64) - 127)
+    Xv = _decode_e4m3(X) * 2.0 ** (Sx[:, blk].astype(np.float64) - 127)
+    share = D[n, 128:256] @ Xv[:, 128:256].T
+    np.testing.assert_allclose(e1[0, n] - e0[0, n], share, rtol=1e-12, atol=1e-300)
+    keep = np.ones(N, bool)
+    keep[n] = False
+    np.testing.assert_array_equal(e1[0, keep], e0[0, keep])
+    np.testing.assert_array_equal(e1[1], e0[1])
