@@ -15,6 +15,8 @@ The binding has the same names as the C ABI:
 * ``mxfp4_bf16_to_fp8_rows(x, y, y_scales, offs, ...)`` and
   ``mxfp4_bf16_to_fp8_cols_ragged(x, yT, yT_scales, offs, ...)`` (backward FP8 quantizer)
 * ``mxfp4_fp8_grouped_gemm(a, a_scales, w, w_scales, y, offs, ...)`` (FP8 expert GEMM)
+* ``mxfp4_fp8_grouped_gemm_wgrad(dyT, dyT_scales, xT, xT_scales, dw, offs, ...)``
+  (FP8 weight-gradient GEMM over the column layouts)
 * ``mxfp4_cols_scale_capacity(M_cap, K, G)``, ``mxfp4_validate_offsets(offs, ...)``,
   ``mxfp4_status_string(status)``
 
@@ -47,6 +49,7 @@ EXPORTED = (
     "mxfp4_bf16_to_fp8_rows",
     "mxfp4_bf16_to_fp8_cols_ragged",
     "mxfp4_fp8_grouped_gemm",
+    "mxfp4_fp8_grouped_gemm_wgrad",
     "mxfp4_cols_scale_capacity",
     "mxfp4_validate_offsets",
     "mxfp4_status_string",
@@ -85,6 +88,8 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_bf16_to_fp8_cols_ragged.restype = st
     lib.mxfp4_fp8_grouped_gemm.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
     lib.mxfp4_fp8_grouped_gemm.restype = st
+    lib.mxfp4_fp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
+    lib.mxfp4_fp8_grouped_gemm_wgrad.restype = st
     lib.mxfp4_cols_scale_capacity.argtypes = [I64, I64, I32]
     lib.mxfp4_cols_scale_capacity.restype = I64
     lib.mxfp4_validate_offsets.argtypes = [P, I32, I64, P]
@@ -251,6 +256,30 @@ def mxfp4_fp8_grouped_gemm(a, a_scales, w, w_scales, y, offs, G=None, M_cap=None
     lib = load_library()
     _check(lib.mxfp4_fp8_grouped_gemm(_ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scales), _ptr(y), _ptr(offs),
                                       G, M_cap, N, K, _stream(stream)), "mxfp4_fp8_grouped_gemm")
+
+
+def mxfp4_fp8_grouped_gemm_wgrad(dyT, dyT_scales, xT, xT_scales, dw, offs, N, K, G=None, M_cap=None,
+                                 stream=None):
+    """Column-layout E4M3 dY^T (width N) and X^T (width K) with their block scales ->
+    BF16 dW [G, N, K] (see the header).  M_cap defaults to the capacity of xT (its
+    bytes / K)."""
+    if G is None:
+        G = offs.numel() - 1
+    if M_cap is None:
+        M_cap = xT.numel() // int(K)
+    G, M_cap, N, K = int(G), int(M_cap), int(N), int(K)
+    m, g = max(M_cap, 0), max(G, 0)
+    cap_n = mxfp4_cols_scale_capacity(M_cap, N, G) if N > 0 and G > 0 else 0
+    cap_k = mxfp4_cols_scale_capacity(M_cap, K, G) if K > 0 and G > 0 else 0
+    _need("mxfp4_fp8_grouped_gemm_wgrad",
+          [(dyT, m * max(N, 0), "dyT", _FP8), (dyT_scales, max(cap_n, 0), "dyT_scales", _U8),
+           (xT, m * max(K, 0), "xT", _FP8), (xT_scales, max(cap_k, 0), "xT_scales", _U8),
+           (dw, 2 * g * max(N, 0) * max(K, 0), "dw", ("bfloat16", "int16", "uint16")),
+           (offs, 4 * (G + 1), "group_offsets", ("int32",))])
+    lib = load_library()
+    _check(lib.mxfp4_fp8_grouped_gemm_wgrad(_ptr(dyT), _ptr(dyT_scales), _ptr(xT), _ptr(xT_scales), _ptr(dw),
+                                            _ptr(offs), G, M_cap, N, K, _stream(stream)),
+           "mxfp4_fp8_grouped_gemm_wgrad")
 
 
 def mxfp4_validate_offsets(offs, G=None, M_cap=None, stream=None) -> bool:

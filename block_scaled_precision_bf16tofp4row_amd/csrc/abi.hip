@@ -16,6 +16,8 @@ hipError_t launch_fp8_cols(const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, c
 int64_t cols_block_capacity(int64_t M_cap, int32_t G);
 hipError_t launch_fp8_gemm(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*,
                            const int32_t*, int32_t, int64_t, int64_t, int64_t, hipStream_t);
+hipError_t launch_fp8_wgrad(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*,
+                            const int32_t*, int32_t, int64_t, int64_t, int64_t, int64_t, hipStream_t);
 hipError_t launch_fp8q_cols(const uint16_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
                             int64_t, hipStream_t);
 hipError_t launch_fp8q_rows(const uint16_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
@@ -32,6 +34,8 @@ constexpr int64_t kMaxElems = (int64_t)1 << 50;
 constexpr int64_t kMaxColsK = (int64_t)1 << 24;
 // Largest N and K of the GEMM (its per-tile byte offsets are 32-bit).
 constexpr int64_t kMaxGemmDim = (int64_t)1 << 20;
+// Largest width * M_cap of a weight-gradient operand (its byte offsets are 32-bit).
+constexpr int64_t kMaxWgradBytes = (int64_t)1 << 30;
 
 mxfp4_status check_shape(int32_t G, int64_t M_cap, int64_t K, int64_t k_multiple)
 {
@@ -169,6 +173,29 @@ mxfp4_status mxfp4_fp8_grouped_gemm(const uint8_t* a_e4m3, const uint8_t* a_scal
         return MXFP4_OK;
     return from_hip(mxfp4::launch_fp8_gemm(a_e4m3, a_scales, w_e4m3, w_scales, y_bf16, group_offsets,
                                            G, M_cap, N, K, stream));
+}
+
+mxfp4_status mxfp4_fp8_grouped_gemm_wgrad(const uint8_t* dyT_e4m3, const uint8_t* dyT_scales,
+                                          const uint8_t* xT_e4m3, const uint8_t* xT_scales, uint16_t* dw_bf16,
+                                          const int32_t* group_offsets, int32_t G, int64_t M_cap, int64_t N,
+                                          int64_t K, hipStream_t stream)
+{
+    if (!dyT_e4m3 || !dyT_scales || !xT_e4m3 || !xT_scales || !dw_bf16 || !group_offsets)
+        return MXFP4_ERR_NULL;
+    mxfp4_status st = check_shape(G, M_cap, K, 256);
+    if (st != MXFP4_OK)
+        return st;
+    if (N <= 0 || N % 256 != 0 || N > kMaxGemmDim || K > kMaxGemmDim)
+        return MXFP4_ERR_SHAPE;
+    if (M_cap > 0 && (N > kMaxWgradBytes / M_cap || K > kMaxWgradBytes / M_cap))
+        return MXFP4_ERR_SHAPE;
+    if ((int64_t)G > kMaxElems / (N * K))             // output elements
+        return MXFP4_ERR_SHAPE;
+    if (!aligned(dyT_e4m3, 16) || !aligned(dyT_scales, 16) || !aligned(xT_e4m3, 16) ||
+        !aligned(xT_scales, 16) || !aligned(dw_bf16, 16) || !aligned(group_offsets, 4))
+        return MXFP4_ERR_ALIGN;
+    return from_hip(mxfp4::launch_fp8_wgrad(dyT_e4m3, dyT_scales, xT_e4m3, xT_scales, dw_bf16, group_offsets, G,
+                                            M_cap, mxfp4::cols_block_capacity(M_cap, G), N, K, stream));
 }
 
 int64_t mxfp4_cols_scale_capacity(int64_t M_cap, int64_t K, int32_t G)

@@ -149,6 +149,29 @@ mxfp4_status mxfp4_fp8_grouped_gemm(const uint8_t* a_e4m3, const uint8_t* a_scal
                                     uint16_t* y_bf16, const int32_t* group_offsets, int32_t G,
                                     int64_t M_cap, int64_t N, int64_t K, hipStream_t stream);
 
+/* Expert-grouped FP8 GEMM, weight gradient (technical summary section 2: compute stays
+ * FP8 on the block-scaled pipeline, item 1; the column conversion fuses the transpose
+ * into the Wgrad operands over ragged experts with no padding, item 3).  For expert g
+ * with M_g = offs[g+1] - offs[g] tokens, B_g = the 128-token blocks of the experts
+ * before it, and b = m / 128:
+ *   dW[g, n, k] = bf16( sum_{m < M_g} dY_g[m, n] 2^(sdy_g[b, n]-127) * X_g[m, k] 2^(sx_g[b, k]-127) )
+ *   dyT_e4m3    column layout for width N, as mxfp4_bf16_to_fp8_cols_ragged writes it
+ *               for a gradient [M_cap, N]: expert g [N, M_g] at byte N*offs[g];
+ *               capacity N*M_cap bytes.
+ *   dyT_scales  [nb_g, N] at byte N*B_g; capacity mxfp4_cols_scale_capacity(M_cap, N, G).
+ *   xT_e4m3     the same layout for width K, as mxfp4_to_fp8_cols_ragged writes it for
+ *               the activations [M_cap, K]; capacity K*M_cap bytes.
+ *   xT_scales   [nb_g, K] at byte K*B_g; capacity mxfp4_cols_scale_capacity(M_cap, K, G).
+ *   dw_bf16     [G, N, K] BF16 bits; every element is written (0 for an expert with no
+ *               tokens, also when M_cap == 0).
+ *   Accumulation and rounding as in mxfp4_fp8_grouped_gemm.  Reads stay within the
+ *   stated capacities.  N and K must be multiples of 256 and at most 2^20, and N*M_cap
+ *   and K*M_cap at most 2^30 (else MXFP4_ERR_SHAPE).  No NaN bytes in the operands. */
+mxfp4_status mxfp4_fp8_grouped_gemm_wgrad(const uint8_t* dyT_e4m3, const uint8_t* dyT_scales,
+                                          const uint8_t* xT_e4m3, const uint8_t* xT_scales,
+                                          uint16_t* dw_bf16, const int32_t* group_offsets, int32_t G,
+                                          int64_t M_cap, int64_t N, int64_t K, hipStream_t stream);
+
 /* Bytes the column-layout scale buffer needs for any offsets with offs[G] <= M_cap:
  * K * (ceil(M_cap / 128) + G).  Returns -1 for invalid sizes. */
 int64_t mxfp4_cols_scale_capacity(int64_t M_cap, int64_t K, int32_t G);

@@ -165,6 +165,31 @@ def test_grouped_gemm_argument_errors(lib):
     assert _gm(lib, M=0) == mx.MXFP4_OK
 
 
+def _wg(lib, dy=A, sdy=A2, x=A3, sx=A4, dw=A, o=OFFS, G=1, M=4, N=256, K=256):
+    return lib.mxfp4_fp8_grouped_gemm_wgrad(dy, sdy, x, sx, dw, o, G, M, N, K, None)
+
+
+def test_wgrad_gemm_argument_errors(lib):
+    # every case is rejected before anything is enqueued (the valid call, which writes
+    # the zero gradient even for M_cap == 0, needs a GPU)
+    for kw in ("dy", "sdy", "x", "sx", "dw", "o"):
+        assert _wg(lib, **{kw: None}) == mx.MXFP4_ERR_NULL
+    assert _wg(lib, K=128) == mx.MXFP4_ERR_SHAPE          # K % 256
+    assert _wg(lib, N=128) == mx.MXFP4_ERR_SHAPE          # N % 256
+    assert _wg(lib, N=0) == mx.MXFP4_ERR_SHAPE
+    assert _wg(lib, K=(1 << 20) + 256) == mx.MXFP4_ERR_SHAPE
+    assert _wg(lib, N=(1 << 20) + 256) == mx.MXFP4_ERR_SHAPE
+    assert _wg(lib, M=(1 << 22) + 1, N=256) == mx.MXFP4_ERR_SHAPE      # N * M_cap > 2^30
+    assert _wg(lib, M=(1 << 21) + 1, K=512) == mx.MXFP4_ERR_SHAPE      # K * M_cap > 2^30
+    assert _wg(lib, G=0) == mx.MXFP4_ERR_SHAPE
+    assert _wg(lib, M=-1) == mx.MXFP4_ERR_SHAPE
+    assert _wg(lib, dy=A + 4) == mx.MXFP4_ERR_ALIGN
+    assert _wg(lib, x=A3 + 8) == mx.MXFP4_ERR_ALIGN
+    assert _wg(lib, sx=A4 + 1) == mx.MXFP4_ERR_ALIGN
+    assert _wg(lib, dw=A + 2) == mx.MXFP4_ERR_ALIGN
+    assert _wg(lib, o=OFFS + 2) == mx.MXFP4_ERR_ALIGN
+
+
 def test_validate_offsets_argument_errors(lib):
     assert lib.mxfp4_validate_offsets(None, 1, 4, None) == mx.MXFP4_ERR_NULL
     assert lib.mxfp4_validate_offsets(OFFS, 0, 4, None) == mx.MXFP4_ERR_SHAPE
