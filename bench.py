@@ -21,7 +21,9 @@ moving the same bytes.  ``backward`` times the FP8 gradient quantizer
 (mxfp4_bf16_to_fp8_rows and mxfp4_bf16_to_fp8_cols_ragged) on the same segments,
 outside ``value``; the scrubbed medians include it.  ``gemm`` times the forward expert
 GEMM (mxfp4_fp8_grouped_gemm) on the hidden segment's FP8 row output against
-per-expert E4M3 weights ([8, 4096, 7168], synthetic), with its MFMA roofline.  ``cpu_baseline`` times the CPU oracle on a bounded
+per-expert E4M3 weights ([8, 4096, 7168], synthetic), with its MFMA roofline; ``wgrad``
+times the weight-gradient GEMM (mxfp4_fp8_grouped_gemm_wgrad) on the hidden segment's
+FP8 column output and a column-quantized synthetic [M, 4096] gradient.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same workload on this host (all allowed threads, and one thread).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload config5] [--no-scrubbed]
@@ -53,6 +55,7 @@ KERNEL_SOURCES = {
     "fp8q_rows": ["fp8q.hip", "common.h"],
     "fp8q_cols": ["fp8q_cols.hip", "strips.h", "common.h"],
     "gemm": ["gemm.hip", "strips.h", "common.h"],
+    "wgrad": ["wgrad.hip", "strips.h", "common.h"],
 }
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix throughput, vendor datasheet
 
@@ -351,6 +354,30 @@ def main():
     achieved = dom["GBps"]
     traffic = read_traffic(dom["kernel"], w.name, dom["segment"])
 
+    def time_launches(fn):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        tev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a_, b_ in tev:
+            a_.record()
+            fn()
+            b_.record()
+        torch.cuda.synchronize()
+        return [a_.elapsed_time(b_) for a_, b_ in tev]
+
+    def mfma_entry(what, shape, flop, ms):
+        us = float(np.mean(ms)) * 1000.0
+        tflops = flop / (us * 1e-6) / 1e12
+        log(f"[bench] {what}: {us:.1f} us, {tflops:.0f} TFLOP/s ({tflops / FP8_MFMA_PEAK_TFLOPS:.1%} of the FP8 peak)")
+        return {
+            "what": what, "shape": shape, "flop_per_launch": flop,
+            "mean_us": round(us, 2), "median_us": round(float(np.median(ms)) * 1000.0, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP8_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / FP8_MFMA_PEAK_TFLOPS, 4)},
+        }
+
     # the forward expert GEMM on the hidden segment's FP8 row output (not in `value`)
     gemm = None
     if args.gemm_n > 0 and "y" in segs[0]:
@@ -363,32 +390,31 @@ def main():
         wq = torch.where((wq & 0x7F) == 0x7F, wq - 1, wq).to(torch.uint8)        # no NaN bytes
         wqs = torch.randint(118, 136, (Gg, Ng, Kg // 128), device=dev, dtype=torch.int32, generator=gen).to(torch.uint8)
         yg = torch.empty((sg.M_cap, Ng), dtype=torch.int16, device=dev)
-        gfn = lambda: mx.mxfp4_fp8_grouped_gemm(seg0["y"], seg0["ys"], wq, wqs, yg, seg0["offs"])
-        for _ in range(max(1, args.warmup)):
-            gfn()
-        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for a_, b_ in gev:
-            a_.record()
-            gfn()
-            b_.record()
-        torch.cuda.synchronize()
-        gms = [a_.elapsed_time(b_) for a_, b_ in gev]
-        flop = 2.0 * sg.M_tot * Ng * Kg
-        g_us = float(np.mean(gms)) * 1000.0
-        tflops = flop / (g_us * 1e-6) / 1e12
-        gemm = {
-            "what": "forward expert GEMM: hidden-segment FP8 row output x per-expert E4M3 weights -> BF16",
-            "shape": {"M_tot": sg.M_tot, "K": Kg, "N": Ng, "G": Gg},
-            "flop_per_launch": flop,
-            "mean_us": round(g_us, 2), "median_us": round(float(np.median(gms)) * 1000.0, 2),
-            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP8_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / FP8_MFMA_PEAK_TFLOPS, 4)},
-        }
-        log(f"[bench] expert GEMM {sg.M_tot} x {Kg} x {Ng} over {Gg} experts: {g_us:.1f} us, "
-            f"{tflops:.0f} TFLOP/s ({tflops / FP8_MFMA_PEAK_TFLOPS:.1%} of the FP8 peak)")
+        gms = time_launches(lambda: mx.mxfp4_fp8_grouped_gemm(seg0["y"], seg0["ys"], wq, wqs, yg, seg0["offs"]))
+        gemm = mfma_entry("forward expert GEMM: hidden-segment FP8 row output x per-expert E4M3 weights -> BF16",
+                          {"M_tot": sg.M_tot, "K": Kg, "N": Ng, "G": Gg}, 2.0 * sg.M_tot * Ng * Kg, gms)
         del wq, wqs, yg
+
+    # the weight-gradient GEMM on the hidden segment's FP8 column output and the column
+    # quantization of a synthetic [M_cap, N] BF16 gradient (not in `value`)
+    wgrad = None
+    if args.gemm_n > 0 and "yT" in segs[0]:
+        seg0 = segs[0]
+        sg = seg0["seg"]
+        Ng, Kg, Gg = int(args.gemm_n), sg.K, sg.G
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1)
+        grad = (torch.randn((sg.M_cap, Ng), device=dev, generator=gen) * 0.01).to(torch.bfloat16)
+        dyT, dysT = mx.alloc_cols_outputs(sg.M_cap, Ng, Gg, dev)
+        mx.mxfp4_bf16_to_fp8_cols_ragged(grad, dyT, dysT, seg0["offs"])
+        del grad
+        dw = torch.empty((Gg * Ng * Kg,), dtype=torch.int16, device=dev)
+        wms = time_launches(lambda: mx.mxfp4_fp8_grouped_gemm_wgrad(
+            dyT, dysT, seg0["yT"], seg0["ysT"], dw, seg0["offs"], N=Ng, K=Kg, G=Gg, M_cap=sg.M_cap))
+        wgrad = mfma_entry("weight-gradient GEMM: column-quantized [M, N] gradient x hidden-segment FP8 column "
+                           "output -> BF16 dW [G, N, K]",
+                           {"M_tot": sg.M_tot, "K": Kg, "N": Ng, "G": Gg}, 2.0 * sg.M_tot * Ng * Kg, wms)
+        del dyT, dysT, dw
 
     # the backward FP8 quantizer on the same segments, timed the same way (not in `value`)
     bsegs, blaunches = build_launches(mx, w, dev, torch, backward=True)
@@ -476,6 +502,7 @@ def main():
         "per_kernel": per_kernel,
         "backward": backward,
         "gemm": gemm,
+        "wgrad": wgrad,
         "per_config_scrubbed": None,
         "cpu_baseline": None,
     }
