@@ -17,9 +17,10 @@
 // operand row.  X^T rows are the first operand and dY^T rows the second, so a lane's
 // results are 4 consecutive k of one n (one 8-byte store into dW_g [N, K]).
 //
-// Work: a workgroup of 4 waves owns a 256 (n) x 256 (k) tile of one expert's dW and walks
-// the expert's tokens in steps of 128; wave (wm, wn) computes n 128 wm .. + 127 x
-// k 128 wn .. + 127 as 4 x 4 MFMA tiles (256 fp32 accumulators per lane).  A column row
+// Work: a workgroup of 8 waves (two per SIMD, so one wave's matrix work covers the
+// other's loads and LDS traffic) owns a 256 (n) x 256 (k) tile of one expert's dW and
+// walks the expert's tokens in steps of 128; wave (wm, wn) computes n 128 wm .. + 127 x
+// k 64 wn .. + 63 as 4 x 2 MFMA tiles (128 fp32 accumulators per lane).  A column row
 // has M_g bytes, so the 128-token piece of a row starts at any byte: a thread loads the
 // aligned 16 bytes at or below its 16-byte slice and the dword after them, and shifts
 // them into place with v_alignbyte by the row start's offset mod 4 (fixed per row).
@@ -39,7 +40,7 @@ typedef int wg_i32x8 __attribute__((ext_vector_type(8)));
 typedef float wg_f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 wg_bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWgThreads = 256;                   // 4 waves
+constexpr int kWgThreads = 512;                   // 8 waves, two per SIMD
 constexpr int kWT = 256;                          // n and k per workgroup tile
 constexpr int kWS = 128;                          // tokens per step (one scale block)
 constexpr int kWStage = 2 * kWT * kWS;            // bytes of one LDS buffer (64 KB)
@@ -116,32 +117,33 @@ __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
         strip_rsrc(sx + K * (int64_t)Bg, (uint64_t)K * (uint64_t)(scale_blocks_cap - Bg));
 
     // loader role: thread t takes the 16-byte slice c = t & 7 of the step's piece of
-    // local rows (t >> 3) + 32 i, i = 0..7, of both operands
+    // local rows (t >> 3) + 64 i, i = 0..3, of both operands
     const uint32_t lrow = (uint32_t)(tid >> 3), lchunk = (uint32_t)(tid & 7);
-    const uint32_t lds_w = lrow * kWS + 16 * (lchunk ^ ((lrow >> 1) & 7));   // + 32 i kWS
-    uint32_t o_dy[8], o_x[8];                     // byte offset of the slice at step 0
+    const uint32_t lds_w = lrow * kWS + 16 * (lchunk ^ ((lrow >> 1) & 7));   // + 64 i kWS
+    uint32_t o_dy[4], o_x[4];                     // byte offset of the slice at step 0
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        o_dy[i] = (uint32_t)(n0 + lrow + 32 * i) * Mg + 16 * lchunk;
-        o_x[i] = (uint32_t)(k0 + lrow + 32 * i) * Mg + 16 * lchunk;
+    for (int i = 0; i < 4; ++i) {
+        o_dy[i] = (uint32_t)(n0 + lrow + 64 * i) * Mg + 16 * lchunk;
+        o_x[i] = (uint32_t)(k0 + lrow + 64 * i) * Mg + 16 * lchunk;
     }
     // compute role: wave (wm, wn), lane (r, h)
     const int wm = wave & 1, wn = wave >> 1;
     const uint32_t r = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
     const uint32_t sw8 = (r >> 1) & 7;                                 // the swizzle of rows r + 32 x
-    uint32_t soff_x[4], soff_dy[4];               // scale bytes of the lane's rows
+    uint32_t soff_x[2], soff_dy[4];               // scale bytes of the lane's rows
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        soff_x[q] = (uint32_t)(k0 + 128 * wn + 32 * q + r);
+    for (int q = 0; q < 4; ++q)
         soff_dy[q] = (uint32_t)(n0 + 128 * wm + 32 * q + r);
-    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        soff_x[q] = (uint32_t)(k0 + 64 * wn + 32 * q + r);
 
-    u32x4 dq[8], xq[8];                           // staged slices (aligned 16 bytes)
-    uint32_t de[8], xe[8];                        // and the dword after them
+    u32x4 dq[4], xq[4];                           // staged slices (aligned 16 bytes)
+    uint32_t de[4], xe[4];                        // and the dword after them
     auto load_tiles = [&](uint32_t t) {
         const uint32_t step = t * kWS;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const uint32_t ad = (o_dy[i] + step) & ~3u, ax = (o_x[i] + step) & ~3u;
             dq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdy, (int)ad, 0, 0));
             de[i] = __builtin_amdgcn_raw_buffer_load_b32(rdy, (int)(ad + 16), 0, 0);
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
         uint8_t* const s_dy = lds + buf * kWStage;           // dY^T rows: bytes [0, 32 KB)
         uint8_t* const s_x = s_dy + kWT * kWS;                // X^T rows: bytes [32 KB, 64 KB)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const uint32_t sd = o_dy[i] & 3, sx_ = o_x[i] & 3;          // step * 128 keeps the byte offset mod 4
             const u32x4 q = dq[i], p = xq[i];
             const u32x4 vd = {__builtin_amdgcn_alignbyte(q.y, q.x, sd) & mask[0],
@@ -172,25 +174,26 @@ __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
                               __builtin_amdgcn_alignbyte(p.z, p.y, sx_) & mask[1],
                               __builtin_amdgcn_alignbyte(p.w, p.z, sx_) & mask[2],
                               __builtin_amdgcn_alignbyte(xe[i], p.w, sx_) & mask[3]};
-            *reinterpret_cast<u32x4*>(s_dy + lds_w + 32 * i * kWS) = vd;
-            *reinterpret_cast<u32x4*>(s_x + lds_w + 32 * i * kWS) = vx;
+            *reinterpret_cast<u32x4*>(s_dy + lds_w + 64 * i * kWS) = vd;
+            *reinterpret_cast<u32x4*>(s_x + lds_w + 64 * i * kWS) = vx;
         }
     };
-    uint32_t sc_x[4], sc_dy[4];                   // current step's scale bytes
-    uint32_t nx_x[4], nx_dy[4];
-    auto load_scales = [&](uint32_t t, uint32_t (&dx)[4], uint32_t (&ddy)[4]) {
+    uint32_t sc_x[2], sc_dy[4];                   // current step's scale bytes
+    uint32_t nx_x[2], nx_dy[4];
+    auto load_scales = [&](uint32_t t, uint32_t (&dx)[2], uint32_t (&ddy)[4]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            dx[q] = __builtin_amdgcn_raw_buffer_load_b8(rsx, (int)(soff_x[q] + t * (uint32_t)K), 0, 0);
+        for (int q = 0; q < 4; ++q)
             ddy[q] = __builtin_amdgcn_raw_buffer_load_b8(rsdy, (int)(soff_dy[q] + t * (uint32_t)N), 0, 0);
-        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            dx[q] = __builtin_amdgcn_raw_buffer_load_b8(rsx, (int)(soff_x[q] + t * (uint32_t)K), 0, 0);
     };
 
-    wg_f32x16 acc[4][4];
+    wg_f32x16 acc[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 2; ++nt)
             acc[mt][nt] = wg_f32x16{};
 
     if (T > 0) {                                  // uniform: an empty expert writes zeros
@@ -204,49 +207,53 @@ __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
             load_tiles(tn);
             load_scales(tn, nx_x, nx_dy);
             const uint8_t* const tdy = lds + (t & 1) * kWStage + (128 * wm) * kWS;
-            const uint8_t* const tx = lds + (t & 1) * kWStage + kWT * kWS + (128 * wn) * kWS;
+            const uint8_t* const tx = lds + (t & 1) * kWStage + kWT * kWS + (64 * wn) * kWS;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 const uint32_t c0 = 16 * ((4 * kh + h) ^ sw8), c1 = 16 * ((4 * kh + 2 + h) ^ sw8);
-                wg_i32x8 fx[4], fdy[4];
+                wg_i32x8 fx[2], fdy[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < 2; ++q) {
                     const uint8_t* const rowp_x = tx + (32 * q + r) * kWS;
-                    const uint8_t* const rowp_d = tdy + (32 * q + r) * kWS;
                     const u32x4 x0 = *reinterpret_cast<const u32x4*>(rowp_x + c0);
                     const u32x4 x1 = *reinterpret_cast<const u32x4*>(rowp_x + c1);
-                    const u32x4 d0 = *reinterpret_cast<const u32x4*>(rowp_d + c0);
-                    const u32x4 d1 = *reinterpret_cast<const u32x4*>(rowp_d + c1);
                     fx[q] = wg_i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint8_t* const rowp_d = tdy + (32 * q + r) * kWS;
+                    const u32x4 d0 = *reinterpret_cast<const u32x4*>(rowp_d + c0);
+                    const u32x4 d1 = *reinterpret_cast<const u32x4*>(rowp_d + c1);
                     fdy[q] = wg_i32x8{(int)d0.x, (int)d0.y, (int)d0.z, (int)d0.w,
                                       (int)d1.x, (int)d1.y, (int)d1.z, (int)d1.w};
                 }
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
+                    for (int nt = 0; nt < 2; ++nt)
                         acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                             fx[nt], fdy[mt], acc[mt][nt], 0, 0, 0, (int)sc_x[nt], 0, (int)sc_dy[mt]);
             }
             // the other buffer was last read in step t - 1, before the previous barrier
             store_tiles((t + 1) & 1, tn);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                sc_x[q] = nx_x[q];
+            for (int q = 0; q < 4; ++q)
                 sc_dy[q] = nx_dy[q];
-            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                sc_x[q] = nx_x[q];
             __syncthreads();
         }
     }
 
     // epilogue: lane (r, h) of MFMA tile (mt, nt) holds n = 128 wm + 32 mt + r and
-    // k = 128 wn + 32 nt + 8 q + 4 h + (0..3) in values 4q .. 4q + 3
+    // k = 64 wn + 32 nt + 8 q + 4 h + (0..3) in values 4q .. 4q + 3
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        uint16_t* const yrow = dw + ((int64_t)g * N + n0 + 128 * wm + 32 * mt + r) * K + k0 + 128 * wn + 4 * h;
+        uint16_t* const yrow = dw + ((int64_t)g * N + n0 + 128 * wm + 32 * mt + r) * K + k0 + 64 * wn + 4 * h;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const wg_f32x16& v = acc[mt][nt];
