@@ -72,6 +72,13 @@ def _load():
     lib.oracle_fp8q_cols.argtypes = [P, P, ctypes.c_int32, I64, I64, I64, P, P]
     lib.oracle_fp8_gemm_at.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, P, P, I64, P, P, P]
     lib.oracle_fp8_wgrad_at.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, P, P, P, I64, P, P, P]
+    F = ctypes.c_float
+    lib.oracle_nvfp4_block.argtypes = [P, F, P, P]
+    lib.oracle_nvfp4_amax.argtypes = [P, I64, I64, I64]
+    lib.oracle_nvfp4_amax.restype = F
+    lib.oracle_nvfp4_encode_scale.argtypes = [F]
+    lib.oracle_nvfp4_encode_scale.restype = F
+    lib.oracle_nvfp4_rows.argtypes = [P, I64, I64, I64, F, P, P]
     lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_value.restype = ctypes.c_double
     lib.oracle_bf16_round.argtypes = [ctypes.c_double]
@@ -162,6 +169,50 @@ def quantize_rows(x_bits: np.ndarray, rows: int | None = None, threads: int = 1,
 
     _run_ranges(run, _ranges(rows, threads * 4), threads)
     return codes, scales
+
+
+def nvfp4_block(x16_bits, t: float):
+    """One 16-element NVFP4 block with the tensor's FP32 encode scale t:
+    (8 packed code bytes, E4M3 scale byte)."""
+    lib = _load()
+    x = np.ascontiguousarray(x16_bits, dtype=np.uint16)
+    assert x.size == 16
+    packed = np.zeros(8, np.uint8)
+    sc = np.zeros(1, np.uint8)
+    lib.oracle_nvfp4_block(_ptr(x), float(t), _ptr(packed), _ptr(sc))
+    return packed, int(sc[0])
+
+
+def nvfp4_encode_scale(amax: float) -> float:
+    """FP32(2688 / amax) (1 for 0, FLT_MAX on overflow), as an FP32 value."""
+    return float(_load().oracle_nvfp4_encode_scale(float(amax)))
+
+
+def nvfp4_quantize_rows(x_bits: np.ndarray, rows: int | None = None, threads: int = 1):
+    """NVFP4 over rows [0, rows) of BF16 bits [M, K] (K a multiple of 16):
+    (codes [M, K/2], E4M3 block scales [M, K/16], tensor amax, FP32 encode scale t);
+    rows past `rows` stay zero."""
+    lib = _load()
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    assert K % 16 == 0
+    rows = M if rows is None else rows
+    codes = np.zeros((M, K // 2), np.uint8)
+    scales = np.zeros((M, K // 16), np.uint8)
+    parts = []
+
+    def run_amax(r):
+        parts.append(float(lib.oracle_nvfp4_amax(_ptr(x_bits), K, r[0], r[1])))
+
+    _run_ranges(run_amax, _ranges(rows, threads * 4), threads)
+    amax = max(parts) if parts else 0.0
+    t = nvfp4_encode_scale(amax)
+
+    def run(r):
+        lib.oracle_nvfp4_rows(_ptr(x_bits), K, r[0], r[1], t, _ptr(codes), _ptr(scales))
+
+    _run_ranges(run, _ranges(rows, threads * 4), threads)
+    return codes, scales, amax, t
 
 
 def fp8_rows(codes: np.ndarray, scales: np.ndarray, rows: int | None = None,

@@ -31,6 +31,7 @@
  *   - the sign of zero is kept (a negative value that rounds to 0 gives -0);
  *   - element 2i goes in the low nibble of byte i, element 2i+1 in the high nibble.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -475,6 +476,89 @@ void oracle_fp8_wgrad_at(const uint8_t *dyT, const uint8_t *dyT_scales, const ui
         if (absum)
             absum[i] = t;
     }
+}
+
+/* ---- NVFP4 variant quantizer ------------------------------------------- */
+/* Page "Train models faster with JAX and MaxText using NVFP4 on NVIDIA Blackwell",
+ * section on the NVFP4 pre-training recipe: E2M1 values in 16-element microblocks, one
+ * E4M3 scale per block (mantissa bits, not a power of two) under one FP32 scale per
+ * tensor; activations and weights round to nearest even.  Reading (the page gives no
+ * formulas), in FP32 the way the recipe's GPU implementation computes it:
+ *   amax_t = max |x| over the tensor (the routed rows);
+ *   t      = FP32(2688 / amax_t), 2688 = 6 * 448 (E2M1 max times E4M3 max), so the
+ *            largest block maps to the largest E4M3 scale; 1 for an all-zero tensor,
+ *            FLT_MAX where the quotient overflows;
+ *   block  : amax_b over its 16 elements; S = E4M3(FP32(FP32(amax_b / 6) * t)), nearest
+ *            even with subnormals, saturating at 448;
+ *            e = FP32(t / E4M3value(S)) (0 when S is 0, FLT_MAX where it overflows);
+ *   element: y = FP32(x * e); code = E2M1(|y|) nearest even, saturating at 6, sign of x
+ *            kept (a negative that rounds to 0 is 0x8).
+ * A value decodes as E2M1value(code) * E4M3value(S) / t.  Inputs are finite. */
+
+/* The tensor's FP32 encode scale for its largest magnitude. */
+static float nvfp4_encode_scale(float amax)
+{
+    if (amax == 0.0f)
+        return 1.0f;
+    float t = 2688.0f / amax;
+    return t > FLT_MAX ? FLT_MAX : t;
+}
+
+/* One 16-element block with the tensor's encode scale t: 8 packed bytes + 1 E4M3
+ * scale byte. */
+void oracle_nvfp4_block(const uint16_t *x, float t, uint8_t *packed8, uint8_t *scale)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+        float a = fabsf((float)bf16_value(x[i]));
+        if (a > amax)
+            amax = a;
+    }
+    float sb = amax / 6.0f;
+    sb = sb * t;
+    int S = e4m3_encode((double)sb);
+    *scale = (uint8_t)S;
+    float e = 0.0f;
+    if (S != 0) {
+        e = t / (float)e4m3_value((uint8_t)S);
+        if (e > FLT_MAX)
+            e = FLT_MAX;
+    }
+    uint8_t codes[16];
+    for (int i = 0; i < 16; ++i) {
+        float y = (float)bf16_value(x[i]) * e;
+        int c = fabsf(y) >= 6.0f ? 7 : e2m1_encode((double)fabsf(y));
+        if (signbit(y))
+            c |= 8;
+        codes[i] = (uint8_t)c;
+    }
+    for (int i = 0; i < 8; ++i)
+        packed8[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+}
+
+/* max |x| over rows [row_begin, row_end) of a BF16 matrix with K columns. */
+float oracle_nvfp4_amax(const uint16_t *x, int64_t K, int64_t row_begin, int64_t row_end)
+{
+    float amax = 0.0f;
+    for (int64_t i = row_begin * K; i < row_end * K; ++i) {
+        float a = fabsf((float)bf16_value(x[i]));
+        if (a > amax)
+            amax = a;
+    }
+    return amax;
+}
+
+float oracle_nvfp4_encode_scale(float amax) { return nvfp4_encode_scale(amax); }
+
+/* Rows [row_begin, row_end) with the tensor's encode scale t (K a multiple of 16):
+ * codes [*, K/2], scales [*, K/16]. */
+void oracle_nvfp4_rows(const uint16_t *x, int64_t K, int64_t row_begin, int64_t row_end, float t,
+                       uint8_t *codes, uint8_t *scales)
+{
+    int64_t nb = K / 16;
+    for (int64_t m = row_begin; m < row_end; ++m)
+        for (int64_t j = 0; j < nb; ++j)
+            oracle_nvfp4_block(x + m * K + 16 * j, t, codes + m * (K / 2) + 8 * j, scales + m * nb + j);
 }
 
 /* ---- small helpers exported for the pins ------------------------------- */

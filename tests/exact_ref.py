@@ -229,3 +229,42 @@ def fp8q_cols(x_bits: np.ndarray, offs: np.ndarray):
                     yT[K * r0 + k * Mg + (m - r0)] = code | (0x80 if int(x_bits[m, k]) & 0x8000 else 0)
         B += nb[g]
     return yT, ys
+
+
+def nvfp4_rows(x_bits: np.ndarray):
+    """NVFP4 by the FP32 steps of the recipe (numpy float32 arithmetic) with the
+    nearest-value encoders above: (codes [M, K/2], E4M3 scales [M, K/16], t)."""
+    M, K = x_bits.shape
+    xf = (np.asarray(x_bits, np.uint32) << 16).view(np.float32)
+    big = np.float32(np.finfo(np.float32).max)
+    amax = np.float32(np.max(np.abs(xf))) if xf.size else np.float32(0)
+    with np.errstate(over="ignore", divide="ignore"):
+        t = np.float32(1) if amax == 0 else np.float32(np.float32(2688) / amax)
+    if not np.isfinite(t):
+        t = big
+    e4 = _e4m3()
+    codes = np.zeros((M, K // 2), np.uint8)
+    scales = np.zeros((M, K // 16), np.uint8)
+    for m in range(M):
+        for j in range(K // 16):
+            blk = xf[m, 16 * j:16 * j + 16]
+            ab = np.float32(np.max(np.abs(blk)))
+            sb = np.float32(np.float32(ab / np.float32(6)) * t)
+            S = e4m3_encode_saturating(Fraction(float(sb)))
+            scales[m, j] = S
+            if S == 0:
+                e = np.float32(0)
+            else:
+                with np.errstate(over="ignore"):
+                    e = np.float32(t / np.float32(float(e4[S])))
+                if not np.isfinite(e):
+                    e = big
+            for i in range(16):
+                with np.errstate(over="ignore"):
+                    y = np.float32(blk[i] * e)
+                c = e2m1_encode(Fraction(abs(float(y)))) if np.isfinite(y) else 7
+                if np.signbit(y):
+                    c |= 8
+                k = 16 * j + i
+                codes[m, k // 2] |= c << (4 * (k & 1))
+    return codes, scales, t

@@ -18,6 +18,7 @@ import torch
 
 import exact_ref
 import oracle
+import workloads
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "formats.json")
 
@@ -840,3 +841,101 @@ def test_fp8_wgrad_block_scale_moves_only_its_block():
     keep[n] = False
     np.testing.assert_array_equal(e1[0, keep], e0[0, keep])
     np.testing.assert_array_equal(e1[1], e0[1])
+
+
+# ---- NVFP4 variant quantizer ------------------------------------------------------
+
+def _nvfp4_bits(rng, M, K, kind):
+    if kind == "normal":
+        v = rng.standard_normal((M, K)).astype(np.float32)
+    elif kind == "wide":          # magnitudes over many binades, blocks of very different size
+        v = (rng.standard_normal((M, K)) * 2.0 ** rng.integers(-30, 30, (M, K // 16)).repeat(16, axis=1)).astype(np.float32)
+    elif kind == "e2m1grid":      # values on scaled E2M1 grids and their midpoints (rounding ties)
+        grid = np.array([0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6], np.float32)
+        v = rng.choice(grid, (M, K)) * rng.choice([-1, 1], (M, K)).astype(np.float32)
+        v = v * (2.0 ** rng.integers(-3, 4, (M, K // 16))).repeat(16, axis=1).astype(np.float32)
+    elif kind == "tiny":          # a tensor whose scale quotient overflows FP32
+        v = (rng.standard_normal((M, K)) * 2.0 ** -120).astype(np.float32)
+    else:
+        raise ValueError(kind)
+    return workloads.to_bf16_bits(v)
+
+
+@pytest.mark.parametrize("kind", ["normal", "wide", "e2m1grid", "tiny"])
+def test_nvfp4_matches_exact_reference(kind):
+    rng = np.random.default_rng({"normal": 71, "wide": 72, "e2m1grid": 73, "tiny": 74}[kind])
+    x = _nvfp4_bits(rng, 6, 64, kind)
+    x[0, :16] = 0                                             # an all-zero block
+    x[1, 16:32] |= 0x8000                                     # a negative block
+    codes, scales, amax, t = oracle.nvfp4_quantize_rows(x, threads=2)
+    c_ref, s_ref, t_ref = exact_ref.nvfp4_rows(x)
+    assert np.float32(t) == t_ref
+    np.testing.assert_array_equal(scales, s_ref)
+    np.testing.assert_array_equal(codes, c_ref)
+
+
+def test_nvfp4_hand_values():
+    # amax 2688 gives t = 1 exactly; a block with max 6 gets scale 1.0 (0x38) and
+    # E2M1 values encode exactly; the 2688 block gets the largest scale 448 (0x7E)
+    vals = np.zeros((1, 32), np.float32)
+    vals[0, :8] = [6, -4, 3, 2, 1.5, 1, 0.5, -0.0]
+    vals[0, 16] = 2688
+    vals[0, 17] = -1344
+    x = workloads.to_bf16_bits(vals)
+    codes, scales, amax, t = oracle.nvfp4_quantize_rows(x)
+    assert amax == 2688 and t == 1.0
+    assert scales[0, 0] == 0x38 and scales[0, 1] == 0x7E
+    assert list(codes[0, :4]) == [0x7 | (0xE << 4), 0x5 | (0x4 << 4), 0x3 | (0x2 << 4), 0x1 | (0x8 << 4)]
+    assert codes[0, 8] == 0x7 | (0xD << 4)                    # 2688 / 448 = 6, -1344 / 448 = -3
+    assert np.all(codes[0, 4:8] == 0) and np.all(codes[0, 9:] == 0)
+
+
+def test_nvfp4_all_zero_tensor():
+    x = np.zeros((2, 32), np.uint16)
+    codes, scales, amax, t = oracle.nvfp4_quantize_rows(x)
+    assert amax == 0 and t == 1.0 and not codes.any() and not scales.any()
+
+
+def test_nvfp4_scale_is_the_torch_e4m3_cast():
+    """The block scale byte is the FP32 quotient cast to E4M3FN by torch (nearest even),
+    for every block whose quotient is in range."""
+    rng = np.random.default_rng(75)
+    x = _nvfp4_bits(rng, 8, 256, "wide")
+    codes, scales, amax, t = oracle.nvfp4_quantize_rows(x)
+    xf = (x.astype(np.uint32) << 16).view(np.float32).reshape(8, 16, 16)
+    ab = np.abs(xf).max(axis=2).astype(np.float32)
+    sb = ((ab / np.float32(6)).astype(np.float32) * np.float32(t)).astype(np.float32)
+    ok = sb <= 448
+    cast = torch.from_numpy(sb).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(scales[ok], cast[ok])
+    assert np.all(scales[~ok] == 0x7E)
+
+
+def test_nvfp4_power_of_two_scaling_leaves_codes_and_scales():
+    rng = np.random.default_rng(76)
+    x = _nvfp4_bits(rng, 4, 128, "normal")
+    c0, s0, a0, t0 = oracle.nvfp4_quantize_rows(x)
+    for k in (-20, -3, 5, 40):
+        xs = workloads.to_bf16_bits(((x.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** k)))
+        c1, s1, a1, t1 = oracle.nvfp4_quantize_rows(xs)
+        np.testing.assert_array_equal(c1, c0)
+        np.testing.assert_array_equal(s1, s0)
+        assert t1 == t0 * 2.0 ** -k
+
+
+def test_nvfp4_block_maxima():
+    """The block holding the tensor's largest magnitude gets the largest scale 448, and
+    every block with a normal E4M3 scale encodes its largest element as 6 (code 7)."""
+    rng = np.random.default_rng(77)
+    x = _nvfp4_bits(rng, 8, 256, "wide")
+    codes, scales, amax, t = oracle.nvfp4_quantize_rows(x)
+    xf = np.abs((x.astype(np.uint32) << 16).view(np.float32)).reshape(8, 16, 16)
+    blk_max = xf.max(axis=2)
+    top = np.argwhere(blk_max == amax)
+    assert top.size and all(scales[m, j] == 0x7E for m, j in top)
+    nib = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(8, 16, 16) & 7
+    arg = xf.argmax(axis=2)
+    for m in range(8):
+        for j in range(16):
+            if 0x08 <= scales[m, j] < 0x7E:
+                assert nib[m, j, arg[m, j]] == 7, (m, j)
