@@ -10,6 +10,7 @@ technical summary section 2 (Methodology), items 1-3.
 The binding has the same names as the C ABI:
 
 * ``mxfp4_quantize_rows(x, codes, scales, offs, ...)``
+* ``mxfp4_nvfp4_quantize_rows(x, codes, scales, tensor_amax, offs, ...)`` (NVFP4 variant)
 * ``mxfp4_to_fp8_rows(codes, scales, y, y_scales, offs, ...)``
 * ``mxfp4_to_fp8_cols_ragged(codes, scales, yT, yT_scales, offs, ...)``
 * ``mxfp4_bf16_to_fp8_rows(x, y, y_scales, offs, ...)`` and
@@ -44,6 +45,7 @@ MXFP4_ERR_HIP = 4
 
 EXPORTED = (
     "mxfp4_quantize_rows",
+    "mxfp4_nvfp4_quantize_rows",
     "mxfp4_to_fp8_rows",
     "mxfp4_to_fp8_cols_ragged",
     "mxfp4_bf16_to_fp8_rows",
@@ -89,6 +91,8 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_fp8_grouped_gemm.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
     lib.mxfp4_fp8_grouped_gemm.restype = st
     lib.mxfp4_fp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
+    lib.mxfp4_nvfp4_quantize_rows.argtypes = [P, P, P, P, P, I32, I64, I64, P]
+    lib.mxfp4_nvfp4_quantize_rows.restype = st
     lib.mxfp4_fp8_grouped_gemm_wgrad.restype = st
     lib.mxfp4_cols_scale_capacity.argtypes = [I64, I64, I32]
     lib.mxfp4_cols_scale_capacity.restype = I64
@@ -280,6 +284,33 @@ def mxfp4_fp8_grouped_gemm_wgrad(dyT, dyT_scales, xT, xT_scales, dw, offs, N, K,
     _check(lib.mxfp4_fp8_grouped_gemm_wgrad(_ptr(dyT), _ptr(dyT_scales), _ptr(xT), _ptr(xT_scales), _ptr(dw),
                                             _ptr(offs), G, M_cap, N, K, _stream(stream)),
            "mxfp4_fp8_grouped_gemm_wgrad")
+
+
+def mxfp4_nvfp4_quantize_rows(x, codes, scales, tensor_amax, offs, G=None, M_cap=None, K=None, stream=None):
+    """BF16 [M_cap, K] -> NVFP4 codes [M_cap, K/2], E4M3 block scales [M_cap, K/16] and
+    the tensor amax (one float32 on the GPU); see the header."""
+    if G is None:
+        G = offs.numel() - 1
+    if M_cap is None:
+        M_cap = x.shape[0]
+    if K is None:
+        K = x.shape[1]
+    G, M_cap, K = int(G), int(M_cap), int(K)
+    m, k = max(M_cap, 0), max(K, 0)
+    _need("mxfp4_nvfp4_quantize_rows", [(x, 2 * m * k, "x", ("bfloat16", "int16", "uint16")), (codes, m * k // 2, "codes", _U8),
+                                        (scales, m * k // 16, "scales", _U8),
+                                        (tensor_amax, 4, "tensor_amax", ("float32",)),
+                                        (offs, 4 * (G + 1), "group_offsets", ("int32",))])
+    lib = load_library()
+    _check(lib.mxfp4_nvfp4_quantize_rows(_ptr(x), _ptr(codes), _ptr(scales), _ptr(tensor_amax), _ptr(offs),
+                                         G, M_cap, K, _stream(stream)), "mxfp4_nvfp4_quantize_rows")
+
+
+def alloc_nvfp4_outputs(M_cap: int, K: int, device="cuda"):
+    import torch
+    return (torch.empty((max(1, M_cap), K // 2), dtype=torch.uint8, device=device),
+            torch.empty((max(1, M_cap), K // 16), dtype=torch.uint8, device=device),
+            torch.empty(1, dtype=torch.float32, device=device))
 
 
 def mxfp4_validate_offsets(offs, G=None, M_cap=None, stream=None) -> bool:

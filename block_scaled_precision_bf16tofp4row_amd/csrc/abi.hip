@@ -18,6 +18,8 @@ hipError_t launch_fp8_gemm(const uint8_t*, const uint8_t*, const uint8_t*, const
                            const int32_t*, int32_t, int64_t, int64_t, int64_t, hipStream_t);
 hipError_t launch_fp8_wgrad(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*,
                             const int32_t*, int32_t, int64_t, int64_t, int64_t, int64_t, hipStream_t);
+hipError_t launch_nvfp4_quantize_rows(const uint16_t*, uint8_t*, uint8_t*, float*, const int32_t*, int32_t,
+                                      int64_t, int64_t, hipStream_t);
 hipError_t launch_fp8q_cols(const uint16_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
                             int64_t, hipStream_t);
 hipError_t launch_fp8q_rows(const uint16_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
@@ -70,6 +72,22 @@ mxfp4_status mxfp4_quantize_rows(const uint16_t* x_bf16, uint8_t* codes, uint8_t
         return MXFP4_OK;
     return from_hip(mxfp4::launch_quantize_rows(x_bf16, codes, scales, group_offsets, G, M_cap,
                                                 K, stream));
+}
+
+mxfp4_status mxfp4_nvfp4_quantize_rows(const uint16_t* x_bf16, uint8_t* codes, uint8_t* scales_e4m3,
+                                       float* tensor_amax, const int32_t* group_offsets, int32_t G,
+                                       int64_t M_cap, int64_t K, hipStream_t stream)
+{
+    if (!x_bf16 || !codes || !scales_e4m3 || !tensor_amax || !group_offsets)
+        return MXFP4_ERR_NULL;
+    mxfp4_status st = check_shape(G, M_cap, K, 16);
+    if (st != MXFP4_OK)
+        return st;
+    if (!aligned(x_bf16, 16) || !aligned(codes, 16) || !aligned(scales_e4m3, 16) || !aligned(tensor_amax, 4) ||
+        !aligned(group_offsets, 4))
+        return MXFP4_ERR_ALIGN;
+    return from_hip(mxfp4::launch_nvfp4_quantize_rows(x_bf16, codes, scales_e4m3, tensor_amax, group_offsets, G,
+                                                      M_cap, K, stream));
 }
 
 mxfp4_status mxfp4_to_fp8_rows(const uint8_t* codes, const uint8_t* scales, uint8_t* y_e4m3,

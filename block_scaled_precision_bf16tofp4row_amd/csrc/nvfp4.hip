@@ -1,0 +1,185 @@
+// nvfp4.hip -- NVFP4 variant quantizer: BF16 -> E2M1 codes in 16-element blocks, one
+// E4M3 scale per block under one FP32 scale per tensor.
+//
+// Format: "Train models faster with JAX and MaxText using NVFP4 on NVIDIA Blackwell",
+// the NVFP4 pre-training recipe: 16-element microblocks (half the MXFP4 block), E4M3
+// block scales with mantissa bits instead of a power of two, under a per-tensor FP32
+// scale; activations and weights round to nearest even.  The arithmetic, in FP32 as the
+// recipe's GPU code takes it (the page gives the format, not the formulas):
+//   t = FP32(2688 / amax_tensor)    (2688 = 6 * 448; 1 for a zero tensor; FLT_MAX on
+//                                    overflow)
+//   S = E4M3(FP32(FP32(amax_b / 6) * t)), nearest even, subnormals, saturating at 448
+//   e = FP32(t / E4M3value(S))      (0 for S = 0; FLT_MAX on overflow)
+//   code = E2M1(FP32(x * e)), nearest even, saturating at 6, sign of x kept.
+// The FP32 divisions are IEEE (HIP's default correctly rounded division).
+//
+// Three launches on the stream: zero the amax word; a grid-stride max of |x| over the
+// routed rows, one vector atomic max per wave on the float bits (non-negative floats
+// order as their bit patterns); the quantizer, which reads the amax, derives t, and
+// converts.  The quantizer's layout is the MXFP4 quantizer's with 16-element blocks: a
+// lane takes 16 bytes (8 BF16), a lane pair one block, four loads per thread in flight;
+// the E4M3 scale is encoded with integer rounding on the FP32 bits (no conversion
+// instruction), and the elements with gfx950's scaled FP4 convert at scale 1 (FP32 in,
+// nearest even, saturating), after a clamp to [-8, 8] that keeps an overflowed product
+// finite without changing its code.
+#include <float.h>
+
+#include "strips.h"
+
+namespace mxfp4 {
+
+namespace {
+
+constexpr int kNvU = 4;                           // 16-byte chunks per thread in flight
+constexpr int kAmaxU = 8;
+
+__device__ __forceinline__ uint32_t nv_max_bits8(u32x4 v)
+{
+    u16x2 a = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
+    u16x2 b = __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu);
+    u16x2 c = __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu);
+    u16x2 d = __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu);
+    u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+    return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// Non-negative finite v -> E4M3FN magnitude code, nearest even (subnormals included),
+// saturating at 0x7E (448).
+__device__ __forceinline__ uint32_t e4m3_code_rne_sat(float v)
+{
+    if (v >= 448.0f)
+        return 0x7E;                               // [448, 464] rounds to 448, the rest saturates
+    const uint32_t bits = __float_as_uint(v);
+    if ((bits >> 23) < 121)                        // below 2^-6: multiples of 2^-9
+        return (uint32_t)__builtin_rintf(v * 512.0f);
+    const uint32_t r = bits + 0x7FFFFu + ((bits >> 20) & 1u);   // nearest even at 3 mantissa bits
+    return (r >> 20) - (120u << 3);                // exponent bias 127 -> 7
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c)
+{
+    return c < 8 ? (float)c * (1.0f / 512.0f) : __uint_as_float((((c >> 3) + 120u) << 23) | ((c & 7u) << 20));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int kSel>
+__device__ __forceinline__ uint32_t cvt_pair(uint32_t old, float a, float b, float e)
+{
+    const float ya = __builtin_amdgcn_fmed3f(a * e, -8.0f, 8.0f);
+    const float yb = __builtin_amdgcn_fmed3f(b * e, -8.0f, 8.0f);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, ya, yb, 1.0f, kSel);
+}
+
+}  // namespace
+
+__global__ void nvfp4_amax_init_kernel(uint32_t* __restrict__ amax_bits) { *amax_bits = 0u; }
+
+__global__ __launch_bounds__(kThreads) void nvfp4_amax_kernel(const u32x4* __restrict__ x,
+                                                              uint32_t* __restrict__ amax_bits,
+                                                              const int32_t* __restrict__ offs, int G, int64_t K)
+{
+    const int64_t nchunks = (int64_t)offs[G] * (K / 8);
+    const int64_t stride = (int64_t)gridDim.x * kThreads * kAmaxU;
+    uint32_t m = 0;
+    for (int64_t base = (int64_t)blockIdx.x * kThreads * kAmaxU; base < nchunks; base += stride) {
+        u32x4 v[kAmaxU];
+#pragma unroll
+        for (int u = 0; u < kAmaxU; ++u) {
+            const int64_t idx = base + u * kThreads + threadIdx.x;
+            v[u] = idx < nchunks ? load_stream(x + idx) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kAmaxU; ++u)
+            m = max(m, nv_max_bits8(v[u]));
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
+    if ((threadIdx.x & 63) == 0 && m != 0)
+        atomicMax(amax_bits, m << 16);             // the BF16 magnitude as FP32 bits
+}
+
+__global__ __launch_bounds__(kThreads) void nvfp4_quantize_kernel(const u32x4* __restrict__ x,
+                                                                  uint32_t* __restrict__ codes,
+                                                                  uint8_t* __restrict__ scales,
+                                                                  const uint32_t* __restrict__ amax_bits,
+                                                                  const int32_t* __restrict__ offs, int G,
+                                                                  int64_t K)
+{
+    const int64_t nchunks = (int64_t)offs[G] * (K / 8);
+    const int64_t base = (int64_t)blockIdx.x * (kThreads * kNvU);
+    if (base >= nchunks)
+        return;
+    const int tid = threadIdx.x;
+    u32x4 v[kNvU];
+#pragma unroll
+    for (int u = 0; u < kNvU; ++u) {
+        const int64_t idx = base + u * kThreads + tid;
+        v[u] = idx < nchunks ? load_stream(x + idx) : u32x4{0, 0, 0, 0};
+    }
+    const float amax = __uint_as_float(*amax_bits);
+    float t = amax == 0.0f ? 1.0f : 2688.0f / amax;
+    if (!(t <= FLT_MAX))
+        t = FLT_MAX;
+#pragma unroll
+    for (int u = 0; u < kNvU; ++u) {
+        const int64_t idx = base + u * kThreads + tid;
+        // nchunks is even (K is a multiple of 16), so a lane pair is entirely in or out
+        // of range and the exchange below never mixes a valid and a padding lane
+        uint32_t mb = nv_max_bits8(v[u]);
+        mb = max(mb, (uint32_t)__builtin_amdgcn_mov_dpp((int)mb, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+        const float ab = __uint_as_float(mb << 16);
+        float sb = ab / 6.0f;
+        sb = sb * t;
+        const uint32_t S = e4m3_code_rne_sat(sb);
+        float e = 0.0f;
+        if (S != 0) {
+            e = t / e4m3_value(S);
+            if (!(e <= FLT_MAX))
+                e = FLT_MAX;
+        }
+        uint32_t w = cvt_pair<0>(0u, bf16_lo(v[u].x), bf16_hi(v[u].x), e);
+        w = cvt_pair<1>(w, bf16_lo(v[u].y), bf16_hi(v[u].y), e);
+        w = cvt_pair<2>(w, bf16_lo(v[u].z), bf16_hi(v[u].z), e);
+        w = cvt_pair<3>(w, bf16_lo(v[u].w), bf16_hi(v[u].w), e);
+        if (idx < nchunks) {
+            store_stream(codes + idx, w);
+            if ((tid & 1) == 0)
+                scales[idx >> 1] = (uint8_t)S;
+        }
+    }
+}
+
+hipError_t launch_nvfp4_quantize_rows(const uint16_t* x, uint8_t* codes, uint8_t* scales, float* tensor_amax,
+                                      const int32_t* offs, int32_t G, int64_t M_cap, int64_t K, hipStream_t stream)
+{
+    const int64_t nchunks_cap = M_cap * (K / 8);
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+    uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
+    uint32_t* ab = reinterpret_cast<uint32_t*>(tensor_amax);
+    int g = G;
+    int64_t k = K;
+    hipLaunchKernelGGL(nvfp4_amax_init_kernel, dim3(1), dim3(1), 0, stream, ab);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || nchunks_cap == 0)
+        return err;
+    const int64_t per_amax = (int64_t)kThreads * kAmaxU;
+    const int64_t grid_amax = min((nchunks_cap + per_amax - 1) / per_amax, (int64_t)(device_cus() * 8));
+    void* aargs[] = {(void*)&xv, (void*)&ab, (void*)&offs, (void*)&g, (void*)&k};
+    err = hipLaunchKernel((const void*)nvfp4_amax_kernel, dim3((unsigned)grid_amax), dim3(kThreads), aargs, 0,
+                          stream);
+    if (err != hipSuccess)
+        return err;
+    const int64_t per_block = (int64_t)kThreads * kNvU;
+    const int64_t grid = (nchunks_cap + per_block - 1) / per_block;
+    if (grid > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    const uint32_t* abc = ab;
+    void* qargs[] = {(void*)&xv, (void*)&cv, (void*)&scales, (void*)&abc, (void*)&offs, (void*)&g, (void*)&k};
+    return hipLaunchKernel((const void*)nvfp4_quantize_kernel, dim3((unsigned)grid), dim3(kThreads), qargs, 0,
+                           stream);
+}
+
+}  // namespace mxfp4

@@ -67,6 +67,25 @@ mxfp4_status mxfp4_quantize_rows(const uint16_t* x_bf16, uint8_t* codes, uint8_t
                                  const int32_t* group_offsets, int32_t G, int64_t M_cap,
                                  int64_t K, hipStream_t stream);
 
+/* BF16 -> NVFP4, the variant format of the NVFP4 recipe page ("Train models faster with
+ * JAX and MaxText using NVFP4 on NVIDIA Blackwell": 16-element microblocks, E4M3 block
+ * scales under one FP32 scale per tensor, nearest-even rounding for activations).
+ *   x_bf16       [M_cap, K] row-major BF16 bits (finite values).
+ *   codes        [M_cap, K/2]  E2M1 codes, element 2i in the low nibble of byte i.
+ *   scales_e4m3  [M_cap, K/16] E4M3FN block scale bytes.
+ *   tensor_amax  one float (device): max |x| over rows [0, offs[G]), 0 if there are none.
+ *   With t = FP32(2688 / amax) (1 for amax 0, FLT_MAX if the quotient overflows), each
+ *   16-element block with largest magnitude amax_b has scale S = E4M3(FP32(FP32(amax_b/6)
+ *   * t)) (nearest even, subnormals, saturating at 448), and each element the code
+ *   E2M1(FP32(x * FP32(t / S))) (nearest even, saturating at 6, sign kept; 0 codes where
+ *   S is 0); it decodes as E2M1(code) * E4M3(S) / t.
+ *   Rows [0, offs[G]) are written; tensor_amax is written even when there are none.
+ *   K must be a multiple of 16.  Three launches on the stream (amax reset, tensor amax,
+ *   quantize); calls that share tensor_amax must not overlap. */
+mxfp4_status mxfp4_nvfp4_quantize_rows(const uint16_t* x_bf16, uint8_t* codes, uint8_t* scales_e4m3,
+                                       float* tensor_amax, const int32_t* group_offsets, int32_t G,
+                                       int64_t M_cap, int64_t K, hipStream_t stream);
+
 /* MXFP4 -> FP8 E4M3FN, row layout for FPROP (the page's FP4RowToFP8Row; technical
  * summary section 2, item 1, hierarchical scale alignment).
  *   codes, scales  as produced by mxfp4_quantize_rows.

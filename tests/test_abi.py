@@ -165,6 +165,26 @@ def test_grouped_gemm_argument_errors(lib):
     assert _gm(lib, M=0) == mx.MXFP4_OK
 
 
+def _nv(lib, x=A, c=A2, s=A3, am=A4, o=OFFS, G=1, M=4, K=32):
+    return lib.mxfp4_nvfp4_quantize_rows(x, c, s, am, o, G, M, K, None)
+
+
+def test_nvfp4_quantizer_argument_errors(lib):
+    # rejected before anything is enqueued (a valid call writes the amax even for
+    # M_cap == 0, so it needs a GPU)
+    for kw in ("x", "c", "s", "am", "o"):
+        assert _nv(lib, **{kw: None}) == mx.MXFP4_ERR_NULL
+    assert _nv(lib, K=8) == mx.MXFP4_ERR_SHAPE            # K % 16
+    assert _nv(lib, K=0) == mx.MXFP4_ERR_SHAPE
+    assert _nv(lib, G=0) == mx.MXFP4_ERR_SHAPE
+    assert _nv(lib, M=-1) == mx.MXFP4_ERR_SHAPE
+    assert _nv(lib, x=A + 8) == mx.MXFP4_ERR_ALIGN
+    assert _nv(lib, c=A2 + 4) == mx.MXFP4_ERR_ALIGN
+    assert _nv(lib, s=A3 + 1) == mx.MXFP4_ERR_ALIGN
+    assert _nv(lib, am=A4 + 2) == mx.MXFP4_ERR_ALIGN
+    assert _nv(lib, o=OFFS + 2) == mx.MXFP4_ERR_ALIGN
+
+
 def _wg(lib, dy=A, sdy=A2, x=A3, sx=A4, dw=A, o=OFFS, G=1, M=4, N=256, K=256):
     return lib.mxfp4_fp8_grouped_gemm_wgrad(dy, sdy, x, sx, dw, o, G, M, N, K, None)
 

@@ -104,6 +104,23 @@ def test_gemm_small_every_output(counts, N, K, slack):
     assert np.all(y[M_tot:] == CANARY16), "rows past offs[G] were written"
 
 
+def test_gemm_as_dgrad():
+    """The activation gradient dX[m, k] = sum_n dY[m, n] W_g[n, k] through the same entry
+    point: A = the backward row quantizer's output of an [M, N] gradient (1x128 blocks
+    along N), and each expert's weight transposed to [K, N] and quantized along N."""
+    threads = oracle.default_threads()
+    counts, N, K = [0, 37, 300, 5], 768, 512
+    M_tot = sum(counts)
+    say(f"gemm as dgrad: counts={counts} N={N} K={K}")
+    grad = workloads.ragged_case(counts, N, seed=21, M_cap=M_tot + 5)
+    a, sa = oracle.fp8q_rows(grad.x_bits, rows=M_tot, threads=threads)
+    wT, swT = weights(len(counts), K, N, seed=22, threads=threads)       # W_g^T [K, N]
+    y = run_gemm(a, sa, wT, swT, grad.offs, grad.M_cap)
+    exact, ybf, absum = oracle.fp8_gemm(a, sa, wT, swT, grad.offs, threads=threads)
+    check_points(y[:M_tot].reshape(-1), exact.reshape(-1), ybf.reshape(-1), absum.reshape(-1), N, "dgrad")
+    assert np.all(y[M_tot:] == CANARY16), "rows past offs[G] were written"
+
+
 def test_gemm_no_rows_writes_nothing():
     G, N, K, M_cap = 3, 256, 256, 100
     a = np.zeros((M_cap, K), np.uint8)
