@@ -14,8 +14,9 @@
 // The FP32 divisions are IEEE (HIP's default correctly rounded division).
 //
 // Three launches on the stream: zero the amax word; a grid-stride max of |x| over the
-// routed rows, one vector atomic max per wave on the float bits (non-negative floats
-// order as their bit patterns); the quantizer, which reads the amax, derives t, and
+// routed rows (two workgroups per CU), one vector atomic max per workgroup on the float
+// bits (non-negative floats order as their bit patterns), skipped when the stored value
+// is already as large; the quantizer, which reads the amax, derives t, and
 // converts.  The quantizer's layout is the MXFP4 quantizer's with 16-element blocks: a
 // lane takes 16 bytes (8 BF16), a lane pair one block, four loads per thread in flight;
 // the E4M3 scale is encoded with integer rounding on the FP32 bits (no conversion
@@ -97,8 +98,21 @@ __global__ __launch_bounds__(kThreads) void nvfp4_amax_kernel(const u32x4* __res
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1)
         m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
-    if ((threadIdx.x & 63) == 0 && m != 0)
-        atomicMax(amax_bits, m << 16);             // the BF16 magnitude as FP32 bits
+    // one atomic per workgroup, and none when the stored maximum is already as large:
+    // it only grows, so a stale read can cost an atomic but never skip a needed one
+    __shared__ uint32_t wave_max[kThreads / 64];
+    if ((threadIdx.x & 63) == 0)
+        wave_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t b = wave_max[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w)
+            b = max(b, wave_max[w]);
+        const uint32_t bits = b << 16;             // the BF16 magnitude as FP32 bits
+        if (b != 0 && bits > __hip_atomic_load(amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMax(amax_bits, bits);
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void nvfp4_quantize_kernel(const u32x4* __restrict__ x,
@@ -166,7 +180,7 @@ hipError_t launch_nvfp4_quantize_rows(const uint16_t* x, uint8_t* codes, uint8_t
     if (err != hipSuccess || nchunks_cap == 0)
         return err;
     const int64_t per_amax = (int64_t)kThreads * kAmaxU;
-    const int64_t grid_amax = min((nchunks_cap + per_amax - 1) / per_amax, (int64_t)(device_cus() * 8));
+    const int64_t grid_amax = min((nchunks_cap + per_amax - 1) / per_amax, (int64_t)(device_cus() * 2));
     void* aargs[] = {(void*)&xv, (void*)&ab, (void*)&offs, (void*)&g, (void*)&k};
     err = hipLaunchKernel((const void*)nvfp4_amax_kernel, dim3((unsigned)grid_amax), dim3(kThreads), aargs, 0,
                           stream);
