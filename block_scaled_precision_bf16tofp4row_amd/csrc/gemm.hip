@@ -38,7 +38,9 @@
 // t's barrier a lane waits for its own loads of stage t.  Stages run in pairs (one per
 // buffer) whose load issues are fixed at compile time, the last pair peeled, so that a
 // pair is one basic block and the compiler keeps each stage's matrix work in its stage
-// instead of sinking it towards the stores.
+// instead of sinking it towards the stores.  A wave raises its priority while it issues
+// a stage's MFMAs (s_setprio), so the SIMD's other wave does its waiting meanwhile
+// instead of both contending for the issue slots in lockstep.
 // The tile's block scales (256 rows x K/128 bytes per operand) are staged in LDS once,
 // laid out so that one 4-byte read gives a lane the scales of its four MFMA tiles; they
 // take no registers across stages and no place in the memory-operation count.  Operand
@@ -325,6 +327,9 @@ __device__ __forceinline__ void fast_group(const FastCtx& cx, uint32_t t0, f32x1
         const uint32_t scw4 =
             *reinterpret_cast<const uint32_t*>(cx.scl_w + t * kTN + (cx.wn >> 1) * 128 + cx.r * 4) >>
             (16 * (cx.wn & 1));
+        // the wave with matrix work to issue goes first: of a SIMD's two waves, one
+        // computes while the other waits for its loads and fragments
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {             // the stage's two MFMA K-steps of 64
             const uint32_t c0 = 16 * ((4 * j + cx.h) ^ sw8), c1 = 16 * ((4 * j + 2 + cx.h) ^ sw8);
@@ -349,6 +354,7 @@ __device__ __forceinline__ void fast_group(const FastCtx& cx, uint32_t t0, f32x1
                         (int)((sca4 >> (8 * mt)) & 0xFF));
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
     }
 }

@@ -208,6 +208,7 @@ __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
             load_scales(tn, nx_x, nx_dy);
             const uint8_t* const tdy = lds + (t & 1) * kWStage + (128 * wm) * kWS;
             const uint8_t* const tx = lds + (t & 1) * kWStage + kWT * kWS + (64 * wn) * kWS;
+            __builtin_amdgcn_s_setprio(1);        // as in the forward GEMM: matrix work first
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 const uint32_t c0 = 16 * ((4 * kh + h) ^ sw8), c1 = 16 * ((4 * kh + 2 + h) ^ sw8);
@@ -235,6 +236,7 @@ __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
                         acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                             fx[nt], fdy[mt], acc[mt][nt], 0, 0, 0, (int)sc_x[nt], 0, (int)sc_dy[mt]);
             }
+            __builtin_amdgcn_s_setprio(0);
             // the other buffer was last read in step t - 1, before the previous barrier
             store_tiles((t + 1) & 1, tn);
 #pragma unroll
