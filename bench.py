@@ -298,9 +298,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards by rows "
-              f"and experts across GPUs but multi-GPU runs are not part of this build.",
-              file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path shards by rows and "
+              f"experts across GPUs (one process per GPU, each running this single-GPU path on its share), "
+              f"but this benchmark measures one GPU's share.", file=sys.stderr)
         sys.exit(2)
 
     import torch
