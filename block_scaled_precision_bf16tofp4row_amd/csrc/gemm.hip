@@ -225,6 +225,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_general_kernel(
         }
         const uint8_t* const ta = lds + cur * kStage1 + (128 * wm) * kTK1;
         const uint8_t* const tw = lds + cur * kStage1 + kTM * kTK1 + (128 * wn) * kTK1;
+        __builtin_amdgcn_s_setprio(1);            // matrix work first, as in the fast path
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
             const uint32_t c0 = 16 * ((4 * kh + h) ^ sw8), c1 = 16 * ((4 * kh + 2 + h) ^ sw8);
@@ -247,6 +248,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void fp8_gemm_general_kernel(
                     acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         fw[nt], fa[mt], acc[mt][nt], 0, 0, 0, (int)sc_w[nt], 0, (int)sc_a[mt]);
         }
+        __builtin_amdgcn_s_setprio(0);
         if (more) {
             store_tiles(cur ^ 1);
 #pragma unroll

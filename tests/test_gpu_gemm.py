@@ -87,6 +87,8 @@ CASES = [
     ([0, 37, 300, 5], 512, 512, 11),          # empty expert, partial tiles, a 2-tile expert
     ([256], 256, 128, 0),                     # one full tile, a single K step
     ([1, 0, 513], 768, 1024, 7),              # one-row expert, tiles 256 + 256 + 1
+    ([300, 45], 256, 7296, 3),                # K past the fast path's staged scales: general kernel
+    ([130], 512, 384, 0),                     # K not a multiple of 256: general kernel
 ]
 
 
