@@ -123,6 +123,24 @@ def test_gemm_as_dgrad():
     assert np.all(y[M_tot:] == CANARY16), "rows past offs[G] were written"
 
 
+def test_gemm_many_experts():
+    """300 experts, 12 of them with tokens (the tile -> expert walk over many groups)."""
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(12)
+    counts = [0] * 300
+    for g in rng.choice(300, 12, replace=False):
+        counts[int(g)] = int(rng.integers(1, 300))
+    N, K = 256, 256
+    M_tot = sum(counts)
+    seg = workloads.ragged_case(counts, K, seed=13, values="normal", M_cap=M_tot + 4)
+    a, sa = activations(seg.x_bits, M_tot, threads)
+    w, sw = weights(300, N, K, seed=14, threads=threads)
+    y = run_gemm(a, sa, w, sw, seg.offs, seg.M_cap)
+    exact, ybf, absum = oracle.fp8_gemm(a, sa, w, sw, seg.offs, threads=threads)
+    check_points(y[:M_tot].reshape(-1), exact.reshape(-1), ybf.reshape(-1), absum.reshape(-1), K, "300 experts")
+    assert np.all(y[M_tot:] == CANARY16)
+
+
 def test_gemm_no_rows_writes_nothing():
     G, N, K, M_cap = 3, 256, 256, 100
     a = np.zeros((M_cap, K), np.uint8)

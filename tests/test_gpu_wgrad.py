@@ -140,6 +140,26 @@ def test_wgrad_random_bytes_and_scales():
     check_points(y.reshape(-1), exact.reshape(-1), ybf.reshape(-1), absum.reshape(-1), mg.reshape(-1), "random")
 
 
+def test_wgrad_many_experts():
+    """More than 64 experts (tiles in expert order instead of largest first), many empty."""
+    rng = np.random.default_rng(62)
+    counts = [int(c) if rng.random() < 0.6 else 0 for c in rng.integers(1, 160, 70)]
+    N, K = 256, 256
+    M_cap = sum(counts) + 17
+    say(f"wgrad many experts: G={len(counts)} tokens={sum(counts)}")
+    threads = oracle.default_threads()
+    offs, dyT, sdyT, xT, sxT = column_operands(counts, N, K, M_cap, seed=62, threads=threads)
+    y = run_wgrad(dyT, sdyT, xT, sxT, offs, M_cap, N, K)
+    gs = np.repeat(np.arange(len(counts)), 40)
+    ns = rng.integers(0, N, gs.size)
+    ks = rng.integers(0, K, gs.size)
+    exact, ybf, absum = oracle.fp8_wgrad_at(dyT, sdyT, xT, sxT, offs, N, K, gs, ns, ks, threads=threads)
+    check_points(y[gs, ns, ks], exact, ybf, absum, np.diff(offs.astype(np.int64))[gs], "many experts")
+    for g, c in enumerate(counts):
+        if c == 0:
+            assert np.all(y[g] == 0), g
+
+
 def test_wgrad_no_tokens_writes_zeros():
     G, N, K = 3, 256, 256
     y = run_wgrad(np.zeros(0, np.uint8), np.zeros(0, np.uint8), np.zeros(0, np.uint8), np.zeros(0, np.uint8),
