@@ -67,7 +67,6 @@ constexpr int kTK = 128;                          // K per stage (one scale bloc
 constexpr int kStages = 2;                        // LDS buffers; loads run one stage ahead
 constexpr int kStage = (kTM + kTN) * kTK;         // bytes of one LDS stage (64 KB)
 constexpr int kFastThreads = 512;                 // 8 waves, two per SIMD
-constexpr int kFastLoadsPerStep = 8;              // LDS loads a lane issues per stage
 constexpr int kMaxFastBlocks = 56;                // scale blocks staged in LDS (K <= 7168)
 // general path
 constexpr int kTK1 = 128;
