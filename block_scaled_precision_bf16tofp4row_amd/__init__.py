@@ -14,7 +14,9 @@ The binding has the same names as the C ABI:
 * ``mxfp4_to_fp8_rows(codes, scales, y, y_scales, offs, ...)``
 * ``mxfp4_to_fp8_cols_ragged(codes, scales, yT, yT_scales, offs, ...)``
 * ``mxfp4_bf16_to_fp8_rows(x, y, y_scales, offs, ...)`` and
-  ``mxfp4_bf16_to_fp8_cols_ragged(x, yT, yT_scales, offs, ...)`` (backward FP8 quantizer)
+  ``mxfp4_bf16_to_fp8_cols_ragged(x, yT, yT_scales, offs, ...)`` (backward FP8 quantizer), and
+  ``mxfp4_bf16_to_fp8_rows_cols_ragged(x, y, y_scales, yT, yT_scales, offs, ...)`` (both
+  layouts from one read)
 * ``mxfp4_fp8_grouped_gemm(a, a_scales, w, w_scales, y, offs, ...)`` (FP8 expert GEMM)
 * ``mxfp4_fp8_grouped_gemm_wgrad(dyT, dyT_scales, xT, xT_scales, dw, offs, ...)``
   (FP8 weight-gradient GEMM over the column layouts)
@@ -50,6 +52,7 @@ EXPORTED = (
     "mxfp4_to_fp8_cols_ragged",
     "mxfp4_bf16_to_fp8_rows",
     "mxfp4_bf16_to_fp8_cols_ragged",
+    "mxfp4_bf16_to_fp8_rows_cols_ragged",
     "mxfp4_fp8_grouped_gemm",
     "mxfp4_fp8_grouped_gemm_wgrad",
     "mxfp4_cols_scale_capacity",
@@ -92,6 +95,8 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_fp8_grouped_gemm.restype = st
     lib.mxfp4_fp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
     lib.mxfp4_nvfp4_quantize_rows.argtypes = [P, P, P, P, P, I32, I64, I64, P]
+    lib.mxfp4_bf16_to_fp8_rows_cols_ragged.argtypes = [P, P, P, P, P, P, I32, I64, I64, P]
+    lib.mxfp4_bf16_to_fp8_rows_cols_ragged.restype = st
     lib.mxfp4_nvfp4_quantize_rows.restype = st
     lib.mxfp4_fp8_grouped_gemm_wgrad.restype = st
     lib.mxfp4_cols_scale_capacity.argtypes = [I64, I64, I32]
@@ -236,6 +241,23 @@ def mxfp4_bf16_to_fp8_cols_ragged(x, yT, yT_scales, offs, G=None, M_cap=None, K=
     lib = load_library()
     _check(lib.mxfp4_bf16_to_fp8_cols_ragged(_ptr(x), _ptr(yT), _ptr(yT_scales), _ptr(offs), G, M_cap, K,
                                              _stream(stream)), "mxfp4_bf16_to_fp8_cols_ragged")
+
+
+def mxfp4_bf16_to_fp8_rows_cols_ragged(x, y, y_scales, yT, yT_scales, offs, G=None, M_cap=None, K=None,
+                                       stream=None):
+    """Both layouts of the backward FP8 quantizer from one read of x: what
+    mxfp4_bf16_to_fp8_rows and mxfp4_bf16_to_fp8_cols_ragged write (see the header)."""
+    G, M_cap, K = _dims(x, offs, G, M_cap, K)
+    n = max(M_cap, 0) * max(K, 0)
+    cap = mxfp4_cols_scale_capacity(M_cap, K, G) if n > 0 and G >= 1 else 0
+    _need("mxfp4_bf16_to_fp8_rows_cols_ragged",
+          [(x, 2 * n, "x", ("bfloat16", "int16", "uint16")), (y, n, "y", _FP8), (y_scales, n // 128, "y_scales", _U8),
+           (yT, n, "yT", _FP8), (yT_scales, max(cap, 0), "yT_scales", _U8),
+           (offs, 4 * (G + 1), "group_offsets", ("int32",))])
+    lib = load_library()
+    _check(lib.mxfp4_bf16_to_fp8_rows_cols_ragged(_ptr(x), _ptr(y), _ptr(y_scales), _ptr(yT), _ptr(yT_scales),
+                                                  _ptr(offs), G, M_cap, K, _stream(stream)),
+           "mxfp4_bf16_to_fp8_rows_cols_ragged")
 
 
 def mxfp4_fp8_grouped_gemm(a, a_scales, w, w_scales, y, offs, G=None, M_cap=None, N=None, K=None,

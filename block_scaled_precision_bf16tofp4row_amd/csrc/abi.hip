@@ -20,7 +20,7 @@ hipError_t launch_fp8_wgrad(const uint8_t*, const uint8_t*, const uint8_t*, cons
                             const int32_t*, int32_t, int64_t, int64_t, int64_t, int64_t, hipStream_t);
 hipError_t launch_nvfp4_quantize_rows(const uint16_t*, uint8_t*, uint8_t*, float*, const int32_t*, int32_t,
                                       int64_t, int64_t, hipStream_t);
-hipError_t launch_fp8q_cols(const uint16_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
+hipError_t launch_fp8q_cols(const uint16_t*, uint8_t*, uint8_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
                             int64_t, hipStream_t);
 hipError_t launch_fp8q_rows(const uint16_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
                             int64_t, hipStream_t);
@@ -164,8 +164,29 @@ mxfp4_status mxfp4_bf16_to_fp8_cols_ragged(const uint16_t* x_bf16, uint8_t* yT_e
         return MXFP4_ERR_ALIGN;
     if (M_cap == 0)
         return MXFP4_OK;
-    return from_hip(mxfp4::launch_fp8q_cols(x_bf16, yT_e4m3, yT_scales, group_offsets, G, M_cap,
-                                            K, stream));
+    return from_hip(mxfp4::launch_fp8q_cols(x_bf16, yT_e4m3, yT_scales, nullptr, nullptr, group_offsets, G,
+                                            M_cap, K, stream));
+}
+
+mxfp4_status mxfp4_bf16_to_fp8_rows_cols_ragged(const uint16_t* x_bf16, uint8_t* y_e4m3, uint8_t* y_scales,
+                                                uint8_t* yT_e4m3, uint8_t* yT_scales,
+                                                const int32_t* group_offsets, int32_t G, int64_t M_cap,
+                                                int64_t K, hipStream_t stream)
+{
+    if (!x_bf16 || !y_e4m3 || !y_scales || !yT_e4m3 || !yT_scales || !group_offsets)
+        return MXFP4_ERR_NULL;
+    mxfp4_status st = check_shape(G, M_cap, K, 128);
+    if (st != MXFP4_OK)
+        return st;
+    if (K > kMaxColsK)                       // the kernel's per-strip row offsets are 32-bit
+        return MXFP4_ERR_SHAPE;
+    if (!aligned(x_bf16, 16) || !aligned(y_e4m3, 16) || !aligned(y_scales, 16) || !aligned(yT_e4m3, 16) ||
+        !aligned(yT_scales, 16) || !aligned(group_offsets, 4))
+        return MXFP4_ERR_ALIGN;
+    if (M_cap == 0)
+        return MXFP4_OK;
+    return from_hip(mxfp4::launch_fp8q_cols(x_bf16, yT_e4m3, yT_scales, y_e4m3, y_scales, group_offsets, G,
+                                            M_cap, K, stream));
 }
 
 mxfp4_status mxfp4_fp8_grouped_gemm(const uint8_t* a_e4m3, const uint8_t* a_scales,

@@ -115,9 +115,12 @@ __device__ __forceinline__ u16x2 cvt_pair(u16x2 acc, uint32_t w, uint32_t clamp2
 
 }  // namespace
 
+// kRows: also write the row layout (1 x 128 blocks along K) from the same read of x.
+template <bool kRows>
 __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     const uint8_t* __restrict__ x, uint8_t* __restrict__ yT, uint8_t* __restrict__ yT_scales,
-    const int32_t* __restrict__ offs, int G, int64_t K, int parts)
+    uint8_t* __restrict__ y, uint8_t* __restrict__ y_scales, const int32_t* __restrict__ offs, int G,
+    int64_t K, int parts)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
     __shared__ __attribute__((aligned(16))) SlotInfo info[kSlots];
@@ -128,6 +131,10 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     // per ring slot the strips drained by the consumer waves (all monotonic)
     __shared__ __attribute__((aligned(16))) uint32_t produced[kQProducerWaves];
     __shared__ uint32_t drained[kSlots];
+    // row layout: per ring slot, each producer wave's maximum magnitude (BF16 bits) of
+    // every strip row over its 32 columns, and per wave the strips so published
+    __shared__ __attribute__((aligned(16))) uint16_t rowmax[kRows ? kSlots : 1][kQProducerWaves][kStripRows];
+    __shared__ __attribute__((aligned(16))) uint32_t rowpub[kQProducerWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -153,8 +160,10 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     const uint32_t n = s1 - s0 + lead;
 
     if (tid == 0) {
-        for (int k = 0; k < kQProducerWaves; ++k)
+        for (int k = 0; k < kQProducerWaves; ++k) {
             produced[k] = 0;
+            rowpub[k] = 0;
+        }
         for (int k = 0; k < kSlots; ++k)
             drained[k] = 0;
     }
@@ -174,7 +183,75 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
         for (int i = 0; i < 8; ++i)
             off[i] = (uint32_t)(row_g + i) * (uint32_t)(2 * K) + cbyte;
         // tile column 32w + 8c + j sits at LDS byte lds_col(32w + 8c) + 544 j
-        const uint32_t wbase = lds_col(32 * wave + 8 * c) + row_g;
+
+        // row layout, step 1: this wave's maximum of each of the lane's eight rows over
+        // its 32 columns (the four lanes of a quad hold one row group's 32 columns),
+        // published for the other three waves of the 128-column block
+        auto publish_row_max = [&](const QRows& in, uint32_t slot) {
+            uint32_t rm[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t m = pk_max_u16(pk_max_u16(in.v[i][0] & 0x7FFF7FFFu, in.v[i][1] & 0x7FFF7FFFu),
+                                        pk_max_u16(in.v[i][2] & 0x7FFF7FFFu, in.v[i][3] & 0x7FFF7FFFu));
+                m = max(m & 0xFFFFu, m >> 16);
+                m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+                m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+                rm[i] = m;
+            }
+            uint32_t ln = (uint32_t)lane;            // opaque, as in produce_rows
+            asm volatile("" : "+v"(ln));
+            if ((ln & 3) == 0)
+                *reinterpret_cast<u32x4*>(&rowmax[slot][wave][8 * (ln >> 2)]) =
+                    u32x4{rm[0] | (rm[1] << 16), rm[2] | (rm[3] << 16), rm[4] | (rm[5] << 16), rm[6] | (rm[7] << 16)};
+        };
+        // row layout, step 2 (once the block's four waves have published strip t): the
+        // block scale of each of the lane's rows, its eight bytes of each row and, from
+        // the first wave of the block, the scale bytes.  Stores go through resources over
+        // the strip's rows, empty for a lead-in strip and for the repeated columns of a
+        // narrow tile, so nothing else is written.
+        auto produce_rows = [&](const StripInfo& st, const QRows& in, uint32_t slot, uint32_t flags) {
+            // lane-dependent offsets are derived from a lane index the compiler cannot
+            // see through (the empty asm), so that it recomputes them here instead of
+            // holding them in registers of their own across the strip loop (which spills)
+            uint32_t ln = (uint32_t)lane;
+            asm volatile("" : "+v"(ln));
+            const uint32_t lrow = 8 * (ln >> 2), lc = ln & 3;
+            const int wb = wave & ~3;
+            const u32x4 p0 = *reinterpret_cast<const u32x4*>(&rowmax[slot][wb + 0][lrow]);
+            const u32x4 p1 = *reinterpret_cast<const u32x4*>(&rowmax[slot][wb + 1][lrow]);
+            const u32x4 p2 = *reinterpret_cast<const u32x4*>(&rowmax[slot][wb + 2][lrow]);
+            const u32x4 p3 = *reinterpret_cast<const u32x4*>(&rowmax[slot][wb + 3][lrow]);
+            const uint32_t bm[4] = {pk_max_u16(pk_max_u16(p0.x, p1.x), pk_max_u16(p2.x, p3.x)),
+                                    pk_max_u16(pk_max_u16(p0.y, p1.y), pk_max_u16(p2.y, p3.y)),
+                                    pk_max_u16(pk_max_u16(p0.z, p1.z), pk_max_u16(p2.z, p3.z)),
+                                    pk_max_u16(pk_max_u16(p0.w, p1.w), pk_max_u16(p2.w, p3.w))};
+            const bool writes = (flags & 4u) == 0 && (ncols > 128 || wave < 4);
+            const int64_t r0 = st.row0 + st.r_lo;
+            const uint32_t nr = writes ? (uint32_t)st.nrows : 0u;
+            const __amdgpu_buffer_rsrc_t ry = strip_rsrc(y + r0 * K, (uint64_t)nr * (uint64_t)K);
+            const __amdgpu_buffer_rsrc_t rs = strip_rsrc(y_scales + r0 * (K / 128), (uint64_t)nr * (uint64_t)(K / 128));
+            // byte offsets of the lane's first row
+            const uint32_t vrow = lrow * (uint32_t)K + (uint32_t)(kTileCols * kt) + 32 * (uint32_t)wave + 8 * lc;
+            const uint32_t vscl = lrow * (uint32_t)(K / 128) + (uint32_t)(2 * kt) + (uint32_t)(wave >> 2);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t m = (bm[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                const uint32_t S = (m >> 7) > 8 ? (m >> 7) - 8 : 0u;
+                const uint32_t clamp2 = (((S + 8) << 7) | 0x60u) * 0x00010001u;
+                const float scale = __uint_as_float(max(S << 23, 0x00400000u));   // S = 0: 2^-127
+                u16x2 lo = {0, 0}, hi = {0, 0};
+                lo = cvt_pair<false>(lo, in.v[i][0], clamp2, scale);
+                lo = cvt_pair<true>(lo, in.v[i][1], clamp2, scale);
+                hi = cvt_pair<false>(hi, in.v[i][2], clamp2, scale);
+                hi = cvt_pair<true>(hi, in.v[i][3], clamp2, scale);
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)}, ry,
+                    (int)(vrow + (uint32_t)i * (uint32_t)K), 0, 0);
+                if (lc == 0 && (wave & 3) == 0)
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)S, rs, (int)(vscl + (uint32_t)i * (uint32_t)(K / 128)), 0,
+                                                         0);
+            }
+        };
 
         auto produce = [&](const StripInfo& st, const QRows& in, uint32_t slot, uint32_t flags) {
             // column maxima over the strip (pairs of columns 8c + 2d, 8c + 2d + 1)
@@ -195,8 +272,15 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                 const u16x2 eight = {8, 8};
                 S2[d] = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(e, eight));
             }
-            if (rg == 0)
-                *reinterpret_cast<u32x2*>(&sbytes[slot][32 * wave + 8 * c]) =
+            // with the row layout there are not enough registers to keep these offsets
+            // across the strip loop: derive them from an opaque lane index (see
+            // produce_rows)
+            uint32_t ln = (uint32_t)lane;
+            if constexpr (kRows)
+                asm volatile("" : "+v"(ln));
+            const uint32_t lrg = ln >> 2, lcc = ln & 3;
+            if (lrg == 0)
+                *reinterpret_cast<u32x2*>(&sbytes[slot][32 * wave + 8 * lcc]) =
                     u32x2{perm(S2[1], S2[0], 0x06040200u), perm(S2[3], S2[2], 0x06040200u)};
             if (wave == 0 && lane == 0) {
                 info[slot].A0 = K * st.row0 + st.r_lo + (int64_t)kTileCols * kt * st.mg;
@@ -207,7 +291,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
             }
             // quantize column by column: rows (0, 1), (2, 3), (4, 5), (6, 7) form the
             // four pairs; the two result dwords are the column's eight ring bytes
-            uint8_t* const w = tile + wbase + kStripRows * slot;
+            uint8_t* const w = tile + lds_col(32 * wave + 8 * lcc) + 8 * lrg + kStripRows * slot;
             u32x2 T[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -227,7 +311,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
             }
             // ring bytes 0..31 (rows 0..31 of slot 0: row groups 0-3) are repeated after
             // the ring, so a 32-byte read window never wraps
-            if (slot == 0 && rg < 4) {
+            if (slot == 0 && lrg < 4) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     *reinterpret_cast<u32x2*>(w + kRing + kColBytes * j) = T[j];
@@ -262,13 +346,42 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                 const int ld = (u + kQPrefetch) % kSets;          // set receiving strip tt + kQPrefetch
                 const int pv = (u + kQPrefetch - 1) % kSets;      // set of strip tt + kQPrefetch - 1
                 I[ld] = tt + kQPrefetch < n ? next_strip(offs, G, I[pv]) : I[pv];
-                R[ld] = load_rows(x, K, I[ld], kt, off);
+                if constexpr (kRows) {
+                    // not enough registers to keep the eight row offsets across the loop:
+                    // recompute them from an opaque lane index (see produce_rows)
+                    uint32_t ln = (uint32_t)lane;
+                    asm volatile("" : "+v"(ln));
+                    uint32_t offk[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        offk[i] = (8 * (ln >> 2) + (uint32_t)i) * (uint32_t)(2 * K) + 64 * wcol + 16 * (ln & 3);
+                    R[ld] = load_rows(x, K, I[ld], kt, offk);
+                } else {
+                    R[ld] = load_rows(x, K, I[ld], kt, off);
+                }
                 if (tt >= 3 && !wait_at_least(&drained[(tt - 3) % kSlots],
                                               kQConsumerWaves * ((tt - 3) / kSlots + 1)))
                     return;
-                produce(I[u], R[u], tt % kSlots, flags_of(prev_sb, I[u], tt == 0 && lead != 0));
+                const uint32_t fl = flags_of(prev_sb, I[u], tt == 0 && lead != 0);
+                if constexpr (kRows) {
+                    // slot tt % 4 of rowmax is rewritten only in strip tt + 4, which starts
+                    // after the consumers drained strip tt + 1, so after every producer
+                    // finished strip tt (its row bytes included)
+                    publish_row_max(R[u], tt % kSlots);
+                    signal(&rowpub[wave]);
+                }
+                produce(I[u], R[u], tt % kSlots, fl);
                 prev_sb = I[u].sb;
                 signal(&produced[wave]);
+                if constexpr (kRows) {
+                    // the block's other three waves published while this one converted
+                    // the columns
+                    const int wb = wave & ~3;
+                    if (!wait_at_least(&rowpub[wb], tt + 1) || !wait_at_least(&rowpub[wb + 1], tt + 1) ||
+                        !wait_at_least(&rowpub[wb + 2], tt + 1) || !wait_at_least(&rowpub[wb + 3], tt + 1))
+                        return;
+                    produce_rows(I[u], R[u], tt % kSlots, fl);
+                }
                 if (tt + 1 >= n)
                     return;
             }
@@ -287,8 +400,8 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
         });
 }
 
-hipError_t launch_fp8q_cols(const uint16_t* x, uint8_t* yT, uint8_t* yT_scales, const int32_t* offs,
-                            int32_t G, int64_t M_cap, int64_t K, hipStream_t stream)
+hipError_t launch_fp8q_cols(const uint16_t* x, uint8_t* yT, uint8_t* yT_scales, uint8_t* y, uint8_t* y_scales,
+                            const int32_t* offs, int32_t G, int64_t M_cap, int64_t K, hipStream_t stream)
 {
     if (M_cap == 0)
         return hipSuccess;
@@ -306,9 +419,10 @@ hipError_t launch_fp8q_cols(const uint16_t* x, uint8_t* yT, uint8_t* yT_scales, 
     int g = G;
     int64_t k = K;
     int p = (int)parts;
-    void* args[] = {(void*)&xb, (void*)&yT, (void*)&yT_scales, (void*)&offs, (void*)&g, (void*)&k, (void*)&p};
-    return hipLaunchKernel((const void*)fp8q_cols_kernel, dim3((unsigned)grid), dim3(kQThreads), args, 0,
-                           stream);
+    void* args[] = {(void*)&xb, (void*)&yT, (void*)&yT_scales, (void*)&y, (void*)&y_scales, (void*)&offs,
+                    (void*)&g, (void*)&k, (void*)&p};
+    const void* kern = y ? (const void*)fp8q_cols_kernel<true> : (const void*)fp8q_cols_kernel<false>;
+    return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kQThreads), args, 0, stream);
 }
 
 }  // namespace mxfp4

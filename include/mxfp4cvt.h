@@ -149,6 +149,18 @@ mxfp4_status mxfp4_bf16_to_fp8_cols_ragged(const uint16_t* x_bf16, uint8_t* yT_e
                                            int32_t G, int64_t M_cap, int64_t K,
                                            hipStream_t stream);
 
+/* The backward FP8 quantizer in both layouts from one read of the gradient (technical
+ * summary section 2, item 2: the backward pass runs in FP8; DGRAD takes the row layout and
+ * WGRAD the transposed column layout of the same gradient).  Writes exactly what
+ * mxfp4_bf16_to_fp8_rows writes to y_e4m3 / y_scales and what
+ * mxfp4_bf16_to_fp8_cols_ragged writes to yT_e4m3 / yT_scales, with the same layouts,
+ * capacities and untouched bytes, reading x once.
+ *   K must be a multiple of 128 and at most 2^24 (else MXFP4_ERR_SHAPE). */
+mxfp4_status mxfp4_bf16_to_fp8_rows_cols_ragged(const uint16_t* x_bf16, uint8_t* y_e4m3, uint8_t* y_scales,
+                                                uint8_t* yT_e4m3, uint8_t* yT_scales,
+                                                const int32_t* group_offsets, int32_t G, int64_t M_cap,
+                                                int64_t K, hipStream_t stream);
+
 /* Expert-grouped FP8 GEMM, forward (technical summary section 2: compute stays FP8 on
  * the block-scaled pipeline, E4M3 with 128-element blocks, item 1; it consumes the row
  * layout FP8 activations).  For the expert g owning row m (offs[g] <= m < offs[g+1]):

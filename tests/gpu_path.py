@@ -159,3 +159,34 @@ def check_chain(x_bits: np.ndarray, offs: np.ndarray, kernels=("quantize", "rows
         assert_bytes_equal(ysT_g[:used_s], ysT_o[:used_s], "fp8 col scales")
         assert_untouched(ysT_g[used_s:], "fp8 col scales past the used blocks")
     return out
+
+
+def check_fp8q_both(x_bits: np.ndarray, offs: np.ndarray, threads: int | None = None):
+    """Backward FP8 quantizer, both layouts from one read: the row outputs against the
+    oracle's row quantizer and the column outputs against its column quantizer, canary
+    beyond both."""
+    threads = oracle.default_threads() if threads is None else threads
+    M_cap, K = x_bits.shape
+    G = offs.size - 1
+    M_tot = int(offs[-1])
+    y = canary((max(1, M_cap), K))
+    ys = canary((max(1, M_cap), K // 128))
+    yT = canary((max(1, M_cap * K),))
+    cap = mx.mxfp4_cols_scale_capacity(M_cap, K, G)
+    ysT = canary((max(1, cap),))
+    x_d = dev(x_bits) if M_cap else canary((1, K)).view(torch.int16)
+    mx.mxfp4_bf16_to_fp8_rows_cols_ragged(x_d, y, ys, yT, ysT, dev(offs), G=G, M_cap=M_cap, K=K)
+    y_o, ys_o = oracle.fp8q_rows(x_bits, rows=M_tot, threads=threads)
+    used_s = oracle.cols_scale_size(offs, K)
+    yT_o = np.full(max(1, M_cap * K), CANARY, np.uint8)
+    ysT_o = np.full(max(1, used_s), CANARY, np.uint8)
+    oracle.fp8q_cols(x_bits, offs, threads=threads, yT=yT_o, yT_scales=ysT_o)
+    y_g, ys_g, yT_g, ysT_g = host(y), host(ys), host(yT), host(ysT)
+    assert_bytes_equal(ys_g[:M_tot], ys_o[:M_tot], "both: row scales", row_len=K // 128)
+    assert_bytes_equal(y_g[:M_tot], y_o[:M_tot], "both: rows", row_len=K)
+    assert_untouched(y_g[M_tot:], "both: rows past offs[G]")
+    assert_untouched(ys_g[M_tot:], "both: row scales past offs[G]")
+    assert_bytes_equal(ysT_g[:used_s], ysT_o[:used_s], "both: col scales")
+    assert_bytes_equal(yT_g[:M_tot * K], yT_o[:M_tot * K], "both: cols")
+    assert_untouched(yT_g[M_tot * K:], "both: cols past K*offs[G]")
+    assert_untouched(ysT_g[used_s:], "both: col scales past the used blocks")

@@ -144,6 +144,26 @@ def test_fp8_column_quantizer_argument_errors(lib):
     assert _fc(lib, M=0, K=1 << 24) == mx.MXFP4_OK
 
 
+def _fb(lib, x=A, y=A2, ys=A3, yT=A4, ysT=A, o=OFFS, G=1, M=4, K=128):
+    return lib.mxfp4_bf16_to_fp8_rows_cols_ragged(x, y, ys, yT, ysT, o, G, M, K, None)
+
+
+def test_fp8_both_layouts_quantizer_argument_errors(lib):
+    for kw in ("x", "y", "ys", "yT", "ysT", "o"):
+        assert _fb(lib, **{kw: None}) == mx.MXFP4_ERR_NULL
+    assert _fb(lib, K=64) == mx.MXFP4_ERR_SHAPE
+    assert _fb(lib, G=0) == mx.MXFP4_ERR_SHAPE
+    assert _fb(lib, M=-1) == mx.MXFP4_ERR_SHAPE
+    assert _fb(lib, M=1, K=(1 << 24) + 128) == mx.MXFP4_ERR_SHAPE
+    assert _fb(lib, x=A + 2) == mx.MXFP4_ERR_ALIGN
+    assert _fb(lib, y=A2 + 1) == mx.MXFP4_ERR_ALIGN
+    assert _fb(lib, ys=A3 + 8) == mx.MXFP4_ERR_ALIGN
+    assert _fb(lib, yT=A4 + 4) == mx.MXFP4_ERR_ALIGN
+    assert _fb(lib, ysT=A + 3) == mx.MXFP4_ERR_ALIGN
+    assert _fb(lib, o=OFFS + 1) == mx.MXFP4_ERR_ALIGN
+    assert _fb(lib, M=0) == mx.MXFP4_OK
+
+
 def _gm(lib, a=A, sa=A2, w=A3, sw=A4, y=A, o=OFFS, G=1, M=4, N=256, K=128):
     return lib.mxfp4_fp8_grouped_gemm(a, sa, w, sw, y, o, G, M, N, K, None)
 
