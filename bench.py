@@ -19,7 +19,8 @@ forward chain, every launch's median over 20 launches each preceded by a 512 MB
 scrub read (so inputs come from HBM, not the caches), next to a device copy
 moving the same bytes.  ``backward`` times the FP8 gradient quantizer
 (mxfp4_bf16_to_fp8_rows and mxfp4_bf16_to_fp8_cols_ragged) on the same segments,
-outside ``value``; the scrubbed medians include it.  ``gemm`` times the forward expert
+outside ``value``, and the same quantizer writing both layouts from one read
+(mxfp4_bf16_to_fp8_rows_cols_ragged); the scrubbed medians include the separate launches.  ``gemm`` times the forward expert
 GEMM (mxfp4_fp8_grouped_gemm) on the hidden segment's FP8 row output against
 per-expert E4M3 weights ([8, 4096, 7168], synthetic), with its MFMA roofline; ``wgrad``
 times the weight-gradient GEMM (mxfp4_fp8_grouped_gemm_wgrad) on the hidden segment's
@@ -474,6 +475,25 @@ def main():
         "GBps": round(b_step_bytes / (b_ms_per_step / 1000.0) / 1e9, 1),
         "per_kernel": b_per_kernel,
     }
+    # the same quantizer writing both layouts from one read of the gradient
+    both = []
+    for d in bsegs:
+        sg = d["seg"]
+        yb, ysb = mx.alloc_fp8q_rows_outputs(sg.M_cap, sg.K, dev)
+        yTb, ysTb = mx.alloc_cols_outputs(sg.M_cap, sg.K, sg.G, dev)
+        fms = time_launches(lambda d=d: mx.mxfp4_bf16_to_fp8_rows_cols_ragged(d["x"], yb, ysb, yTb, ysTb, d["offs"]))
+        nb = (np.diff(sg.offs.astype(np.int64)) + 127) // 128
+        nbytes = int(sg.M_tot * sg.K * (2 + 1 + 1 / 128 + 1) + int(nb.sum()) * sg.K)
+        us = float(np.mean(fms)) * 1000.0
+        gbs = nbytes / (us * 1e-6) / 1e9
+        sep = sum(p["mean_us"] for p in b_per_kernel if p["segment"] == sg.name)
+        both.append({"segment": sg.name, "alg_bytes": nbytes, "mean_us": round(us, 2),
+                     "median_us": round(float(np.median(fms)) * 1000.0, 2), "GBps": round(gbs, 1),
+                     "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "separate_mean_us": round(sep, 2)})
+        log(f"[bench] both layouts {sg.name}: {us:.1f} us ({gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.1%} of 8 TB/s) "
+            f"against {sep:.1f} us for the two separate launches")
+        del yb, ysb, yTb, ysTb
+    backward["both_layouts"] = both
     del bsegs, blaunches, bev
 
     if args.calibrate_copy:
