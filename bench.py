@@ -321,31 +321,33 @@ def main():
     torch.cuda.synchronize()
     step_bytes = sum(l[3] for l in launches)
 
-    def step(events=None):
+    def step(events=None, only=None):
         for i, (_, _, fn, _) in enumerate(launches):
-            if events is not None:
+            rec = events is not None and (only is None or i == only)
+            if rec:
                 events[i][0].record()
             fn()
-            if events is not None:
+            if rec:
                 events[i][1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in launches] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    ms_per_step = (t_end - t_start) * 1000.0 / args.steps
+    def new_events():
+        return [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                 for _ in launches] for _ in range(args.steps)]
 
+    # per-launch means from an untimed pass with events around every launch; the timed
+    # region then records events only around the dominant launch, so the step rate does
+    # not pay for the other event records
+    pev = new_events()
+    for s in range(args.steps):
+        step(pev[s])
+    torch.cuda.synchronize()
     per_kernel = []
     for i, (kern, segname, _, nbytes) in enumerate(launches):
-        ms = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        ms = [pev[s][i][0].elapsed_time(pev[s][i][1]) for s in range(args.steps)]
         mean_ms = float(np.mean(ms))
         per_kernel.append({
             "kernel": kern, "segment": segname, "alg_bytes": nbytes,
@@ -353,7 +355,23 @@ def main():
             "GBps": round(nbytes / (mean_ms / 1000.0) / 1e9, 1),
             "frac_of_peak": round(nbytes / (mean_ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
         })
-    dom = max(per_kernel, key=lambda p: p["mean_us"])
+    dom_i = max(range(len(per_kernel)), key=lambda i: per_kernel[i]["mean_us"])
+
+    ev = new_events()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s], only=dom_i)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1000.0 / args.steps
+
+    # the dominant launch as measured inside the timed region
+    dms = [ev[s][dom_i][0].elapsed_time(ev[s][dom_i][1]) for s in range(args.steps)]
+    d_mean = float(np.mean(dms))
+    dnb = per_kernel[dom_i]["alg_bytes"]
+    dom = dict(per_kernel[dom_i])
+    dom.update({"mean_us": round(d_mean * 1000.0, 2), "GBps": round(dnb / (d_mean / 1000.0) / 1e9, 1)})
     achieved = dom["GBps"]
     traffic = read_traffic(dom["kernel"], w.name, dom["segment"])
 
@@ -541,8 +559,11 @@ def main():
             "traffic": traffic,
             "alg_bytes_per_launch": dom["alg_bytes"],
             "mean_launch_us": dom["mean_us"],
+            "measured": "HIP events around this launch inside the timed region",
         },
         "per_kernel": per_kernel,
+        "per_kernel_measured": "HIP events around every launch, in an untimed pass of the same steps before "
+                               "the timed region",
         "backward": backward,
         "gemm": gemm,
         "wgrad": wgrad,
