@@ -19,8 +19,9 @@
 // per row; the lanes of a load instruction read 16 rows x 64 bytes).  Loads run
 // kQPrefetch strips ahead.  The column amax is reduced over the lane's eight rows
 // (packed 16-bit max on the magnitude bits) and over the sixteen row groups (two DPP
-// row rotations, then the gfx950 16- and 32-lane swaps); no cross-wave step, so each
-// producer wave runs its strips on its own and only the consumers wait for all of them.
+// row rotations, then the gfx950 16- and 32-lane swaps); no cross-wave step (in the
+// column-only mode), so each producer wave runs its strips on its own and only the
+// consumers wait for all of them.
 // The element convert, v_cvt_scalef32_pk_fp8_bf16, takes one scale for a pair of
 // BF16, and neighbouring columns have different scales, so a pair is two rows of one
 // column (one v_perm_b32): the four converts of a column's eight rows give its eight
@@ -28,6 +29,17 @@
 // magnitudes are clamped to 448 * 2^(S-127) before the convert (it returns NaN for
 // quotients of 464 or more instead of saturating).
 // Consumers (waves 8-15): strips.h.
+//
+// With kRows the kernel also writes the row layout of the same gradient (DGRAD operand,
+// 1x128 blocks along K, the row quantizer's output) from the same read.  A row's
+// 128-column block spans four producer waves, so this mode adds the one cross-wave
+// step: each wave publishes its per-row maxima over its 32 columns to a per-slot LDS
+// array before converting the columns, and afterwards waits (bounded, on per-wave
+// counters) for the block's other three waves, takes each row's block maximum and
+// stores its eight bytes of each row and the scale bytes through resources over the
+// strip's rows.  Loop-invariant offsets are then recomputed from an opaque lane index
+// each strip, because holding them spills, and a spill reload in the loop would wait
+// for the prefetched strip.
 #include "strips.h"
 
 namespace mxfp4 {
