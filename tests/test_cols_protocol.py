@@ -16,7 +16,11 @@ shared access:
     t - 4 (its own reader) and strip t - 3 (which reads strip t - 4 as carry);
   * a producer reads the partial maxima of strip t only once all producer waves
     published them, and no wave overwrites them while another still needs them;
-  * the slot's strip info (written by producer wave 0) is the strip a consumer expects.
+  * the slot's strip info (written by producer wave 0) is the strip a consumer expects;
+  * with the row layout on (fp8q_cols.hip's both-layouts mode), a producer reads the
+    per-row maxima of strip t from the other three waves of its 128-column block only
+    once they published them, and no wave overwrites its slot while a block member
+    still needs the previous strip's maxima.
 
 It checks the protocol design (the wait targets), not the compiled kernel; the GPU
 parity tests check the kernel.
@@ -34,9 +38,11 @@ class Violation(AssertionError):
     pass
 
 
-def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None):
+def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, rows=False, rows_wait=True):
     """PMAX None: no partial maxima.  per_wave (default: PMAX is None): one produced
-    counter per producer wave, the consumers wait for the smallest."""
+    counter per producer wave, the consumers wait for the smallest.  rows: the
+    both-layouts mode (per-wave row maxima exchanged within blocks of four waves);
+    rows_wait False drops the wait for the block (the model must catch that)."""
     if per_wave is None:
         per_wave = PMAX is None
     rnd = random.Random(seed)
@@ -50,6 +56,10 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None):
     info = [None] * SLOTS          # slot -> strip
     done_prod = [[False] * n for _ in range(PW)]       # producer w finished produce(t)
     done_cons = [[False] * n for _ in range(CW)]       # consumer v finished strip t
+    rowmax = [[None] * PW for _ in range(SLOTS)]       # slot -> wave -> strip published there
+    rows_done = [[False] * n for _ in range(PW)]       # producer w finished its rows of strip t
+    for w in range(PW):
+        cnt[f"rowpub{w}"] = 0
 
     def need(cond, msg):
         if not cond:
@@ -81,6 +91,18 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None):
                     yield "wait"
                 e = pmax[t % PMAX]
                 need(e is not None and e[0] == t and len(e[1]) == PW, f"P{w} reads pmax {e} for strip {t}")
+            if rows:
+                # publish this wave's row maxima of strip t into slot t % 4
+                old = rowmax[t % SLOTS][w]
+                if old is not None:
+                    need(old == t - SLOTS, f"P{w} row maxima of {t} over strip {old}")
+                    blk = range(w & ~3, (w & ~3) + 4)
+                    need(all(rows_done[x][old] for x in blk),
+                         f"P{w} overwrites the row maxima of strip {old} while its block still needs them")
+                rowmax[t % SLOTS][w] = t
+                yield None
+                cnt[f"rowpub{w}"] += 1
+                yield None
             s = t % SLOTS
             if w == 0:
                 info[s] = t
@@ -98,6 +120,15 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None):
             yield None
             cnt["produced"] += 1
             cnt[f"produced{w}"] += 1
+            if rows:
+                blk = range(w & ~3, (w & ~3) + 4)
+                if rows_wait:
+                    while min(cnt[f"rowpub{x}"] for x in blk) < t + 1:
+                        yield "wait"
+                for x in blk:
+                    need(rowmax[s][x] == t, f"P{w} reads row maxima {rowmax[s][x]} of P{x} for strip {t}")
+                    yield None
+                rows_done[w][t] = True
             if t + 1 >= n:
                 return
             if PMAX:
@@ -156,6 +187,25 @@ def test_protocol_random_schedules(n, cfg):
     pw, cw, pm = cfg
     for seed in range(60 if cfg == CONFIGS[0] else 30):
         _run(n, seed, PW=pw, CW=cw, PMAX=pm)
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 5, 9, 13])
+def test_protocol_both_layouts_random_schedules(n):
+    """fp8q_cols.hip with the row layout on: 8 producer waves in two blocks of four."""
+    for seed in range(30):
+        _run(n, seed, PW=8, CW=8, PMAX=None, rows=True)
+
+
+def test_model_catches_a_missing_row_block_wait():
+    """Without the wait for the block's other waves, some schedule reads another wave's
+    row maxima before that wave published the strip."""
+    caught = 0
+    for seed in range(40):
+        try:
+            _run(6, seed, PW=8, CW=8, PMAX=None, rows=True, rows_wait=False)
+        except Violation:
+            caught += 1
+    assert caught > 0
 
 
 def test_model_catches_a_weaker_wait():
