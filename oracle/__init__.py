@@ -79,6 +79,13 @@ def _load():
     lib.oracle_nvfp4_encode_scale.argtypes = [F]
     lib.oracle_nvfp4_encode_scale.restype = F
     lib.oracle_nvfp4_rows.argtypes = [P, I64, I64, I64, F, P, P]
+    U64 = ctypes.c_uint64
+    lib.oracle_philox4x32_10.argtypes = [P, P, P]
+    lib.oracle_sr_bits16.argtypes = [U64, I64, I64, I64]
+    lib.oracle_sr_bits16.restype = ctypes.c_uint
+    lib.oracle_e2m1_encode_sr.argtypes = [ctypes.c_double, ctypes.c_uint]
+    lib.oracle_e2m1_encode_sr.restype = ctypes.c_int
+    lib.oracle_nvfp4_rows_sr.argtypes = [P, I64, I64, I64, F, U64, P, P]
     lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_value.restype = ctypes.c_double
     lib.oracle_bf16_round.argtypes = [ctypes.c_double]
@@ -210,6 +217,53 @@ def nvfp4_quantize_rows(x_bits: np.ndarray, rows: int | None = None, threads: in
 
     def run(r):
         lib.oracle_nvfp4_rows(_ptr(x_bits), K, r[0], r[1], t, _ptr(codes), _ptr(scales))
+
+    _run_ranges(run, _ranges(rows, threads * 4), threads)
+    return codes, scales, amax, t
+
+
+def philox4x32_10(counter, key) -> list[int]:
+    """Philox4x32-10 (Salmon et al., SC'11): four 32-bit counter words and two key
+    words -> four output words."""
+    lib = _load()
+    c = np.ascontiguousarray(counter, np.uint32)
+    k = np.ascontiguousarray(key, np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib.oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return [int(v) for v in out]
+
+
+def sr_bits16(seed: int, K: int, m: int, k: int) -> int:
+    """The 16 random bits that element (m, k) of a [*, K] matrix draws under `seed`."""
+    return int(_load().oracle_sr_bits16(seed, K, m, k))
+
+
+def e2m1_encode_sr(a: float, r: int) -> int:
+    """E2M1 magnitude code of a >= 0 rounded stochastically with the 16-bit random r."""
+    return int(_load().oracle_e2m1_encode_sr(a, r))
+
+
+def nvfp4_quantize_rows_sr(x_bits: np.ndarray, seed: int, rows: int | None = None, threads: int = 1):
+    """NVFP4 as nvfp4_quantize_rows with the element codes rounded stochastically
+    (Philox4x32-10 random bits under `seed`); block scales, amax and t unchanged."""
+    lib = _load()
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    assert K % 16 == 0
+    rows = M if rows is None else rows
+    codes = np.zeros((M, K // 2), np.uint8)
+    scales = np.zeros((M, K // 16), np.uint8)
+    parts = []
+
+    def run_amax(r):
+        parts.append(float(lib.oracle_nvfp4_amax(_ptr(x_bits), K, r[0], r[1])))
+
+    _run_ranges(run_amax, _ranges(rows, threads * 4), threads)
+    amax = max(parts) if parts else 0.0
+    t = nvfp4_encode_scale(amax)
+
+    def run(r):
+        lib.oracle_nvfp4_rows_sr(_ptr(x_bits), K, r[0], r[1], t, seed, _ptr(codes), _ptr(scales))
 
     _run_ranges(run, _ranges(rows, threads * 4), threads)
     return codes, scales, amax, t

@@ -561,6 +561,100 @@ void oracle_nvfp4_rows(const uint16_t *x, int64_t K, int64_t row_begin, int64_t 
             oracle_nvfp4_block(x + m * K + 16 * j, t, codes + m * (K / 2) + 8 * j, scales + m * nb + j);
 }
 
+/* ---- NVFP4 with stochastic rounding (gradient quantizers) --------------- */
+
+/* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3" (SC'11): ten rounds on a 128-bit
+ * counter (c0, c1, c2, c3) under a 64-bit key (k0, k1).  A round multiplies c0 and c2
+ * by the two round constants into 64-bit products, and the new counter is
+ * (hi(c2 product) ^ c1 ^ k0, lo(c2 product), hi(c0 product) ^ c3 ^ k1, lo(c0 product));
+ * the key grows by the two Weyl constants after every round. */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+        uint64_t p2 = (uint64_t)0xCD9E8D57u * c[2];
+        uint32_t n0 = (uint32_t)(p2 >> 32) ^ c[1] ^ k0;
+        uint32_t n1 = (uint32_t)p2;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c[0] = n0;
+        c[1] = n1;
+        c[2] = n2;
+        c[3] = n3;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    for (int i = 0; i < 4; ++i)
+        out[i] = c[i];
+}
+
+/* The 16 random bits of element (row m, column k) of a [*, K] matrix under `seed`: the
+ * elements are numbered row-major, n = m K + k; the Philox counter is the index of n's
+ * 8-element chunk, (n / 8 low word, high word, 0, 0), the key (seed low word, high
+ * word), and element j = n % 8 of the chunk takes half j % 2 (0: low) of output word
+ * j / 2. */
+unsigned oracle_sr_bits16(uint64_t seed, int64_t K, int64_t m, int64_t k)
+{
+    uint64_t n = (uint64_t)(m * K + k);
+    uint64_t chunk = n / 8;
+    uint32_t ctr[4] = {(uint32_t)chunk, (uint32_t)(chunk >> 32), 0u, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t w[4];
+    oracle_philox4x32_10(ctr, key, w);
+    int j = (int)(n % 8);
+    return (w[j / 2] >> (16 * (j % 2))) & 0xFFFFu;
+}
+
+/* E2M1 magnitude code of a >= 0, rounded stochastically with the 16-bit random r: at or
+ * above 6 the code of 6; otherwise, between the neighbouring E2M1 values lo <= a < hi,
+ * hi with probability (a - lo) / (hi - lo), taken when r < 65536 (a - lo) / (hi - lo)
+ * (exact: the gaps are powers of two).  Values on the grid never move. */
+int oracle_e2m1_encode_sr(double a, unsigned r)
+{
+    if (a >= 6.0)
+        return 7;
+    int c = 0;
+    while (c < 7 && e2m1_magnitude(c + 1) <= a)
+        ++c;
+    double lo = e2m1_magnitude(c), hi = e2m1_magnitude(c + 1);
+    double f = (a - lo) / (hi - lo);
+    return (double)r < 65536.0 * f ? c + 1 : c;
+}
+
+/* Rows [row_begin, row_end) as oracle_nvfp4_rows, the element codes rounded
+ * stochastically instead of to nearest even (block scales unchanged). */
+void oracle_nvfp4_rows_sr(const uint16_t *x, int64_t K, int64_t row_begin, int64_t row_end, float t,
+                          uint64_t seed, uint8_t *codes, uint8_t *scales)
+{
+    int64_t nb = K / 16;
+    for (int64_t m = row_begin; m < row_end; ++m)
+        for (int64_t j = 0; j < nb; ++j) {
+            const uint16_t *xb = x + m * K + 16 * j;
+            uint8_t unused[8];
+            oracle_nvfp4_block(xb, t, unused, scales + m * nb + j);
+            uint8_t S = scales[m * nb + j];
+            float e = 0.0f;
+            if (S != 0) {
+                e = t / (float)e4m3_value(S);
+                if (e > FLT_MAX)
+                    e = FLT_MAX;
+            }
+            uint8_t c[16];
+            for (int i = 0; i < 16; ++i) {
+                float y = (float)bf16_value(xb[i]) * e;
+                int code = oracle_e2m1_encode_sr((double)fabsf(y), oracle_sr_bits16(seed, K, m, 16 * j + i));
+                if (signbit(y))
+                    code |= 8;
+                c[i] = (uint8_t)code;
+            }
+            for (int i = 0; i < 8; ++i)
+                codes[m * (K / 2) + 8 * j + i] = (uint8_t)(c[2 * i] | (c[2 * i + 1] << 4));
+        }
+}
+
 /* ---- small helpers exported for the pins ------------------------------- */
 
 int oracle_e2m1_encode(double y) { return e2m1_encode(y); }

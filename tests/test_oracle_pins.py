@@ -939,3 +939,121 @@ def test_nvfp4_block_maxima():
         for j in range(16):
             if 0x08 <= scales[m, j] < 0x7E:
                 assert nib[m, j, arg[m, j]] == 7, (m, j)
+
+
+# ---- NVFP4 with stochastic rounding ------------------------------------------------
+# The recipe page rounds the gradient quantizers stochastically (unbiased); the random
+# bits come from Philox4x32-10, pinned to its published known-answer vectors.
+
+def test_philox_known_answers():
+    for v in golden()["philox4x32_10"]["vectors"]:
+        got = oracle.philox4x32_10([int(w, 16) for w in v["counter"]], [int(w, 16) for w in v["key"]])
+        assert got == [int(w, 16) for w in v["out"]]
+
+
+def test_sr_bits_layout_and_uniformity():
+    """Element n of the row-major matrix takes half n % 2 of word (n % 8) / 2 of the
+    Philox block of chunk n / 8; the bits are uniform."""
+    seed, K = 0x0123456789ABCDEF, 48
+    for m, k in [(0, 0), (0, 7), (3, 13), (5, 47)]:
+        n = m * K + k
+        w = oracle.philox4x32_10([n // 8, 0, 0, 0], [seed & 0xFFFFFFFF, seed >> 32])
+        assert oracle.sr_bits16(seed, K, m, k) == (w[(n % 8) // 2] >> (16 * (n % 2))) & 0xFFFF
+    r = np.array([oracle.sr_bits16(7, 64, m, k) for m in range(16) for k in range(64)])
+    counts = np.bincount(r >> 12, minlength=16)          # 1024 draws in 16 bins
+    chi2 = float(((counts - 64.0) ** 2 / 64.0).sum())
+    assert chi2 < 40.0                                    # 15 d.o.f.: p ~ 5e-4
+    assert len(set(r.tolist())) > 990
+
+
+E2M1_GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+@pytest.mark.parametrize("a", [0.0, 0.1, 0.25, 0.5, 0.7, 1.25, 1.75, 2.2, 2.5, 3.9, 4.0, 5.0, 5.999, 6.0, 7.5,
+                               2.0 ** -140, 1e30])
+def test_e2m1_sr_probability_is_exact(a):
+    """Over all 65536 random values, the count that rounds up is ceil(65536 (a - lo) / gap)
+    (brute force, rational arithmetic); results are the two neighbours only."""
+    a32 = float(np.float32(a))
+    codes = np.array([oracle.e2m1_encode_sr(a32, r) for r in range(0, 65536, 1)])
+    if a32 >= 6.0:
+        assert np.all(codes == 7)
+        return
+    lo = max(i for i, v in enumerate(E2M1_GRID) if v <= a32)
+    f = (Fraction(a32) - Fraction(E2M1_GRID[lo])) / (Fraction(E2M1_GRID[lo + 1]) - Fraction(E2M1_GRID[lo]))
+    ups = math.ceil(f * 65536)
+    assert set(codes.tolist()) <= {lo, lo + 1}
+    assert int((codes == lo + 1).sum()) == ups
+    assert np.all(codes[:ups] == lo + 1) and np.all(codes[ups:] == lo)   # r < 65536 f rounds up
+
+
+def _nvfp4_decode(codes, scales, t, K):
+    c = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(codes.shape[0], K)
+    mag = np.array(E2M1_GRID)[c & 7] * np.where(c & 8, -1.0, 1.0)
+    s = np.array([oracle.e4m3_value(int(b)) for b in range(256)])[scales].repeat(16, axis=1)
+    return mag * s / t
+
+
+def test_nvfp4_sr_scales_match_and_codes_bracket():
+    """Block scales, amax and t equal the nearest-even quantizer's; each element decodes to
+    one of the two E2M1 neighbours of FP32(x * e), e from the block scale (numpy FP32)."""
+    seg = workloads.ragged_case([70, 33], 64, seed=9, values="swiglu")
+    x = seg.x_bits[: seg.M_tot]
+    c_sr, s_sr, a_sr, t_sr = oracle.nvfp4_quantize_rows_sr(x, seed=5)
+    c_rn, s_rn, a_rn, t_rn = oracle.nvfp4_quantize_rows(x)
+    assert np.array_equal(s_sr, s_rn) and a_sr == a_rn and t_sr == t_rn
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    Sv = np.array([oracle.e4m3_value(int(b)) for b in range(256)], np.float64)[s_sr].repeat(16, axis=1)
+    e = np.where(Sv > 0, np.float32(t_sr) / Sv.astype(np.float32), np.float32(0)).astype(np.float32)
+    y = np.abs((xf * e).astype(np.float32)).astype(np.float64)
+    c = np.stack([c_sr & 0xF, c_sr >> 4], axis=-1).reshape(x.shape)
+    got = np.array(E2M1_GRID)[c & 7]
+    grid = np.array(E2M1_GRID)
+    lo = grid[np.searchsorted(grid, np.minimum(y, 6.0), side="right") - 1]
+    hi = grid[np.minimum(np.searchsorted(grid, np.minimum(y, 6.0), side="right"), 7)]
+    assert np.all((got == lo) | (got == hi))
+    assert np.all(((c & 8) != 0) == np.signbit(xf))
+    moved = (got != lo)
+    assert 0.2 < moved.mean() < 0.8                      # both neighbours occur
+
+
+def test_nvfp4_sr_is_unbiased_and_keeps_grid_values():
+    """Averaged over seeds, the decoded value approaches x (stochastic rounding is
+    unbiased); elements already on the scaled E2M1 grid never move; a seed is
+    reproducible and different seeds differ."""
+    rng = np.random.default_rng(12)
+    M, K = 4, 32
+    v = rng.standard_normal((M, K)).astype(np.float32)
+    x = workloads.to_bf16_bits(v)
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    n = 400
+    acc = np.zeros((M, K))
+    first = None
+    for s in range(n):
+        codes, scales, _, t = oracle.nvfp4_quantize_rows_sr(x, seed=1000 + s)
+        d = _nvfp4_decode(codes, scales, t, K)
+        acc += d
+        if s == 0:
+            first = codes
+            again, _, _, _ = oracle.nvfp4_quantize_rows_sr(x, seed=1000)
+            assert np.array_equal(first, again)
+        elif s == 1:
+            assert not np.array_equal(first, codes)
+    mean = acc / n
+    # per element the draw is lo or hi: std <= gap / 2, gap <= 2 * scale; 6 sigma
+    _, scales, _, t = oracle.nvfp4_quantize_rows_sr(x, seed=0)
+    step = 2.0 * np.array([oracle.e4m3_value(int(b)) for b in range(256)])[scales].repeat(16, axis=1) / t
+    assert np.all(np.abs(mean - xf) <= 6 * (step / 2) / np.sqrt(n) + 1e-12)
+    # a tensor of scaled grid values: every seed gives the nearest-even codes
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    g = rng.choice(grid, (M, K)) * rng.choice([-1, 1], (M, K))
+    g[:, ::16] = 6.0                                       # each block's max is 6: e = 1 at t ... S
+    xg = workloads.to_bf16_bits(g.astype(np.float32))
+    c_rn, _, _, _ = oracle.nvfp4_quantize_rows(xg)
+    for s in range(4):
+        c_sr, _, _, _ = oracle.nvfp4_quantize_rows_sr(xg, seed=s)
+        dr = _nvfp4_decode(c_rn, *oracle.nvfp4_quantize_rows(xg)[1:2], oracle.nvfp4_quantize_rows(xg)[3], K)
+        ds = _nvfp4_decode(c_sr, *oracle.nvfp4_quantize_rows_sr(xg, seed=s)[1:2],
+                           oracle.nvfp4_quantize_rows_sr(xg, seed=s)[3], K)
+        exact = np.abs(dr - (xg.astype(np.uint32) << 16).view(np.float32)) == 0
+        assert np.array_equal(ds[exact], dr[exact])
