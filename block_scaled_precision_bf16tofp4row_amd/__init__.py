@@ -11,6 +11,8 @@ The binding has the same names as the C ABI:
 
 * ``mxfp4_quantize_rows(x, codes, scales, offs, ...)``
 * ``mxfp4_nvfp4_quantize_rows(x, codes, scales, tensor_amax, offs, ...)`` (NVFP4 variant)
+* ``mxfp4_nvfp4_quantize_rows_sr(x, codes, scales, tensor_amax, offs, seed, ...)`` (the same,
+  element codes rounded stochastically)
 * ``mxfp4_to_fp8_rows(codes, scales, y, y_scales, offs, ...)``
 * ``mxfp4_to_fp8_cols_ragged(codes, scales, yT, yT_scales, offs, ...)``
 * ``mxfp4_bf16_to_fp8_rows(x, y, y_scales, offs, ...)`` and
@@ -48,6 +50,7 @@ MXFP4_ERR_HIP = 4
 EXPORTED = (
     "mxfp4_quantize_rows",
     "mxfp4_nvfp4_quantize_rows",
+    "mxfp4_nvfp4_quantize_rows_sr",
     "mxfp4_to_fp8_rows",
     "mxfp4_to_fp8_cols_ragged",
     "mxfp4_bf16_to_fp8_rows",
@@ -95,9 +98,11 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_fp8_grouped_gemm.restype = st
     lib.mxfp4_fp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
     lib.mxfp4_nvfp4_quantize_rows.argtypes = [P, P, P, P, P, I32, I64, I64, P]
+    lib.mxfp4_nvfp4_quantize_rows_sr.argtypes = [P, P, P, P, P, I32, I64, I64, ctypes.c_uint64, P]
     lib.mxfp4_bf16_to_fp8_rows_cols_ragged.argtypes = [P, P, P, P, P, P, I32, I64, I64, P]
     lib.mxfp4_bf16_to_fp8_rows_cols_ragged.restype = st
     lib.mxfp4_nvfp4_quantize_rows.restype = st
+    lib.mxfp4_nvfp4_quantize_rows_sr.restype = st
     lib.mxfp4_fp8_grouped_gemm_wgrad.restype = st
     lib.mxfp4_cols_scale_capacity.argtypes = [I64, I64, I32]
     lib.mxfp4_cols_scale_capacity.restype = I64
@@ -308,9 +313,11 @@ def mxfp4_fp8_grouped_gemm_wgrad(dyT, dyT_scales, xT, xT_scales, dw, offs, N, K,
            "mxfp4_fp8_grouped_gemm_wgrad")
 
 
-def mxfp4_nvfp4_quantize_rows(x, codes, scales, tensor_amax, offs, G=None, M_cap=None, K=None, stream=None):
+def mxfp4_nvfp4_quantize_rows(x, codes, scales, tensor_amax, offs, G=None, M_cap=None, K=None, stream=None,
+                              seed=None):
     """BF16 [M_cap, K] -> NVFP4 codes [M_cap, K/2], E4M3 block scales [M_cap, K/16] and
-    the tensor amax (one float32 on the GPU); see the header."""
+    the tensor amax (one float32 on the GPU); see the header.  With a seed the element
+    codes are rounded stochastically (mxfp4_nvfp4_quantize_rows_sr)."""
     if G is None:
         G = offs.numel() - 1
     if M_cap is None:
@@ -324,8 +331,20 @@ def mxfp4_nvfp4_quantize_rows(x, codes, scales, tensor_amax, offs, G=None, M_cap
                                         (tensor_amax, 4, "tensor_amax", ("float32",)),
                                         (offs, 4 * (G + 1), "group_offsets", ("int32",))])
     lib = load_library()
-    _check(lib.mxfp4_nvfp4_quantize_rows(_ptr(x), _ptr(codes), _ptr(scales), _ptr(tensor_amax), _ptr(offs),
-                                         G, M_cap, K, _stream(stream)), "mxfp4_nvfp4_quantize_rows")
+    if seed is None:
+        _check(lib.mxfp4_nvfp4_quantize_rows(_ptr(x), _ptr(codes), _ptr(scales), _ptr(tensor_amax), _ptr(offs),
+                                             G, M_cap, K, _stream(stream)), "mxfp4_nvfp4_quantize_rows")
+    else:
+        _check(lib.mxfp4_nvfp4_quantize_rows_sr(_ptr(x), _ptr(codes), _ptr(scales), _ptr(tensor_amax), _ptr(offs),
+                                                G, M_cap, K, int(seed) & 0xFFFFFFFFFFFFFFFF, _stream(stream)),
+               "mxfp4_nvfp4_quantize_rows_sr")
+
+
+def mxfp4_nvfp4_quantize_rows_sr(x, codes, scales, tensor_amax, offs, seed, G=None, M_cap=None, K=None,
+                                 stream=None):
+    """NVFP4 with the element codes rounded stochastically (Philox4x32-10 bits under the
+    64-bit seed); see the header."""
+    mxfp4_nvfp4_quantize_rows(x, codes, scales, tensor_amax, offs, G=G, M_cap=M_cap, K=K, stream=stream, seed=seed)
 
 
 def alloc_nvfp4_outputs(M_cap: int, K: int, device="cuda"):

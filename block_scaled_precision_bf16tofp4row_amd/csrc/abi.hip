@@ -19,7 +19,7 @@ hipError_t launch_fp8_gemm(const uint8_t*, const uint8_t*, const uint8_t*, const
 hipError_t launch_fp8_wgrad(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*,
                             const int32_t*, int32_t, int64_t, int64_t, int64_t, int64_t, hipStream_t);
 hipError_t launch_nvfp4_quantize_rows(const uint16_t*, uint8_t*, uint8_t*, float*, const int32_t*, int32_t,
-                                      int64_t, int64_t, hipStream_t);
+                                      int64_t, int64_t, bool, uint64_t, hipStream_t);
 hipError_t launch_fp8q_cols(const uint16_t*, uint8_t*, uint8_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
                             int64_t, hipStream_t);
 hipError_t launch_fp8q_rows(const uint16_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
@@ -74,9 +74,9 @@ mxfp4_status mxfp4_quantize_rows(const uint16_t* x_bf16, uint8_t* codes, uint8_t
                                                 K, stream));
 }
 
-mxfp4_status mxfp4_nvfp4_quantize_rows(const uint16_t* x_bf16, uint8_t* codes, uint8_t* scales_e4m3,
-                                       float* tensor_amax, const int32_t* group_offsets, int32_t G,
-                                       int64_t M_cap, int64_t K, hipStream_t stream)
+static mxfp4_status nvfp4_entry(const uint16_t* x_bf16, uint8_t* codes, uint8_t* scales_e4m3, float* tensor_amax,
+                                const int32_t* group_offsets, int32_t G, int64_t M_cap, int64_t K, bool sr,
+                                uint64_t seed, hipStream_t stream)
 {
     if (!x_bf16 || !codes || !scales_e4m3 || !tensor_amax || !group_offsets)
         return MXFP4_ERR_NULL;
@@ -87,7 +87,21 @@ mxfp4_status mxfp4_nvfp4_quantize_rows(const uint16_t* x_bf16, uint8_t* codes, u
         !aligned(group_offsets, 4))
         return MXFP4_ERR_ALIGN;
     return from_hip(mxfp4::launch_nvfp4_quantize_rows(x_bf16, codes, scales_e4m3, tensor_amax, group_offsets, G,
-                                                      M_cap, K, stream));
+                                                      M_cap, K, sr, seed, stream));
+}
+
+mxfp4_status mxfp4_nvfp4_quantize_rows(const uint16_t* x_bf16, uint8_t* codes, uint8_t* scales_e4m3,
+                                       float* tensor_amax, const int32_t* group_offsets, int32_t G,
+                                       int64_t M_cap, int64_t K, hipStream_t stream)
+{
+    return nvfp4_entry(x_bf16, codes, scales_e4m3, tensor_amax, group_offsets, G, M_cap, K, false, 0, stream);
+}
+
+mxfp4_status mxfp4_nvfp4_quantize_rows_sr(const uint16_t* x_bf16, uint8_t* codes, uint8_t* scales_e4m3,
+                                          float* tensor_amax, const int32_t* group_offsets, int32_t G,
+                                          int64_t M_cap, int64_t K, uint64_t seed, hipStream_t stream)
+{
+    return nvfp4_entry(x_bf16, codes, scales_e4m3, tensor_amax, group_offsets, G, M_cap, K, true, seed, stream);
 }
 
 mxfp4_status mxfp4_to_fp8_rows(const uint8_t* codes, const uint8_t* scales, uint8_t* y_e4m3,

@@ -23,6 +23,17 @@
 // instruction), and the elements with gfx950's scaled FP4 convert at scale 1 (FP32 in,
 // nearest even, saturating), after a clamp to [-8, 8] that keeps an overflowed product
 // finite without changing its code.
+//
+// Stochastic rounding (the recipe's gradient quantizers, unbiased): the block scales
+// are the same; an element with |y| = |FP32(x * e)| below 6, between the E2M1 values
+// lo <= |y| < hi, takes hi when its 16 random bits r satisfy r < 65536 (|y| - lo) /
+// (hi - lo), else lo (at or above 6: the code of 6).  The gaps are powers of two, so the
+// fraction and the comparison are exact in FP32.  The bits come from Philox4x32-10
+// (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11)
+// keyed by the 64-bit seed, one generator call per 8-element chunk: the counter is the
+// chunk's index in the row-major matrix (low word, high word, 0, 0), and element j of
+// the chunk takes half j % 2 (0: low) of output word j / 2.  A lane computes its own
+// chunk's call, so the conversion is software: the caller picks the mode per call.
 #include <float.h>
 
 #include "strips.h"
@@ -73,6 +84,40 @@ __device__ __forceinline__ uint32_t cvt_pair(uint32_t old, float a, float b, flo
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, ya, yb, 1.0f, kSel);
 }
 
+// Philox4x32-10: ten rounds, each two 32x32 -> 64-bit products of counter words 0 and 2
+// with the round constants; the next counter is (hi2 ^ c1 ^ k0, lo2, hi0 ^ c3 ^ k1, lo0)
+// and the key advances by the Weyl constants (on the scalar unit: it is wave-uniform).
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint32_t lo0 = 0xD2511F53u * c.x;
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
+        const uint32_t lo2 = 0xCD9E8D57u * c.z;
+        const uint32_t hi2 = __umulhi(0xCD9E8D57u, c.z);
+        c = u32x4{hi2 ^ c.y ^ k0, lo2, hi0 ^ c.w ^ k1, lo0};
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// E2M1 code (sign in bit 3) of y rounded stochastically with the random r < 2^16.
+// Below 2 the grid step is 0.5 (codes 0..3 = 2|y| rounded down), in [2, 4) it is 1
+// (codes 4, 5), in [4, 6) it is 2 (code 6); q = |y| / step and its fraction are exact.
+__device__ __forceinline__ uint32_t e2m1_code_sr(float y, uint32_t r)
+{
+    const float a = __builtin_fminf(__builtin_fabsf(y), 6.0f);   // keeps q finite
+    const float inv_step = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+    const uint32_t base = a < 2.0f ? 0u : (a < 4.0f ? 2u : 4u);
+    const float q = a * inv_step;
+    const float fl = __builtin_floorf(q);
+    const uint32_t up = (float)r < (q - fl) * 65536.0f ? 1u : 0u;
+    uint32_t c = (uint32_t)fl + base + up;
+    c = a >= 6.0f ? 7u : c;                        // saturation, an overflowed product included
+    return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
 }  // namespace
 
 __global__ void nvfp4_amax_init_kernel(uint32_t* __restrict__ amax_bits) { *amax_bits = 0u; }
@@ -115,12 +160,13 @@ __global__ __launch_bounds__(kThreads) void nvfp4_amax_kernel(const u32x4* __res
     }
 }
 
+template <bool kSR>
 __global__ __launch_bounds__(kThreads) void nvfp4_quantize_kernel(const u32x4* __restrict__ x,
                                                                   uint32_t* __restrict__ codes,
                                                                   uint8_t* __restrict__ scales,
                                                                   const uint32_t* __restrict__ amax_bits,
                                                                   const int32_t* __restrict__ offs, int G,
-                                                                  int64_t K)
+                                                                  int64_t K, uint32_t seed_lo, uint32_t seed_hi)
 {
     const int64_t nchunks = (int64_t)offs[G] * (K / 8);
     const int64_t base = (int64_t)blockIdx.x * (kThreads * kNvU);
@@ -154,10 +200,24 @@ __global__ __launch_bounds__(kThreads) void nvfp4_quantize_kernel(const u32x4* _
             if (!(e <= FLT_MAX))
                 e = FLT_MAX;
         }
-        uint32_t w = cvt_pair<0>(0u, bf16_lo(v[u].x), bf16_hi(v[u].x), e);
-        w = cvt_pair<1>(w, bf16_lo(v[u].y), bf16_hi(v[u].y), e);
-        w = cvt_pair<2>(w, bf16_lo(v[u].z), bf16_hi(v[u].z), e);
-        w = cvt_pair<3>(w, bf16_lo(v[u].w), bf16_hi(v[u].w), e);
+        uint32_t w;
+        if constexpr (kSR) {
+            const u32x4 r = philox4x32_10(u32x4{(uint32_t)idx, (uint32_t)((uint64_t)idx >> 32), 0u, 0u},
+                                          seed_lo, seed_hi);
+            const uint32_t xs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            const uint32_t rs[4] = {r.x, r.y, r.z, r.w};
+            w = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                w |= e2m1_code_sr(bf16_lo(xs[q]) * e, rs[q] & 0xFFFFu) << (8 * q);
+                w |= e2m1_code_sr(bf16_hi(xs[q]) * e, rs[q] >> 16) << (8 * q + 4);
+            }
+        } else {
+            w = cvt_pair<0>(0u, bf16_lo(v[u].x), bf16_hi(v[u].x), e);
+            w = cvt_pair<1>(w, bf16_lo(v[u].y), bf16_hi(v[u].y), e);
+            w = cvt_pair<2>(w, bf16_lo(v[u].z), bf16_hi(v[u].z), e);
+            w = cvt_pair<3>(w, bf16_lo(v[u].w), bf16_hi(v[u].w), e);
+        }
         if (idx < nchunks) {
             store_stream(codes + idx, w);
             if ((tid & 1) == 0)
@@ -167,7 +227,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_quantize_kernel(const u32x4* _
 }
 
 hipError_t launch_nvfp4_quantize_rows(const uint16_t* x, uint8_t* codes, uint8_t* scales, float* tensor_amax,
-                                      const int32_t* offs, int32_t G, int64_t M_cap, int64_t K, hipStream_t stream)
+                                      const int32_t* offs, int32_t G, int64_t M_cap, int64_t K, bool sr,
+                                      uint64_t seed, hipStream_t stream)
 {
     const int64_t nchunks_cap = M_cap * (K / 8);
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
@@ -191,9 +252,11 @@ hipError_t launch_nvfp4_quantize_rows(const uint16_t* x, uint8_t* codes, uint8_t
     if (grid > 0x7FFFFFFF)
         return hipErrorInvalidValue;
     const uint32_t* abc = ab;
-    void* qargs[] = {(void*)&xv, (void*)&cv, (void*)&scales, (void*)&abc, (void*)&offs, (void*)&g, (void*)&k};
-    return hipLaunchKernel((const void*)nvfp4_quantize_kernel, dim3((unsigned)grid), dim3(kThreads), qargs, 0,
-                           stream);
+    uint32_t seed_lo = (uint32_t)seed, seed_hi = (uint32_t)(seed >> 32);
+    void* qargs[] = {(void*)&xv, (void*)&cv,   (void*)&scales,  (void*)&abc,    (void*)&offs,
+                     (void*)&g,  (void*)&k, (void*)&seed_lo, (void*)&seed_hi};
+    const void* fn = sr ? (const void*)nvfp4_quantize_kernel<true> : (const void*)nvfp4_quantize_kernel<false>;
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), qargs, 0, stream);
 }
 
 }  // namespace mxfp4

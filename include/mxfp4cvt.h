@@ -86,6 +86,21 @@ mxfp4_status mxfp4_nvfp4_quantize_rows(const uint16_t* x_bf16, uint8_t* codes, u
                                        float* tensor_amax, const int32_t* group_offsets, int32_t G,
                                        int64_t M_cap, int64_t K, hipStream_t stream);
 
+/* BF16 -> NVFP4 with stochastic rounding of the element codes: the NVFP4 recipe page
+ * rounds its gradient quantizers stochastically to keep small updates unbiased.  The
+ * arguments, block scales, tensor amax, errors and launches are mxfp4_nvfp4_quantize_rows';
+ * only the element codes differ.  With y = FP32(x * FP32(t / S)) as there: |y| >= 6 gives
+ * the code of 6; otherwise, between the E2M1 values lo <= |y| < hi, the code of hi when
+ * r < 65536 (|y| - lo) / (hi - lo) and of lo else (sign of x kept).  r is 16 random bits
+ * from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+ * 1, 2, 3", SC'11) under key (seed & 0xFFFFFFFF, seed >> 32): element (m, k), numbered
+ * n = m K + k from row 0 of x, takes half n % 2 (0: the low 16 bits) of output word
+ * (n % 8) / 2 of the call on counter (n / 8 low word, high word, 0, 0).  The same seed
+ * gives the same codes; callers pass a new seed per step. */
+mxfp4_status mxfp4_nvfp4_quantize_rows_sr(const uint16_t* x_bf16, uint8_t* codes, uint8_t* scales_e4m3,
+                                          float* tensor_amax, const int32_t* group_offsets, int32_t G,
+                                          int64_t M_cap, int64_t K, uint64_t seed, hipStream_t stream);
+
 /* MXFP4 -> FP8 E4M3FN, row layout for FPROP (the page's FP4RowToFP8Row; technical
  * summary section 2, item 1, hierarchical scale alignment).
  *   codes, scales  as produced by mxfp4_quantize_rows.

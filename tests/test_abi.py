@@ -2,6 +2,7 @@
 header declares, and rejects bad arguments synchronously (before any HIP call)
 with the documented status codes."""
 import ctypes
+import functools
 import os
 import re
 
@@ -185,13 +186,17 @@ def test_grouped_gemm_argument_errors(lib):
     assert _gm(lib, M=0) == mx.MXFP4_OK
 
 
-def _nv(lib, x=A, c=A2, s=A3, am=A4, o=OFFS, G=1, M=4, K=32):
+def _nv(lib, x=A, c=A2, s=A3, am=A4, o=OFFS, G=1, M=4, K=32, sr=False):
+    if sr:
+        return lib.mxfp4_nvfp4_quantize_rows_sr(x, c, s, am, o, G, M, K, 0x1234, None)
     return lib.mxfp4_nvfp4_quantize_rows(x, c, s, am, o, G, M, K, None)
 
 
-def test_nvfp4_quantizer_argument_errors(lib):
+@pytest.mark.parametrize("sr", [False, True])
+def test_nvfp4_quantizer_argument_errors(lib, sr):
     # rejected before anything is enqueued (a valid call writes the amax even for
-    # M_cap == 0, so it needs a GPU)
+    # M_cap == 0, so it needs a GPU); the stochastic-rounding entry checks the same
+    _nv = functools.partial(globals()["_nv"], sr=sr)
     for kw in ("x", "c", "s", "am", "o"):
         assert _nv(lib, **{kw: None}) == mx.MXFP4_ERR_NULL
     assert _nv(lib, K=8) == mx.MXFP4_ERR_SHAPE            # K % 16
