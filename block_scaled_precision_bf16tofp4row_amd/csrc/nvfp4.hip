@@ -91,11 +91,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
 {
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
-        const uint32_t lo0 = 0xD2511F53u * c.x;
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
-        const uint32_t lo2 = 0xCD9E8D57u * c.z;
-        const uint32_t hi2 = __umulhi(0xCD9E8D57u, c.z);
-        c = u32x4{hi2 ^ c.y ^ k0, lo2, hi0 ^ c.w ^ k1, lo0};
+        const uint64_t p0 = (uint64_t)c.x * 0xD2511F53u;
+        const uint64_t p2 = (uint64_t)c.z * 0xCD9E8D57u;
+        c = u32x4{(uint32_t)(p2 >> 32) ^ c.y ^ k0, (uint32_t)p2, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0};
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
