@@ -25,7 +25,8 @@ GEMM (mxfp4_fp8_grouped_gemm) on the hidden segment's FP8 row output against
 per-expert E4M3 weights ([8, 4096, 7168], synthetic), with its MFMA roofline; ``wgrad``
 times the weight-gradient GEMM (mxfp4_fp8_grouped_gemm_wgrad) on the hidden segment's
 FP8 column output and a column-quantized synthetic [M, 4096] gradient; ``nvfp4`` times
-the NVFP4 variant quantizer (mxfp4_nvfp4_quantize_rows) per forward segment.  ``cpu_baseline`` times the CPU oracle on a bounded
+the NVFP4 variant quantizer (mxfp4_nvfp4_quantize_rows, nearest even and stochastic
+rounding) per forward segment.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same workload on this host (all allowed threads, and one thread).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload config5] [--no-scrubbed]
@@ -446,16 +447,19 @@ def main():
         if sg.K % 16:
             continue
         nc, ns, na = mx.alloc_nvfp4_outputs(sg.M_cap, sg.K, dev)
-        nms = time_launches(lambda d=d: mx.mxfp4_nvfp4_quantize_rows(d["x"], nc, ns, na, d["offs"]))
         n_el = sg.M_tot * sg.K
         nbytes = int(n_el * (2 + 2 + 0.5 + 1 / 16))
-        us = float(np.mean(nms)) * 1000.0
-        gbs = nbytes / (us * 1e-6) / 1e9
-        nvfp4.append({"segment": sg.name, "bytes_per_call": nbytes, "mean_us": round(us, 2),
-                      "median_us": round(float(np.median(nms)) * 1000.0, 2), "GBps": round(gbs, 1),
-                      "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)})
-        log(f"[bench] nvfp4 {sg.name}: {us:.1f} us per call (3 launches), {gbs:.0f} GB/s "
-            f"({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+        # nearest even, then stochastic rounding (Philox4x32-10 bits, a fixed seed)
+        for rounding, seed in (("nearest_even", None), ("stochastic", 0x5EED)):
+            nms = time_launches(lambda d=d, seed=seed: mx.mxfp4_nvfp4_quantize_rows(d["x"], nc, ns, na, d["offs"],
+                                                                                    seed=seed))
+            us = float(np.mean(nms)) * 1000.0
+            gbs = nbytes / (us * 1e-6) / 1e9
+            nvfp4.append({"segment": sg.name, "rounding": rounding, "bytes_per_call": nbytes,
+                          "mean_us": round(us, 2), "median_us": round(float(np.median(nms)) * 1000.0, 2),
+                          "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)})
+            log(f"[bench] nvfp4 {rounding} {sg.name}: {us:.1f} us per call (3 launches), {gbs:.0f} GB/s "
+                f"({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
         del nc, ns, na
 
     # the backward FP8 quantizer on the same segments, timed the same way (not in `value`)
