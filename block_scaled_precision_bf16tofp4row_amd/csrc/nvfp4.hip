@@ -101,19 +101,20 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
 }
 
 // E2M1 code (sign in bit 3) of y rounded stochastically with the random r < 2^16.
-// Below 2 the grid step is 0.5 (codes 0..3 = 2|y| rounded down), in [2, 4) it is 1
-// (codes 4, 5), in [4, 6) it is 2 (code 6); q = |y| / step and its fraction are exact.
+// The grid step is 2^(E - 128) with E = max(binade of |y|, 127): 0.5 below 2, 1 in
+// [2, 4), 2 from 4.  q = |y| / step is exact (a power-of-two scaling up, or down to at
+// least 2); the code is floor(q) + 2 (E - 127), plus one when r < 65536 frac(q) (exact:
+// frac(q) is (|y| - lo) / step).  Magnitudes from 6 up reach code 7 or more and are
+// clamped; the min with 4 keeps q finite for an overflowed product.
 __device__ __forceinline__ uint32_t e2m1_code_sr(float y, uint32_t r)
 {
-    const float a = __builtin_fminf(__builtin_fabsf(y), 6.0f);   // keeps q finite
-    const float inv_step = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
-    const uint32_t base = a < 2.0f ? 0u : (a < 4.0f ? 2u : 4u);
-    const float q = a * inv_step;
+    const uint32_t yb = __float_as_uint(y);
+    const uint32_t E = max((yb >> 23) & 0xFFu, 127u);
+    const float q = __builtin_fminf(__builtin_ldexpf(__builtin_fabsf(y), 128 - (int)E), 4.0f);
     const float fl = __builtin_floorf(q);
     const uint32_t up = (float)r < (q - fl) * 65536.0f ? 1u : 0u;
-    uint32_t c = (uint32_t)fl + base + up;
-    c = a >= 6.0f ? 7u : c;                        // saturation, an overflowed product included
-    return c | ((__float_as_uint(y) >> 28) & 8u);
+    const uint32_t c = min((uint32_t)fl + 2u * (E - 127u) + up, 7u);
+    return c | ((yb >> 28) & 8u);
 }
 
 }  // namespace
