@@ -64,10 +64,7 @@ constexpr int kProducerWaves = 4;
 constexpr int kConsumerWaves = 12;
 // a strip is 32 store instructions (256 columns x 128 bytes); consumer wave v issues
 // instructions v, v + 12, v + 24 (< 32)
-#ifndef MXFP4_COLS_PREFETCH
-#define MXFP4_COLS_PREFETCH 2
-#endif
-constexpr int kPrefetch = MXFP4_COLS_PREFETCH;    // strips of loads in flight per producer wave
+constexpr int kPrefetch = 2;                      // strips of loads in flight per producer wave
 constexpr int kColsThreads = 64 * (kProducerWaves + kConsumerWaves);
 static_assert(kStripRows == 32 * kProducerWaves, "a producer wave converts 32 rows");
 static_assert(kTileCols == 32 * 8, "a producer lane converts one MX group of 8");

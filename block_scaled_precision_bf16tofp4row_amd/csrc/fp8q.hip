@@ -103,11 +103,14 @@ __global__ __launch_bounds__(kThreads) void fp8q_rows_kernel(
     const u32x4* __restrict__ x, u32x2* __restrict__ y, uint8_t* __restrict__ y_scales,
     const int32_t* __restrict__ offs, int G, int64_t K)
 {
+    // the workgroup's scale bytes (one per 16-lane row), consecutive in y_scales
+    constexpr int kScaleBytes = kThreads * U / 16;
+    __shared__ __attribute__((aligned(16))) uint8_t sbuf[kScaleBytes];
     const int64_t m_tot = offs[G];
     const int64_t nchunks = m_tot * (K / 8);           // 16-byte chunks of 8 BF16
     const int64_t base = (int64_t)blockIdx.x * (kThreads * U);
     if (base >= nchunks)
-        return;
+        return;                                        // uniform over the workgroup
     const int tid = threadIdx.x;
     u32x4 v[U];
 #pragma unroll
@@ -125,18 +128,29 @@ __global__ __launch_bounds__(kThreads) void fp8q_rows_kernel(
         if (idx < nchunks) {
             store_stream(y + idx, out);
             if ((tid & 15) == 0)
-                y_scales[idx >> 4] = (uint8_t)S;
+                sbuf[(u * kThreads + tid) >> 4] = (uint8_t)S;
         }
+    }
+    // The scale bytes go out as whole 16-byte pieces (single-byte stores from every
+    // sixteenth lane, spread over workgroups, would each be a partial write to memory).
+    // The last workgroup may end inside a piece: its bytes past m_tot * K / 128 stay
+    // untouched.
+    __syncthreads();
+    if (tid < kScaleBytes / 16) {
+        const int64_t nb = nchunks >> 4;
+        const int64_t p = (base >> 4) + 16 * tid;
+        if (p + 16 <= nb)
+            store_stream(reinterpret_cast<u32x4*>(y_scales + p), *reinterpret_cast<const u32x4*>(sbuf + 16 * tid));
+        else
+            for (int q = 0; q < 16 && p + q < nb; ++q)
+                y_scales[p + q] = sbuf[16 * tid + q];
     }
 }
 
 }  // namespace
 
-#ifndef MXFP4_FP8Q_UNROLL
-#define MXFP4_FP8Q_UNROLL 4
-#endif
 // 16-byte chunks per thread (all loads issued before any conversion)
-constexpr int kFp8qU = MXFP4_FP8Q_UNROLL;
+constexpr int kFp8qU = 4;
 
 hipError_t launch_fp8q_rows(const uint16_t* x, uint8_t* y, uint8_t* y_scales,
                             const int32_t* offs, int32_t G, int64_t M_cap, int64_t K,

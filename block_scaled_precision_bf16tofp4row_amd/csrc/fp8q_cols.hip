@@ -46,15 +46,9 @@ namespace mxfp4 {
 
 typedef __bf16 qbf16x2 __attribute__((ext_vector_type(2)));
 
-#ifndef MXFP4_FP8QC_CONSUMERS
-#define MXFP4_FP8QC_CONSUMERS 8
-#endif
-#ifndef MXFP4_FP8QC_PREFETCH
-#define MXFP4_FP8QC_PREFETCH 1
-#endif
 constexpr int kQProducerWaves = 8;                          // 32 columns each
-constexpr int kQConsumerWaves = MXFP4_FP8QC_CONSUMERS;
-constexpr int kQPrefetch = MXFP4_FP8QC_PREFETCH;            // strips of loads in flight
+constexpr int kQConsumerWaves = 8;
+constexpr int kQPrefetch = 1;                               // strips of loads in flight
 constexpr int kQThreads = 64 * (kQProducerWaves + kQConsumerWaves);
 static_assert(kTileCols == 32 * kQProducerWaves, "a producer wave quantizes 32 columns");
 static_assert(kStripRows == 128, "sixteen row groups of eight rows");

@@ -15,7 +15,8 @@
 // and writes 16 FP8 bytes, so a wave's code loads (512 B) and FP8 stores (1 KiB) are
 // each one contiguous run.  The conversion is integer-only: the 8-entry byte table
 // for the lane's gap (from a 14-entry LDS table) is indexed four codes at a time by
-// one v_perm_b32.
+// one v_perm_b32.  The FP8 block-scale bytes of a workgroup (one per 128-block) are
+// gathered in LDS and written as whole 16-byte pieces.
 #include "common.h"
 
 namespace mxfp4 {
@@ -29,16 +30,15 @@ __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(
     const int32_t* __restrict__ offs, int G, int64_t K)
 {
     __shared__ uint32_t lut[2 * (kMaxGap + 1)];
+    // the workgroup's FP8 block-scale bytes, consecutive in y_scales
+    constexpr int kScaleBytes = kThreads * U / 8;
+    __shared__ __attribute__((aligned(16))) uint8_t sbuf[kScaleBytes];
     const int tid = threadIdx.x;
-    if (tid < 2 * (kMaxGap + 1))
-        lut[tid] = kRowsGapLut.w[tid >> 1][tid & 1];
-    __syncthreads();
-
     const int64_t m_tot = offs[G];
     const int64_t nunits = m_tot * (K / 16);           // units of 16 codes (8 bytes)
     const int64_t base = (int64_t)blockIdx.x * (kThreads * U);
-    if (base >= nunits)
-        return;
+    // the loads go out before the gap table is staged and the barrier, so a workgroup's
+    // first memory requests do not wait for its set-up
     u32x2 c[U];
     uint32_t sc[U];
 #pragma unroll
@@ -48,6 +48,11 @@ __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(
         c[u] = ok ? load_stream(codes + idx) : u32x2{0, 0};
         sc[u] = ok ? scales4[idx >> 3] : 0u;
     }
+    if (tid < 2 * (kMaxGap + 1))
+        lut[tid] = kRowsGapLut.w[tid >> 1][tid & 1];
+    __syncthreads();
+    if (base >= nunits)
+        return;                                        // uniform over the workgroup
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int64_t idx = base + u * kThreads + tid;
@@ -63,16 +68,26 @@ __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(
         u32x4 o = {a.x, a.y, bb.x, bb.y};
         store_stream(y + idx, o);
         if ((idx & 7) == 0)
-            y_scales[idx >> 3] = (uint8_t)S;
+            sbuf[(u * kThreads + tid) >> 3] = (uint8_t)S;
+    }
+    // The block-scale bytes go out as whole 16-byte pieces (single-byte stores from every
+    // eighth lane, spread over workgroups, would each be a partial write to memory).  The
+    // last workgroup may end inside a piece: its bytes past m_tot * K / 128 stay untouched.
+    __syncthreads();
+    if (tid < kScaleBytes / 16) {
+        const int64_t nb = nunits >> 3;
+        const int64_t p = (base >> 3) + 16 * tid;
+        if (p + 16 <= nb)
+            store_stream(reinterpret_cast<u32x4*>(y_scales + p), *reinterpret_cast<const u32x4*>(sbuf + 16 * tid));
+        else
+            for (int q = 0; q < 16 && p + q < nb; ++q)
+                y_scales[p + q] = sbuf[16 * tid + q];
     }
 }
 
-#ifndef MXFP4_ROWS_UNROLL
-#define MXFP4_ROWS_UNROLL 2
-#endif
 // 8-byte code units per thread (all loads issued before any conversion); two measured
-// slightly faster than one, four or eight on MI355X
-constexpr int kRowsU = MXFP4_ROWS_UNROLL;
+// faster than one, three, four or eight on MI355X
+constexpr int kRowsU = 2;
 
 hipError_t launch_fp8_rows(const uint8_t* codes, const uint8_t* scales, uint8_t* y,
                            uint8_t* y_scales, const int32_t* offs, int32_t G, int64_t M_cap,
