@@ -14,10 +14,11 @@ step / wall time per step.  ``roofline`` reports the dominant kernel (largest
 time per step): algorithmic bytes per launch / its mean launch time, measured
 with HIP events on the launch stream inside the timed region, against the
 8 TB/s HBM peak.  ``per_config_scrubbed`` adds, for the dispatch workload
-(32768 x 7168 over 32 experts), the dense workload (65536 x 7168) and the
-forward chain, every launch's median over 20 launches each preceded by a 512 MB
-scrub read (so inputs come from HBM, not the caches), next to a device copy
-moving the same bytes.  ``backward`` times the FP8 gradient quantizer
+(32768 x 7168 over 32 experts), the weight-gradient conversion workload (quantize
+and columns over 32768 x 7168, 32 experts), the dense workload (65536 x 7168) and
+the forward chain, every launch's median over 20 launches each preceded by a 512 MB
+scrub read (so inputs come from HBM, not the caches), next to a hand-written
+16-byte streaming copy (libmxfp4bench) moving the same bytes.  ``backward`` times the FP8 gradient quantizer
 (mxfp4_bf16_to_fp8_rows and mxfp4_bf16_to_fp8_cols_ragged) on the same segments,
 outside ``value``, and the same quantizer writing both layouts from one read
 (mxfp4_bf16_to_fp8_rows_cols_ragged); the scrubbed medians include the separate launches.  ``gemm`` times the forward expert
@@ -27,7 +28,7 @@ times the weight-gradient GEMM (mxfp4_fp8_grouped_gemm_wgrad) on the hidden segm
 FP8 column output and a column-quantized synthetic [M, 4096] gradient; ``nvfp4`` times
 the NVFP4 variant quantizer (mxfp4_nvfp4_quantize_rows, nearest even and stochastic
 rounding) per forward segment.  ``cpu_baseline`` times the CPU oracle on a bounded
-sample of the same workload on this host (all allowed threads, and one thread).
+sample of the same workload on this host (up to 16 threads, and one thread).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload config5] [--no-scrubbed]
 """
@@ -62,6 +63,8 @@ KERNEL_SOURCES = {
     "nvfp4": ["nvfp4.hip", "strips.h", "common.h"],
 }
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix throughput, vendor datasheet
+DTYPE = "bf16 -> mxfp4 (e2m1 + ue8m0 per 32) -> fp8 (e4m3fn + ue8m0 per 128)"
+BENCH_LIB = os.path.join(ROOT, "block_scaled_precision_bf16tofp4row_amd", "libmxfp4bench.so")
 
 
 def log(msg):
@@ -109,12 +112,20 @@ def read_traffic(kernel: str, workload: str, segment: str):
     return ent.get("bytes_per_launch")
 
 
-def affinity_threads() -> int:
+def affinity_cpus() -> int:
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        return os.cpu_count() or 1
+
+
+# The oracle's thread pool: the CPUs this process may run on, at most 16 (the host
+# share that goes with one GPU on a shared multi-GPU host).
+MAX_ORACLE_THREADS = 16
+
+
+def affinity_threads() -> int:
+    return max(1, min(MAX_ORACLE_THREADS, affinity_cpus()))
 
 
 # ---- CPU baseline (oracle, bounded sample) --------------------------------------------
@@ -160,6 +171,8 @@ def cpu_baseline(workload, target_s: float = 15.0):
         "value": round(b / t / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
+        "threads_used": threads,
+        "affinity_cpus": affinity_cpus(),
         "kind": "oracle",
         "sample": (f"first {rows} of {max_rows} routed rows of every segment "
                    f"({frac:.1%} of a step: the same kernels, offsets clipped to the sample), "
@@ -230,11 +243,12 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
     scrub that reads `scrub_bytes` (evicting the L2s and the memory-side cache, whose
     dirty lines from the previous launch are written back before the timed region,
     while the scrub's own lines are clean), timed with HIP events on the launch
-    stream; next to it a device copy (torch copy_) moving the same number of bytes
-    (half read, half written), timed the same way."""
+    stream; next to it the hand-written copy (bench_copy16, the fastest unroll measured
+    here) moving the same number of bytes (half read, half written), timed the same way."""
     import workloads
     stream = torch.cuda.current_stream()
     scrub = torch.ones(scrub_bytes // 4, dtype=torch.int32, device=dev)
+    copy = DeviceCopy(torch, dev)
 
     def median_us(fn):
         for i in range(warmup):
@@ -264,7 +278,7 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
             half = (nbytes // 2 + 15) // 16 * 16
             src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
             dst = torch.empty(half, dtype=torch.uint8, device=dev)
-            cus = median_us(lambda: dst.copy_(src))
+            cus = median_us(lambda: copy(dst, src))
             del src, dst
             gbs = nbytes / (us * 1e-6) / 1e9
             copy_gbs = 2 * half / (cus * 1e-6) / 1e9
@@ -279,7 +293,56 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
         torch.cuda.empty_cache()
     del scrub
     torch.cuda.empty_cache()
+    out["copy_kernel"] = {"what": "bench_copy16: 16-byte nontemporal loads then stores, one-shot grid",
+                          "unroll": copy.unroll, "unroll_GBps_1GiB": copy.sweep}
     return out
+
+
+class DeviceCopy:
+    """The hand-written streaming copy of libmxfp4bench, with the unroll (16-byte pieces
+    per thread) that moves 1 GiB fastest on this GPU."""
+
+    @staticmethod
+    def load():
+        import ctypes
+        if not os.path.exists(BENCH_LIB):
+            raise RuntimeError(f"{BENCH_LIB} is missing: build with "
+                               "`python -m block_scaled_precision_bf16tofp4row_amd.build`")
+        lib = ctypes.CDLL(BENCH_LIB)
+        lib.bench_copy16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_void_p]
+        lib.bench_copy16.restype = ctypes.c_int
+        return lib
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.lib = self.load()
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.sweep = {}
+        for u in (1, 2, 4, 8):
+            self.unroll = u
+            for _ in range(3):
+                self(dst, src)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(10):
+                self(dst, src)
+            b.record()
+            torch.cuda.synchronize()
+            self.sweep[u] = round(2 * n * 10 / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+        assert torch.equal(dst[:: 1 << 20], src[:: 1 << 20])
+        self.unroll = max(self.sweep, key=self.sweep.get)
+        log(f"[bench] copy kernel GB/s by unroll (1 GiB): {self.sweep}; using {self.unroll}")
+        del src, dst
+
+    def __call__(self, dst, src):
+        n = min(dst.numel() * dst.element_size(), src.numel() * src.element_size())
+        st = self.lib.bench_copy16(dst.data_ptr(), src.data_ptr(), n // 16, self.unroll,
+                                   self.torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"bench_copy16 failed: {st}")
 
 
 # ---- GPU run -----------------------------------------------------------------------
@@ -296,7 +359,7 @@ def main():
     ap.add_argument("--gemm-n", type=int, default=4096,
                     help="output features of the expert GEMM timed on the hidden segment (0: skip)")
     ap.add_argument("--no-scrubbed", action="store_true",
-                    help="skip the per-kernel scrubbed medians of configs 2, 4 and 5")
+                    help="skip the per-kernel scrubbed medians of configs 2, 3, 4 and 5")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -519,14 +582,19 @@ def main():
     del bsegs, blaunches, bev
 
     if args.calibrate_copy:
+        # three copies of exactly 1 GiB by the hand-written copy kernel (unroll 4), whose
+        # HBM counters scale the counters of the kernels above
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         b = torch.empty(n, dtype=torch.uint8, device=dev)
+        cp = DeviceCopy.__new__(DeviceCopy)
+        cp.torch, cp.unroll = torch, 4
+        cp.lib = DeviceCopy.load()
         torch.cuda.synchronize()
         for _ in range(3):
-            b.copy_(a)
+            cp(b, a)
         torch.cuda.synchronize()
-        log(f"[bench] calibration copy: 3 x {n} bytes read + {n} bytes written")
+        log(f"[bench] calibration copy (copy16_kernel<4>): 3 x {n} bytes read + {n} bytes written")
         del a, b
 
     value = step_bytes / (ms_per_step / 1000.0) / 1e9
@@ -541,7 +609,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u8",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {
             "workload": w.name + ": " + w.description,
@@ -578,8 +646,8 @@ def main():
     if not args.no_scrubbed:
         del segs, launches, ev
         torch.cuda.empty_cache()
-        log("[bench] per-kernel medians with the caches scrubbed (configs 2, 4, 5)")
-        result["per_config_scrubbed"] = scrubbed_medians(mx, torch, dev, (2, 4, 5))
+        log("[bench] per-kernel medians with the caches scrubbed (configs 2, 3, 4, 5)")
+        result["per_config_scrubbed"] = scrubbed_medians(mx, torch, dev, (2, 3, 4, 5))
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w)

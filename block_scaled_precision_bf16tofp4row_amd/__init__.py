@@ -24,6 +24,8 @@ The binding has the same names as the C ABI:
   (FP8 weight-gradient GEMM over the column layouts)
 * ``mxfp4_cols_scale_capacity(M_cap, K, G)``, ``mxfp4_validate_offsets(offs, ...)``,
   ``mxfp4_status_string(status)``
+* ``mxfp4_wait_status(stream)`` (raises if a column conversion's bounded wait gave up
+  since the last check) and ``mxfp4_set_wait_limit(polls)`` (its test hook)
 
 Array arguments are torch tensors on the GPU (BF16 input as ``torch.bfloat16``
 or ``torch.int16``/``torch.uint16`` bits; uint8 outputs; int32 offsets), or raw
@@ -60,6 +62,8 @@ EXPORTED = (
     "mxfp4_fp8_grouped_gemm_wgrad",
     "mxfp4_cols_scale_capacity",
     "mxfp4_validate_offsets",
+    "mxfp4_wait_status",
+    "mxfp4_set_wait_limit",
     "mxfp4_status_string",
 )
 
@@ -108,6 +112,10 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_cols_scale_capacity.restype = I64
     lib.mxfp4_validate_offsets.argtypes = [P, I32, I64, P]
     lib.mxfp4_validate_offsets.restype = st
+    lib.mxfp4_wait_status.argtypes = [P]
+    lib.mxfp4_wait_status.restype = st
+    lib.mxfp4_set_wait_limit.argtypes = [ctypes.c_uint32]
+    lib.mxfp4_set_wait_limit.restype = None
     lib.mxfp4_status_string.argtypes = [st]
     lib.mxfp4_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -366,6 +374,22 @@ def mxfp4_validate_offsets(offs, G=None, M_cap=None, stream=None) -> bool:
         return False
     _check(st, "mxfp4_validate_offsets")
     return True
+
+
+def mxfp4_wait_status(stream=None) -> None:
+    """Synchronize the stream; raise Mxfp4Error (MXFP4_ERR_HIP) if a bounded wait of a
+    column conversion on this device gave up since the last check (the status is
+    cleared by the check)."""
+    _check(load_library().mxfp4_wait_status(_stream(stream)),
+           "mxfp4_wait_status (a column conversion left part of its output unwritten)")
+
+
+def mxfp4_set_wait_limit(polls: int) -> None:
+    """Polls per bounded wait of the column conversions launched after this call
+    (0: the default, 2^24).  A test hook for the give-up path."""
+    if not 0 <= int(polls) < 2 ** 32:
+        raise ValueError("polls must fit in 32 bits")
+    load_library().mxfp4_set_wait_limit(int(polls))
 
 
 # ---- output allocation (plumbing: torch device memory) ----------------------------

@@ -3,7 +3,9 @@
     python -m block_scaled_precision_bf16tofp4row_amd.build
 
 Compiles every ``csrc/*.hip`` to an object (in parallel) and links them into
-``block_scaled_precision_bf16tofp4row_amd/libmxfp4cvt.so``.
+``block_scaled_precision_bf16tofp4row_amd/libmxfp4cvt.so``; then builds the
+benchmark's copy kernel (``csrc/bench/copy16.hip``) into ``libmxfp4bench.so``, a
+separate library the product never loads.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmxfp4cvt.so")
+BENCH_SRC = os.path.join(CSRC, "bench", "copy16.hip")
+BENCH_LIB = os.path.join(PKG, "libmxfp4bench.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -37,6 +41,9 @@ def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     procs = []
     objs = []
+    bench_tmp = BENCH_LIB + ".tmp"
+    bench_cmd = [HIPCC, *CFLAGS, "-shared", BENCH_SRC, "-o", bench_tmp]
+    procs.append((BENCH_SRC, subprocess.Popen(bench_cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     for src in sources():
         obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
@@ -63,6 +70,7 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
+    os.replace(bench_tmp, BENCH_LIB)
     return LIB
 
 

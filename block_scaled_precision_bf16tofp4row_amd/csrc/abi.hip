@@ -3,6 +3,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "mxfp4cvt.h"
 #include "common.h"
 
@@ -12,7 +15,7 @@ hipError_t launch_quantize_rows(const uint16_t*, uint8_t*, uint8_t*, const int32
 hipError_t launch_fp8_rows(const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, const int32_t*,
                            int32_t, int64_t, int64_t, hipStream_t);
 hipError_t launch_fp8_cols(const uint8_t*, const uint8_t*, uint8_t*, uint8_t*, const int32_t*,
-                           int32_t, int64_t, int64_t, hipStream_t);
+                           int32_t, int64_t, int64_t, WaitCtl, hipStream_t);
 int64_t cols_block_capacity(int64_t M_cap, int32_t G);
 hipError_t launch_fp8_gemm(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, uint16_t*,
                            const int32_t*, int32_t, int64_t, int64_t, int64_t, hipStream_t);
@@ -21,7 +24,7 @@ hipError_t launch_fp8_wgrad(const uint8_t*, const uint8_t*, const uint8_t*, cons
 hipError_t launch_nvfp4_quantize_rows(const uint16_t*, uint8_t*, uint8_t*, float*, const int32_t*, int32_t,
                                       int64_t, int64_t, bool, uint64_t, hipStream_t);
 hipError_t launch_fp8q_cols(const uint16_t*, uint8_t*, uint8_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
-                            int64_t, hipStream_t);
+                            int64_t, WaitCtl, hipStream_t);
 hipError_t launch_fp8q_rows(const uint16_t*, uint8_t*, uint8_t*, const int32_t*, int32_t, int64_t,
                             int64_t, hipStream_t);
 }  // namespace mxfp4
@@ -51,6 +54,61 @@ mxfp4_status check_shape(int32_t G, int64_t M_cap, int64_t K, int64_t k_multiple
 }
 
 mxfp4_status from_hip(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP; }
+
+// ---- bounded-wait give-up status ----------------------------------------------------
+
+// Set (to nonzero) by any column-kernel wave whose bounded wait ran out of polls; each
+// device holds its own copy, zero when the code object loads.  Host code uses the
+// address hipGetSymbolAddress gives for the device, never this name.
+__device__ uint32_t wait_status;
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t*> status_addr[kMaxDevices];
+std::mutex status_mu;
+std::atomic<uint32_t> spin_limit{0};         // 0: the default
+
+// The current device's status word address (looked up once per device).
+hipError_t status_word(uint32_t** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    uint32_t* p = status_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(status_mu);
+        p = status_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(wait_status));
+            if (e != hipSuccess)
+                return e;
+            status_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+hipError_t wait_ctl(mxfp4::WaitCtl* w)
+{
+    const uint32_t lim = spin_limit.load(std::memory_order_relaxed);
+    w->limit = lim ? lim : mxfp4::kDefaultSpinLimit;
+    return status_word(&w->status);
+}
+
+// Copies the current device's status word to *flag, stream-ordered, and waits for it.
+hipError_t read_status(uint32_t* flag, hipStream_t stream)
+{
+    uint32_t* p = nullptr;
+    hipError_t e = status_word(&p);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(flag, p, sizeof(uint32_t), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    return e;
+}
 
 }  // namespace
 
@@ -139,8 +197,11 @@ mxfp4_status mxfp4_to_fp8_cols_ragged(const uint8_t* codes, const uint8_t* scale
         return MXFP4_ERR_ALIGN;
     if (M_cap == 0)
         return MXFP4_OK;
-    return from_hip(mxfp4::launch_fp8_cols(codes, scales, yT_e4m3, yT_scales, group_offsets, G,
-                                           M_cap, K, stream));
+    mxfp4::WaitCtl wc;
+    hipError_t e = wait_ctl(&wc);
+    if (e == hipSuccess)
+        e = mxfp4::launch_fp8_cols(codes, scales, yT_e4m3, yT_scales, group_offsets, G, M_cap, K, wc, stream);
+    return from_hip(e);
 }
 
 mxfp4_status mxfp4_bf16_to_fp8_rows(const uint16_t* x_bf16, uint8_t* y_e4m3, uint8_t* y_scales,
@@ -178,8 +239,12 @@ mxfp4_status mxfp4_bf16_to_fp8_cols_ragged(const uint16_t* x_bf16, uint8_t* yT_e
         return MXFP4_ERR_ALIGN;
     if (M_cap == 0)
         return MXFP4_OK;
-    return from_hip(mxfp4::launch_fp8q_cols(x_bf16, yT_e4m3, yT_scales, nullptr, nullptr, group_offsets, G,
-                                            M_cap, K, stream));
+    mxfp4::WaitCtl wc;
+    hipError_t e = wait_ctl(&wc);
+    if (e == hipSuccess)
+        e = mxfp4::launch_fp8q_cols(x_bf16, yT_e4m3, yT_scales, nullptr, nullptr, group_offsets, G, M_cap, K,
+                                    wc, stream);
+    return from_hip(e);
 }
 
 mxfp4_status mxfp4_bf16_to_fp8_rows_cols_ragged(const uint16_t* x_bf16, uint8_t* y_e4m3, uint8_t* y_scales,
@@ -199,8 +264,12 @@ mxfp4_status mxfp4_bf16_to_fp8_rows_cols_ragged(const uint16_t* x_bf16, uint8_t*
         return MXFP4_ERR_ALIGN;
     if (M_cap == 0)
         return MXFP4_OK;
-    return from_hip(mxfp4::launch_fp8q_cols(x_bf16, yT_e4m3, yT_scales, y_e4m3, y_scales, group_offsets, G,
-                                            M_cap, K, stream));
+    mxfp4::WaitCtl wc;
+    hipError_t e = wait_ctl(&wc);
+    if (e == hipSuccess)
+        e = mxfp4::launch_fp8q_cols(x_bf16, yT_e4m3, yT_scales, y_e4m3, y_scales, group_offsets, G, M_cap, K,
+                                    wc, stream);
+    return from_hip(e);
 }
 
 mxfp4_status mxfp4_fp8_grouped_gemm(const uint8_t* a_e4m3, const uint8_t* a_scales,
@@ -283,8 +352,34 @@ mxfp4_status mxfp4_validate_offsets(const int32_t* group_offsets, int32_t G, int
             st = MXFP4_ERR_SHAPE;
     }
     free(h);
+    if (st == MXFP4_OK) {
+        uint32_t flag = 0;
+        st = from_hip(read_status(&flag, stream));
+        if (st == MXFP4_OK && flag)
+            st = MXFP4_ERR_HIP;
+    }
     return st;
 }
+
+mxfp4_status mxfp4_wait_status(hipStream_t stream)
+{
+    uint32_t flag = 0;
+    hipError_t e = read_status(&flag, stream);
+    if (e == hipSuccess && flag) {
+        uint32_t* p = nullptr;
+        static const uint32_t zero = 0;
+        e = status_word(&p);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(p, &zero, sizeof(uint32_t), hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(stream);
+    }
+    if (e != hipSuccess)
+        return MXFP4_ERR_HIP;
+    return flag ? MXFP4_ERR_HIP : MXFP4_OK;
+}
+
+void mxfp4_set_wait_limit(uint32_t polls) { spin_limit.store(polls, std::memory_order_relaxed); }
 
 const char* mxfp4_status_string(mxfp4_status status)
 {

@@ -130,7 +130,7 @@ __device__ __forceinline__ Scales load_scales(const uint8_t* __restrict__ scales
 __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     uint8_t* __restrict__ yT, uint8_t* __restrict__ yT_scales,
-    const int32_t* __restrict__ offs, int G, int64_t K, int parts)
+    const int32_t* __restrict__ offs, int G, int64_t K, int parts, WaitCtl wc)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
     __shared__ __attribute__((aligned(16))) SlotInfo info[kSlots];
@@ -317,9 +317,10 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                 Sc[ld] = load_scales(scales, K, I[ld], kt, soff);
                 C[ld] = load_codes(codes, K, I[ld], kt, coff);
                 const int nx = (u + 1) % kSets;                  // set of strip tt + 1
-                if (tt >= 3 && !wait_at_least(&drained[(tt - 3) % kSlots], kConsumerWaves * ((tt - 3) / kSlots + 1)))
+                if (tt >= 3 && !wait_at_least(&drained[(tt - 3) % kSlots],
+                                              kConsumerWaves * ((tt - 3) / kSlots + 1), wc))
                     return;
-                if (!wait_at_least(&published, kProducerWaves * (tt + 1)))
+                if (!wait_at_least(&published, kProducerWaves * (tt + 1), wc))
                     return;
                 produce(I[u], C[u], sc, tt % kSlots, flags_of(prev_sb, I[u], tt == 0 && lead != 0));
                 prev_sb = I[u].sb;
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     // before converting it), so one summed counter shows that all of them wrote strip t
     consume_strips<kConsumerWaves>(
         tile, info, drained, yT, ncols, n, wave - kProducerWaves,
-        [&](uint32_t t) { return wait_at_least(&produced, kProducerWaves * (t + 1)); },
+        [&](uint32_t t) { return wait_at_least(&produced, kProducerWaves * (t + 1), wc); },
         [&](uint32_t slot) {
             if (lane < 16 && 16 * lane < ncols) {
                 const uint32_t word = info[slot].S[lane >> 3];
@@ -356,7 +357,7 @@ int64_t cols_block_capacity(int64_t M_cap, int32_t G)
 
 hipError_t launch_fp8_cols(const uint8_t* codes, const uint8_t* scales, uint8_t* yT,
                            uint8_t* yT_scales, const int32_t* offs, int32_t G, int64_t M_cap,
-                           int64_t K, hipStream_t stream)
+                           int64_t K, WaitCtl wc, hipStream_t stream)
 {
     if (M_cap == 0)
         return hipSuccess;
@@ -374,7 +375,7 @@ hipError_t launch_fp8_cols(const uint8_t* codes, const uint8_t* scales, uint8_t*
     int64_t k = K;
     int p = (int)parts;
     void* args[] = {(void*)&codes, (void*)&scales, (void*)&yT, (void*)&yT_scales, (void*)&offs,
-                    (void*)&g, (void*)&k, (void*)&p};
+                    (void*)&g, (void*)&k, (void*)&p, (void*)&wc};
     return hipLaunchKernel((const void*)fp8_cols_kernel, dim3((unsigned)grid), dim3(kColsThreads), args,
                            0, stream);
 }

@@ -21,6 +21,17 @@ typedef u32x4 u32x4_unaligned __attribute__((aligned(1)));
 
 constexpr int kThreads = 256;   // 4 wave64 per workgroup
 
+// Bounded waits of the column kernels: the polls a wave makes before it gives up, and
+// the device's status word, where a wave that gave up records that it did (the kernels
+// only set it; the host reads and clears it).
+struct WaitCtl {
+    uint32_t* status;
+    uint32_t limit;
+};
+// Polls before a wave gives up by default (about a second of polling): only a broken
+// protocol could wait that long.
+constexpr uint32_t kDefaultSpinLimit = 1u << 24;
+
 // ---- memory ---------------------------------------------------------------------
 
 // Every byte of this path is touched exactly once: stream it past the caches.

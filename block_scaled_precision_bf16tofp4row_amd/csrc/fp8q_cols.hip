@@ -126,7 +126,7 @@ template <bool kRows>
 __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     const uint8_t* __restrict__ x, uint8_t* __restrict__ yT, uint8_t* __restrict__ yT_scales,
     uint8_t* __restrict__ y, uint8_t* __restrict__ y_scales, const int32_t* __restrict__ offs, int G,
-    int64_t K, int parts)
+    int64_t K, int parts, WaitCtl wc)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kTileBytes];
     __shared__ __attribute__((aligned(16))) SlotInfo info[kSlots];
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                     R[ld] = load_rows(x, K, I[ld], kt, off);
                 }
                 if (tt >= 3 && !wait_at_least(&drained[(tt - 3) % kSlots],
-                                              kQConsumerWaves * ((tt - 3) / kSlots + 1)))
+                                              kQConsumerWaves * ((tt - 3) / kSlots + 1), wc))
                     return;
                 const uint32_t fl = flags_of(prev_sb, I[u], tt == 0 && lead != 0);
                 if constexpr (kRows) {
@@ -383,8 +383,8 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                     // the block's other three waves published while this one converted
                     // the columns
                     const int wb = wave & ~3;
-                    if (!wait_at_least(&rowpub[wb], tt + 1) || !wait_at_least(&rowpub[wb + 1], tt + 1) ||
-                        !wait_at_least(&rowpub[wb + 2], tt + 1) || !wait_at_least(&rowpub[wb + 3], tt + 1))
+                    if (!wait_at_least(&rowpub[wb], tt + 1, wc) || !wait_at_least(&rowpub[wb + 1], tt + 1, wc) ||
+                        !wait_at_least(&rowpub[wb + 2], tt + 1, wc) || !wait_at_least(&rowpub[wb + 3], tt + 1, wc))
                         return;
                     produce_rows(I[u], R[u], tt % kSlots, fl);
                 }
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     // ================= consumers =================
     consume_strips<kQConsumerWaves>(
         tile, info, drained, yT, ncols, n, wave - kQProducerWaves,
-        [&](uint32_t t) { return wait_all_at_least<kQProducerWaves>(produced, t + 1); },
+        [&](uint32_t t) { return wait_all_at_least<kQProducerWaves>(produced, t + 1, wc); },
         [&](uint32_t slot) {
             if (lane < 16 && 16 * lane < ncols)
                 *reinterpret_cast<u32x4*>(yT_scales + K * (int64_t)uniform(info[slot].blk) +
@@ -407,7 +407,8 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
 }
 
 hipError_t launch_fp8q_cols(const uint16_t* x, uint8_t* yT, uint8_t* yT_scales, uint8_t* y, uint8_t* y_scales,
-                            const int32_t* offs, int32_t G, int64_t M_cap, int64_t K, hipStream_t stream)
+                            const int32_t* offs, int32_t G, int64_t M_cap, int64_t K, WaitCtl wc,
+                            hipStream_t stream)
 {
     if (M_cap == 0)
         return hipSuccess;
@@ -426,7 +427,7 @@ hipError_t launch_fp8q_cols(const uint16_t* x, uint8_t* yT, uint8_t* yT_scales, 
     int64_t k = K;
     int p = (int)parts;
     void* args[] = {(void*)&xb, (void*)&yT, (void*)&yT_scales, (void*)&y, (void*)&y_scales, (void*)&offs,
-                    (void*)&g, (void*)&k, (void*)&p};
+                    (void*)&g, (void*)&k, (void*)&p, (void*)&wc};
     const void* kern = y ? (const void*)fp8q_cols_kernel<true> : (const void*)fp8q_cols_kernel<false>;
     return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kQThreads), args, 0, stream);
 }

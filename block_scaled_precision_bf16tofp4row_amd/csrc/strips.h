@@ -29,8 +29,11 @@
 // after it so a 32-byte read window never wraps) starts at byte 544k + 32 (k >> 5), the
 // skew against bank conflicts.  Synchronisation is by monotonic counters in LDS (no
 // barrier inside the strip loop); every wait is bounded (a wave that waits about a
-// second gives up and leaves the kernel instead of hanging).
+// second gives up, marks the device's status word and leaves the kernel instead of
+// hanging).
 #pragma once
+
+#include <atomic>
 
 #include "common.h"
 
@@ -82,27 +85,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t strip_rsrc(const void* base, u
 
 // ---- progress counters in LDS --------------------------------------------------------
 
-// Polls of a counter before a wave gives up (about a second): only a broken protocol
-// could wait that long, and the wave then leaves the kernel instead of hanging.
-constexpr uint32_t kSpinLimit = 1u << 24;
-
-// Wait (wave-uniformly) until *ctr >= target.  The acquire orders this wave's later
-// LDS reads after the writes that the counter's release published.
-__device__ __forceinline__ bool wait_at_least(uint32_t* ctr, uint32_t target)
+// A wave whose wait ran out of polls sets the device's status word (a vector atomic,
+// the same value from every lane) and then leaves the kernel instead of hanging.
+__device__ __forceinline__ void give_up(const WaitCtl& w)
 {
-    for (uint32_t i = 0; i < kSpinLimit; ++i) {
+    __hip_atomic_fetch_or(w.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait (wave-uniformly) until *ctr >= target, at most w.limit polls (false: gave up).
+// The acquire orders this wave's later LDS reads after the writes that the counter's
+// release published.
+__device__ __forceinline__ bool wait_at_least(uint32_t* ctr, uint32_t target, const WaitCtl& w)
+{
+    for (uint32_t i = 0; i < w.limit; ++i) {
         if (uniform(__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) >= target)
             return true;
         __builtin_amdgcn_s_sleep(1);
     }
+    give_up(w);
     return false;
 }
 
 // Wait (wave-uniformly) until each of the N counters ctr[0..N-1] is >= target.
 template <int N>
-__device__ __forceinline__ bool wait_all_at_least(uint32_t* ctr, uint32_t target)
+__device__ __forceinline__ bool wait_all_at_least(uint32_t* ctr, uint32_t target, const WaitCtl& w)
 {
-    for (uint32_t i = 0; i < kSpinLimit; ++i) {
+    for (uint32_t i = 0; i < w.limit; ++i) {
         uint32_t m = 0xFFFFFFFFu;
 #pragma unroll
         for (int k = 0; k < N; ++k)
@@ -111,6 +119,7 @@ __device__ __forceinline__ bool wait_all_at_least(uint32_t* ctr, uint32_t target
             return true;
         __builtin_amdgcn_s_sleep(1);
     }
+    give_up(w);
     return false;
 }
 
@@ -361,19 +370,21 @@ __device__ __forceinline__ void consume_strips(uint8_t* tile, const SlotInfo* in
     }
 }
 
+// Compute units of the current device, read once per device.  Concurrent first calls
+// may both read the attribute; they store the same value.
 static inline int device_cus()
 {
-    static int cached[64];
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 }  // namespace mxfp4

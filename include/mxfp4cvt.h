@@ -224,9 +224,32 @@ int64_t mxfp4_cols_scale_capacity(int64_t M_cap, int64_t K, int32_t G);
 
 /* Debug helper: copies the G+1 offsets to the host (synchronizing `stream`) and
  * checks offs[0] == 0, non-decreasing, offs[G] <= M_cap.  MXFP4_OK if they hold,
- * MXFP4_ERR_SHAPE if not, MXFP4_ERR_NULL / MXFP4_ERR_HIP as usual. */
+ * MXFP4_ERR_SHAPE if not, MXFP4_ERR_NULL / MXFP4_ERR_HIP as usual.  With valid
+ * offsets it also returns MXFP4_ERR_HIP while the current device's wait status (see
+ * mxfp4_wait_status) is set; it does not clear it. */
 mxfp4_status mxfp4_validate_offsets(const int32_t* group_offsets, int32_t G, int64_t M_cap,
                                     hipStream_t stream);
+
+/* Not an operation of the method: the failure report of the column conversions
+ * (mxfp4_to_fp8_cols_ragged, mxfp4_bf16_to_fp8_cols_ragged,
+ * mxfp4_bf16_to_fp8_rows_cols_ragged).  Their waves hand strips to one another through
+ * counters, and every wait for a counter is bounded: a wave that polls a counter the
+ * wait limit's number of times without seeing it advance gives up, sets the current
+ * device's wait status (one word per device, shared by every stream and call on it)
+ * and leaves the kernel, so the call ends with part of its output unwritten instead of
+ * hanging the GPU.  Only a protocol fault (or a limit set far too low) makes a wave give
+ * up; the default limit is 2^24 polls, about a second.
+ * mxfp4_wait_status synchronizes `stream`, then reports MXFP4_ERR_HIP if the status is
+ * set (and clears it) or MXFP4_OK if not; a HIP failure also gives MXFP4_ERR_HIP.  It
+ * sees every give-up of work finished before it; a kernel still running on another
+ * stream may set the status after the check. */
+mxfp4_status mxfp4_wait_status(hipStream_t stream);
+
+/* Test hook for the give-up path: the polls each bounded wait of a column conversion
+ * makes before it gives up, for launches made after this call by any thread of the
+ * process; 0 restores the default (2^24).  A tiny limit makes waves give up early (each
+ * still leaves the kernel normally) and the call's output incomplete. */
+void mxfp4_set_wait_limit(uint32_t polls);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* mxfp4_status_string(mxfp4_status status);

@@ -32,24 +32,38 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
+def compile_oracle(src: str, out: str) -> str:
+    """gcc one oracle source into a shared library (plain -O2, no fast-math)."""
+    tmp = out + ".tmp"
+    subprocess.check_call(
+        ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+         "-ffp-contract=off", "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (plain -O2, no fast-math)."""
+    """Compile oracle.c into liboracle.so."""
     if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
-             "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
+        compile_oracle(_SRC, _LIB)
     return _LIB
+
+
+# The pins' own test loads deliberately broken copies of oracle.c through this
+# variable (one per test process) to show that each plausible mistake fails a pin.
+_LIB_OVERRIDE = "MXFP4_ORACLE_LIB"
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB)
+    path = os.environ.get(_LIB_OVERRIDE)
+    if not path:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     lib.oracle_quantize_block.argtypes = [P, P, P]

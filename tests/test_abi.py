@@ -298,3 +298,34 @@ def test_product_package_does_not_import_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "oracle.c" not in text, f
+
+
+# Valid calls with a launch to make: without a GPU the launch itself fails and the call
+# reports MXFP4_ERR_HIP (never a crash, never OK).  Only run where no GPU exists: on a
+# GPU these fake addresses would reach a kernel.
+needs_no_gpu = pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present")
+
+
+@needs_no_gpu
+def test_valid_calls_without_a_device_report_hip_error(lib):
+    E = mx.MXFP4_ERR_HIP
+    assert _q(lib, M=4, K=64) == E
+    assert _r(lib, "mxfp4_to_fp8_rows") == E
+    assert _r(lib, "mxfp4_to_fp8_cols_ragged") == E
+    assert _f(lib) == E
+    assert _fc(lib) == E
+    assert _fb(lib) == E
+    assert _gm(lib) == E
+    assert lib.mxfp4_fp8_grouped_gemm_wgrad(A, A2, A3, A4, A, OFFS, 1, 4, 256, 256, None) == E
+    assert _nv(lib) == E
+    assert _nv(lib, sr=True) == E
+    assert lib.mxfp4_validate_offsets(OFFS, 1, 4, None) == E
+    assert lib.mxfp4_wait_status(None) == E
+
+
+def test_wait_limit_hook_is_host_only(lib):
+    # sets a process-wide number; no HIP call, so it works without a device
+    lib.mxfp4_set_wait_limit(3)
+    lib.mxfp4_set_wait_limit(0)
+    with pytest.raises(ValueError):
+        mx.mxfp4_set_wait_limit(-1)

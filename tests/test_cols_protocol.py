@@ -22,6 +22,12 @@ shared access:
     once they published them, and no wave overwrites its slot while a block member
     still needs the previous strip's maxima.
 
+Every wait is bounded in the kernels: a wave that polls a counter `polls` times in vain
+sets the device's status word and leaves.  With a poll budget the model checks that
+every wave then leaves (no deadlock), that the accesses made on the way out are still
+in order, and that a run whose column output is incomplete always has a wave that gave
+up, so an incomplete output is never reported as success.
+
 It checks the protocol design (the wait targets), not the compiled kernel; the GPU
 parity tests check the kernel.
 """
@@ -38,11 +44,14 @@ class Violation(AssertionError):
     pass
 
 
-def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, rows=False, rows_wait=True):
+def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, rows=False, rows_wait=True,
+         polls=None):
     """PMAX None: no partial maxima.  per_wave (default: PMAX is None): one produced
     counter per producer wave, the consumers wait for the smallest.  rows: the
     both-layouts mode (per-wave row maxima exchanged within blocks of four waves);
-    rows_wait False drops the wait for the block (the model must catch that)."""
+    rows_wait False drops the wait for the block (the model must catch that).  polls:
+    the bound of every wait (None: unbounded).  Returns (column output complete, some
+    wave gave up)."""
     if per_wave is None:
         per_wave = PMAX is None
     rnd = random.Random(seed)
@@ -65,6 +74,20 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, r
         if not cond:
             raise Violation(msg)
 
+    gave_up = []
+
+    def wait(agent, cond):
+        # the kernel's bounded wait: cond is polled at most `polls` times; a wave that
+        # runs out sets the status word (recorded here) and leaves the kernel
+        k = 0
+        while polls is None or k < polls:
+            if cond():
+                return True
+            k += 1
+            yield "wait"
+        gave_up.append(agent)
+        return False
+
     def publish(w, t):
         s = t % PMAX
         e = pmax[s]
@@ -84,11 +107,12 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, r
         for t in range(n):
             # the kernel waits until strip t - 3 is drained (drain_lag = 3)
             if t >= drain_lag:
-                while cnt[f"drained{(t - drain_lag) % SLOTS}"] < CW * ((t - drain_lag) // SLOTS + 1):
-                    yield "wait"
+                k = (t - drain_lag) % SLOTS
+                if not (yield from wait(f"P{w}", lambda: cnt[f"drained{k}"] >= CW * ((t - drain_lag) // SLOTS + 1))):
+                    return
             if PMAX:
-                while cnt["published"] < PW * (t + 1):
-                    yield "wait"
+                if not (yield from wait(f"P{w}", lambda: cnt["published"] >= PW * (t + 1))):
+                    return
                 e = pmax[t % PMAX]
                 need(e is not None and e[0] == t and len(e[1]) == PW, f"P{w} reads pmax {e} for strip {t}")
             if rows:
@@ -123,8 +147,8 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, r
             if rows:
                 blk = range(w & ~3, (w & ~3) + 4)
                 if rows_wait:
-                    while min(cnt[f"rowpub{x}"] for x in blk) < t + 1:
-                        yield "wait"
+                    if not (yield from wait(f"P{w}", lambda: min(cnt[f"rowpub{x}"] for x in blk) >= t + 1)):
+                        return
                 for x in blk:
                     need(rowmax[s][x] == t, f"P{w} reads row maxima {rowmax[s][x]} of P{x} for strip {t}")
                     yield None
@@ -140,11 +164,11 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, r
     def consumer(v):
         for t in range(n):
             if per_wave:
-                while min(cnt[f"produced{w}"] for w in range(PW)) < t + 1:
-                    yield "wait"
+                ok = yield from wait(f"C{v}", lambda: min(cnt[f"produced{w}"] for w in range(PW)) >= t + 1)
             else:
-                while cnt["produced"] < PW * (t + 1):
-                    yield "wait"
+                ok = yield from wait(f"C{v}", lambda: cnt["produced"] >= PW * (t + 1))
+            if not ok:
+                return
             s = t % SLOTS
             need(info[s] == t, f"C{v} expects strip {t}, slot info says {info[s]}")
             e = ring[s]
@@ -176,9 +200,11 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, r
         stalled = stalled + 1 if r == "wait" else 0
         if stalled > 100000:
             raise Violation(f"deadlock at n={n}: counters {cnt}")
-    for v in range(CW):
-        need(all(done_cons[v]), f"C{v} did not write every strip")
-    return steps
+    complete = all(all(done_cons[v]) for v in range(CW))
+    if not gave_up:
+        for v in range(CW):
+            need(all(done_cons[v]), f"C{v} did not write every strip")
+    return complete, bool(gave_up)
 
 
 @pytest.mark.parametrize("cfg", CONFIGS)
@@ -247,3 +273,26 @@ def test_model_catches_a_single_partial_maximum_slot():
             caught = True
             break
     assert caught
+
+
+@pytest.mark.parametrize("cfg", CONFIGS + ["both"])
+def test_give_up_leaves_every_wave_and_is_reported(cfg):
+    """With a tiny poll budget (the host's wait-limit hook), waves give up: every wave
+    still leaves (the scheduler would flag a deadlock), the accesses made before they
+    leave stay in order (the model's checks hold), and every run whose column output
+    is incomplete has a wave that gave up, so the status word reports it."""
+    kw = dict(PW=8, CW=8, PMAX=None, rows=True) if cfg == "both" else dict(PW=cfg[0], CW=cfg[1], PMAX=cfg[2])
+    outcomes = set()
+    for polls in (1, 2, 3, 8, 40, 400):
+        for seed in range(20):
+            complete, gave_up = _run(9, seed, polls=polls, **kw)
+            assert complete or gave_up, f"incomplete output with no give-up (polls {polls}, seed {seed})"
+            outcomes.add((complete, gave_up))
+    # both sides are exercised: runs that gave up and runs that finished
+    assert (False, True) in outcomes and (True, False) in outcomes, outcomes
+
+
+def test_give_up_budget_does_not_change_a_run_that_finishes():
+    """A budget large enough for the schedule changes nothing: the run completes."""
+    for seed in range(20):
+        assert _run(6, seed, polls=10 ** 6) == (True, False)

@@ -57,6 +57,17 @@ def test_small_ragged_chain(counts, K, values, slack):
     check_chain(seg.x_bits, seg.offs)
 
 
+@pytest.mark.parametrize("K", [32, 96, 160, 416])
+def test_quantize_ragged_k_not_multiple_of_128(K):
+    """The quantizer accepts any K that is a multiple of 32 (one MX block): K of one,
+    three, five and thirteen blocks, ragged experts (empty ones, single rows, partial
+    tails), capacity slack past offs[G] that must keep its canary."""
+    counts = [0, 1, 127, 3, 300, 0, 65, 2]
+    say(f"quantize counts={counts} K={K}")
+    seg = workloads.ragged_case(counts, K, seed=K, values="t3", M_cap=sum(counts) + 9)
+    check_chain(seg.x_bits, seg.offs, kernels=("quantize",))
+
+
 def test_many_experts_scan_chunks():
     """G = 300 (the tile search scans experts 64 at a time), mostly empty."""
     rng = np.random.default_rng(1)

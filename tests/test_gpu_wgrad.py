@@ -6,8 +6,9 @@ conversion (width K); dY^T is a BF16 gradient of width N through the oracle's ba
 column quantizer.  Outputs are compared within the bound of the forward GEMM's test,
 with the contraction running over an expert's tokens:
     |y - exact| <= 2^-8 |exact| + (1 + 2^-8) (eps_dot + (M_g / 64) 2^-24) sum|terms| + 2^-133
-(half a BF16 step; fp32 accumulation over 64-token chunks; eps_dot = 2^-10 for one
-64-term dot product inside the matrix core, implementation-defined in the OCP MX spec).
+(half a BF16 step; fp32 accumulation over 64-token chunks; eps_dot = 2^-11 for the
+matrix core's own rounding, measured by the zero-sum probes), and the same one-step
+checks as the forward GEMM's.
 Every element of dW is written, zeros for experts with no tokens.
 """
 from __future__ import annotations
@@ -29,7 +30,11 @@ import oracle  # noqa: E402
 import workloads  # noqa: E402
 from gpu_path import dev, host  # noqa: E402
 
-EPS_DOT = 2.0 ** -10
+# Allowance for the matrix core's own rounding of one dot product, relative to its
+# sum|terms|: the zero-sum probes below (test_gpu_gemm.py, test_gpu_wgrad.py) measured
+# at most 2^-12.48 on MI355X (two 64-term chunks, terms over 36 binades); 2^-11 leaves a
+# margin of 2^1.48 (about 2.8x) over that.
+EPS_DOT = 2.0 ** -11
 CANARY16 = 0xA5A5
 CANARY8 = 0x5A
 
@@ -80,17 +85,29 @@ def run_wgrad(dyT, sdyT, xT, sxT, offs, M_cap, N, K):
 
 
 def check_points(y_bits, exact, ybf, absum, mg, what):
+    """As the forward GEMM's check: every output within the bound, and within one BF16
+    step of the oracle's rounding wherever the dot-product allowance is below one step
+    of |exact|."""
     got = bf16_to_float(y_bits)
-    bound = 2.0 ** -8 * np.abs(exact) + (1 + 2.0 ** -8) * (EPS_DOT + (mg / 64) * 2.0 ** -24) * absum + 2.0 ** -133
+    allow = (1 + 2.0 ** -8) * (EPS_DOT + (mg / 64) * 2.0 ** -24) * absum
+    bound = 2.0 ** -8 * np.abs(exact) + allow + 2.0 ** -133
     err = np.abs(got - exact)
     ratio = err / bound
     worst = int(np.argmax(ratio))
     steps = np.abs(y_bits.astype(np.int64) - ybf.astype(np.int64))
     steps = np.where((y_bits ^ ybf) & 0x8000, 2 ** 16, steps)
+    plain = allow < 2.0 ** -8 * np.abs(exact)
     say(f"{what}: {err.size} outputs, worst err/bound {ratio[worst]:.3g}, "
-        f"equal to the oracle's BF16 {np.mean(steps == 0):.4f}, within one step {np.mean(steps <= 1):.4f}")
+        f"equal to the oracle's BF16 {np.mean(steps == 0):.4f}, within one step {np.mean(steps <= 1):.4f}, "
+        f"{np.mean(plain):.4f} without cancellation, max steps there {int(steps[plain].max(initial=0))}, "
+        f"max steps at |exact| >= 2^-6 sum|terms| {int(steps[np.abs(exact) >= 2.0 ** -6 * absum].max(initial=0))}")
     assert ratio[worst] <= 1.0, (what, worst, got[worst], exact[worst], absum[worst])
-    assert np.mean(steps <= 1) >= 0.99, what
+    far = np.nonzero(plain & (steps > 1))[0]
+    assert far.size == 0, (what, far[:5], got[far[:5]], exact[far[:5]], absum[far[:5]])
+    # On these inputs the matrix core's rounding stays far below EPS_DOT: every output
+    # whose sum does not cancel to below 2^-6 sum|terms| is within one BF16 step.
+    far = np.nonzero((np.abs(exact) >= 2.0 ** -6 * absum) & (steps > 1))[0]
+    assert far.size == 0, (what, far[:5], got[far[:5]], exact[far[:5]], absum[far[:5]])
 
 
 CASES = [
@@ -200,3 +217,40 @@ def test_wgrad_full_size_sampled():
     for g in range(G):
         if seg.offs[g + 1] == seg.offs[g]:
             assert np.all(y[g] == 0), g
+
+
+def test_wgrad_dot_error_probe():
+    """The matrix core's own rounding over the token contraction, measured as in the
+    forward GEMM's probe: one expert of 1024 tokens, token j = half + perm(i) carrying
+    x_j = x_i and dy_j = -dy_i, one scale per column, so every exact dW is 0 and the GPU
+    output is the rounding error alone."""
+    rng = np.random.default_rng(91)
+    M, N, K = 1024, 256, 256
+    half = M // 2
+    perm = rng.permutation(half)
+
+    def codes(shape):
+        b = rng.integers(0, 256, shape)
+        return np.where((b & 0x7F) == 0x7F, b - 1, b).astype(np.uint8)
+
+    dyT = np.zeros((N, M), np.uint8)
+    xT = np.zeros((K, M), np.uint8)
+    dyT[:, :half] = codes((N, half))
+    xT[:, :half] = codes((K, half))
+    dyT[:, half + perm] = dyT[:, :half] ^ 0x80
+    xT[:, half + perm] = xT[:, :half]
+    nb = M // 128
+    sdyT = np.repeat(rng.integers(117, 138, (1, N)), nb, axis=0).astype(np.uint8)
+    sxT = np.repeat(rng.integers(117, 138, (1, K)), nb, axis=0).astype(np.uint8)
+    offs = np.array([0, M], np.int32)
+    y = run_wgrad(dyT.reshape(-1), sdyT.reshape(-1), xT.reshape(-1), sxT.reshape(-1), offs, M, N, K)
+    exact, ybf, absum = oracle.fp8_wgrad(dyT.reshape(-1), sdyT.reshape(-1), xT.reshape(-1), sxT.reshape(-1),
+                                         offs, N, K, threads=oracle.default_threads())
+    assert np.all(exact == 0)
+    got = np.abs(bf16_to_float(y.reshape(-1)))
+    rel = got / np.maximum(absum.reshape(-1), 1e-300)
+    acc = (M / 64) * 2.0 ** -24
+    say(f"wgrad dot error probe: max |dW| / sum|terms| = 2^{np.log2(max(rel.max(), 2.0 ** -200)):.2f} "
+        f"(fp32 accumulation allowance 2^{np.log2(acc):.2f}, EPS_DOT 2^{np.log2(EPS_DOT):.2f}), "
+        f"nonzero outputs {np.mean(got > 0):.4f}")
+    assert rel.max() <= (1 + 2.0 ** -8) * (EPS_DOT + acc)
