@@ -244,7 +244,10 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
     dirty lines from the previous launch are written back before the timed region,
     while the scrub's own lines are clean), timed with HIP events on the launch
     stream; next to it the hand-written copy (bench_copy16, the fastest unroll measured
-    here) moving the same number of bytes (half read, half written), timed the same way."""
+    here) moving the same number of bytes (half read, half written), timed the same way.
+    Each row also gives `net_us`, the median less that of a one-workgroup launch timed
+    the same way (the events' and the dispatch's own share), and the fraction of peak
+    it implies."""
     import workloads
     stream = torch.cuda.current_stream()
     scrub = torch.ones(scrub_bytes // 4, dtype=torch.int32, device=dev)
@@ -263,6 +266,12 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1000.0
 
+    # the same timing around a one-workgroup launch: what the events and the dispatch
+    # add to every median below (reported, not subtracted, in `median_us`)
+    tiny_src = torch.ones(16, dtype=torch.uint8, device=dev)
+    tiny_dst = torch.empty(16, dtype=torch.uint8, device=dev)
+    empty_us = median_us(lambda: copy(tiny_dst, tiny_src))
+    log(f"[bench] scrubbed timing of a one-workgroup launch: {empty_us:.2f} us")
     out = {}
     for cid in config_ids:
         w = workloads.make_config(cid, 0)
@@ -282,10 +291,12 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
             del src, dst
             gbs = nbytes / (us * 1e-6) / 1e9
             copy_gbs = 2 * half / (cus * 1e-6) / 1e9
+            net = max(us - empty_us, 1e-3)
             rows.append({"kernel": kern, "segment": segname, "alg_bytes": nbytes,
                          "median_us": round(us, 2), "GBps": round(gbs, 1),
                          "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                         "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4)})
+                         "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4),
+                         "net_us": round(net, 2), "frac_of_peak_net": round(nbytes / (net * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
             log(f"[bench] scrubbed {w.name} {kern}/{segname}: {us:.1f} us, {gbs:.0f} GB/s "
                 f"({gbs / HBM_PEAK_GBS:.1%} of peak, {gbs / copy_gbs:.1%} of a same-size copy)")
         out[w.name] = rows
@@ -295,6 +306,8 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
     torch.cuda.empty_cache()
     out["copy_kernel"] = {"what": "bench_copy16: 16-byte nontemporal loads then stores, one-shot grid",
                           "unroll": copy.unroll, "unroll_GBps_1GiB": copy.sweep}
+    out["launch_overhead_us"] = {"what": "median of the same scrub + event timing around a one-workgroup launch; "
+                                         "net_us = median_us minus this", "median_us": round(empty_us, 2)}
     return out
 
 
