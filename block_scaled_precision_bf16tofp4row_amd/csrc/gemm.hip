@@ -43,7 +43,10 @@
 // instead of both contending for the issue slots in lockstep.
 // The tile's block scales (256 rows x K/128 bytes per operand) are staged in LDS once,
 // laid out so that one 4-byte read gives a lane the scales of its four MFMA tiles; they
-// take no registers across stages and no place in the memory-operation count.  Operand
+// take no registers across stages and no place in the memory-operation count.  Their
+// loads (one dword per four blocks, all independent) go out together with stage 0's
+// operand loads, so a workgroup's start waits for one memory round trip, not one per
+// scale byte.  Operand
 // and scale loads are buffer loads whose range is the tile's rows that exist: rows past
 // the last partial tile of an expert read as zero (they add nothing), and the output
 // stores go through a resource of the same rows, so those rows are never written.  The
@@ -404,6 +407,7 @@ __global__ __launch_bounds__(kFastThreads, 1) void fp8_gemm_kernel(
     // lane (r, h)
     const int wm = wave & 1, wn = wave >> 1;
     const uint32_t r = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
+    const FastCtx cx{{lds0, lds1}, scl_a, scl_w, ra, rw, {loff[0], loff[1], loff[2], loff[3]}, wave, wm, wn, r, h};
     // stage the tile's block scales: thread t < 256 owns token row t, thread 256 + t
     // feature row t (row 128 x + 32 q + y goes to byte [block][x][y][q]); rows past the
     // tile read as zero
@@ -413,11 +417,26 @@ __global__ __launch_bounds__(kFastThreads, 1) void fp8_gemm_kernel(
         const uint32_t dst = x * 128 + yy * 4 + q;
         const __amdgpu_buffer_rsrc_t rs = wave < 4 ? rsa : rsw;
         uint8_t* const scl = wave < 4 ? scl_a : scl_w;
-        for (uint32_t b = 0; b < kb_n; ++b)
-            scl[b * kTM + dst] = (uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)(t8 * kb_n + b), 0, 0);
+        if ((kb_n & 3) == 0) {
+            // a row's scale bytes as independent dword loads, all in flight together and
+            // with stage 0's operand loads (issued next); dwords past the row's kb_n bytes
+            // (the next row's, or zero past the range) land in block slots no stage reads
+            uint32_t v4[kMaxFastBlocks / 4];
+#pragma unroll
+            for (int j = 0; j < kMaxFastBlocks / 4; ++j)
+                v4[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(t8 * kb_n + 4 * j), 0, 0);
+            fast_issue(cx, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kMaxFastBlocks / 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    scl[(4 * j + i) * kTM + dst] = (uint8_t)(v4[j] >> (8 * i));
+        } else {
+            for (uint32_t b = 0; b < kb_n; ++b)
+                scl[b * kTM + dst] = (uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (int)(t8 * kb_n + b), 0, 0);
+            fast_issue(cx, 0, 0);
+        }
     }
-    // the scale loads above are awaited here, before any LDS load is in flight
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
     f32x16 acc[4][2];
 #pragma unroll
@@ -426,9 +445,7 @@ __global__ __launch_bounds__(kFastThreads, 1) void fp8_gemm_kernel(
         for (int nt = 0; nt < 2; ++nt)
             acc[mt][nt] = f32x16{};
 
-    const FastCtx cx{{lds0, lds1}, scl_a, scl_w, ra, rw, {loff[0], loff[1], loff[2], loff[3]}, wave, wm, wn, r, h};
     __syncthreads();                              // scales staged
-    fast_issue(cx, 0, 0);
     // T is even (K is a multiple of 256 on this path): stages run in pairs, one per LDS
     // buffer; the last pair is peeled so that every load issue in a pair is fixed at
     // compile time and a pair is one basic block
