@@ -145,6 +145,58 @@ __device__ __forceinline__ u32x4 read_window16(const uint8_t* src, uint32_t o)
                  __builtin_amdgcn_alignbyte(d3, d2, b), __builtin_amdgcn_alignbyte(d4, d3, b)};
 }
 
+// Bytes [x, y) (0 <= x < y <= 16, not the whole piece) of the 16-byte value v, to
+// p + x .. p + y - 1 (p 16-byte aligned), touching no other byte, with naturally aligned
+// stores of 1, 2, 4 and 8 bytes.  The partial pieces at a column's ends are a suffix
+// [x, 16) or a prefix [0, y): the binary digits of 16 - x (of y) give at most one store
+// of each size, so a wave issues four masked stores for all its suffix and prefix
+// pieces.  A piece cut on both sides (a column shorter than 16 bytes) grows from x to
+// the next boundary and shrinks towards y, at most two stores of each size.
+__device__ __forceinline__ void store_part16(uint8_t* p, const u32x4 v, uint32_t x, uint32_t y)
+{
+    auto dword_at = [&](uint32_t a) {             // the dword holding byte a
+        return a < 8 ? (a < 4 ? v.x : v.y) : (a < 12 ? v.z : v.w);
+    };
+    auto put = [&](uint32_t a, int size) {        // `size` bytes at offset a (a multiple of size)
+        if (size == 8) {
+            const uint64_t q = a < 8 ? (((uint64_t)v.y << 32) | v.x) : (((uint64_t)v.w << 32) | v.z);
+            __builtin_nontemporal_store(q, reinterpret_cast<uint64_t*>(p + a));
+        } else if (size == 4) {
+            __builtin_nontemporal_store(dword_at(a), reinterpret_cast<uint32_t*>(p + a));
+        } else if (size == 2) {
+            __builtin_nontemporal_store((uint16_t)(dword_at(a) >> (8 * (a & 3))), reinterpret_cast<uint16_t*>(p + a));
+        } else {
+            __builtin_nontemporal_store((uint8_t)(dword_at(a) >> (8 * (a & 3))), p + a);
+        }
+    };
+    if (x > 0 && y < 16) {
+        uint32_t a = x;
+#pragma unroll
+        for (int size = 1; size <= 8; size <<= 1)
+            if ((a & (uint32_t)size) && a + size <= y) {
+                put(a, size);
+                a += size;
+            }
+#pragma unroll
+        for (int size = 8; size >= 1; size >>= 1)
+            if (a + size <= y) {
+                put(a, size);
+                a += size;
+            }
+        return;
+    }
+    const bool suffix = x > 0;
+#pragma unroll
+    for (int size = 1; size <= 8; size <<= 1) {
+        const uint32_t s = (uint32_t)size;
+        // suffix: x rounded up to a multiple of the size; prefix: y's bits above the size
+        const bool has = suffix ? ((16u - x) & s) != 0 : (y & s) != 0;
+        const uint32_t at = suffix ? (x + s - 1) & ~(s - 1) : y & ~(2 * s - 1);
+        if (has)
+            put(at, size);
+    }
+}
+
 // ---- strips of experts ----------------------------------------------------------------
 
 // Per-lane expert table for experts g0 + lane: first strip, strip count, first row and
@@ -357,10 +409,8 @@ __device__ __forceinline__ void consume_strips(uint8_t* tile, const SlotInfo* in
                     if (b0 >= W_lo && b0 + 16 <= W_hi) {
                         store_stream(reinterpret_cast<u32x4*>(yT + b0), val);
                     } else {
-                        const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
-                        for (int q = 0; q < 16; ++q)
-                            if (b0 + q >= W_lo && b0 + q < W_hi)
-                                yT[b0 + q] = (uint8_t)(w4[q >> 2] >> (8 * (q & 3)));
+                        store_part16(yT + b0, val, (uint32_t)max<int64_t>(W_lo - b0, 0),
+                                     (uint32_t)min<int64_t>(W_hi - b0, 16));
                     }
                 }
                 cs.p[k] += kStripRows;
