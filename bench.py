@@ -242,21 +242,31 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
     """Per launch of each workload: median over `reps` launches, each preceded by a
     scrub that reads `scrub_bytes` (evicting the L2s and the memory-side cache, whose
     dirty lines from the previous launch are written back before the timed region,
-    while the scrub's own lines are clean), timed with HIP events on the launch
-    stream; next to it the hand-written copy (bench_copy16, the fastest unroll measured
-    here) moving the same number of bytes (half read, half written), timed the same way.
-    Each row also gives `net_us`, the median less that of a one-workgroup launch timed
-    the same way (the events' and the dispatch's own share), and the fraction of peak
-    it implies."""
+    while the scrub's own lines are clean), timed by HIP events bound to the kernel's
+    own start and end (KernelEvents); next to it the hand-written copy (bench_copy16,
+    the fastest unroll measured here) moving the same number of bytes (half read, half
+    written), timed the same way.  Each row also gives `median_us_markers`: the same
+    launches timed by event records of their own before and after the launch on the
+    stream, which add the events' commands and the dispatch gap to every launch."""
     import workloads
     stream = torch.cuda.current_stream()
     scrub = torch.ones(scrub_bytes // 4, dtype=torch.int32, device=dev)
     copy = DeviceCopy(torch, dev)
+    kev = KernelEvents(reps)
 
-    def median_us(fn):
+    def median_us(fn, is_copy=False):
+        """(kernel-event median, marker-event median) in microseconds."""
         for i in range(warmup):
             torch.amax(scrub)
             fn()
+        for i in range(reps):
+            torch.amax(scrub)
+            if is_copy:
+                fn(events=kev.pairs[i])
+            else:
+                kev.arm(mx, i)
+                fn()
+        k_us = float(np.median(kev.elapsed(reps)))
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b in ev:
             torch.amax(scrub)
@@ -264,14 +274,14 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
             fn()
             b.record(stream)
         torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1000.0
+        return k_us, float(np.median([a.elapsed_time(b) for a, b in ev])) * 1000.0
 
-    # the same timing around a one-workgroup launch: what the events and the dispatch
-    # add to every median below (reported, not subtracted, in `median_us`)
+    # a one-workgroup launch timed both ways: the kernel events give a trivial kernel's
+    # dispatch-to-completion time, the marker events add their own share on top
     tiny_src = torch.ones(16, dtype=torch.uint8, device=dev)
     tiny_dst = torch.empty(16, dtype=torch.uint8, device=dev)
-    empty_us = median_us(lambda: copy(tiny_dst, tiny_src))
-    log(f"[bench] scrubbed timing of a one-workgroup launch: {empty_us:.2f} us")
+    tiny_k, tiny_m = median_us(lambda events=None: copy(tiny_dst, tiny_src, events), is_copy=True)
+    log(f"[bench] scrubbed timing of a one-workgroup launch: {tiny_k:.2f} us kernel, {tiny_m:.2f} us with markers")
     out = {}
     for cid in config_ids:
         w = workloads.make_config(cid, 0)
@@ -283,32 +293,69 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
         torch.cuda.synchronize()
         rows = []
         for kern, segname, fn, nbytes in launches:
-            us = median_us(fn)
+            us, us_m = median_us(fn)
             half = (nbytes // 2 + 15) // 16 * 16
             src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
             dst = torch.empty(half, dtype=torch.uint8, device=dev)
-            cus = median_us(lambda: copy(dst, src))
+            cus, _ = median_us(lambda events=None: copy(dst, src, events), is_copy=True)
             del src, dst
             gbs = nbytes / (us * 1e-6) / 1e9
             copy_gbs = 2 * half / (cus * 1e-6) / 1e9
-            net = max(us - empty_us, 1e-3)
             rows.append({"kernel": kern, "segment": segname, "alg_bytes": nbytes,
                          "median_us": round(us, 2), "GBps": round(gbs, 1),
                          "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                          "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4),
-                         "net_us": round(net, 2), "frac_of_peak_net": round(nbytes / (net * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
-            log(f"[bench] scrubbed {w.name} {kern}/{segname}: {us:.1f} us, {gbs:.0f} GB/s "
-                f"({gbs / HBM_PEAK_GBS:.1%} of peak, {gbs / copy_gbs:.1%} of a same-size copy)")
+                         "median_us_markers": round(us_m, 2),
+                         "frac_of_peak_markers": round(nbytes / (us_m * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+            log(f"[bench] scrubbed {w.name} {kern}/{segname}: {us:.1f} us ({us_m:.1f} with markers), "
+                f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of peak, {gbs / copy_gbs:.1%} of a same-size copy)")
         out[w.name] = rows
         del segs, launches, bsegs, blaunches
         torch.cuda.empty_cache()
     del scrub
+    kev.close()
     torch.cuda.empty_cache()
     out["copy_kernel"] = {"what": "bench_copy16: 16-byte nontemporal loads then stores, one-shot grid",
                           "unroll": copy.unroll, "unroll_GBps_1GiB": copy.sweep}
-    out["launch_overhead_us"] = {"what": "median of the same scrub + event timing around a one-workgroup launch; "
-                                         "net_us = median_us minus this", "median_us": round(empty_us, 2)}
+    out["timing"] = {"median_us": "HIP events bound to the kernels' own start and end (hipExtLaunchKernel "
+                                  "through mxfp4_time_next_launch; the copy's own event arguments)",
+                     "median_us_markers": "HIP event records before and after the launch on its stream",
+                     "one_workgroup_launch_us": round(tiny_k, 2),
+                     "one_workgroup_launch_us_markers": round(tiny_m, 2)}
     return out
+
+
+class KernelEvents:
+    """Pairs of HIP events (libmxfp4bench) bound by the launches themselves to their
+    kernels' start and end: the conversion library's timing hook
+    (mxfp4_time_next_launch) arms them for the next call, the copy kernel takes them as
+    arguments.  Their elapsed time is the kernels' execution, as a kernel trace reports
+    it, and no event commands of their own go on the stream between launches."""
+
+    def __init__(self, n):
+        self.lib = DeviceCopy.load()
+        self.pairs = [(self.lib.bench_event_create(), self.lib.bench_event_create()) for _ in range(n)]
+        if not all(a and b for a, b in self.pairs):
+            raise RuntimeError("hipEventCreate failed")
+
+    def arm(self, mx, i):
+        mx.mxfp4_time_next_launch(*self.pairs[i])
+
+    def elapsed(self, n=None):
+        """Microseconds of pairs 0..n-1 (waits for each stop event)."""
+        out = []
+        for a, b in self.pairs[: len(self.pairs) if n is None else n]:
+            us = self.lib.bench_event_elapsed_us(a, b)
+            if us < 0:
+                raise RuntimeError("a timing event was not recorded by its launch")
+            out.append(us)
+        return out
+
+    def close(self):
+        for a, b in self.pairs:
+            self.lib.bench_event_destroy(a)
+            self.lib.bench_event_destroy(b)
+        self.pairs = []
 
 
 class DeviceCopy:
@@ -322,9 +369,15 @@ class DeviceCopy:
             raise RuntimeError(f"{BENCH_LIB} is missing: build with "
                                "`python -m block_scaled_precision_bf16tofp4row_amd.build`")
         lib = ctypes.CDLL(BENCH_LIB)
-        lib.bench_copy16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
-                                     ctypes.c_void_p]
+        P = ctypes.c_void_p
+        lib.bench_copy16.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, P, P, P]
         lib.bench_copy16.restype = ctypes.c_int
+        lib.bench_event_create.argtypes = []
+        lib.bench_event_create.restype = P
+        lib.bench_event_destroy.argtypes = [P]
+        lib.bench_event_destroy.restype = None
+        lib.bench_event_elapsed_us.argtypes = [P, P]
+        lib.bench_event_elapsed_us.restype = ctypes.c_double
         return lib
 
     def __init__(self, torch, dev):
@@ -350,10 +403,11 @@ class DeviceCopy:
         log(f"[bench] copy kernel GB/s by unroll (1 GiB): {self.sweep}; using {self.unroll}")
         del src, dst
 
-    def __call__(self, dst, src):
+    def __call__(self, dst, src, events=None):
         n = min(dst.numel() * dst.element_size(), src.numel() * src.element_size())
+        start, stop = events if events else (None, None)
         st = self.lib.bench_copy16(dst.data_ptr(), src.data_ptr(), n // 16, self.unroll,
-                                   self.torch.cuda.current_stream().cuda_stream)
+                                   self.torch.cuda.current_stream().cuda_stream, start, stop)
         if st != 0:
             raise RuntimeError(f"bench_copy16 failed: {st}")
 
@@ -398,33 +452,30 @@ def main():
     torch.cuda.synchronize()
     step_bytes = sum(l[3] for l in launches)
 
-    def step(events=None, only=None):
+    nl = len(launches)
+
+    def step(kev=None, s=0, only=None):
+        """One pass of the chain; with `kev`, launch i of step s is timed by event pair
+        s * nl + i (only launch `only` when given)."""
         for i, (_, _, fn, _) in enumerate(launches):
-            rec = events is not None and (only is None or i == only)
-            if rec:
-                events[i][0].record()
+            if kev is not None and (only is None or i == only):
+                kev.arm(mx, s * nl + i)
             fn()
-            if rec:
-                events[i][1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    def new_events():
-        return [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-                 for _ in launches] for _ in range(args.steps)]
-
-    # per-launch means from an untimed pass with events around every launch; the timed
-    # region then records events only around the dominant launch, so the step rate does
-    # not pay for the other event records
-    pev = new_events()
+    # per-launch means from an untimed pass with every launch timed; the timed region
+    # then times only the dominant launch (the events are bound to the kernels, so the
+    # timing puts no commands of its own between the launches either way)
+    kev = KernelEvents(args.steps * nl)
     for s in range(args.steps):
-        step(pev[s])
-    torch.cuda.synchronize()
+        step(kev, s)
+    pus = kev.elapsed()
     per_kernel = []
     for i, (kern, segname, _, nbytes) in enumerate(launches):
-        ms = [pev[s][i][0].elapsed_time(pev[s][i][1]) for s in range(args.steps)]
+        ms = [pus[s * nl + i] / 1000.0 for s in range(args.steps)]
         mean_ms = float(np.mean(ms))
         per_kernel.append({
             "kernel": kern, "segment": segname, "alg_bytes": nbytes,
@@ -434,17 +485,18 @@ def main():
         })
     dom_i = max(range(len(per_kernel)), key=lambda i: per_kernel[i]["mean_us"])
 
-    ev = new_events()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
-        step(ev[s], only=dom_i)
+        step(kev, s, only=dom_i)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1000.0 / args.steps
 
     # the dominant launch as measured inside the timed region
-    dms = [ev[s][dom_i][0].elapsed_time(ev[s][dom_i][1]) for s in range(args.steps)]
+    dus = kev.elapsed()
+    dms = [dus[s * nl + dom_i] / 1000.0 for s in range(args.steps)]
+    kev.close()
     d_mean = float(np.mean(dms))
     dnb = per_kernel[dom_i]["alg_bytes"]
     dom = dict(per_kernel[dom_i])
@@ -453,17 +505,17 @@ def main():
     traffic = read_traffic(dom["kernel"], w.name, dom["segment"])
 
     def time_launches(fn):
+        """Milliseconds per call of `fn` (one entry-point call), kernel events."""
         for _ in range(max(1, args.warmup)):
             fn()
-        tev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+        tev = KernelEvents(args.steps)
         torch.cuda.synchronize()
-        for a_, b_ in tev:
-            a_.record()
+        for i in range(args.steps):
+            tev.arm(mx, i)
             fn()
-            b_.record()
-        torch.cuda.synchronize()
-        return [a_.elapsed_time(b_) for a_, b_ in tev]
+        ms = [us / 1000.0 for us in tev.elapsed()]
+        tev.close()
+        return ms
 
     def mfma_entry(what, shape, flop, ms):
         us = float(np.mean(ms)) * 1000.0
@@ -543,20 +595,21 @@ def main():
     for _ in range(args.warmup):
         for _, _, fn, _ in blaunches:
             fn()
-    bev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in blaunches] for _ in range(args.steps)]
+    nb_l = len(blaunches)
+    bev = KernelEvents(args.steps * nb_l)
     torch.cuda.synchronize()
     tb0 = time.perf_counter()
     for s in range(args.steps):
         for i, (_, _, fn, _) in enumerate(blaunches):
-            bev[s][i][0].record()
+            bev.arm(mx, s * nb_l + i)
             fn()
-            bev[s][i][1].record()
     torch.cuda.synchronize()
     b_ms_per_step = (time.perf_counter() - tb0) * 1000.0 / args.steps
+    bus = bev.elapsed()
+    bev.close()
     b_per_kernel = []
     for i, (kern, segname, _, nbytes) in enumerate(blaunches):
-        ms = [bev[s][i][0].elapsed_time(bev[s][i][1]) for s in range(args.steps)]
+        ms = [bus[s * nb_l + i] / 1000.0 for s in range(args.steps)]
         mean_ms = float(np.mean(ms))
         b_per_kernel.append({
             "kernel": kern, "segment": segname, "alg_bytes": nbytes,
@@ -644,11 +697,11 @@ def main():
             "traffic": traffic,
             "alg_bytes_per_launch": dom["alg_bytes"],
             "mean_launch_us": dom["mean_us"],
-            "measured": "HIP events around this launch inside the timed region",
+            "measured": "HIP events bound to this launch's kernel (mxfp4_time_next_launch) inside the timed region",
         },
         "per_kernel": per_kernel,
-        "per_kernel_measured": "HIP events around every launch, in an untimed pass of the same steps before "
-                               "the timed region",
+        "per_kernel_measured": "HIP events bound to every launch's kernel, in an untimed pass of the same steps "
+                               "before the timed region",
         "backward": backward,
         "gemm": gemm,
         "wgrad": wgrad,
@@ -657,7 +710,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_scrubbed:
-        del segs, launches, ev
+        del segs, launches
         torch.cuda.empty_cache()
         log("[bench] per-kernel medians with the caches scrubbed (configs 2, 3, 4, 5)")
         result["per_config_scrubbed"] = scrubbed_medians(mx, torch, dev, (2, 3, 4, 5))

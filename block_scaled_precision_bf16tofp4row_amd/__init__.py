@@ -26,6 +26,8 @@ The binding has the same names as the C ABI:
   ``mxfp4_status_string(status)``
 * ``mxfp4_wait_status(stream)`` (raises if a column conversion's bounded wait gave up
   since the last check) and ``mxfp4_set_wait_limit(polls)`` (its test hook)
+* ``mxfp4_time_next_launch(start, stop)`` (binds two HIP event handles to the kernels
+  of this thread's next call, for kernel-only timing)
 
 Array arguments are torch tensors on the GPU (BF16 input as ``torch.bfloat16``
 or ``torch.int16``/``torch.uint16`` bits; uint8 outputs; int32 offsets), or raw
@@ -64,6 +66,7 @@ EXPORTED = (
     "mxfp4_validate_offsets",
     "mxfp4_wait_status",
     "mxfp4_set_wait_limit",
+    "mxfp4_time_next_launch",
     "mxfp4_status_string",
 )
 
@@ -116,6 +119,8 @@ def load_library(path: str = LIB_PATH):
     lib.mxfp4_wait_status.restype = st
     lib.mxfp4_set_wait_limit.argtypes = [ctypes.c_uint32]
     lib.mxfp4_set_wait_limit.restype = None
+    lib.mxfp4_time_next_launch.argtypes = [P, P]
+    lib.mxfp4_time_next_launch.restype = st
     lib.mxfp4_status_string.argtypes = [st]
     lib.mxfp4_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -390,6 +395,13 @@ def mxfp4_set_wait_limit(polls: int) -> None:
     if not 0 <= int(polls) < 2 ** 32:
         raise ValueError("polls must fit in 32 bits")
     load_library().mxfp4_set_wait_limit(int(polls))
+
+
+def mxfp4_time_next_launch(start, stop) -> None:
+    """Bind two HIP event handles (ints, created by the caller with hipEventCreate) to
+    the first and last kernel of this thread's next entry-point call, so that their
+    elapsed time is the kernels' own execution; (None, None) disarms."""
+    _check(load_library().mxfp4_time_next_launch(start or None, stop or None), "mxfp4_time_next_launch")
 
 
 # ---- output allocation (plumbing: torch device memory) ----------------------------

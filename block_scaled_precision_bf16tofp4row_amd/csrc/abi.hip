@@ -6,6 +6,8 @@
 #include <atomic>
 #include <mutex>
 
+#include <hip/hip_ext.h>
+
 #include "mxfp4cvt.h"
 #include "common.h"
 
@@ -110,7 +112,24 @@ hipError_t read_status(uint32_t* flag, hipStream_t stream)
     return e;
 }
 
+// Timing events armed by mxfp4_time_next_launch on this thread.
+thread_local hipEvent_t armed_start = nullptr;
+thread_local hipEvent_t armed_stop = nullptr;
+
 }  // namespace
+
+hipError_t mxfp4::launch_kernel(const void* kernel, dim3 grid, dim3 block, void** args, hipStream_t stream,
+                                bool last_of_call)
+{
+    hipEvent_t start = armed_start;
+    hipEvent_t stop = last_of_call ? armed_stop : nullptr;
+    if (!start && !stop)
+        return hipLaunchKernel(kernel, grid, block, args, 0, stream);
+    armed_start = nullptr;
+    if (last_of_call)
+        armed_stop = nullptr;
+    return hipExtLaunchKernel(kernel, grid, block, args, 0, stream, start, stop, 0);
+}
 
 extern "C" {
 
@@ -380,6 +399,13 @@ mxfp4_status mxfp4_wait_status(hipStream_t stream)
 }
 
 void mxfp4_set_wait_limit(uint32_t polls) { spin_limit.store(polls, std::memory_order_relaxed); }
+
+mxfp4_status mxfp4_time_next_launch(hipEvent_t start, hipEvent_t stop)
+{
+    armed_start = start;
+    armed_stop = stop;
+    return MXFP4_OK;
+}
 
 const char* mxfp4_status_string(mxfp4_status status)
 {

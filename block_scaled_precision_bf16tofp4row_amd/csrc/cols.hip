@@ -376,8 +376,7 @@ hipError_t launch_fp8_cols(const uint8_t* codes, const uint8_t* scales, uint8_t*
     int p = (int)parts;
     void* args[] = {(void*)&codes, (void*)&scales, (void*)&yT, (void*)&yT_scales, (void*)&offs,
                     (void*)&g, (void*)&k, (void*)&p, (void*)&wc};
-    return hipLaunchKernel((const void*)fp8_cols_kernel, dim3((unsigned)grid), dim3(kColsThreads), args,
-                           0, stream);
+    return launch_kernel((const void*)fp8_cols_kernel, dim3((unsigned)grid), dim3(kColsThreads), args, stream);
 }
 
 }  // namespace mxfp4

@@ -32,6 +32,14 @@ struct WaitCtl {
 // protocol could wait that long.
 constexpr uint32_t kDefaultSpinLimit = 1u << 24;
 
+// Every kernel of the library is launched through this (abi.hip).  When the calling
+// thread has armed timing events (mxfp4_time_next_launch), the start event is bound to
+// the first launch of the next entry-point call and the stop event to the launch with
+// last_of_call set (the only one, except in calls that launch two kernels), so their
+// elapsed time is the kernels' own execution; then they are disarmed.
+hipError_t launch_kernel(const void* kernel, dim3 grid, dim3 block, void** args, hipStream_t stream,
+                         bool last_of_call = true);
+
 // ---- memory ---------------------------------------------------------------------
 
 // Every byte of this path is touched exactly once: stream it past the caches.

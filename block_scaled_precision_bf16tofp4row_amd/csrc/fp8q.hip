@@ -168,8 +168,8 @@ hipError_t launch_fp8q_rows(const uint16_t* x, uint8_t* y, uint8_t* y_scales,
     int g = G;
     int64_t k = K;
     void* args[] = {(void*)&xv, (void*)&yv, (void*)&y_scales, (void*)&offs, (void*)&g, (void*)&k};
-    return hipLaunchKernel((const void*)fp8q_rows_kernel<kFp8qU>, dim3((unsigned)grid),
-                           dim3(kThreads), args, 0, stream);
+    return launch_kernel((const void*)fp8q_rows_kernel<kFp8qU>, dim3((unsigned)grid), dim3(kThreads), args,
+                         stream);
 }
 
 }  // namespace mxfp4

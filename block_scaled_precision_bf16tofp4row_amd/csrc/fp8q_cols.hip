@@ -429,7 +429,7 @@ hipError_t launch_fp8q_cols(const uint16_t* x, uint8_t* yT, uint8_t* yT_scales, 
     void* args[] = {(void*)&xb, (void*)&yT, (void*)&yT_scales, (void*)&y, (void*)&y_scales, (void*)&offs,
                     (void*)&g, (void*)&k, (void*)&p, (void*)&wc};
     const void* kern = y ? (const void*)fp8q_cols_kernel<true> : (const void*)fp8q_cols_kernel<false>;
-    return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kQThreads), args, 0, stream);
+    return launch_kernel(kern, dim3((unsigned)grid), dim3(kQThreads), args, stream);
 }
 
 }  // namespace mxfp4

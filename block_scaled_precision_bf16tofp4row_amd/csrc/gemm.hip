@@ -497,7 +497,7 @@ hipError_t launch_fp8_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* w
                     (void*)&n, (void*)&k};
     const bool fast = K <= 128 * kMaxFastBlocks && K % (kTK * kStages) == 0;
     const void* kern = fast ? (const void*)fp8_gemm_kernel : (const void*)fp8_gemm_general_kernel;
-    return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(fast ? kFastThreads : kGemmThreads), args, 0, stream);
+    return launch_kernel(kern, dim3((unsigned)grid), dim3(fast ? kFastThreads : kGemmThreads), args, stream);
 }
 
 }  // namespace mxfp4

@@ -235,15 +235,16 @@ hipError_t launch_nvfp4_quantize_rows(const uint16_t* x, uint8_t* codes, uint8_t
     uint32_t* ab = reinterpret_cast<uint32_t*>(tensor_amax);
     int g = G;
     int64_t k = K;
-    hipLaunchKernelGGL(nvfp4_amax_init_kernel, dim3(1), dim3(1), 0, stream, ab);
-    hipError_t err = hipGetLastError();
+    void* iargs[] = {(void*)&ab};
+    hipError_t err = launch_kernel((const void*)nvfp4_amax_init_kernel, dim3(1), dim3(1), iargs, stream,
+                                   nchunks_cap == 0);
     if (err != hipSuccess || nchunks_cap == 0)
         return err;
     const int64_t per_amax = (int64_t)kThreads * kAmaxU;
     const int64_t grid_amax = min((nchunks_cap + per_amax - 1) / per_amax, (int64_t)(device_cus() * 2));
     void* aargs[] = {(void*)&xv, (void*)&ab, (void*)&offs, (void*)&g, (void*)&k};
-    err = hipLaunchKernel((const void*)nvfp4_amax_kernel, dim3((unsigned)grid_amax), dim3(kThreads), aargs, 0,
-                          stream);
+    err = launch_kernel((const void*)nvfp4_amax_kernel, dim3((unsigned)grid_amax), dim3(kThreads), aargs, stream,
+                        false);
     if (err != hipSuccess)
         return err;
     const int64_t per_block = (int64_t)kThreads * kNvU;
@@ -255,7 +256,7 @@ hipError_t launch_nvfp4_quantize_rows(const uint16_t* x, uint8_t* codes, uint8_t
     void* qargs[] = {(void*)&xv, (void*)&cv,   (void*)&scales,  (void*)&abc,    (void*)&offs,
                      (void*)&g,  (void*)&k, (void*)&seed_lo, (void*)&seed_hi};
     const void* fn = sr ? (const void*)nvfp4_quantize_kernel<true> : (const void*)nvfp4_quantize_kernel<false>;
-    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), qargs, 0, stream);
+    return launch_kernel(fn, dim3((unsigned)grid), dim3(kThreads), qargs, stream);
 }
 
 }  // namespace mxfp4

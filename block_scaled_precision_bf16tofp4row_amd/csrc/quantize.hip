@@ -114,8 +114,8 @@ hipError_t launch_quantize_rows(const uint16_t* x, uint8_t* codes, uint8_t* scal
     int g = G;
     int64_t k = K;
     void* args[] = {(void*)&xv, (void*)&cv, (void*)&scales, (void*)&offs, (void*)&g, (void*)&k};
-    return hipLaunchKernel((const void*)quantize_rows_kernel<kQuantU>, dim3((unsigned)grid),
-                           dim3(kThreads), args, 0, stream);
+    return launch_kernel((const void*)quantize_rows_kernel<kQuantU>, dim3((unsigned)grid), dim3(kThreads), args,
+                         stream);
 }
 
 }  // namespace mxfp4

@@ -106,8 +106,8 @@ hipError_t launch_fp8_rows(const uint8_t* codes, const uint8_t* scales, uint8_t*
     int g = G;
     int64_t k = K;
     void* args[] = {(void*)&cv, (void*)&sv, (void*)&yv, (void*)&y_scales, (void*)&offs, (void*)&g, (void*)&k};
-    return hipLaunchKernel((const void*)fp8_rows_kernel<kRowsU>, dim3((unsigned)grid), dim3(kThreads),
-                           args, 0, stream);
+    return launch_kernel((const void*)fp8_rows_kernel<kRowsU>, dim3((unsigned)grid), dim3(kThreads), args,
+                         stream);
 }
 
 }  // namespace mxfp4

@@ -279,8 +279,7 @@ hipError_t launch_fp8_wgrad(const uint8_t* dyT, const uint8_t* sdy, const uint8_
     int g = G;
     void* args[] = {(void*)&dyT, (void*)&sdy, (void*)&xT, (void*)&sx, (void*)&dw, (void*)&offs, (void*)&g,
                     (void*)&M_cap, (void*)&scale_blocks_cap, (void*)&N, (void*)&K};
-    return hipLaunchKernel((const void*)fp8_wgrad_kernel, dim3((unsigned)grid), dim3(kWgThreads), args, 0,
-                           stream);
+    return launch_kernel((const void*)fp8_wgrad_kernel, dim3((unsigned)grid), dim3(kWgThreads), args, stream);
 }
 
 }  // namespace mxfp4

@@ -251,6 +251,16 @@ mxfp4_status mxfp4_wait_status(hipStream_t stream);
  * still leaves the kernel normally) and the call's output incomplete. */
 void mxfp4_set_wait_limit(uint32_t polls);
 
+/* Measurement hook: binds two caller-created HIP events (hipEventCreate, owned by the
+ * caller) to the kernel launches of the calling thread's next entry-point call: `start`
+ * to its first kernel and `stop` to its last (hipExtLaunchKernel), so that
+ * hipEventElapsedTime(start, stop) is the kernels' own execution time, with no marker
+ * commands of their own on the stream.  The events are used once and then dropped; a
+ * call that launches nothing (an argument error, M_cap = 0) leaves them armed, and
+ * NULL, NULL disarms.  Either may be NULL.  Calls on other threads are not affected.
+ * Returns MXFP4_OK. */
+mxfp4_status mxfp4_time_next_launch(hipEvent_t start, hipEvent_t stop);
+
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* mxfp4_status_string(mxfp4_status status);
 
