@@ -164,9 +164,12 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     // strip that writes nothing): its bytes past its last line boundary complete the
     // first output line of the range, so the workgroup writes that line whole and the
     // workgroup before it stops at its last line boundary.  Lines split between two
-    // workgroups would otherwise be written partially twice.
+    // workgroups would otherwise be written partially twice.  An expert whose row count
+    // is a multiple of 128 needs none: every strip of it starts and ends on a line
+    // boundary of every column (K, the strip starts and the column length M_g are then
+    // all multiples of 128), so nothing is carried.
     const StripInfo first = locate(offs, G, t0, s0);
-    const uint32_t lead = first.s > first.sb ? 1u : 0u;
+    const uint32_t lead = first.s > first.sb && (first.mg & (kStripRows - 1)) != 0 ? 1u : 0u;
     const uint32_t n = s1 - s0 + lead;            // strips this workgroup converts
 
     if (tid < 2 * (kMaxGap + 1))

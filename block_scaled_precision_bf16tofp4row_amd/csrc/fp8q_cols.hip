@@ -160,9 +160,10 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     if (s0 >= s1)
         return;                                   // uniform over the workgroup
     // a range that starts inside an expert also quantizes the strip before it (a
-    // lead-in strip that writes nothing), so its first output line is written whole
+    // lead-in strip that writes nothing), so its first output line is written whole; an
+    // expert whose row count is a multiple of 128 carries nothing and needs none
     const StripInfo first = locate(offs, G, t0, s0);
-    const uint32_t lead = first.s > first.sb ? 1u : 0u;
+    const uint32_t lead = first.s > first.sb && (first.mg & (kStripRows - 1)) != 0 ? 1u : 0u;
     const uint32_t n = s1 - s0 + lead;
 
     if (tid == 0) {

@@ -91,6 +91,21 @@ def test_cols_carry_across_strips():
     check_chain(seg.x_bits, seg.offs, kernels=("quantize", "cols"))
 
 
+def test_cols_aligned_experts_without_lead_in():
+    """Experts whose row counts are multiples of 128 carry nothing across strips, so a
+    workgroup range starting inside one needs no lead-in strip: ranges start inside
+    such experts (56 column tiles, a few parts each), next to ragged ones whose ranges
+    still take a lead-in; the backward column quantizer and its both-layouts mode take
+    the same rule."""
+    from gpu_path import check_fp8q_both, check_fp8q_cols
+    counts = [2048, 1280, 131, 3072, 640, 1025, 1024, 0, 384]
+    say(f"aligned experts counts={counts} K=7168")
+    seg = workloads.ragged_case(counts, 7168, seed=23, values="t3", M_cap=sum(counts) + 5)
+    check_chain(seg.x_bits, seg.offs, kernels=("quantize", "cols"))
+    check_fp8q_cols(seg.x_bits, seg.offs)
+    check_fp8q_both(seg.x_bits, seg.offs)
+
+
 def test_config1_full_chain():
     w = workloads.config1(0)
     seg = w.segments[0]
