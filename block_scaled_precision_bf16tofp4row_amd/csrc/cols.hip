@@ -27,8 +27,8 @@
 //            (rq = lane >> 3, c = lane & 7) holds the 16 code bytes of group c for
 //            rows 32w + 4rq .. + 3, loaded two strips ahead.  The block scale of a
 //            group is the max over the strip's 128 rows: each wave reduces its 32
-//            rows (DPP and lane shuffles) and publishes the partial max in LDS, and
-//            every wave takes the max of the four.  Each row is converted with the
+//            rows (a DPP row rotation and the 16- and 32-lane swaps) and publishes
+//            the partial max in LDS, and every wave takes the max of the four.  Each row is converted with the
 //            gap table of its own scale; 4x4 byte transposes turn 4 rows x 32 columns
 //            into 32 dwords (4 rows of one column each), written into a k-major LDS
 //            ring: one ring per output column k holding the column's bytes of the
@@ -224,8 +224,11 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
         auto publish_max = [&](const RowScales& sc, uint32_t slot) {
             uint32_t m = max(max(sc.b[0], sc.b[1]), max(sc.b[2], sc.b[3]));
             m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x128, 0xF, 0xF, false)); // row_ror:8
-            m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
-            m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+            // the 16- and 32-lane swaps of gfx950 (VALU, no LDS round trip)
+            const auto a16 = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+            m = max((uint32_t)a16[0], (uint32_t)a16[1]);
+            const auto a32 = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+            m = max((uint32_t)a32[0], (uint32_t)a32[1]);
             if (rq == 0)
                 reinterpret_cast<uint8_t*>(pmax[slot])[4 * c + wave] = (uint8_t)m;
         };
