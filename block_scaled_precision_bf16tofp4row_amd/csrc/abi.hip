@@ -1,5 +1,6 @@
 // abi.hip -- the C ABI of libmxfp4cvt (declared in include/mxfp4cvt.h): synchronous
-// argument validation, then one kernel launch on the caller's stream.
+// argument validation, then the call's kernel launches on the caller's stream (one per
+// call, three for the NVFP4 quantizer), all through launch_kernel.
 #include <stdlib.h>
 #include <string.h>
 
