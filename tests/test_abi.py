@@ -329,3 +329,10 @@ def test_wait_limit_hook_is_host_only(lib):
     lib.mxfp4_set_wait_limit(0)
     with pytest.raises(ValueError):
         mx.mxfp4_set_wait_limit(-1)
+
+
+def test_timing_hook_is_host_only(lib):
+    # arming and disarming only set this thread's two handles: no HIP call, works
+    # without a device (the events themselves are used by the next launch)
+    assert lib.mxfp4_time_next_launch(None, None) == mx.MXFP4_OK
+    mx.mxfp4_time_next_launch(None, None)
