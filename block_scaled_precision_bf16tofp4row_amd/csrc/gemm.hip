@@ -34,13 +34,18 @@
 // stored at chunk c ^ ((r >> 1) & 7), so the fragment reads of 16 consecutive rows
 // (one LDS cycle of a 16-byte read) hit distinct banks (a lane of the load picks the
 // global chunk that belongs in its LDS slot).  The compiler does not see that the
-// fragment reads depend on these loads, so a stage is awaited explicitly: before stage
-// t's barrier a lane waits for its own loads of stage t.  Stages run in pairs (one per
-// buffer) whose load issues are fixed at compile time, the last pair peeled, so that a
-// pair is one basic block and the compiler keeps each stage's matrix work in its stage
-// instead of sinking it towards the stores.  A wave raises its priority while it issues
-// a stage's MFMAs (s_setprio), so the SIMD's other wave does its waiting meanwhile
-// instead of both contending for the issue slots in lockstep.
+// fragment reads depend on these loads, so a stage is awaited explicitly: before the
+// barrier that opens stage t + 1 a lane waits for its own loads of it.  The loop is
+// software-pipelined by MFMA K-step: that barrier sits between the second K-step's
+// fragment reads of stage t and its MFMAs, so after it every wave has eight MFMAs
+// queued on registers it already holds while it reads stage t + 1's first fragments
+// (and the first K-step's MFMAs cover the second K-step's reads the same way).  Stages
+// run in pairs (one per buffer) whose load issues are fixed at compile time, the last
+// pair peeled, so that a pair is one basic block and the compiler keeps each stage's
+// matrix work in its stage instead of sinking it towards the stores.  A wave raises its
+// priority while it issues MFMAs (s_setprio), so the SIMD's other wave does its waiting
+// meanwhile instead of both contending for the issue slots in lockstep.  The epilogue
+// stages the BF16 tile in the free LDS buffers and stores whole 512-byte row segments.
 // The tile's block scales (256 rows x K/128 bytes per operand) are staged in LDS once,
 // laid out so that one 4-byte read gives a lane the scales of its four MFMA tiles; they
 // take no registers across stages and no place in the memory-operation count.  Their
@@ -309,56 +314,89 @@ __device__ __forceinline__ void fast_issue(const FastCtx& cx, uint32_t s, int bu
     }
 }
 
-// Stages t0 and t0 + 1 (buffers 0 and 1).  Before stage t's barrier a lane waits for
-// its loads of stage t; after it (every wave is done with stage t - 1), the lane issues
-// stage t + 1 into the other buffer.  kLast: t0 + 2 == T.
-template <bool kLast>
-__device__ __forceinline__ void fast_group(const FastCtx& cx, uint32_t t0, f32x16 (&acc)[4][2])
+// The fragments of one MFMA K-step (64 of K) of a wave: two feature tiles, four token tiles.
+struct FastFrag {
+    i32x8 w[2];
+    i32x8 a[4];
+};
+
+// A lane's fragment of one operand row for one MFMA K-step: the row's 16-byte LDS chunks
+// at byte offsets c0 and c1.
+__device__ __forceinline__ i32x8 fast_frag(const uint8_t* rowp, uint32_t c0, uint32_t c1)
+{
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(rowp + c0);
+    const u32x4 v1 = *reinterpret_cast<const u32x4*>(rowp + c1);
+    return i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+}
+
+// The stage's block scales for the lane's four token tiles and two feature tiles.
+__device__ __forceinline__ void fast_scales(const FastCtx& cx, uint32_t t, uint32_t& sca4, uint32_t& scw4)
+{
+    sca4 = *reinterpret_cast<const uint32_t*>(cx.scl_a + t * kTM + cx.wm * 128 + cx.r * 4);
+    // features 64 wn + 32 nt + r are scale row 128 (wn / 2) + 32 (2 (wn % 2) + nt) + r
+    scw4 = *reinterpret_cast<const uint32_t*>(cx.scl_w + t * kTN + (cx.wn >> 1) * 128 + cx.r * 4) >>
+           (16 * (cx.wn & 1));
+}
+
+// The eight MFMAs of one K-step on `cur`.  With kRead, the fragments of K-step j of the
+// stage in buffer buf are read into `next` between them (the feature tiles first, then
+// one token tile after each token tile's MFMAs), so that a wave's reads overlap its own
+// matrix work and the registers of `cur` free up as `next` fills.  The wave with matrix
+// work to issue goes first: of a SIMD's two waves, one computes while the other waits.
+template <bool kRead>
+__device__ __forceinline__ void fast_step(const FastCtx& cx, const FastFrag& cur, uint32_t sca4, uint32_t scw4,
+                                          f32x16 (&acc)[4][2], int buf, int j, FastFrag& next)
 {
     const uint32_t sw8 = (cx.r >> 1) & 7;                              // the swizzle of rows r + 32 x
+    const uint8_t* const ta = cx.stage[buf] + (128 * cx.wm + cx.r) * kTK;
+    const uint8_t* const tw = cx.stage[buf] + (kTM + 64 * cx.wn + cx.r) * kTK;
+    const uint32_t c0 = 16 * ((4 * j + cx.h) ^ sw8), c1 = 16 * ((4 * j + 2 + cx.h) ^ sw8);
+    if (kRead) {
+        next.w[0] = fast_frag(tw, c0, c1);
+        next.w[1] = fast_frag(tw + 32 * kTK, c0, c1);
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                cur.w[nt], cur.a[mt], acc[mt][nt], 0, 0, 0, (int)((scw4 >> (8 * nt)) & 0xFF), 0,
+                (int)((sca4 >> (8 * mt)) & 0xFF));
+        if (kRead)
+            next.a[mt] = fast_frag(ta + 32 * mt * kTK, c0, c1);
+    }
+    __builtin_amdgcn_s_setprio(0);
+}
+
+// Stages t0 (buffer 0) and t0 + 1 (buffer 1), software-pipelined by K-step.  On entry
+// f holds the fragments of stage t0's first K-step and (sca, scw) its scales.  Per
+// stage t in buffer u: the first K-step's MFMAs issue while the second K-step's
+// fragments are read; the lane waits for its loads of stage t + 1 and meets the other
+// waves at the barrier (every wave's part of stage t + 1 is then in LDS, and every wave
+// has read all of buffer u); stage t + 2 is loaded into buffer u; the second K-step's
+// MFMAs issue while the first K-step of stage t + 1 is read.  The barrier thus never
+// leaves a wave without matrix work queued behind it.  kLast: t0 + 2 == T.
+template <bool kLast>
+__device__ __forceinline__ void fast_pair(const FastCtx& cx, uint32_t t0, FastFrag& f, uint32_t& sca,
+                                          uint32_t& scw, f32x16 (&acc)[4][2])
+{
 #pragma unroll
     for (int u = 0; u < kStages; ++u) {
         const uint32_t t = t0 + u;
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __syncthreads();                          // every lane's part of stage t is in LDS,
-                                                  // and every wave is done with stage t - 1
-        if (!kLast || u == 0)
-            fast_issue(cx, t + 1, u ^ 1);
-        const uint8_t* const ta = cx.stage[u] + (128 * cx.wm) * kTK;
-        const uint8_t* const tw = cx.stage[u] + kTM * kTK + (64 * cx.wn) * kTK;
-        const uint32_t sca4 = *reinterpret_cast<const uint32_t*>(cx.scl_a + t * kTM + cx.wm * 128 + cx.r * 4);
-        // features 64 wn + 32 nt + r are scale row 128 (wn / 2) + 32 (2 (wn % 2) + nt) + r
-        const uint32_t scw4 =
-            *reinterpret_cast<const uint32_t*>(cx.scl_w + t * kTN + (cx.wn >> 1) * 128 + cx.r * 4) >>
-            (16 * (cx.wn & 1));
-        // the wave with matrix work to issue goes first: of a SIMD's two waves, one
-        // computes while the other waits for its loads and fragments
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {             // the stage's two MFMA K-steps of 64
-            const uint32_t c0 = 16 * ((4 * j + cx.h) ^ sw8), c1 = 16 * ((4 * j + 2 + cx.h) ^ sw8);
-            i32x8 fw[2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const uint8_t* const rowp_w = tw + (32 * q + cx.r) * kTK;
-                const u32x4 w0 = *reinterpret_cast<const u32x4*>(rowp_w + c0);
-                const u32x4 w1 = *reinterpret_cast<const u32x4*>(rowp_w + c1);
-                fw[q] = i32x8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
-            }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const uint8_t* const rowp_a = ta + (32 * mt + cx.r) * kTK;
-                const u32x4 a0 = *reinterpret_cast<const u32x4*>(rowp_a + c0);
-                const u32x4 a1 = *reinterpret_cast<const u32x4*>(rowp_a + c1);
-                const i32x8 fa = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fw[nt], fa, acc[mt][nt], 0, 0, 0, (int)((scw4 >> (8 * nt)) & 0xFF), 0,
-                        (int)((sca4 >> (8 * mt)) & 0xFF));
-            }
+        FastFrag g;
+        fast_step<true>(cx, f, sca, scw, acc, u, 1, g);
+        const uint32_t sca_t = sca, scw_t = scw;
+        if (!kLast || u == 0) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __syncthreads();
+            if (!kLast)
+                fast_issue(cx, t + 2, u);
+            fast_scales(cx, t + 1, sca, scw);
+            fast_step<true>(cx, g, sca_t, scw_t, acc, u ^ 1, 0, f);
+        } else {
+            fast_step<false>(cx, g, sca_t, scw_t, acc, 0, 0, f);
         }
-        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -445,35 +483,69 @@ __global__ __launch_bounds__(kFastThreads, 1) void fp8_gemm_kernel(
         for (int nt = 0; nt < 2; ++nt)
             acc[mt][nt] = f32x16{};
 
-    __syncthreads();                              // scales staged
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();                              // scales staged, stage 0 in LDS
+    fast_issue(cx, 1, 1);
+    FastFrag f;
+    uint32_t sca, scw;
+    fast_scales(cx, 0, sca, scw);
+    {
+        const uint32_t sw8 = (cx.r >> 1) & 7;
+        const uint8_t* const ta = cx.stage[0] + (128 * cx.wm + cx.r) * kTK;
+        const uint8_t* const tw = cx.stage[0] + (kTM + 64 * cx.wn + cx.r) * kTK;
+        const uint32_t c0 = 16 * (cx.h ^ sw8), c1 = 16 * ((2 + cx.h) ^ sw8);
+        f.w[0] = fast_frag(tw, c0, c1);
+        f.w[1] = fast_frag(tw + 32 * kTK, c0, c1);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            f.a[mt] = fast_frag(ta + 32 * mt * kTK, c0, c1);
+    }
     // T is even (K is a multiple of 256 on this path): stages run in pairs, one per LDS
     // buffer; the last pair is peeled so that every load issue in a pair is fixed at
     // compile time and a pair is one basic block
     uint32_t t0 = 0;
     for (; t0 + kStages < T; t0 += kStages)
-        fast_group<false>(cx, t0, acc);
-    fast_group<true>(cx, t0, acc);
+        fast_pair<false>(cx, t0, f, sca, scw, acc);
+    fast_pair<true>(cx, t0, f, sca, scw, acc);
 
-    // epilogue: lane (r, h) of MFMA tile (mt, nt) holds token 128 wm + 32 mt + r and
-    // features 64 wn + 32 nt + 8 q + 4 h + (0..3) in values 4q .. 4q + 3.  The stores
-    // go through a buffer resource whose range is the tile's existing rows, so stores
-    // of rows past them are dropped without a branch.
+    // epilogue through LDS: lane (r, h) of MFMA tile (mt, nt) holds token 128 wm + 32 mt + r
+    // and features 64 wn + 32 nt + 8 q + 4 h + (0..3) in values 4q .. 4q + 3.  The waves
+    // write their BF16 results into the stage buffers (tokens 128 wm .. + 127 into
+    // buffer wm, 512 bytes per token, the 16-byte chunk c of token row x at chunk
+    // c ^ (x % 32), so that neither the writes nor the row reads below conflict), then
+    // every lane stores 16-byte pieces of whole rows: one store instruction of a wave
+    // covers two 512-byte row segments (four whole 128-byte lines each), where the
+    // registers alone would give 32 rows of 16 bytes.  The stores go through a buffer
+    // resource whose range is the tile's existing rows, so rows past them are dropped
+    // without a branch.
+    __syncthreads();                              // every wave is done reading the last stage
+    {
+        uint8_t* const ob = wm ? lds1 : lds0;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16& v = acc[mt][nt];
+                    const bf16x2_g p0 = {(__bf16)v[4 * q + 0], (__bf16)v[4 * q + 1]};
+                    const bf16x2_g p1 = {(__bf16)v[4 * q + 2], (__bf16)v[4 * q + 3]};
+                    const uint32_t c = 8 * (uint32_t)wn + 4 * nt + q;
+                    *reinterpret_cast<u32x2*>(ob + (32 * mt + r) * 512 + 16 * (c ^ r) + 8 * h) =
+                        u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+                }
+    }
+    __syncthreads();
     const __amdgpu_buffer_rsrc_t ry = strip_rsrc(y + row0 * N, (uint64_t)rows * (uint64_t)N * 2);
+    {
+        const uint32_t c = (uint32_t)tid & 31;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const uint32_t mloc = 128 * wm + 32 * mt + r;
-        const uint32_t yoff = (mloc * (uint32_t)N + (uint32_t)n0 + 64 * wn + 4 * h) * 2;
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x16& v = acc[mt][nt];
-                const bf16x2_g p0 = {(__bf16)v[4 * q + 0], (__bf16)v[4 * q + 1]};
-                const bf16x2_g p1 = {(__bf16)v[4 * q + 2], (__bf16)v[4 * q + 3]};
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)}, ry,
-                    (int)(yoff + 2 * (32 * nt + 8 * q)), 0, 0);
-            }
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t row = ((uint32_t)tid >> 5) + 16 * i;          // tile row 0 .. 255
+            const uint8_t* const src = (i < 8 ? lds0 : lds1) + (row & 127) * 512 + 16 * (c ^ (row & 31));
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src), ry,
+                                                   (int)((row * (uint32_t)N + (uint32_t)n0) * 2 + 16 * c), 0, 0);
+        }
     }
 }
 
