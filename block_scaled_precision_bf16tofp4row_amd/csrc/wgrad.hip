@@ -21,15 +21,17 @@
 // other's loads and LDS traffic) owns a 256 (n) x 256 (k) tile of one expert's dW and
 // walks the expert's tokens in steps of 128; wave (wm, wn) computes n 128 wm .. + 127 x
 // k 64 wn .. + 63 as 4 x 2 MFMA tiles (128 fp32 accumulators per lane).  A column row
-// has M_g bytes, so the 128-token piece of a row starts at any byte: a thread loads the
-// aligned 16 bytes at or below its 16-byte slice and the dword after them, and shifts
-// them into place with v_alignbyte by the row start's offset mod 4 (fixed per row).
-// Bytes past token M_g (the next row's) are masked to zero, so the partial last block
-// adds nothing.  The realigned slices go through registers into two 64 KB LDS buffers
-// (128-byte rows, chunk c of row r at c ^ ((r >> 1) & 7), as in the forward GEMM), the
-// next step's loads in flight during the current step's matrix work.  Loads are buffer
+// has M_g bytes, so the 128-token piece of a row starts at any byte.  The pieces go
+// straight from memory into two 64 KB LDS buffers with buffer_load ... lds, whose
+// 16-byte lanes take any byte alignment (checked on MI355X with an in-bounds probe: the
+// bytes land as they are at a misaligned address), so no register staging or shifting
+// is needed; LDS rows are 128 bytes with chunk c of row r at c ^ ((r >> 1) & 7), as in
+// the forward GEMM, and the loop is software-pipelined the same way.  Bytes past token
+// M_g in the last step belong to the next row: both operands' fragments are masked to
+// zero there in registers, so the partial last block adds nothing.  Loads are buffer
 // loads with the whole offset in the per-lane part, over the caller's capacity from the
-// expert's first byte, so no access leaves the operand buffers.
+// expert's first byte, so no access leaves the operand buffers.  The epilogue stages
+// the BF16 tile in LDS and stores whole 512-byte row segments.
 #include "strips.h"
 
 namespace mxfp4 {
@@ -74,6 +76,99 @@ __device__ __forceinline__ int wg_expert_of_rank(const int32_t* __restrict__ off
     return (int)uniform((uint32_t)(__builtin_ffsll((long long)hit) - 1));
 }
 
+// What a wave needs in the step loop.
+struct WgCtx {
+    uint8_t* lds;                                 // two step buffers of kWStage bytes
+    __amdgpu_buffer_rsrc_t rdy, rx;
+    int wm, wn;
+    uint32_t r, h;
+};
+
+// The fragments of one MFMA K-step (64 tokens) of a wave: two X^T tiles, four dY^T tiles.
+struct WgFrag {
+    wg_i32x8 x[2];
+    wg_i32x8 d[4];
+};
+
+// A lane's fragment of one operand row: the row's 16-byte LDS chunks at c0 and c1.
+__device__ __forceinline__ wg_i32x8 wg_frag(const uint8_t* rowp, uint32_t c0, uint32_t c1)
+{
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(rowp + c0);
+    const u32x4 v1 = *reinterpret_cast<const u32x4*>(rowp + c1);
+    return wg_i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+}
+
+// Where lane (r, h) reads K-step j of buffer b: tokens 64 j + 16 h .. + 15 and
+// 64 j + 32 + 16 h .. + 15 of its rows (logical chunks 4 j + h and 4 j + 2 + h; LDS rows
+// are 128 bytes with chunk c of row x at c ^ ((x >> 1) & 7)).
+struct WgAddr {
+    const uint8_t* td;
+    const uint8_t* tx;
+    uint32_t c0, c1;
+};
+__device__ __forceinline__ WgAddr wg_addr(const WgCtx& cx, uint32_t b, int j)
+{
+    const uint32_t sw8 = (cx.r >> 1) & 7;
+    const uint8_t* const base = cx.lds + b * kWStage;
+    return WgAddr{base + (128 * cx.wm + cx.r) * kWS, base + (kWT + 64 * cx.wn + cx.r) * kWS,
+                  16 * ((4 * j + cx.h) ^ sw8), 16 * ((4 * j + 2 + cx.h) ^ sw8)};
+}
+
+__device__ __forceinline__ void wg_read(const WgCtx& cx, uint32_t b, int j, WgFrag& f)
+{
+    const WgAddr ad = wg_addr(cx, b, j);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        f.x[q] = wg_frag(ad.tx + 32 * q * kWS, ad.c0, ad.c1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        f.d[q] = wg_frag(ad.td + 32 * q * kWS, ad.c0, ad.c1);
+}
+
+// Zero the bytes of tokens >= valid (counted from the step's first token) in the
+// fragments of K-step j read by lane half h: dword e holds tokens
+// 64 j + 16 h + 32 (e / 4) + 4 (e % 4) .. + 3.
+__device__ __forceinline__ void wg_mask(WgFrag& f, int valid, int j, uint32_t h)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int v = min(max(valid - (64 * j + 16 * (int)h + 32 * (e >> 2) + 4 * (e & 3)), 0), 4);
+        const int m = v >= 4 ? -1 : (int)((1u << (8 * v)) - 1u);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            f.x[q][e] &= m;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            f.d[q][e] &= m;
+    }
+}
+
+// The eight MFMAs of one K-step on `cur`.  With kRead, K-step j of buffer b is read into
+// `next` between them (the X^T tiles first, then one dY^T tile after each dY^T tile's
+// MFMAs).  As in the forward GEMM, a wave raises its priority while it issues MFMAs.
+template <bool kRead>
+__device__ __forceinline__ void wg_step(const WgCtx& cx, const WgFrag& cur, const uint32_t (&sx)[2],
+                                        const uint32_t (&sdy)[4], wg_f32x16 (&acc)[4][2], uint32_t b, int j,
+                                        WgFrag& next)
+{
+    const WgAddr ad = wg_addr(cx, b, j);
+    if (kRead) {
+        next.x[0] = wg_frag(ad.tx, ad.c0, ad.c1);
+        next.x[1] = wg_frag(ad.tx + 32 * kWS, ad.c0, ad.c1);
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.x[nt], cur.d[mt], acc[mt][nt], 0, 0,
+                                                                          0, (int)sx[nt], 0, (int)sdy[mt]);
+        if (kRead)
+            next.d[mt] = wg_frag(ad.td + 32 * mt * kWS, ad.c0, ad.c1);
+    }
+    __builtin_amdgcn_s_setprio(0);
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
@@ -116,20 +211,21 @@ __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
     const __amdgpu_buffer_rsrc_t rsx =
         strip_rsrc(sx + K * (int64_t)Bg, (uint64_t)K * (uint64_t)(scale_blocks_cap - Bg));
 
-    // loader role: thread t takes the 16-byte slice c = t & 7 of the step's piece of
-    // local rows (t >> 3) + 64 i, i = 0..3, of both operands
-    const uint32_t lrow = (uint32_t)(tid >> 3), lchunk = (uint32_t)(tid & 7);
-    const uint32_t lds_w = lrow * kWS + 16 * (lchunk ^ ((lrow >> 1) & 7));   // + 64 i kWS
-    uint32_t o_dy[4], o_x[4];                     // byte offset of the slice at step 0
+    // loader role: instruction i of wave w fills LDS rows 32 w + 8 i .. + 7 of each
+    // operand with the step's 128-byte pieces (LDS DMA takes any byte alignment, so a
+    // piece lands as it is, whatever the row start); lane L takes row 32 w + 8 i + L / 8
+    // and LDS chunk L % 8, that is chunk (L % 8) ^ ((row >> 1) & 7) of the piece
+    uint32_t ld_dy[4], ld_x[4];                   // byte offsets of the lane's slices at step 0
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        o_dy[i] = (uint32_t)(n0 + lrow + 64 * i) * Mg + 16 * lchunk;
-        o_x[i] = (uint32_t)(k0 + lrow + 64 * i) * Mg + 16 * lchunk;
+        const uint32_t lrow = (uint32_t)(32 * wave + 8 * i + (lane >> 3));
+        const uint32_t gc = (uint32_t)(lane & 7) ^ ((lrow >> 1) & 7);
+        ld_dy[i] = (uint32_t)(n0 + lrow) * Mg + 16 * gc;
+        ld_x[i] = (uint32_t)(k0 + lrow) * Mg + 16 * gc;
     }
     // compute role: wave (wm, wn), lane (r, h)
     const int wm = wave & 1, wn = wave >> 1;
     const uint32_t r = (uint32_t)(lane & 31), h = (uint32_t)(lane >> 5);
-    const uint32_t sw8 = (r >> 1) & 7;                                 // the swizzle of rows r + 32 x
     uint32_t soff_x[2], soff_dy[4];               // scale bytes of the lane's rows
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -137,49 +233,57 @@ __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
 #pragma unroll
     for (int q = 0; q < 2; ++q)
         soff_x[q] = (uint32_t)(k0 + 64 * wn + 32 * q + r);
+    const WgCtx cx{lds, rdy, rx, wm, wn, r, h};
 
-    u32x4 dq[4], xq[4];                           // staged slices (aligned 16 bytes)
-    uint32_t de[4], xe[4];                        // and the dword after them
-    auto load_tiles = [&](uint32_t t) {
+    // The step's loads into buffer b.  The whole offset is in the per-lane part, so the
+    // range of the resource bounds every access.
+    auto issue = [&](uint32_t t, uint32_t b) {
+        typedef __attribute__((address_space(3))) uint8_t lds_u8;
+        lds_u8* const st = (lds_u8*)(lds + b * kWStage);
         const uint32_t step = t * kWS;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t ad = (o_dy[i] + step) & ~3u, ax = (o_x[i] + step) & ~3u;
-            dq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdy, (int)ad, 0, 0));
-            de[i] = __builtin_amdgcn_raw_buffer_load_b32(rdy, (int)(ad + 16), 0, 0);
-            xq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)ax, 0, 0));
-            xe[i] = __builtin_amdgcn_raw_buffer_load_b32(rx, (int)(ax + 16), 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rdy, st + (32 * wave + 8 * i) * kWS, 16, ld_dy[i] + step, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, st + (kWT + 32 * wave + 8 * i) * kWS, 16, ld_x[i] + step, 0,
+                                                     0, 0);
         }
     };
-    // realign the staged slices of step t, mask tokens >= M_g, write LDS buffer `buf`
-    auto store_tiles = [&](uint32_t buf, uint32_t t) {
-        const int valid = (int)Mg - (int)(t * kWS) - 16 * (int)lchunk;   // tokens in the slice
-        uint32_t mask[4];
+    // A 16-byte slice that runs past the end of a resource's range reads as zero as a
+    // whole, its bytes inside the range too.  Only the last step's slices can reach past
+    // an expert's data (every earlier step ends inside its row), and past the range only
+    // in tiles that reach the end of the operand buffers (an expert that ends at the
+    // capacity).  In those tiles a lane re-reads each fragment chunk of the last step
+    // whose slice crossed the end as aligned dwords (each checked on its own; the range
+    // is a multiple of 4) and shifts it into place, before the mask.
+    const uint32_t rng_dy = (uint32_t)min((uint64_t)N * (uint64_t)(M_cap - m0), (uint64_t)0xFFFFFFFFu);
+    const uint32_t rng_x = (uint32_t)min((uint64_t)K * (uint64_t)(M_cap - m0), (uint64_t)0xFFFFFFFFu);
+    const bool tail_tile = (uint64_t)(n0 + kWT) * Mg + (uint64_t)T * kWS > rng_dy ||
+                           (uint64_t)(k0 + kWT) * Mg + (uint64_t)T * kWS > rng_x;
+    auto refetch = [&](__amdgpu_buffer_rsrc_t rs, uint32_t rng, uint32_t row, uint32_t lc, wg_i32x8& fr, int half) {
+        const uint32_t o = row * Mg + (T - 1) * kWS + 16 * lc;
+        if (o < rng && o + 16 > rng) {
+            const uint32_t a0 = o & ~3u, sh = o & 3u;
+            uint32_t wv[5];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int v = min(max(valid - 4 * j, 0), 4);
-            mask[j] = v >= 4 ? 0xFFFFFFFFu : ((1u << (8 * v)) - 1u);
-        }
-        uint8_t* const s_dy = lds + buf * kWStage;           // dY^T rows: bytes [0, 32 KB)
-        uint8_t* const s_x = s_dy + kWT * kWS;                // X^T rows: bytes [32 KB, 64 KB)
+            for (int j = 0; j < 5; ++j)
+                wv[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(a0 + 4 * j), 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t sd = o_dy[i] & 3, sx_ = o_x[i] & 3;          // step * 128 keeps the byte offset mod 4
-            const u32x4 q = dq[i], p = xq[i];
-            const u32x4 vd = {__builtin_amdgcn_alignbyte(q.y, q.x, sd) & mask[0],
-                              __builtin_amdgcn_alignbyte(q.z, q.y, sd) & mask[1],
-                              __builtin_amdgcn_alignbyte(q.w, q.z, sd) & mask[2],
-                              __builtin_amdgcn_alignbyte(de[i], q.w, sd) & mask[3]};
-            const u32x4 vx = {__builtin_amdgcn_alignbyte(p.y, p.x, sx_) & mask[0],
-                              __builtin_amdgcn_alignbyte(p.z, p.y, sx_) & mask[1],
-                              __builtin_amdgcn_alignbyte(p.w, p.z, sx_) & mask[2],
-                              __builtin_amdgcn_alignbyte(xe[i], p.w, sx_) & mask[3]};
-            *reinterpret_cast<u32x4*>(s_dy + lds_w + 64 * i * kWS) = vd;
-            *reinterpret_cast<u32x4*>(s_x + lds_w + 64 * i * kWS) = vx;
+            for (int j = 0; j < 4; ++j)
+                fr[4 * half + j] = (int)__builtin_amdgcn_alignbyte(wv[j + 1], wv[j], sh);
         }
     };
-    uint32_t sc_x[2], sc_dy[4];                   // current step's scale bytes
-    uint32_t nx_x[2], nx_dy[4];
+    auto refetch_step = [&](WgFrag& fr, int j) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint32_t lc = 4 * j + 2 * half + h;                     // the chunk's tokens / 16
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                refetch(rx, rng_x, (uint32_t)(k0 + 64 * wn + 32 * q) + r, lc, fr.x[q], half);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                refetch(rdy, rng_dy, (uint32_t)(n0 + 128 * wm + 32 * q) + r, lc, fr.d[q], half);
+        }
+    };
     auto load_scales = [&](uint32_t t, uint32_t (&dx)[2], uint32_t (&ddy)[4]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -197,63 +301,65 @@ __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
             acc[mt][nt] = wg_f32x16{};
 
     if (T > 0) {                                  // uniform: an empty expert writes zeros
-        load_tiles(0);
+        uint32_t sc_x[2], sc_dy[4];               // scale bytes of the step in flight
         load_scales(0, sc_x, sc_dy);
-        store_tiles(0, 0);
+        issue(0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        for (uint32_t t = 0; t < T; ++t) {
-            // the next step (the last one again on the last step: in range, unused)
-            const uint32_t tn = min(t + 1, T - 1);
-            load_tiles(tn);
-            load_scales(tn, nx_x, nx_dy);
-            const uint8_t* const tdy = lds + (t & 1) * kWStage + (128 * wm) * kWS;
-            const uint8_t* const tx = lds + (t & 1) * kWStage + kWT * kWS + (64 * wn) * kWS;
-            __builtin_amdgcn_s_setprio(1);        // as in the forward GEMM: matrix work first
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                const uint32_t c0 = 16 * ((4 * kh + h) ^ sw8), c1 = 16 * ((4 * kh + 2 + h) ^ sw8);
-                wg_i32x8 fx[2], fdy[4];
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const uint8_t* const rowp_x = tx + (32 * q + r) * kWS;
-                    const u32x4 x0 = *reinterpret_cast<const u32x4*>(rowp_x + c0);
-                    const u32x4 x1 = *reinterpret_cast<const u32x4*>(rowp_x + c1);
-                    fx[q] = wg_i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint8_t* const rowp_d = tdy + (32 * q + r) * kWS;
-                    const u32x4 d0 = *reinterpret_cast<const u32x4*>(rowp_d + c0);
-                    const u32x4 d1 = *reinterpret_cast<const u32x4*>(rowp_d + c1);
-                    fdy[q] = wg_i32x8{(int)d0.x, (int)d0.y, (int)d0.z, (int)d0.w,
-                                      (int)d1.x, (int)d1.y, (int)d1.z, (int)d1.w};
-                }
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-                        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fx[nt], fdy[mt], acc[mt][nt], 0, 0, 0, (int)sc_x[nt], 0, (int)sc_dy[mt]);
-            }
-            __builtin_amdgcn_s_setprio(0);
-            // the other buffer was last read in step t - 1, before the previous barrier
-            store_tiles((t + 1) & 1, tn);
+        issue(T > 1 ? 1 : 0, 1);                  // (with one step: in range, unused)
+        WgFrag f;
+        wg_read(cx, 0, 0, f);
+        // Per step t in buffer u = t % 2, software-pipelined by MFMA K-step as in the
+        // forward GEMM: the second K-step's fragments are read while the first K-step's
+        // MFMAs issue; the barrier (every lane's loads of step t + 1 have landed, every
+        // wave has read all of buffer u) sits before the second K-step's MFMAs, which
+        // issue while step t + 1's first fragments are read.  Step t + 2 goes into buffer
+        // u (on the second-to-last step that is the last step again: in range, unused).
+        for (uint32_t t = 0; t + 1 < T; ++t) {
+            const uint32_t u = t & 1;
+            uint32_t nx_x[2], nx_dy[4];
+            load_scales(t + 1, nx_x, nx_dy);
+            WgFrag g;
+            wg_step<true>(cx, f, sc_x, sc_dy, acc, u, 1, g);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            issue(min(t + 2, T - 1), u);
+            wg_step<true>(cx, g, sc_x, sc_dy, acc, u ^ 1, 0, f);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 sc_dy[q] = nx_dy[q];
 #pragma unroll
             for (int q = 0; q < 2; ++q)
                 sc_x[q] = nx_x[q];
-            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the last step: its bytes past token M_g belong to the next row (or lie past
+        // the capacity, where they read as zero); both operands are masked to zero there
+        // in registers, so the partial block adds nothing
+        {
+            WgFrag g;
+            wg_read(cx, (T - 1) & 1, 1, g);
+            if (tail_tile) {
+                refetch_step(f, 0);
+                refetch_step(g, 1);
+            }
+            const int valid = (int)Mg - (int)(kWS * (T - 1));                  // 1 .. 128
+            wg_mask(f, valid, 0, h);
+            wg_mask(g, valid, 1, h);
+            wg_step<false>(cx, f, sc_x, sc_dy, acc, 0, 0, g);
+            wg_step<false>(cx, g, sc_x, sc_dy, acc, 0, 0, f);
         }
     }
 
-    // epilogue: lane (r, h) of MFMA tile (mt, nt) holds n = 128 wm + 32 mt + r and
-    // k = 64 wn + 32 nt + 8 q + 4 h + (0..3) in values 4q .. 4q + 3
+    // epilogue through LDS, as in the forward GEMM: lane (r, h) of MFMA tile (mt, nt)
+    // holds n = 128 wm + 32 mt + r and k = 64 wn + 32 nt + 8 q + 4 h + (0..3) in values
+    // 4q .. 4q + 3.  The waves write their BF16 results into the LDS buffers (tile row x,
+    // 512 bytes, at x * 512, the 16-byte chunk c of the row at chunk c ^ (x % 32)), then
+    // every lane stores 16-byte pieces of whole rows.
+    __builtin_amdgcn_s_waitcnt(0);                // the last (unused) loads have landed too
+    __syncthreads();                              // every wave is done with the last step
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        uint16_t* const yrow = dw + ((int64_t)g * N + n0 + 128 * wm + 32 * mt + r) * K + k0 + 64 * wn + 4 * h;
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -261,9 +367,20 @@ __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
                 const wg_f32x16& v = acc[mt][nt];
                 const wg_bf16x2 p0 = {(__bf16)v[4 * q + 0], (__bf16)v[4 * q + 1]};
                 const wg_bf16x2 p1 = {(__bf16)v[4 * q + 2], (__bf16)v[4 * q + 3]};
-                *reinterpret_cast<u32x2*>(yrow + 32 * nt + 8 * q) =
+                const uint32_t c = 8 * (uint32_t)wn + 4 * nt + q;
+                *reinterpret_cast<u32x2*>(lds + (128 * wm + 32 * mt + r) * 512 + 16 * (c ^ r) + 8 * h) =
                     u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
             }
+    __syncthreads();
+    {
+        const uint32_t c = (uint32_t)tid & 31;
+        uint16_t* const tile = dw + ((int64_t)g * N + n0) * K + k0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t row = ((uint32_t)tid >> 5) + 16 * i;          // tile row 0 .. 255
+            *reinterpret_cast<u32x4*>(tile + (int64_t)row * K + 8 * c) =
+                *reinterpret_cast<const u32x4*>(lds + row * 512 + 16 * (c ^ (row & 31)));
+        }
     }
 }
 

@@ -116,6 +116,10 @@ CASES = [
     ([128, 256], 512, 256, 3),                  # whole blocks
     ([1000], 256, 256, 0),
     ([7, 0, 290, 64, 2], 256, 256, 130),
+    # a multi-step expert ending at the capacity: slices of its last step reach past the
+    # end of the operand buffers, whose bytes inside them must still count
+    ([200, 333], 512, 256, 0),
+    ([13, 0, 1021], 256, 512, 0),
 ]
 
 
