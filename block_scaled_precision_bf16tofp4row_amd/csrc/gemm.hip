@@ -126,6 +126,22 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offs, int 
 // the group's token tiles innermost, so the workgroups one XCD holds at a time share a
 // few operand tiles of each kind in its L2.
 constexpr uint32_t kGroupM = 4;
+
+// Workgroup -> position in that order for the fast kernel.  Workgroups are dealt
+// round-robin over the 8 XCDs; XCD x takes tile groups x, x + 8, x + 16, ... (a group is
+// kGroupM token tiles across all feature tiles), so that an XCD's workgroups share a
+// group's operand tiles in its L2 while the eight XCDs work on neighbouring groups, that
+// is on the same expert's weights at the same time.  The remainder past the last whole
+// round of 8 groups keeps its order.
+__device__ __forceinline__ uint32_t group_interleave(uint32_t bid, uint32_t nblocks, uint32_t gsz)
+{
+    const uint32_t round = 8 * gsz;
+    const uint32_t full = nblocks / round * round;
+    if (bid >= full)
+        return bid;
+    const uint32_t x = bid & 7, slot = bid >> 3;
+    return (x + 8 * (slot / gsz)) * gsz + slot % gsz;
+}
 __device__ __forceinline__ void tile_of(uint32_t lin, uint32_t nblocks, uint32_t ntn, uint32_t& mtile,
                                         uint32_t& ntile)
 {
@@ -416,7 +432,8 @@ __global__ __launch_bounds__(kFastThreads, 1) void fp8_gemm_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint32_t mtile, ntile;
-    tile_of(xcd_remap(blockIdx.x, gridDim.x), gridDim.x, (uint32_t)(N / kTN), mtile, ntile);
+    const uint32_t ntn = (uint32_t)(N / kTN);
+    tile_of(group_interleave(blockIdx.x, gridDim.x, kGroupM * ntn), gridDim.x, ntn, mtile, ntile);
     int g;
     int64_t row0;
     int rows;
