@@ -561,7 +561,8 @@ __global__ __launch_bounds__(kFastThreads, 1) void fp8_gemm_kernel(
             const uint32_t row = ((uint32_t)tid >> 5) + 16 * i;          // tile row 0 .. 255
             const uint8_t* const src = (i < 8 ? lds0 : lds1) + (row & 127) * 512 + 16 * (c ^ (row & 31));
             __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src), ry,
-                                                   (int)((row * (uint32_t)N + (uint32_t)n0) * 2 + 16 * c), 0, 0);
+                                                   (int)((row * (uint32_t)N + (uint32_t)n0) * 2 + 16 * c), 0,
+                                                   2);            // non-temporal: written once
         }
     }
 }

@@ -378,8 +378,8 @@ __global__ __launch_bounds__(kWgThreads, 1) void fp8_wgrad_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const uint32_t row = ((uint32_t)tid >> 5) + 16 * i;          // tile row 0 .. 255
-            *reinterpret_cast<u32x4*>(tile + (int64_t)row * K + 8 * c) =
-                *reinterpret_cast<const u32x4*>(lds + row * 512 + 16 * (c ^ (row & 31)));
+            store_stream(reinterpret_cast<u32x4*>(tile + (int64_t)row * K + 8 * c),
+                         *reinterpret_cast<const u32x4*>(lds + row * 512 + 16 * (c ^ (row & 31))));
         }
     }
 }
