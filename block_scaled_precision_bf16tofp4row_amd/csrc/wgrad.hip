@@ -46,7 +46,7 @@ constexpr int kWgThreads = 512;                   // 8 waves, two per SIMD
 constexpr int kWT = 256;                          // n and k per workgroup tile
 constexpr int kWS = 128;                          // tokens per step (one scale block)
 constexpr int kWStage = 2 * kWT * kWS;            // bytes of one LDS buffer (64 KB)
-constexpr uint32_t kWGroupN = 4;                  // n tiles swept together (L2 reuse)
+constexpr uint32_t kWGroupN = 2;                  // n tiles swept together (L2 reuse)
 
 // 128-token blocks of the experts before g, summed over one wave (uniform result).
 __device__ __forceinline__ uint32_t wg_blocks_before(const int32_t* __restrict__ offs, int g)
