@@ -252,6 +252,7 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
     stream = torch.cuda.current_stream()
     scrub = torch.ones(scrub_bytes // 4, dtype=torch.int32, device=dev)
     copy = DeviceCopy(torch, dev)
+    traffic = ColsTraffic()
     kev = KernelEvents(reps)
 
     def median_us(fn, is_copy=False):
@@ -291,6 +292,8 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
         for _, _, fn, _ in launches:      # valid codes for the conversions
             fn()
         torch.cuda.synchronize()
+        fwd = {d["seg"].name: d for d in segs}
+        bwd = {d["seg"].name: d for d in bsegs}
         rows = []
         for kern, segname, fn, nbytes in launches:
             us, us_m = median_us(fn)
@@ -301,14 +304,27 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
             del src, dst
             gbs = nbytes / (us * 1e-6) / 1e9
             copy_gbs = 2 * half / (cus * 1e-6) / 1e9
-            rows.append({"kernel": kern, "segment": segname, "alg_bytes": nbytes,
-                         "median_us": round(us, 2), "GBps": round(gbs, 1),
-                         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                         "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4),
-                         "median_us_markers": round(us_m, 2),
-                         "frac_of_peak_markers": round(nbytes / (us_m * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+            row = {"kernel": kern, "segment": segname, "alg_bytes": nbytes,
+                   "median_us": round(us, 2), "GBps": round(gbs, 1),
+                   "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                   "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4),
+                   "median_us_markers": round(us_m, 2),
+                   "frac_of_peak_markers": round(nbytes / (us_m * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            note = ""
+            if kern in ("cols", "fp8q_cols"):
+                d = fwd[segname] if kern == "cols" else bwd[segname]
+                ceil_us, seq_us = cols_traffic_us(torch, dev, traffic, median_us, d, kern)
+                row.update({"pattern_ceiling_us": round(ceil_us, 2),
+                            "pattern_ceiling_frac_of_peak": round(nbytes / (ceil_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "frac_of_pattern_ceiling": round(ceil_us / us, 4),
+                            "sequential_writes_us": round(seq_us, 2),
+                            "sequential_writes_frac_of_peak": round(nbytes / (seq_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+                note = (f"; memory-only traffic {ceil_us:.1f} us ({row['pattern_ceiling_frac_of_peak']:.1%} of peak, "
+                        f"kernel at {ceil_us / us:.1%} of it), same reads with sequential writes {seq_us:.1f} us "
+                        f"({row['sequential_writes_frac_of_peak']:.1%})")
+            rows.append(row)
             log(f"[bench] scrubbed {w.name} {kern}/{segname}: {us:.1f} us ({us_m:.1f} with markers), "
-                f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of peak, {gbs / copy_gbs:.1%} of a same-size copy)")
+                f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of peak, {gbs / copy_gbs:.1%} of a same-size copy){note}")
         out[w.name] = rows
         del segs, launches, bsegs, blaunches
         torch.cuda.empty_cache()
@@ -317,12 +333,77 @@ def scrubbed_medians(mx, torch, dev, config_ids, reps=20, warmup=5, scrub_bytes=
     torch.cuda.empty_cache()
     out["copy_kernel"] = {"what": "bench_copy16: 16-byte nontemporal loads then stores, one-shot grid",
                           "unroll": copy.unroll, "unroll_GBps_1GiB": copy.sweep}
+    out["pattern_ceiling"] = {"what": "bench_cols_traffic: the column kernel's loads and whole-line stores of each "
+                                      "(256-column tile, 128-row strip) on the launch's own ragged layout, one "
+                                      "workgroup per pair, tile by tile over consecutive strips, no conversion, LDS or "
+                                      "synchronisation (a memory-only ceiling for this traffic)",
+                              "sequential_writes": "the same loads, each workgroup's stores to one contiguous 32 KB "
+                                                   "block instead of the transposed columns"}
     out["timing"] = {"median_us": "HIP events bound to the kernels' own start and end (hipExtLaunchKernel "
                                   "through mxfp4_time_next_launch; the copy's own event arguments)",
                      "median_us_markers": "HIP event records before and after the launch on its stream",
                      "one_workgroup_launch_us": round(tiny_k, 2),
                      "one_workgroup_launch_us_markers": round(tiny_m, 2)}
     return out
+
+
+def strip_table(offs, K: int):
+    """int64 [strips, 4] of a ragged segment, in expert order: first row, rows, output byte
+    of (column 0, the strip's first row) in the transposed layout, the expert's rows."""
+    rows = []
+    offs = np.asarray(offs, dtype=np.int64)
+    for g in range(len(offs) - 1):
+        r0, mg = int(offs[g]), int(offs[g + 1] - offs[g])
+        for b in range((mg + 127) // 128):
+            rows.append((r0 + 128 * b, min(128, mg - 128 * b), K * r0 + 128 * b, mg))
+    return np.array(rows, dtype=np.int64).reshape(-1, 4)
+
+
+class ColsTraffic:
+    """bench_cols_traffic of libmxfp4bench: the memory-only traffic of a column kernel."""
+
+    def __init__(self):
+        import ctypes
+        self.lib = DeviceCopy.load()
+        P, I64 = ctypes.c_void_p, ctypes.c_int64
+        self.lib.bench_cols_traffic.argtypes = [P, I64, ctypes.c_int, P, I64, P, I64, P, P, I64, I64,
+                                                ctypes.c_int, P, P, P]
+        self.lib.bench_cols_traffic.restype = ctypes.c_int
+
+    def __call__(self, torch, inp, tile_in_bytes, sc, out, out_scales, strips, K, sequential, events=None):
+        start, stop = events if events else (None, None)
+        n = strips.shape[0]
+        st = self.lib.bench_cols_traffic(
+            inp.data_ptr(), inp.shape[1] * inp.element_size(), tile_in_bytes,
+            sc.data_ptr() if sc is not None else None, sc.shape[1] if sc is not None else 0,
+            out.data_ptr(), out.numel() * out.element_size(), out_scales.data_ptr(), strips.data_ptr(), n, K,
+            1 if sequential else 0, torch.cuda.current_stream().cuda_stream, start, stop)
+        if st != 0:
+            raise RuntimeError(f"bench_cols_traffic failed: {st}")
+
+
+def cols_traffic_us(torch, dev, traffic, median_us, d, kern):
+    """Scrubbed medians (us) of the memory-only traffic of a column launch over segment
+    buffers d: in the transposed layout, and with sequential writes."""
+    seg = d["seg"]
+    K = seg.K
+    strips = torch.from_numpy(strip_table(seg.offs, K)).to(dev)
+    n = strips.shape[0]
+    if n == 0:
+        return float("nan"), float("nan")
+    if kern == "cols":
+        inp, tib, sc = d["codes"], 128, d["scales"]
+    else:
+        inp, tib, sc = d["x"], 512, None
+    out_scales = torch.empty(n * K, dtype=torch.uint8, device=dev)
+    ceil_us, _ = median_us(lambda events=None: traffic(torch, inp, tib, sc, d["yT"], out_scales, strips, K, False,
+                                                       events), is_copy=True)
+    nkt = (K + 255) // 256
+    seq_out = torch.empty(nkt * n * 256 * 128, dtype=torch.uint8, device=dev)
+    seq_us, _ = median_us(lambda events=None: traffic(torch, inp, tib, sc, seq_out, out_scales, strips, K, True,
+                                                      events), is_copy=True)
+    del seq_out, out_scales, strips
+    return ceil_us, seq_us
 
 
 class KernelEvents:

@@ -4,8 +4,9 @@
 
 Compiles every ``csrc/*.hip`` to an object (in parallel) and links them into
 ``block_scaled_precision_bf16tofp4row_amd/libmxfp4cvt.so``; then builds the
-benchmark's copy kernel (``csrc/bench/copy16.hip``) into ``libmxfp4bench.so``, a
-separate library the product never loads.
+benchmark's measurement kernels (``csrc/bench/*.hip``: the streaming copy and the
+memory-only column traffic) into ``libmxfp4bench.so``, a separate library the product
+never loads.
 """
 from __future__ import annotations
 
@@ -20,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmxfp4cvt.so")
-BENCH_SRC = os.path.join(CSRC, "bench", "copy16.hip")
+BENCH_SRCS = sorted(glob.glob(os.path.join(CSRC, "bench", "*.hip")))
 BENCH_LIB = os.path.join(PKG, "libmxfp4bench.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -42,8 +43,8 @@ def build(verbose: bool = False) -> str:
     procs = []
     objs = []
     bench_tmp = BENCH_LIB + ".tmp"
-    bench_cmd = [HIPCC, *CFLAGS, "-shared", BENCH_SRC, "-o", bench_tmp]
-    procs.append((BENCH_SRC, subprocess.Popen(bench_cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    bench_cmd = [HIPCC, *CFLAGS, "-shared", *BENCH_SRCS, "-o", bench_tmp]
+    procs.append(("csrc/bench", subprocess.Popen(bench_cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     for src in sources():
         obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
