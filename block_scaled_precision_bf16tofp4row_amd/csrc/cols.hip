@@ -151,26 +151,14 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
     // the last tile is 128 columns wide when K is an odd multiple of 128
     const int ncols = (int)min<int64_t>(kTileCols, K - (int64_t)kTileCols * kt);
 
-    // strips of all experts; this workgroup takes strips [s0, s1) of column tile kt
+    // this workgroup's strips of column tile kt (strip_run, strips.h): a contiguous range,
+    // with a lead-in strip where it starts inside an expert, or every parts-th strip of
+    // a segment whose strips are independent
     const ExpertTable t0 = expert_chunk(offs, G, 0, 0);
-    uint32_t n_strips = t0.total;
-    for (int g0 = 64; g0 < G; g0 += 64)
-        n_strips = uniform(n_strips + expert_chunk(offs, G, g0, n_strips).total);
-    const uint32_t s0 = (uint32_t)(((uint64_t)n_strips * part) / (uint32_t)parts);
-    const uint32_t s1 = (uint32_t)(((uint64_t)n_strips * (part + 1)) / (uint32_t)parts);
-    if (s0 >= s1)
+    StripRun run;
+    if (!strip_run(offs, G, t0, part, (uint32_t)parts, run))
         return;                                   // uniform over the workgroup
-    // A range that starts inside an expert also converts the strip before it (a lead-in
-    // strip that writes nothing): its bytes past its last line boundary complete the
-    // first output line of the range, so the workgroup writes that line whole and the
-    // workgroup before it stops at its last line boundary.  Lines split between two
-    // workgroups would otherwise be written partially twice.  An expert whose row count
-    // is a multiple of 128 needs none: every strip of it starts and ends on a line
-    // boundary of every column (K, the strip starts and the column length M_g are then
-    // all multiples of 128), so nothing is carried.
-    const StripInfo first = locate(offs, G, t0, s0);
-    const uint32_t lead = first.s > first.sb && (first.mg & (kStripRows - 1)) != 0 ? 1u : 0u;
-    const uint32_t n = s1 - s0 + lead;            // strips this workgroup converts
+    const uint32_t n = run.n;                     // strips this workgroup converts
 
     if (tid < 2 * (kMaxGap + 1))
         lut[tid] = kColsGapLut.w[tid >> 1][tid & 1];
@@ -282,7 +270,10 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                     *reinterpret_cast<uint32_t*>(w + kRing + kColBytes * j) = T[j];
             }
         };
-        auto flags_of = [](uint32_t prev_sb, const StripInfo& cur, bool lead_in) {
+        // a dealt strip neither continues the ring's previous strip nor carries into the next
+        auto flags_of = [&](uint32_t prev_sb, const StripInfo& cur, bool lead_in) {
+            if (run.dealt)
+                return 0u;
             return (prev_sb == cur.sb ? 1u : 0u) | (cur.s + 1 < cur.sb + cur.ns ? 2u : 0u) | (lead_in ? 4u : 0u);
         };
 
@@ -299,12 +290,10 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
         StripInfo I[kSets];
         Codes C[kSets];
         Scales Sc[kSets];
-        I[0] = first;
-        I[0].s -= lead;
-        set_rows(I[0]);
+        I[0] = run.first;
 #pragma unroll
         for (int u = 1; u < kPrefetch; ++u)
-            I[u] = (uint32_t)u < n ? next_strip(offs, G, I[u - 1]) : I[u - 1];
+            I[u] = (uint32_t)u < n ? next_strip(offs, G, I[u - 1], run.step) : I[u - 1];
 #pragma unroll
         for (int u = 0; u < kPrefetch; ++u) {
             Sc[u] = load_scales(scales, K, I[u], kt, soff);
@@ -319,7 +308,7 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                 const uint32_t tt = t + u;
                 const int ld = (u + kPrefetch) % kSets;          // set receiving strip tt + kPrefetch
                 const int pv = (u + kPrefetch - 1) % kSets;      // set of strip tt + kPrefetch - 1
-                I[ld] = tt + kPrefetch < n ? next_strip(offs, G, I[pv]) : I[pv];
+                I[ld] = tt + kPrefetch < n ? next_strip(offs, G, I[pv], run.step) : I[pv];
                 Sc[ld] = load_scales(scales, K, I[ld], kt, soff);
                 C[ld] = load_codes(codes, K, I[ld], kt, coff);
                 const int nx = (u + 1) % kSets;                  // set of strip tt + 1
@@ -328,7 +317,7 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
                     return;
                 if (!wait_at_least(&published, kProducerWaves * (tt + 1), wc))
                     return;
-                produce(I[u], C[u], sc, tt % kSlots, flags_of(prev_sb, I[u], tt == 0 && lead != 0));
+                produce(I[u], C[u], sc, tt % kSlots, flags_of(prev_sb, I[u], tt == 0 && run.lead));
                 prev_sb = I[u].sb;
                 signal(&produced);
                 if (tt + 1 >= n)

@@ -151,20 +151,14 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     const uint32_t part = lambda / nkt;
     const int ncols = (int)min<int64_t>(kTileCols, K - (int64_t)kTileCols * kt);
 
+    // this workgroup's strips of column tile kt (strip_run, strips.h): a contiguous range,
+    // with a lead-in strip where it starts inside an expert, or every parts-th strip of
+    // a segment whose strips are independent
     const ExpertTable t0 = expert_chunk(offs, G, 0, 0);
-    uint32_t n_strips = t0.total;
-    for (int g0 = 64; g0 < G; g0 += 64)
-        n_strips = uniform(n_strips + expert_chunk(offs, G, g0, n_strips).total);
-    const uint32_t s0 = (uint32_t)(((uint64_t)n_strips * part) / (uint32_t)parts);
-    const uint32_t s1 = (uint32_t)(((uint64_t)n_strips * (part + 1)) / (uint32_t)parts);
-    if (s0 >= s1)
+    StripRun run;
+    if (!strip_run(offs, G, t0, part, (uint32_t)parts, run))
         return;                                   // uniform over the workgroup
-    // a range that starts inside an expert also quantizes the strip before it (a
-    // lead-in strip that writes nothing), so its first output line is written whole; an
-    // expert whose row count is a multiple of 128 carries nothing and needs none
-    const StripInfo first = locate(offs, G, t0, s0);
-    const uint32_t lead = first.s > first.sb && (first.mg & (kStripRows - 1)) != 0 ? 1u : 0u;
-    const uint32_t n = s1 - s0 + lead;
+    const uint32_t n = run.n;
 
     if (tid == 0) {
         for (int k = 0; k < kQProducerWaves; ++k) {
@@ -324,7 +318,10 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                     *reinterpret_cast<u32x2*>(w + kRing + kColBytes * j) = T[j];
             }
         };
-        auto flags_of = [](uint32_t prev_sb, const StripInfo& cur, bool lead_in) {
+        // a dealt strip neither continues the ring's previous strip nor carries into the next
+        auto flags_of = [&](uint32_t prev_sb, const StripInfo& cur, bool lead_in) {
+            if (run.dealt)
+                return 0u;
             return (prev_sb == cur.sb ? 1u : 0u) | (cur.s + 1 < cur.sb + cur.ns ? 2u : 0u) | (lead_in ? 4u : 0u);
         };
 
@@ -337,12 +334,10 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
         uint32_t prev_sb = 0xFFFFFFFFu;
         StripInfo I[kSets];
         QRows R[kSets];
-        I[0] = first;
-        I[0].s -= lead;
-        set_rows(I[0]);
+        I[0] = run.first;
 #pragma unroll
         for (int u = 1; u < kQPrefetch; ++u)
-            I[u] = (uint32_t)u < n ? next_strip(offs, G, I[u - 1]) : I[u - 1];
+            I[u] = (uint32_t)u < n ? next_strip(offs, G, I[u - 1], run.step) : I[u - 1];
 #pragma unroll
         for (int u = 0; u < kQPrefetch; ++u)
             R[u] = load_rows(x, K, I[u], kt, off);
@@ -352,7 +347,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                 const uint32_t tt = t + u;
                 const int ld = (u + kQPrefetch) % kSets;          // set receiving strip tt + kQPrefetch
                 const int pv = (u + kQPrefetch - 1) % kSets;      // set of strip tt + kQPrefetch - 1
-                I[ld] = tt + kQPrefetch < n ? next_strip(offs, G, I[pv]) : I[pv];
+                I[ld] = tt + kQPrefetch < n ? next_strip(offs, G, I[pv], run.step) : I[pv];
                 if constexpr (kRows) {
                     // not enough registers to keep the eight row offsets across the loop:
                     // recompute them from an opaque lane index (see produce_rows)
@@ -369,7 +364,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                 if (tt >= 3 && !wait_at_least(&drained[(tt - 3) % kSlots],
                                               kQConsumerWaves * ((tt - 3) / kSlots + 1), wc))
                     return;
-                const uint32_t fl = flags_of(prev_sb, I[u], tt == 0 && lead != 0);
+                const uint32_t fl = flags_of(prev_sb, I[u], tt == 0 && run.lead);
                 if constexpr (kRows) {
                     // slot tt % 4 of rowmax is rewritten only in strip tt + 4, which starts
                     // after the consumers drained strip tt + 1, so after every producer

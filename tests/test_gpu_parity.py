@@ -106,6 +106,37 @@ def test_cols_aligned_experts_without_lead_in():
     check_fp8q_both(seg.x_bits, seg.offs)
 
 
+@pytest.mark.parametrize("counts,K", [
+    ([4096, 0, 8192, 4096, 0], 7168),              # 28 tiles x 9 parts: strips dealt 9 apart
+    ([4096, 0, 8192, 4096, 0], 2048),
+    ([0, 12288, 4096], 384),                       # last tile 128 wide; one strip per part
+])
+def test_cols_dealt_strips(counts, K):
+    """Every expert's row count a multiple of 4096: the column kernels deal a tile's strips
+    to its workgroups in turn (part, part + parts, ...) instead of contiguous ranges, each
+    strip written alone (empty experts, capacity slack past offs[G], a narrow last tile);
+    the backward column quantizer and its both-layouts mode take the same rule."""
+    from gpu_path import check_fp8q_both, check_fp8q_cols
+    say(f"dealt strips counts={counts} K={K}")
+    seg = workloads.ragged_case(counts, K, seed=K + len(counts), values="t3", M_cap=sum(counts) + 7)
+    check_chain(seg.x_bits, seg.offs, kernels=("quantize", "cols"))
+    check_fp8q_cols(seg.x_bits, seg.offs)
+    check_fp8q_both(seg.x_bits, seg.offs)
+
+
+def test_cols_dealt_strips_many_experts():
+    """G = 300, five experts of 4096 rows and the rest empty: dealt strips walk across
+    the 64-expert chunks of the expert scan, many steps at a time, and the workgroups
+    past the segment's 160 strips (256 parts of the one tile) get none."""
+    from gpu_path import check_fp8q_cols
+    counts = np.zeros(300, np.int64)
+    counts[[3, 70, 71, 200, 299]] = 4096
+    say("dealt strips G=300")
+    seg = workloads.ragged_case(counts, 256, seed=5, values="normal", M_cap=int(counts.sum()))
+    check_chain(seg.x_bits, seg.offs, kernels=("quantize", "cols"))
+    check_fp8q_cols(seg.x_bits, seg.offs)
+
+
 def test_config1_full_chain():
     w = workloads.config1(0)
     seg = w.segments[0]
