@@ -58,8 +58,6 @@
 
 namespace mxfp4 {
 
-__constant__ GapLut kColsGapLut = make_gap_lut();
-
 constexpr int kProducerWaves = 4;
 constexpr int kConsumerWaves = 12;
 // a strip is 32 store instructions (256 columns x 128 bytes); consumer wave v issues
@@ -160,8 +158,46 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
         return;                                   // uniform over the workgroup
     const uint32_t n = run.n;                     // strips this workgroup converts
 
+    // Producer lanes (waves 0 .. kProducerWaves - 1): wave w converts rows 32w..32w+31 of
+    // each strip; lane (rq, c) holds group c (tile columns 32c..32c+31) of rows
+    // 32w + 4rq .. + 3.  Their first kPrefetch strips' loads go out before the barrier,
+    // so they travel while the table and counters are set.
+    const int c = lane & 7;
+    const int rq = lane >> 3;
+    const int row_q = 32 * wave + 4 * rq;         // first of the lane's four rows
+    // the narrow last tile has groups 0..3: lanes of groups 4..7 repeat group c - 4
+    // (their columns are never written out)
+    const uint32_t cl = 32 * c < ncols ? (uint32_t)c : (uint32_t)(c & 3);
+    const uint32_t cbyte = 16 * cl;
+    const uint32_t sshift = 8 * (cl & 3);
+    // byte offsets within a strip of the lane's four code chunks and of its scale dword
+    uint32_t coff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        coff[i] = (uint32_t)(row_q + i) * (uint32_t)(K / 2) + cbyte;
+    const uint32_t soff = (uint32_t)(32 * wave + (lane >> 1)) * (uint32_t)(K / 32) +
+                          4 * (ncols <= 128 ? 0u : (uint32_t)(lane & 1));
+    // Loads run kPrefetch strips ahead of the conversion (repeats of the last strip past
+    // the range, so the load sequence never varies); register sets rotate over
+    // kPrefetch + 1 strips.
+    constexpr int kSets = kPrefetch + 1;
+    StripInfo I[kSets];
+    Codes C[kSets];
+    Scales Sc[kSets];
+    if (wave < kProducerWaves) {
+        I[0] = run.first;
+#pragma unroll
+        for (int u = 1; u < kPrefetch; ++u)
+            I[u] = (uint32_t)u < n ? next_strip(offs, G, I[u - 1], run.step) : I[u - 1];
+#pragma unroll
+        for (int u = 0; u < kPrefetch; ++u) {
+            Sc[u] = load_scales(scales, K, I[u], kt, soff);
+            C[u] = load_codes(codes, K, I[u], kt, coff);
+        }
+    }
+
     if (tid < 2 * (kMaxGap + 1))
-        lut[tid] = kColsGapLut.w[tid >> 1][tid & 1];
+        lut[tid] = gap_lut_word(tid);
     if (tid == 0) {
         produced = 0;
         published = 0;
@@ -172,25 +208,8 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
 
     if (wave < kProducerWaves) {
         // ================= producers =================
-        // wave w converts rows 32w..32w+31 of each strip; lane (rq, c) holds group c
-        // (tile columns 32c..32c+31) of rows 32w + 4rq .. + 3
-        const int c = lane & 7;
-        const int rq = lane >> 3;
-        const int row_q = 32 * wave + 4 * rq;     // first of the lane's four rows
-        // the narrow last tile has groups 0..3: lanes of groups 4..7 repeat group c - 4
-        // (their columns are never written out)
-        const uint32_t cl = 32 * c < ncols ? (uint32_t)c : (uint32_t)(c & 3);
-        const uint32_t cbyte = 16 * cl;
-        const uint32_t sshift = 8 * (cl & 3);
         // column 32c + j of the tile sits at LDS byte lds_col(32c) + 544 j
         const uint32_t wbase = lds_col(32 * c) + row_q;
-        // byte offsets within a strip of the lane's four code chunks and of its scale dword
-        uint32_t coff[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            coff[i] = (uint32_t)(row_q + i) * (uint32_t)(K / 2) + cbyte;
-        const uint32_t soff = (uint32_t)(32 * wave + (lane >> 1)) * (uint32_t)(K / 32) +
-                              4 * (ncols <= 128 ? 0u : (uint32_t)(lane & 1));
 
         // the lane's four MX scale bytes (zero for rows past the strip: those read as zero)
         struct RowScales {
@@ -277,28 +296,13 @@ __global__ __launch_bounds__(kColsThreads, 1) void fp8_cols_kernel(
             return (prev_sb == cur.sb ? 1u : 0u) | (cur.s + 1 < cur.sb + cur.ns ? 2u : 0u) | (lead_in ? 4u : 0u);
         };
 
-        // Loads run kPrefetch strips ahead of the conversion (repeats of the last strip
-        // past the range, so the load sequence never varies): under a full store
-        // stream a load takes several strip-times to land.  Step t waits until the
-        // consumers have drained strip t - 3 (whose slot carries into strip t - 2, the
-        // last reader of slot t % 4) and until all producer waves have published their
-        // partial maxima of strip t, converts strip t, signals it, and publishes its own
-        // partial maxima of strip t + 1.  Register sets rotate over kPrefetch + 1 strips;
-        // the loop is unrolled by that much so each set keeps fixed registers.
-        constexpr int kSets = kPrefetch + 1;
+        // Under a full store stream a load takes several strip-times to land.  Step t
+        // waits until the consumers have drained strip t - 3 (whose slot carries into
+        // strip t - 2, the last reader of slot t % 4) and until all producer waves have
+        // published their partial maxima of strip t, converts strip t, signals it, and
+        // publishes its own partial maxima of strip t + 1.  The loop is unrolled by the
+        // number of register sets so each set keeps fixed registers.
         uint32_t prev_sb = 0xFFFFFFFFu;
-        StripInfo I[kSets];
-        Codes C[kSets];
-        Scales Sc[kSets];
-        I[0] = run.first;
-#pragma unroll
-        for (int u = 1; u < kPrefetch; ++u)
-            I[u] = (uint32_t)u < n ? next_strip(offs, G, I[u - 1], run.step) : I[u - 1];
-#pragma unroll
-        for (int u = 0; u < kPrefetch; ++u) {
-            Sc[u] = load_scales(scales, K, I[u], kt, soff);
-            C[u] = load_codes(codes, K, I[u], kt, coff);
-        }
         RowScales sc = row_scales(Sc[0]);   // strip t
         publish_max(sc, 0);
         signal(&published);

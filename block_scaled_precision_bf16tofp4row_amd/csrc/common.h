@@ -128,6 +128,20 @@ constexpr GapLut make_gap_lut()
     return t;
 }
 
+// Dword i (0 .. 2 kMaxGap + 1) of the gap table, w[i / 2][i % 2], from immediates: a
+// selection over the compile-time table, so staging the table in LDS needs no load from
+// memory (a table in constant memory is one more cold round trip before a workgroup's
+// first barrier).
+__device__ __forceinline__ uint32_t gap_lut_word(int i)
+{
+    constexpr GapLut t = make_gap_lut();
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 2 * (kMaxGap + 1); ++k)
+        w = i == k ? t.w[k >> 1][k & 1] : w;
+    return w;
+}
+
 // Eight codes (one dword of packed nibbles: byte b holds code 2b in its low nibble and
 // code 2b+1 in its high nibble) -> E4M3 bytes, as two dwords: even = codes 0, 2, 4, 6
 // and odd = codes 1, 3, 5, 7.  One v_perm_b32 looks up four magnitudes in the 8-byte

@@ -21,8 +21,6 @@
 
 namespace mxfp4 {
 
-__constant__ GapLut kRowsGapLut = make_gap_lut();
-
 template <int U>
 __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(
     const u32x2* __restrict__ codes, const uint32_t* __restrict__ scales4,
@@ -49,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void fp8_rows_kernel(
         sc[u] = ok ? scales4[idx >> 3] : 0u;
     }
     if (tid < 2 * (kMaxGap + 1))
-        lut[tid] = kRowsGapLut.w[tid >> 1][tid & 1];
+        lut[tid] = gap_lut_word(tid);
     __syncthreads();
     if (base >= nunits)
         return;                                        // uniform over the workgroup
