@@ -131,13 +131,17 @@ __device__ __forceinline__ void signal(uint32_t* ctr)
         __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// The 16 LDS bytes starting `o` (< 16) bytes past the 16-byte aligned address src: five
-// dwords read from the dword-aligned start, each output dword one v_alignbyte_b32 by o & 3
-// (a shift of zero returns the low dword).  No branch on o; the bytes read lie in
-// [src, src + 32).  (An unaligned ds_read_b128 gives the same bytes but measured about
+// The 16 LDS bytes starting `o` (< 16, the same in every lane) bytes past the 16-byte
+// aligned address src: five dwords read from the dword-aligned start, each output dword
+// one v_alignbyte_b32 by o & 3 (a shift of zero returns the low dword), with no branch on
+// o & 3; the bytes read lie in [src, src + 32).  (An unaligned ds_read_b128 gives the same bytes but measured about
 // twelve times slower on MI355X.)
 __device__ __forceinline__ u32x4 read_window16(const uint8_t* src, uint32_t o)
 {
+    // o is wave-uniform: a window that starts on a 16-byte boundary (a column whose
+    // output starts on one, as every column of a dealt segment does) is one aligned read
+    if (uniform(o) == 0)
+        return *reinterpret_cast<const u32x4*>(src);
     const uint32_t* const w = reinterpret_cast<const uint32_t*>(src + (o & ~3u));
     const uint32_t d0 = w[0], d1 = w[1], d2 = w[2], d3 = w[3], d4 = w[4];
     const uint32_t b = o & 3u;
