@@ -20,7 +20,9 @@
 // numbered in expert order (strip s is row s of the block-scale output).  The grid
 // is persistent, one workgroup per compute unit: each owns a 256-column tile (eight
 // MX groups, so every row it reads is one whole 128-byte line of codes) and a
-// contiguous range of strips.  Its sixteen waves have two roles, so that no wave both
+// contiguous range of strips (every parts-th strip instead when all experts are
+// multiples of 4096 rows and no strip carries into the next: strips.h, kDealRows).
+// Its sixteen waves have two roles, so that no wave both
 // loads and stores (a wave's loads and stores share one in-order completion counter,
 // and waiting for a load must not wait for older stores):
 //   producers (waves 0-3)   wave w converts rows 32w..32w+31 of every strip: lane

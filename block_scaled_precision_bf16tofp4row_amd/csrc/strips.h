@@ -12,7 +12,8 @@
 //
 // A strip is one 128-row block of one expert; the strips of all experts are numbered
 // in expert order (strip s is row s of the block-scale output).  A workgroup owns a
-// 256-column tile and a contiguous range of strips; its producer waves write each
+// 256-column tile and a contiguous range of strips (or every parts-th strip of a segment
+// whose strips are independent, kDealRows); its producer waves write each
 // strip into the ring and its consumer waves write the strip before to HBM:
 // 8 lanes per output column, lane c stores bytes [16c, 16c + 16) of the column's
 // 128-byte line, 8 columns per instruction, 32 instructions per strip.  The 8
