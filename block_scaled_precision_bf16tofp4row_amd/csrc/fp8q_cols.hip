@@ -137,10 +137,11 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     // per ring slot the strips drained by the consumer waves (all monotonic)
     __shared__ __attribute__((aligned(16))) uint32_t produced[kQProducerWaves];
     __shared__ uint32_t drained[kSlots];
-    // row layout: per ring slot, each producer wave's maximum magnitude (BF16 bits) of
-    // every strip row over its 32 columns, and per wave the strips so published
-    __shared__ __attribute__((aligned(16))) uint16_t rowmax[kRows ? kSlots : 1][kQProducerWaves][kStripRows];
-    __shared__ __attribute__((aligned(16))) uint32_t rowpub[kQProducerWaves];
+    // both layouts: per ring slot, each producer wave's maximum magnitude (BF16 bits) of
+    // each of its block's 128 columns over its 32 rows, and per wave the strips so
+    // published
+    __shared__ __attribute__((aligned(16))) uint16_t pmax[kRows ? kSlots : 1][kQProducerWaves][128];
+    __shared__ __attribute__((aligned(16))) uint32_t colpub[kQProducerWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     if (tid == 0) {
         for (int k = 0; k < kQProducerWaves; ++k) {
             produced[k] = 0;
-            rowpub[k] = 0;
+            colpub[k] = 0;
         }
         for (int k = 0; k < kSlots; ++k)
             drained[k] = 0;
@@ -172,24 +173,72 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
 
     if (wave < kQProducerWaves) {
         // ================= producers =================
-        const int c = lane & 3;
-        const int rg = lane >> 2;
-        const int row_g = 8 * rg;                 // first of the lane's eight rows
-        // the narrow last tile (128 columns) has waves 0-3 only: waves 4-7 repeat the
-        // columns of wave w - 4 (their ring columns are never written out)
-        const uint32_t wcol = ncols > 128 ? (uint32_t)wave : (uint32_t)(wave & 3);
-        const uint32_t cbyte = 64 * wcol + 16 * (uint32_t)c;
+        // Column layout only: wave w quantizes tile columns 32w..32w+31 over all 128 rows
+        // of each strip (a column's amax never leaves its wave); lane (c = lane & 3,
+        // rg = lane >> 2) holds rows 8rg..8rg+7 of columns 32w + 8c .. + 7.
+        // Both layouts: wave w = 4b + q quantizes the 128 columns of block b over rows
+        // 32q..32q+31 (a row's 128-column block never leaves its wave, so its bytes go out
+        // as one whole 128-byte line, and the column maxima are exchanged between the
+        // block's four waves); lane (c = lane & 15, rg = lane >> 4) holds rows
+        // 32q + 8rg .. + 7 of columns 128b + 8c .. + 7.
+        // The narrow last tile (128 columns) has the first four waves' columns only: the
+        // other waves load those again (their ring columns are never written out).
+        const int c = kRows ? (lane & 15) : (lane & 3);
+        const int rg = kRows ? (lane >> 4) : (lane >> 2);
+        const int blk = wave >> 2;                // both layouts: the wave's 128-column block
+        const int row_g = kRows ? 32 * (wave & 3) + 8 * rg : 8 * rg;   // first of the lane's rows
+        // first tile column of the lane's eight (in the ring) and its byte in a row of x
+        const uint32_t col0 = kRows ? (uint32_t)(128 * blk + 8 * c) : (uint32_t)(32 * wave + 8 * c);
+        const uint32_t ldcol = kRows ? (ncols > 128 ? (uint32_t)blk : 0u) * 128u + 8u * (uint32_t)c
+                                     : (ncols > 128 ? (uint32_t)wave : (uint32_t)(wave & 3)) * 32u + 8u * (uint32_t)c;
         uint32_t off[8];                          // byte offsets of the lane's rows in a strip
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            off[i] = (uint32_t)(row_g + i) * (uint32_t)(2 * K) + cbyte;
-        // tile column 32w + 8c + j sits at LDS byte lds_col(32w + 8c) + 544 j
+            off[i] = (uint32_t)(row_g + i) * (uint32_t)(2 * K) + 2 * ldcol;
+        // tile column col0 + j sits at LDS byte lds_col(col0) + 544 j
 
-        // row layout, step 1: this wave's maximum of each of the lane's eight rows over
-        // its 32 columns (the four lanes of a quad hold one row group's 32 columns),
-        // published for the other three waves of the 128-column block
-        auto publish_row_max = [&](const QRows& in, uint32_t slot) {
-            uint32_t rm[8];
+        // both layouts, column maxima: this wave's maximum of each of the lane's eight
+        // columns over its 32 rows (the four row groups of a column are lanes c, c + 16,
+        // c + 32, c + 48: the gfx950 16- and 32-lane swaps), published for the other three
+        // waves of the block; the block's four are combined once all have published
+        auto publish_col_max = [&](const QRows& in, uint32_t slot) {
+            uint32_t M[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t m = in.v[0][d] & 0x7FFF7FFFu;
+#pragma unroll
+                for (int i = 1; i < 8; ++i)
+                    m = pk_max_u16(m, in.v[i][d] & 0x7FFF7FFFu);
+                const auto a = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+                m = pk_max_u16(a[0], a[1]);
+                const auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+                M[d] = pk_max_u16(b[0], b[1]);
+            }
+            uint32_t ln = (uint32_t)lane;            // opaque, as in produce_rows
+            asm volatile("" : "+v"(ln));
+            if ((ln >> 4) == 0)
+                *reinterpret_cast<u32x4*>(&pmax[slot][wave][8 * (ln & 15)]) = u32x4{M[0], M[1], M[2], M[3]};
+        };
+        // both layouts, rows (no exchange: the row's 128-column block is the wave's): the
+        // block scale of each of the lane's rows (the sixteen lanes of a row group hold its
+        // 128 columns), its eight bytes of each row and, from lane c = 0, the scale byte.
+        // Stores go through resources over the strip's rows, empty for a lead-in strip and
+        // for the repeated columns of a narrow tile, so nothing else is written.
+        auto produce_rows = [&](const StripInfo& st, const QRows& in, uint32_t flags) {
+            // lane-dependent offsets are derived from a lane index the compiler cannot
+            // see through (the empty asm), so that it recomputes them here instead of
+            // holding them in registers of their own across the strip loop (which spills)
+            uint32_t ln = (uint32_t)lane;
+            asm volatile("" : "+v"(ln));
+            const uint32_t lc = ln & 15, lrow = 32 * (uint32_t)(wave & 3) + 8 * (ln >> 4);
+            const bool writes = (flags & 4u) == 0 && (ncols > 128 || wave < 4);
+            const int64_t r0 = st.row0 + st.r_lo;
+            const uint32_t nr = writes ? (uint32_t)st.nrows : 0u;
+            const __amdgpu_buffer_rsrc_t ry = strip_rsrc(y + r0 * K, (uint64_t)nr * (uint64_t)K);
+            const __amdgpu_buffer_rsrc_t rs = strip_rsrc(y_scales + r0 * (K / 128), (uint64_t)nr * (uint64_t)(K / 128));
+            // byte offsets of the lane's first row
+            const uint32_t vrow = lrow * (uint32_t)K + (uint32_t)(kTileCols * kt) + 128 * (uint32_t)blk + 8 * lc;
+            const uint32_t vscl = lrow * (uint32_t)(K / 128) + (uint32_t)(2 * kt) + (uint32_t)blk;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 uint32_t m = pk_max_u16(pk_max_u16(in.v[i][0] & 0x7FFF7FFFu, in.v[i][1] & 0x7FFF7FFFu),
@@ -197,46 +246,8 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                 m = max(m & 0xFFFFu, m >> 16);
                 m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
                 m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-                rm[i] = m;
-            }
-            uint32_t ln = (uint32_t)lane;            // opaque, as in produce_rows
-            asm volatile("" : "+v"(ln));
-            if ((ln & 3) == 0)
-                *reinterpret_cast<u32x4*>(&rowmax[slot][wave][8 * (ln >> 2)]) =
-                    u32x4{rm[0] | (rm[1] << 16), rm[2] | (rm[3] << 16), rm[4] | (rm[5] << 16), rm[6] | (rm[7] << 16)};
-        };
-        // row layout, step 2 (once the block's four waves have published strip t): the
-        // block scale of each of the lane's rows, its eight bytes of each row and, from
-        // the first wave of the block, the scale bytes.  Stores go through resources over
-        // the strip's rows, empty for a lead-in strip and for the repeated columns of a
-        // narrow tile, so nothing else is written.
-        auto produce_rows = [&](const StripInfo& st, const QRows& in, uint32_t slot, uint32_t flags) {
-            // lane-dependent offsets are derived from a lane index the compiler cannot
-            // see through (the empty asm), so that it recomputes them here instead of
-            // holding them in registers of their own across the strip loop (which spills)
-            uint32_t ln = (uint32_t)lane;
-            asm volatile("" : "+v"(ln));
-            const uint32_t lrow = 8 * (ln >> 2), lc = ln & 3;
-            const int wb = wave & ~3;
-            const u32x4 p0 = *reinterpret_cast<const u32x4*>(&rowmax[slot][wb + 0][lrow]);
-            const u32x4 p1 = *reinterpret_cast<const u32x4*>(&rowmax[slot][wb + 1][lrow]);
-            const u32x4 p2 = *reinterpret_cast<const u32x4*>(&rowmax[slot][wb + 2][lrow]);
-            const u32x4 p3 = *reinterpret_cast<const u32x4*>(&rowmax[slot][wb + 3][lrow]);
-            const uint32_t bm[4] = {pk_max_u16(pk_max_u16(p0.x, p1.x), pk_max_u16(p2.x, p3.x)),
-                                    pk_max_u16(pk_max_u16(p0.y, p1.y), pk_max_u16(p2.y, p3.y)),
-                                    pk_max_u16(pk_max_u16(p0.z, p1.z), pk_max_u16(p2.z, p3.z)),
-                                    pk_max_u16(pk_max_u16(p0.w, p1.w), pk_max_u16(p2.w, p3.w))};
-            const bool writes = (flags & 4u) == 0 && (ncols > 128 || wave < 4);
-            const int64_t r0 = st.row0 + st.r_lo;
-            const uint32_t nr = writes ? (uint32_t)st.nrows : 0u;
-            const __amdgpu_buffer_rsrc_t ry = strip_rsrc(y + r0 * K, (uint64_t)nr * (uint64_t)K);
-            const __amdgpu_buffer_rsrc_t rs = strip_rsrc(y_scales + r0 * (K / 128), (uint64_t)nr * (uint64_t)(K / 128));
-            // byte offsets of the lane's first row
-            const uint32_t vrow = lrow * (uint32_t)K + (uint32_t)(kTileCols * kt) + 32 * (uint32_t)wave + 8 * lc;
-            const uint32_t vscl = lrow * (uint32_t)(K / 128) + (uint32_t)(2 * kt) + (uint32_t)(wave >> 2);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t m = (bm[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x124, 0xF, 0xF, false));  // row_ror:4
+                m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x128, 0xF, 0xF, false));  // row_ror:8
                 const uint32_t S = (m >> 7) > 8 ? (m >> 7) - 8 : 0u;
                 const uint32_t clamp2 = (((S + 8) << 7) | 0x60u) * 0x00010001u;
                 const float scale = __uint_as_float(max(S << 23, 0x00400000u));   // S = 0: 2^-127
@@ -248,22 +259,39 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                 __builtin_amdgcn_raw_buffer_store_b64(
                     u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)}, ry,
                     (int)(vrow + (uint32_t)i * (uint32_t)K), 0, 0);
-                if (lc == 0 && (wave & 3) == 0)
+                if (lc == 0)
                     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)S, rs, (int)(vscl + (uint32_t)i * (uint32_t)(K / 128)), 0,
                                                          0);
             }
         };
 
         auto produce = [&](const StripInfo& st, const QRows& in, uint32_t slot, uint32_t flags) {
-            // column maxima over the strip (pairs of columns 8c + 2d, 8c + 2d + 1)
+            // column maxima over the strip (pairs of columns col0 + 2d, col0 + 2d + 1): the
+            // wave's own over all 128 rows, or (both layouts) the block's four published
+            // partial maxima
             uint32_t M[4];
+            if constexpr (kRows) {
+                const int wb = wave & ~3;
+                uint32_t ln = (uint32_t)lane;
+                asm volatile("" : "+v"(ln));
+                const uint32_t pc = 8 * (ln & 15);
+                const u32x4 p0 = *reinterpret_cast<const u32x4*>(&pmax[slot][wb + 0][pc]);
+                const u32x4 p1 = *reinterpret_cast<const u32x4*>(&pmax[slot][wb + 1][pc]);
+                const u32x4 p2 = *reinterpret_cast<const u32x4*>(&pmax[slot][wb + 2][pc]);
+                const u32x4 p3 = *reinterpret_cast<const u32x4*>(&pmax[slot][wb + 3][pc]);
+                M[0] = pk_max_u16(pk_max_u16(p0.x, p1.x), pk_max_u16(p2.x, p3.x));
+                M[1] = pk_max_u16(pk_max_u16(p0.y, p1.y), pk_max_u16(p2.y, p3.y));
+                M[2] = pk_max_u16(pk_max_u16(p0.z, p1.z), pk_max_u16(p2.z, p3.z));
+                M[3] = pk_max_u16(pk_max_u16(p0.w, p1.w), pk_max_u16(p2.w, p3.w));
+            } else {
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint32_t m = in.v[0][d] & 0x7FFF7FFFu;
+                for (int d = 0; d < 4; ++d) {
+                    uint32_t m = in.v[0][d] & 0x7FFF7FFFu;
 #pragma unroll
-                for (int i = 1; i < 8; ++i)
-                    m = pk_max_u16(m, in.v[i][d] & 0x7FFF7FFFu);
-                M[d] = rowgroup_max(m);
+                    for (int i = 1; i < 8; ++i)
+                        m = pk_max_u16(m, in.v[i][d] & 0x7FFF7FFFu);
+                    M[d] = rowgroup_max(m);
+                }
             }
             // scale bytes: biased exponent field of the column max minus 8, at least 0
             uint32_t S2[4];               // S of columns 2d (low half) and 2d + 1 (high half)
@@ -279,9 +307,12 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
             uint32_t ln = (uint32_t)lane;
             if constexpr (kRows)
                 asm volatile("" : "+v"(ln));
-            const uint32_t lrg = ln >> 2, lcc = ln & 3;
-            if (lrg == 0)
-                *reinterpret_cast<u32x2*>(&sbytes[slot][32 * wave + 8 * lcc]) =
+            const uint32_t lrg = kRows ? ln >> 4 : ln >> 2, lcc = kRows ? ln & 15 : ln & 3;
+            const uint32_t lcol0 = kRows ? 128 * (uint32_t)blk + 8 * lcc : 32 * (uint32_t)wave + 8 * lcc;
+            // the block scale bytes, once per tile column: by the lanes holding a column's
+            // first row group (both layouts: of the block's first wave)
+            if (lrg == 0 && (!kRows || (wave & 3) == 0))
+                *reinterpret_cast<u32x2*>(&sbytes[slot][lcol0]) =
                     u32x2{perm(S2[1], S2[0], 0x06040200u), perm(S2[3], S2[2], 0x06040200u)};
             if (wave == 0 && lane == 0) {
                 info[slot].A0 = K * st.row0 + st.r_lo + (int64_t)kTileCols * kt * st.mg;
@@ -292,7 +323,8 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
             }
             // quantize column by column: rows (0, 1), (2, 3), (4, 5), (6, 7) form the
             // four pairs; the two result dwords are the column's eight ring bytes
-            uint8_t* const w = tile + lds_col(32 * wave + 8 * lcc) + 8 * lrg + kStripRows * slot;
+            const uint32_t lrow = kRows ? 32 * (uint32_t)(wave & 3) + 8 * lrg : 8 * lrg;
+            uint8_t* const w = tile + lds_col(lcol0) + lrow + kStripRows * slot;
             u32x2 T[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -310,9 +342,9 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                 T[j] = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
                 *reinterpret_cast<u32x2*>(w + kColBytes * j) = T[j];
             }
-            // ring bytes 0..31 (rows 0..31 of slot 0: row groups 0-3) are repeated after
-            // the ring, so a 32-byte read window never wraps
-            if (slot == 0 && lrg < 4) {
+            // ring bytes 0..31 (rows 0..31 of slot 0) are repeated after the ring, so a
+            // 32-byte read window never wraps
+            if (slot == 0 && lrow < 32) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     *reinterpret_cast<u32x2*>(w + kRing + kColBytes * j) = T[j];
@@ -353,10 +385,11 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                     // recompute them from an opaque lane index (see produce_rows)
                     uint32_t ln = (uint32_t)lane;
                     asm volatile("" : "+v"(ln));
+                    const uint32_t lcol = (ncols > 128 ? (uint32_t)blk : 0u) * 128u + 8u * (ln & 15);
                     uint32_t offk[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        offk[i] = (8 * (ln >> 2) + (uint32_t)i) * (uint32_t)(2 * K) + 64 * wcol + 16 * (ln & 3);
+                        offk[i] = (32 * (uint32_t)(wave & 3) + 8 * (ln >> 4) + (uint32_t)i) * (uint32_t)(2 * K) + 2 * lcol;
                     R[ld] = load_rows(x, K, I[ld], kt, offk);
                 } else {
                     R[ld] = load_rows(x, K, I[ld], kt, off);
@@ -366,24 +399,21 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                     return;
                 const uint32_t fl = flags_of(prev_sb, I[u], tt == 0 && run.lead);
                 if constexpr (kRows) {
-                    // slot tt % 4 of rowmax is rewritten only in strip tt + 4, which starts
+                    // slot tt % 4 of pmax is rewritten only in strip tt + 4, which starts
                     // after the consumers drained strip tt + 1, so after every producer
-                    // finished strip tt (its row bytes included)
-                    publish_row_max(R[u], tt % kSlots);
-                    signal(&rowpub[wave]);
+                    // quantized strip tt (and read its maxima before that)
+                    publish_col_max(R[u], tt % kSlots);
+                    signal(&colpub[wave]);
+                    const int wb = wave & ~3;
+                    if (!wait_at_least(&colpub[wb], tt + 1, wc) || !wait_at_least(&colpub[wb + 1], tt + 1, wc) ||
+                        !wait_at_least(&colpub[wb + 2], tt + 1, wc) || !wait_at_least(&colpub[wb + 3], tt + 1, wc))
+                        return;
                 }
                 produce(I[u], R[u], tt % kSlots, fl);
                 prev_sb = I[u].sb;
                 signal(&produced[wave]);
-                if constexpr (kRows) {
-                    // the block's other three waves published while this one converted
-                    // the columns
-                    const int wb = wave & ~3;
-                    if (!wait_at_least(&rowpub[wb], tt + 1, wc) || !wait_at_least(&rowpub[wb + 1], tt + 1, wc) ||
-                        !wait_at_least(&rowpub[wb + 2], tt + 1, wc) || !wait_at_least(&rowpub[wb + 3], tt + 1, wc))
-                        return;
-                    produce_rows(I[u], R[u], tt % kSlots, fl);
-                }
+                if constexpr (kRows)
+                    produce_rows(I[u], R[u], fl);
                 if (tt + 1 >= n)
                     return;
             }

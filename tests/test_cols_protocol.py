@@ -17,10 +17,11 @@ shared access:
   * a producer reads the partial maxima of strip t only once all producer waves
     published them, and no wave overwrites them while another still needs them;
   * the slot's strip info (written by producer wave 0) is the strip a consumer expects;
-  * with the row layout on (fp8q_cols.hip's both-layouts mode), a producer reads the
-    per-row maxima of strip t from the other three waves of its 128-column block only
-    once they published them, and no wave overwrites its slot while a block member
-    still needs the previous strip's maxima.
+  * with the row layout on (fp8q_cols.hip's both-layouts mode, where a wave holds a
+    128-column block over 32 rows), a producer reads the partial column maxima of
+    strip t from the other three waves of its block only once they published them,
+    before converting the strip's columns, and no wave overwrites its slot while a
+    block member still needs the previous strip's maxima.
 
 Every wait is bounded in the kernels: a wave that polls a counter `polls` times in vain
 sets the device's status word and leaves.  With a poll budget the model checks that
@@ -48,8 +49,9 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, r
          polls=None):
     """PMAX None: no partial maxima.  per_wave (default: PMAX is None): one produced
     counter per producer wave, the consumers wait for the smallest.  rows: the
-    both-layouts mode (per-wave row maxima exchanged within blocks of four waves);
-    rows_wait False drops the wait for the block (the model must catch that).  polls:
+    both-layouts mode (per-wave partial column maxima exchanged within blocks of four
+    waves before the strip's columns are converted); rows_wait False drops the wait for
+    the block (the model must catch that).  polls:
     the bound of every wait (None: unbounded).  Returns (column output complete, some
     wave gave up)."""
     if per_wave is None:
@@ -116,17 +118,26 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, r
                 e = pmax[t % PMAX]
                 need(e is not None and e[0] == t and len(e[1]) == PW, f"P{w} reads pmax {e} for strip {t}")
             if rows:
-                # publish this wave's row maxima of strip t into slot t % 4
+                # publish this wave's partial column maxima of strip t into slot t % 4, then
+                # wait for the other three waves of its block and read theirs: the block's
+                # maxima are needed before the strip's columns are converted into the ring
                 old = rowmax[t % SLOTS][w]
+                blk = range(w & ~3, (w & ~3) + 4)
                 if old is not None:
-                    need(old == t - SLOTS, f"P{w} row maxima of {t} over strip {old}")
-                    blk = range(w & ~3, (w & ~3) + 4)
+                    need(old == t - SLOTS, f"P{w} maxima of {t} over strip {old}")
                     need(all(rows_done[x][old] for x in blk),
-                         f"P{w} overwrites the row maxima of strip {old} while its block still needs them")
+                         f"P{w} overwrites the maxima of strip {old} while its block still needs them")
                 rowmax[t % SLOTS][w] = t
                 yield None
                 cnt[f"rowpub{w}"] += 1
                 yield None
+                if rows_wait:
+                    if not (yield from wait(f"P{w}", lambda: min(cnt[f"rowpub{x}"] for x in blk) >= t + 1)):
+                        return
+                for x in blk:
+                    need(rowmax[t % SLOTS][x] == t, f"P{w} reads maxima {rowmax[t % SLOTS][x]} of P{x} for strip {t}")
+                    yield None
+                rows_done[w][t] = True
             s = t % SLOTS
             if w == 0:
                 info[s] = t
@@ -144,15 +155,6 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, r
             yield None
             cnt["produced"] += 1
             cnt[f"produced{w}"] += 1
-            if rows:
-                blk = range(w & ~3, (w & ~3) + 4)
-                if rows_wait:
-                    if not (yield from wait(f"P{w}", lambda: min(cnt[f"rowpub{x}"] for x in blk) >= t + 1)):
-                        return
-                for x in blk:
-                    need(rowmax[s][x] == t, f"P{w} reads row maxima {rowmax[s][x]} of P{x} for strip {t}")
-                    yield None
-                rows_done[w][t] = True
             if t + 1 >= n:
                 return
             if PMAX:
@@ -224,7 +226,7 @@ def test_protocol_both_layouts_random_schedules(n):
 
 def test_model_catches_a_missing_row_block_wait():
     """Without the wait for the block's other waves, some schedule reads another wave's
-    row maxima before that wave published the strip."""
+    partial column maxima before that wave published the strip."""
     caught = 0
     for seed in range(40):
         try:
