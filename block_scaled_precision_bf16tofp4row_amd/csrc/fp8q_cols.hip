@@ -13,15 +13,19 @@
 // consumer machinery are those of strips.h (same layout as the MXFP4 -> FP8 column
 // conversion).
 //
-// Producers (waves 0-7): wave w quantizes tile columns 32w..32w+31 over all 128 rows
-// of every strip, so a column's amax never leaves its wave.  Lane (c = lane & 3,
-// rg = lane >> 2) holds rows 8rg..8rg+7 of columns 32w + 8c .. + 7 (one 16-byte chunk
-// per row; the lanes of a load instruction read 16 rows x 64 bytes).  Loads run
-// kQPrefetch strips ahead.  The column amax is reduced over the lane's eight rows
-// (packed 16-bit max on the magnitude bits) and over the sixteen row groups (two DPP
-// row rotations, then the gfx950 16- and 32-lane swaps); no cross-wave step (in the
-// column-only mode), so each producer wave runs its strips on its own and only the
-// consumers wait for all of them.
+// Producers (waves 0-7): wave w = 4b + q quantizes the 128 columns of block b (tile
+// columns 128b .. 128b + 127) over rows 32q..32q+31 of every strip.  Lane (c = lane & 15,
+// rg = lane >> 4) holds rows 32q + 8rg .. + 7 of columns 128b + 8c .. + 7 (one 16-byte
+// chunk per row; the lanes of a load instruction read 4 rows x 256 bytes).  Loads run
+// kQPrefetch strips ahead.  A column's amax is reduced over the lane's eight rows
+// (packed 16-bit max on the magnitude bits) and the wave's four row groups (the gfx950
+// 16- and 32-lane swaps), published to a per-slot LDS array, and combined with the
+// other three waves of the block once they have published theirs (bounded waits on
+// per-wave counters); the two blocks run independently, so the consumers wait for every
+// producer wave's own counter.  (A layout in which each wave held 32 columns over all
+// 128 rows needs no exchange, but its load instructions read 16 rows x 64 bytes: 1.5-2.4 %
+// slower for the column layout alone, and 10-14 % slower with the row layout below,
+// whose rows it splits over four waves.)
 // The element convert, v_cvt_scalef32_pk_fp8_bf16, takes one scale for a pair of
 // BF16, and neighbouring columns have different scales, so a pair is two rows of one
 // column (one v_perm_b32): the four converts of a column's eight rows give its eight
@@ -32,21 +36,19 @@
 //
 // With kRows the kernel also writes the row layout of the same gradient (DGRAD operand,
 // 1x128 blocks along K, the row quantizer's output) from the same read.  A row's
-// 128-column block spans four producer waves, so this mode adds the one cross-wave
-// step: each wave publishes its per-row maxima over its 32 columns to a per-slot LDS
-// array before converting the columns, and afterwards waits (bounded, on per-wave
-// counters) for the block's other three waves, takes each row's block maximum and
-// stores its eight bytes of each row and the scale bytes through resources over the
-// strip's rows.  Loop-invariant offsets are then recomputed from an opaque lane index
-// each strip, because holding them spills, and a spill reload in the loop would wait
-// for the prefetched strip.
+// 128-column block is one wave's, so its maximum needs no exchange (the sixteen lanes of
+// a row group, two DPP quad permutes and two row rotations) and its 128 FP8 bytes go out
+// as one whole line; the wave stores its rows and the scale bytes through resources over
+// the strip's rows.  Loop-invariant offsets are then recomputed from an opaque lane
+// index each strip, because holding them spills, and a spill reload in the loop would
+// wait for the prefetched strip.
 #include "strips.h"
 
 namespace mxfp4 {
 
 typedef __bf16 qbf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kQProducerWaves = 8;                          // 32 columns each
+constexpr int kQProducerWaves = 8;                          // 128 columns x 32 rows each
 constexpr int kQConsumerWaves = 8;
 constexpr int kQPrefetch = 1;                               // strips of loads in flight
 constexpr int kQThreads = 64 * (kQProducerWaves + kQConsumerWaves);
@@ -56,8 +58,8 @@ static_assert((kRing & (kRing - 1)) == 0, "the ring position wraps with a mask")
 
 namespace {
 
-// A lane's eight rows of a strip: v[i] holds 8 BF16 (columns 32w + 8c .. + 7) of row
-// 8rg + i.
+// A lane's eight rows of a strip: v[i] holds 8 BF16 (columns 128b + 8c .. + 7) of row
+// 32q + 8rg + i.
 struct QRows {
     u32x4 v[8];
 };
@@ -82,20 +84,6 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
 {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
                                                                   __builtin_bit_cast(u16x2, b)));
-}
-
-// Packed 16-bit max over the lanes that share lane & 3 (the sixteen row groups): DPP
-// row rotations by 4 and 8 inside each 16-lane row, then the gfx950 swaps of 16-lane
-// rows and 32-lane halves (the max of both swap outputs holds the partner's value
-// whichever way the swap pairs the lanes).
-__device__ __forceinline__ uint32_t rowgroup_max(uint32_t m)
-{
-    m = pk_max_u16(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x124, 0xF, 0xF, false));   // row_ror:4
-    m = pk_max_u16(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x128, 0xF, 0xF, false));   // row_ror:8
-    const auto a = __builtin_amdgcn_permlane16_swap(m, m, false, false);
-    m = pk_max_u16(a[0], a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
-    return pk_max_u16(b[0], b[1]);
 }
 
 __device__ __forceinline__ qbf16x2 as_qbf16x2(uint32_t u)
@@ -137,10 +125,9 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
     // per ring slot the strips drained by the consumer waves (all monotonic)
     __shared__ __attribute__((aligned(16))) uint32_t produced[kQProducerWaves];
     __shared__ uint32_t drained[kSlots];
-    // both layouts: per ring slot, each producer wave's maximum magnitude (BF16 bits) of
-    // each of its block's 128 columns over its 32 rows, and per wave the strips so
-    // published
-    __shared__ __attribute__((aligned(16))) uint16_t pmax[kRows ? kSlots : 1][kQProducerWaves][128];
+    // per ring slot, each producer wave's maximum magnitude (BF16 bits) of each of its
+    // block's 128 columns over its 32 rows, and per wave the strips so published
+    __shared__ __attribute__((aligned(16))) uint16_t pmax[kSlots][kQProducerWaves][128];
     __shared__ __attribute__((aligned(16))) uint32_t colpub[kQProducerWaves];
 
     const int tid = threadIdx.x;
@@ -173,31 +160,23 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
 
     if (wave < kQProducerWaves) {
         // ================= producers =================
-        // Column layout only: wave w quantizes tile columns 32w..32w+31 over all 128 rows
-        // of each strip (a column's amax never leaves its wave); lane (c = lane & 3,
-        // rg = lane >> 2) holds rows 8rg..8rg+7 of columns 32w + 8c .. + 7.
-        // Both layouts: wave w = 4b + q quantizes the 128 columns of block b over rows
-        // 32q..32q+31 (a row's 128-column block never leaves its wave, so its bytes go out
-        // as one whole 128-byte line, and the column maxima are exchanged between the
-        // block's four waves); lane (c = lane & 15, rg = lane >> 4) holds rows
-        // 32q + 8rg .. + 7 of columns 128b + 8c .. + 7.
-        // The narrow last tile (128 columns) has the first four waves' columns only: the
-        // other waves load those again (their ring columns are never written out).
-        const int c = kRows ? (lane & 15) : (lane & 3);
-        const int rg = kRows ? (lane >> 4) : (lane >> 2);
-        const int blk = wave >> 2;                // both layouts: the wave's 128-column block
-        const int row_g = kRows ? 32 * (wave & 3) + 8 * rg : 8 * rg;   // first of the lane's rows
-        // first tile column of the lane's eight (in the ring) and its byte in a row of x
-        const uint32_t col0 = kRows ? (uint32_t)(128 * blk + 8 * c) : (uint32_t)(32 * wave + 8 * c);
-        const uint32_t ldcol = kRows ? (ncols > 128 ? (uint32_t)blk : 0u) * 128u + 8u * (uint32_t)c
-                                     : (ncols > 128 ? (uint32_t)wave : (uint32_t)(wave & 3)) * 32u + 8u * (uint32_t)c;
+        // wave w = 4b + q quantizes the 128 columns of block b over rows 32q..32q+31; lane
+        // (c = lane & 15, rg = lane >> 4) holds rows 32q + 8rg .. + 7 of columns
+        // 128b + 8c .. + 7.  The narrow last tile (128 columns) has block 0 only: waves 4-7
+        // load its columns again (their ring columns are never written out).
+        const int c = lane & 15;
+        const int rg = lane >> 4;
+        const int blk = wave >> 2;                // the wave's 128-column block
+        const int row_g = 32 * (wave & 3) + 8 * rg;   // first of the lane's eight rows
+        // first tile column of the lane's eight in a row of x
+                const uint32_t ldcol = (ncols > 128 ? (uint32_t)blk : 0u) * 128u + 8u * (uint32_t)c;
         uint32_t off[8];                          // byte offsets of the lane's rows in a strip
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             off[i] = (uint32_t)(row_g + i) * (uint32_t)(2 * K) + 2 * ldcol;
-        // tile column col0 + j sits at LDS byte lds_col(col0) + 544 j
+        // tile column 128b + 8c + j sits at LDS byte lds_col(128b + 8c) + 544 j
 
-        // both layouts, column maxima: this wave's maximum of each of the lane's eight
+        // column maxima: this wave's maximum of each of the lane's eight
         // columns over its 32 rows (the four row groups of a column are lanes c, c + 16,
         // c + 32, c + 48: the gfx950 16- and 32-lane swaps), published for the other three
         // waves of the block; the block's four are combined once all have published
@@ -219,7 +198,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
             if ((ln >> 4) == 0)
                 *reinterpret_cast<u32x4*>(&pmax[slot][wave][8 * (ln & 15)]) = u32x4{M[0], M[1], M[2], M[3]};
         };
-        // both layouts, rows (no exchange: the row's 128-column block is the wave's): the
+        // row layout (no exchange: the row's 128-column block is the wave's): the
         // block scale of each of the lane's rows (the sixteen lanes of a row group hold its
         // 128 columns), its eight bytes of each row and, from lane c = 0, the scale byte.
         // Stores go through resources over the strip's rows, empty for a lead-in strip and
@@ -266,11 +245,10 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
         };
 
         auto produce = [&](const StripInfo& st, const QRows& in, uint32_t slot, uint32_t flags) {
-            // column maxima over the strip (pairs of columns col0 + 2d, col0 + 2d + 1): the
-            // wave's own over all 128 rows, or (both layouts) the block's four published
-            // partial maxima
+            // column maxima over the strip (pairs of columns 128b + 8c + 2d and + 1): the
+            // block's four published partial maxima
             uint32_t M[4];
-            if constexpr (kRows) {
+            {
                 const int wb = wave & ~3;
                 uint32_t ln = (uint32_t)lane;
                 asm volatile("" : "+v"(ln));
@@ -283,15 +261,6 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                 M[1] = pk_max_u16(pk_max_u16(p0.y, p1.y), pk_max_u16(p2.y, p3.y));
                 M[2] = pk_max_u16(pk_max_u16(p0.z, p1.z), pk_max_u16(p2.z, p3.z));
                 M[3] = pk_max_u16(pk_max_u16(p0.w, p1.w), pk_max_u16(p2.w, p3.w));
-            } else {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    uint32_t m = in.v[0][d] & 0x7FFF7FFFu;
-#pragma unroll
-                    for (int i = 1; i < 8; ++i)
-                        m = pk_max_u16(m, in.v[i][d] & 0x7FFF7FFFu);
-                    M[d] = rowgroup_max(m);
-                }
             }
             // scale bytes: biased exponent field of the column max minus 8, at least 0
             uint32_t S2[4];               // S of columns 2d (low half) and 2d + 1 (high half)
@@ -307,11 +276,11 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
             uint32_t ln = (uint32_t)lane;
             if constexpr (kRows)
                 asm volatile("" : "+v"(ln));
-            const uint32_t lrg = kRows ? ln >> 4 : ln >> 2, lcc = kRows ? ln & 15 : ln & 3;
-            const uint32_t lcol0 = kRows ? 128 * (uint32_t)blk + 8 * lcc : 32 * (uint32_t)wave + 8 * lcc;
+            const uint32_t lrg = ln >> 4, lcc = ln & 15;
+            const uint32_t lcol0 = 128 * (uint32_t)blk + 8 * lcc;
             // the block scale bytes, once per tile column: by the lanes holding a column's
-            // first row group (both layouts: of the block's first wave)
-            if (lrg == 0 && (!kRows || (wave & 3) == 0))
+            // first row group in the block's first wave
+            if (lrg == 0 && (wave & 3) == 0)
                 *reinterpret_cast<u32x2*>(&sbytes[slot][lcol0]) =
                     u32x2{perm(S2[1], S2[0], 0x06040200u), perm(S2[3], S2[2], 0x06040200u)};
             if (wave == 0 && lane == 0) {
@@ -323,7 +292,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
             }
             // quantize column by column: rows (0, 1), (2, 3), (4, 5), (6, 7) form the
             // four pairs; the two result dwords are the column's eight ring bytes
-            const uint32_t lrow = kRows ? 32 * (uint32_t)(wave & 3) + 8 * lrg : 8 * lrg;
+            const uint32_t lrow = 32 * (uint32_t)(wave & 3) + 8 * lrg;
             uint8_t* const w = tile + lds_col(lcol0) + lrow + kStripRows * slot;
             u32x2 T[8];
 #pragma unroll
@@ -398,17 +367,15 @@ __global__ __launch_bounds__(kQThreads, 1) void fp8q_cols_kernel(
                                               kQConsumerWaves * ((tt - 3) / kSlots + 1), wc))
                     return;
                 const uint32_t fl = flags_of(prev_sb, I[u], tt == 0 && run.lead);
-                if constexpr (kRows) {
-                    // slot tt % 4 of pmax is rewritten only in strip tt + 4, which starts
-                    // after the consumers drained strip tt + 1, so after every producer
-                    // quantized strip tt (and read its maxima before that)
-                    publish_col_max(R[u], tt % kSlots);
-                    signal(&colpub[wave]);
-                    const int wb = wave & ~3;
-                    if (!wait_at_least(&colpub[wb], tt + 1, wc) || !wait_at_least(&colpub[wb + 1], tt + 1, wc) ||
-                        !wait_at_least(&colpub[wb + 2], tt + 1, wc) || !wait_at_least(&colpub[wb + 3], tt + 1, wc))
-                        return;
-                }
+                // slot tt % 4 of pmax is rewritten only in strip tt + 4, which starts after
+                // the consumers drained strip tt + 1, so after every producer quantized
+                // strip tt (and read its maxima before that)
+                publish_col_max(R[u], tt % kSlots);
+                signal(&colpub[wave]);
+                const int wb = wave & ~3;
+                if (!wait_at_least(&colpub[wb], tt + 1, wc) || !wait_at_least(&colpub[wb + 1], tt + 1, wc) ||
+                    !wait_at_least(&colpub[wb + 2], tt + 1, wc) || !wait_at_least(&colpub[wb + 3], tt + 1, wc))
+                    return;
                 produce(I[u], R[u], tt % kSlots, fl);
                 prev_sb = I[u].sb;
                 signal(&produced[wave]);

@@ -1,9 +1,10 @@
 """CPU model of the column kernels' LDS progress-counter protocol.
 
 The column kernels (csrc/cols.hip: 4 producer and 12 consumer waves that also exchange
-partial block-scale maxima; csrc/fp8q_cols.hip: 8 producer and 8 consumer waves, each
-producer wave owning whole columns, so no partial maxima, and one `produced` counter per
-producer wave) split each workgroup into producer and consumer waves that share a
+partial block-scale maxima; csrc/fp8q_cols.hip: 8 producer and 8 consumer waves, the
+producer waves in two blocks of four that exchange partial column maxima within the
+block, and one `produced` counter per producer wave) split each workgroup into producer
+and consumer waves that share a
 four-slot LDS ring and synchronise only through monotonic counters: `published`
 (partial block-scale maxima), `produced` (strips converted) and `drained[slot]`
 (strips written out).  This model replays the kernel's waits, with the
@@ -17,11 +18,11 @@ shared access:
   * a producer reads the partial maxima of strip t only once all producer waves
     published them, and no wave overwrites them while another still needs them;
   * the slot's strip info (written by producer wave 0) is the strip a consumer expects;
-  * with the row layout on (fp8q_cols.hip's both-layouts mode, where a wave holds a
-    128-column block over 32 rows), a producer reads the partial column maxima of
-    strip t from the other three waves of its block only once they published them,
-    before converting the strip's columns, and no wave overwrites its slot while a
-    block member still needs the previous strip's maxima.
+  * with the block exchange (fp8q_cols.hip, where a wave holds a 128-column block over
+    32 rows), a producer reads the partial column maxima of strip t from the other three
+    waves of its block only once they published them, before converting the strip's
+    columns, and no wave overwrites its slot while a block member still needs the
+    previous strip's maxima.
 
 Every wait is bounded in the kernels: a wave that polls a counter `polls` times in vain
 sets the device's status word and leaves.  With a poll budget the model checks that
@@ -37,21 +38,22 @@ import random
 import pytest
 
 SLOTS = 4
-# (producer waves, consumer waves, partial-maximum slots or None) of the kernels
-CONFIGS = [(4, 12, 4), (8, 8, None)]
+# (producer waves, consumer waves, partial-maximum slots or None, block exchange) of the
+# kernels: cols.hip, and fp8q_cols.hip (both instances)
+CONFIGS = [(4, 12, 4, False), (8, 8, None, True)]
 
 
 class Violation(AssertionError):
     pass
 
 
-def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, rows=False, rows_wait=True,
+def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, blocks=False, blocks_wait=True,
          polls=None):
     """PMAX None: no partial maxima.  per_wave (default: PMAX is None): one produced
-    counter per producer wave, the consumers wait for the smallest.  rows: the
-    both-layouts mode (per-wave partial column maxima exchanged within blocks of four
-    waves before the strip's columns are converted); rows_wait False drops the wait for
-    the block (the model must catch that).  polls:
+    counter per producer wave, the consumers wait for the smallest.  blocks: the
+    backward quantizer's exchange (per-wave partial column maxima exchanged within blocks
+    of four waves before the strip's columns are converted); blocks_wait False drops the
+    wait for the block (the model must catch that).  polls:
     the bound of every wait (None: unbounded).  Returns (column output complete, some
     wave gave up)."""
     if per_wave is None:
@@ -67,10 +69,10 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, r
     info = [None] * SLOTS          # slot -> strip
     done_prod = [[False] * n for _ in range(PW)]       # producer w finished produce(t)
     done_cons = [[False] * n for _ in range(CW)]       # consumer v finished strip t
-    rowmax = [[None] * PW for _ in range(SLOTS)]       # slot -> wave -> strip published there
-    rows_done = [[False] * n for _ in range(PW)]       # producer w finished its rows of strip t
+    cmax = [[None] * PW for _ in range(SLOTS)]         # slot -> wave -> strip published there
+    read_done = [[False] * n for _ in range(PW)]       # producer w read its block's maxima of strip t
     for w in range(PW):
-        cnt[f"rowpub{w}"] = 0
+        cnt[f"colpub{w}"] = 0
 
     def need(cond, msg):
         if not cond:
@@ -117,27 +119,27 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, r
                     return
                 e = pmax[t % PMAX]
                 need(e is not None and e[0] == t and len(e[1]) == PW, f"P{w} reads pmax {e} for strip {t}")
-            if rows:
+            if blocks:
                 # publish this wave's partial column maxima of strip t into slot t % 4, then
                 # wait for the other three waves of its block and read theirs: the block's
                 # maxima are needed before the strip's columns are converted into the ring
-                old = rowmax[t % SLOTS][w]
+                old = cmax[t % SLOTS][w]
                 blk = range(w & ~3, (w & ~3) + 4)
                 if old is not None:
                     need(old == t - SLOTS, f"P{w} maxima of {t} over strip {old}")
-                    need(all(rows_done[x][old] for x in blk),
+                    need(all(read_done[x][old] for x in blk),
                          f"P{w} overwrites the maxima of strip {old} while its block still needs them")
-                rowmax[t % SLOTS][w] = t
+                cmax[t % SLOTS][w] = t
                 yield None
-                cnt[f"rowpub{w}"] += 1
+                cnt[f"colpub{w}"] += 1
                 yield None
-                if rows_wait:
-                    if not (yield from wait(f"P{w}", lambda: min(cnt[f"rowpub{x}"] for x in blk) >= t + 1)):
+                if blocks_wait:
+                    if not (yield from wait(f"P{w}", lambda: min(cnt[f"colpub{x}"] for x in blk) >= t + 1)):
                         return
                 for x in blk:
-                    need(rowmax[t % SLOTS][x] == t, f"P{w} reads maxima {rowmax[t % SLOTS][x]} of P{x} for strip {t}")
+                    need(cmax[t % SLOTS][x] == t, f"P{w} reads maxima {cmax[t % SLOTS][x]} of P{x} for strip {t}")
                     yield None
-                rows_done[w][t] = True
+                read_done[w][t] = True
             s = t % SLOTS
             if w == 0:
                 info[s] = t
@@ -212,16 +214,16 @@ def _run(n, seed, carry=True, drain_lag=3, PW=4, CW=12, PMAX=4, per_wave=None, r
 @pytest.mark.parametrize("cfg", CONFIGS)
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 9, 13])
 def test_protocol_random_schedules(n, cfg):
-    pw, cw, pm = cfg
+    pw, cw, pm, bl = cfg
     for seed in range(60 if cfg == CONFIGS[0] else 30):
-        _run(n, seed, PW=pw, CW=cw, PMAX=pm)
+        _run(n, seed, PW=pw, CW=cw, PMAX=pm, blocks=bl)
 
 
 @pytest.mark.parametrize("n", [1, 2, 4, 5, 9, 13])
 def test_protocol_both_layouts_random_schedules(n):
-    """fp8q_cols.hip with the row layout on: 8 producer waves in two blocks of four."""
+    """fp8q_cols.hip: 8 producer waves in two blocks of four (more schedules)."""
     for seed in range(30):
-        _run(n, seed, PW=8, CW=8, PMAX=None, rows=True)
+        _run(n, seed, PW=8, CW=8, PMAX=None, blocks=True)
 
 
 def test_model_catches_a_missing_row_block_wait():
@@ -230,7 +232,7 @@ def test_model_catches_a_missing_row_block_wait():
     caught = 0
     for seed in range(40):
         try:
-            _run(6, seed, PW=8, CW=8, PMAX=None, rows=True, rows_wait=False)
+            _run(6, seed, PW=8, CW=8, PMAX=None, blocks=True, blocks_wait=False)
         except Violation:
             caught += 1
     assert caught > 0
@@ -252,12 +254,26 @@ def test_model_catches_a_weaker_wait():
 
 
 def test_model_catches_a_summed_produced_counter_without_lockstep():
-    """Without the partial-maximum exchange, producer waves drift apart, so a single
-    summed `produced` counter no longer shows that every wave wrote strip t."""
+    """Without a lockstep exchange over all producer waves (fp8q_cols.hip's two blocks
+    exchange only within themselves; here none at all), producer waves drift apart, so a
+    single summed `produced` counter no longer shows that every wave wrote strip t."""
     caught = False
     for seed in range(300):
         try:
             _run(9, seed, PW=8, CW=8, PMAX=None, per_wave=False)
+        except Violation:
+            caught = True
+            break
+    assert caught
+
+
+def test_model_catches_a_summed_produced_counter_across_two_blocks():
+    """fp8q_cols.hip's two blocks of four producer waves exchange maxima only within the
+    block, so the blocks drift apart and the consumers need one counter per wave."""
+    caught = False
+    for seed in range(300):
+        try:
+            _run(9, seed, PW=8, CW=8, PMAX=None, per_wave=False, blocks=True)
         except Violation:
             caught = True
             break
@@ -283,7 +299,8 @@ def test_give_up_leaves_every_wave_and_is_reported(cfg):
     still leaves (the scheduler would flag a deadlock), the accesses made before they
     leave stay in order (the model's checks hold), and every run whose column output
     is incomplete has a wave that gave up, so the status word reports it."""
-    kw = dict(PW=8, CW=8, PMAX=None, rows=True) if cfg == "both" else dict(PW=cfg[0], CW=cfg[1], PMAX=cfg[2])
+    kw = dict(PW=8, CW=8, PMAX=None, blocks=True) if cfg == "both" else dict(PW=cfg[0], CW=cfg[1], PMAX=cfg[2],
+                                                                               blocks=cfg[3])
     outcomes = set()
     for polls in (1, 2, 3, 8, 40, 400):
         for seed in range(20):
