@@ -57,3 +57,26 @@ def test_traffic_summary_is_read_only_for_matching_sources(tmp_path, monkeypatch
     (tmp_path / "hbm_traffic_config5.md").write_text("<!-- traffic-json " + json.dumps(
         {"rows/hidden": dict(data["rows/hidden"], source_sha=bench.source_hash("rows"))}) + " -->")
     assert bench.read_traffic("rows", "config5", "hidden") == data["rows/hidden"]["bytes_per_launch"]
+
+
+def test_strip_table_covers_every_row_once_in_the_transposed_layout():
+    """The memory-only ceiling kernel's strips: every routed row in exactly one strip, in
+    expert order, each strip 1..128 rows of one expert, and its output byte is where the
+    transposed layout puts (column 0, the strip's first row): K * offs[g] + the row's
+    index within the expert."""
+    import numpy as np
+    K = 384
+    counts = [0, 1, 127, 128, 129, 0, 300, 5]
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    t = bench.strip_table(offs, K)
+    assert t.shape == (sum((c + 127) // 128 for c in counts), 4)
+    seen = np.zeros(offs[-1], np.int64)
+    for row, n, a0, mg in t:
+        assert 1 <= n <= 128
+        g = int(np.searchsorted(offs, row, side="right")) - 1
+        assert mg == offs[g + 1] - offs[g] and row + n <= offs[g + 1]
+        assert a0 == K * offs[g] + (row - offs[g])
+        seen[row:row + n] += 1
+    assert (seen == 1).all()
+    assert list(t[:, 0]) == sorted(t[:, 0])
+    assert bench.strip_table(np.zeros(4, np.int32), K).shape == (0, 4)
