@@ -1,7 +1,8 @@
 """The measurement hook mxfp4_time_next_launch on the GPU: HIP events armed for the next
 call are bound to its kernels (the first and the last of the call), so they time the
 kernels' own execution; the call's output is byte-identical to an unarmed call; the
-events are used once (a second call leaves them as the first one recorded them)."""
+events are used once (a second call leaves them as the first one recorded them).  Also
+the benchmark's memory-only column traffic kernel stays inside the buffers it is given."""
 from __future__ import annotations
 
 import ctypes
@@ -119,3 +120,42 @@ def test_three_kernel_call_is_timed_first_to_last(hip):
     assert 0.0 < one < 1e6 and 0.0 < whole < 1e6
     assert whole > one
     hip.destroy(a, b, c_, d_)
+
+
+@pytest.mark.parametrize("sequential", [False, True])
+@pytest.mark.parametrize("kind", ["codes", "bf16"])
+def test_cols_traffic_ceiling_stays_in_its_buffers(kind, sequential):
+    """The benchmark's memory-only column traffic (libmxfp4bench bench_cols_traffic)
+    writes nothing outside the output and block-scale ranges it is given, and leaves its
+    inputs unchanged: canaries on both sides of every buffer, on a ragged case with a
+    narrow last tile and a partial last strip."""
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    traffic = bench.ColsTraffic()
+    K = 640
+    counts = [0, 300, 129, 5]
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offs[-1])
+    strips = torch.from_numpy(bench.strip_table(offs, K)).cuda()
+    n = strips.shape[0]
+    pad = 4096
+    if kind == "codes":
+        inp = torch.randint(0, 255, (M, K // 2), dtype=torch.uint8, device="cuda")
+        sc = torch.randint(0, 255, (M, K // 32), dtype=torch.uint8, device="cuda")
+        tib = 128
+    else:
+        inp = torch.randint(-2000, 2000, (M, K), dtype=torch.int16, device="cuda")
+        sc = None
+        tib = 512
+    inp0 = inp.clone()
+    sc0 = sc.clone() if sc is not None else None
+    out_bytes = (((K + 255) // 256) * n * 256 * 128) if sequential else M * K
+    big = torch.full((out_bytes + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    out = big[pad:pad + out_bytes]
+    sbig = torch.full((n * K + 2 * pad,), 0x5A, dtype=torch.uint8, device="cuda")
+    out_scales = sbig[pad:pad + n * K]
+    traffic(torch, inp, tib, sc, out, out_scales, strips, K, sequential)
+    torch.cuda.synchronize()
+    assert bool((big[:pad] == 0xA5).all()) and bool((big[pad + out_bytes:] == 0xA5).all())
+    assert bool((sbig[:pad] == 0x5A).all()) and bool((sbig[pad + n * K:] == 0x5A).all())
+    assert torch.equal(inp, inp0) and (sc is None or torch.equal(sc, sc0))
