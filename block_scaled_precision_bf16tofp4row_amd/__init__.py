@@ -88,6 +88,15 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m block_scaled_precision_bf16tofp4row_amd.build`")
+    # The library and PyTorch both ask for the HIP runtime by the same soname
+    # (libamdhip64.so.7), and the first one loaded serves the whole process.  PyTorch
+    # ships its own build of it, and the device memory and streams handed to the
+    # library come from PyTorch, so PyTorch is loaded first: loaded the other way
+    # round, ROCm's system runtime would serve both and the library's calls fail.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     st = ctypes.c_int

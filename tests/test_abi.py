@@ -336,3 +336,23 @@ def test_timing_hook_is_host_only(lib):
     # without a device (the events themselves are used by the next launch)
     assert lib.mxfp4_time_next_launch(None, None) == mx.MXFP4_OK
     mx.mxfp4_time_next_launch(None, None)
+
+
+def test_library_binds_the_hip_runtime_torch_loads():
+    """Loading the library before anything imports torch must still leave one HIP
+    runtime in the process, torch's own copy: both ask for it by the same soname, and
+    the first copy loaded serves every later request."""
+    import subprocess
+    import sys
+    code = (
+        "import sys\n"
+        "import block_scaled_precision_bf16tofp4row_amd as mx\n"
+        "assert 'torch' not in sys.modules\n"
+        "mx.load_library()\n"
+        "import torch, os\n"
+        "maps = open('/proc/self/maps').read().split()\n"
+        "hip = sorted({os.path.realpath(p) for p in maps if '/libamdhip64.so' in p})\n"
+        "want = os.path.realpath(os.path.join(os.path.dirname(torch.__file__), 'lib'))\n"
+        "assert len(hip) == 1 and hip[0].startswith(want + os.sep), hip\n"
+    )
+    subprocess.run([sys.executable, "-c", code], cwd=ROOT, check=True, timeout=300)
